@@ -1,0 +1,28 @@
+"""fp64 CPU oracle of the hybrid-window GQA decode attention block.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the library or its binding.
+It shares no code with the HIP path.  See ``oracle/block.py`` for the
+definitions, their sources on the pages, and the readings taken where the pages
+are silent.
+"""
+from .block import (  # noqa: F401
+    BlockResult,
+    OracleSeq,
+    StackResult,
+    attention_decode,
+    bf16_bits_to_f64,
+    block_decode,
+    gemv,
+    head_gate,
+    kv_slot,
+    kv_window,
+    physical_rows,
+    rms_norm,
+    rope_neox,
+    rope_params_for,
+    sigmoid,
+    split_qkv,
+    stack_decode,
+    to_fp16,
+)
