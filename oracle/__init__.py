@@ -7,10 +7,12 @@ definitions, their sources on the pages, and the readings taken where the pages
 are silent.
 """
 from .block import (  # noqa: F401
+    AttentionStepResult,
     BlockResult,
     OracleSeq,
     StackResult,
     attention_decode,
+    attention_step,
     bf16_bits_to_f64,
     block_decode,
     gemv,

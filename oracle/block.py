@@ -195,9 +195,7 @@ class OracleSeq:
 
 
 @dataclass
-class BlockResult:
-    qkv: np.ndarray          # [B][qkv_rows]
-    gate_logits: np.ndarray  # [B][Hq]
+class AttentionStepResult:
     q_roped: np.ndarray      # [B][Hq][D]
     k16: np.ndarray          # [B][Hk][D] float16: the row written to the slot
     v16: np.ndarray          # [B][Hk][D] float16
@@ -205,27 +203,32 @@ class BlockResult:
     windows: List[Tuple[int, int, int]]
     attn: np.ndarray         # [B][Hq][D] before the gate
     gated: np.ndarray        # [B][Hq*D]
-    out: np.ndarray          # [B][hidden]
     k_caches: List[np.ndarray]
     v_caches: List[np.ndarray]
 
 
-def block_decode(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
-                 x: np.ndarray, seqs: Sequence) -> BlockResult:
-    """One decode step of the attention block for B independent sequences.
+@dataclass
+class BlockResult(AttentionStepResult):
+    qkv: np.ndarray = None          # [B][qkv_rows]
+    gate_logits: np.ndarray = None  # [B][Hq]
+    out: np.ndarray = None          # [B][hidden]
 
-    ``arch`` exposes num_heads, num_kv_heads, head_dim, full_rotary_dim,
-    sliding_window, full_rope_theta, rope_theta and attention_scale; each
-    element of ``seqs`` exposes k, v (fp16 caches), ring_capacity and position.
-    Caches are copied; the returned copies hold this token's rows.
+
+def attention_step(arch, is_full: bool, qkv: np.ndarray, gate_logits: np.ndarray,
+                   seqs: Sequence) -> AttentionStepResult:
+    """Everything between the projections and o_proj, per sequence b:
+
+    split qkv[b] [attn: THE SPLIT]; RoPE q and k with the layer class's
+    (rotary_dim, theta) [attn: per-class RoPE step] -- v is not rotated;
+    write fp16 k and v into the slot of this position [attn: k and v land in
+    their cache slots; kvw: `kv_write_target`]; attend over the window
+    [attn: window step, `encode_attention_any`]; apply the headwise gate
+    [attn: gate step].  Each element of ``seqs`` exposes k, v (fp16 caches),
+    ring_capacity and position; caches are copied and the copies updated.
     """
     hq, hk, d = arch.num_heads, arch.num_kv_heads, arch.head_dim
-    w_qkv = bf16_bits_to_f64(w_qkv_bits)
-    w_g = bf16_bits_to_f64(w_g_bits)
-    w_o = bf16_bits_to_f64(w_o_bits)
-    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
-    qkv = gemv(w_qkv, x)
-    gl = gemv(w_g, x)
+    qkv = np.atleast_2d(np.asarray(qkv, dtype=np.float64))
+    gl = np.atleast_2d(np.asarray(gate_logits, dtype=np.float64))
     rotary_dim, theta = rope_params_for(is_full, arch.full_rotary_dim, d,
                                         arch.full_rope_theta, arch.rope_theta)
     res = dict(q_roped=[], k16=[], v16=[], slots=[], windows=[], attn=[],
@@ -252,13 +255,35 @@ def block_decode(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
         res["gated"].append(head_gate(a, gl[b]).reshape(hq * d))
         res["k_caches"].append(kc)
         res["v_caches"].append(vc)
-    gated = np.stack(res["gated"])
-    out = gemv(w_o, gated)
-    return BlockResult(qkv=qkv, gate_logits=gl, q_roped=np.stack(res["q_roped"]),
-                       k16=np.stack(res["k16"]), v16=np.stack(res["v16"]),
-                       slots=res["slots"], windows=res["windows"],
-                       attn=np.stack(res["attn"]), gated=gated, out=out,
-                       k_caches=res["k_caches"], v_caches=res["v_caches"])
+    return AttentionStepResult(
+        q_roped=np.stack(res["q_roped"]), k16=np.stack(res["k16"]),
+        v16=np.stack(res["v16"]), slots=res["slots"], windows=res["windows"],
+        attn=np.stack(res["attn"]), gated=np.stack(res["gated"]),
+        k_caches=res["k_caches"], v_caches=res["v_caches"])
+
+
+def block_decode(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
+                 x: np.ndarray, seqs: Sequence) -> BlockResult:
+    """One decode step of the attention block for B independent sequences
+    [attn: `encode_attention_block`, steps in its order].
+
+    ``arch`` exposes num_heads, num_kv_heads, head_dim, full_rotary_dim,
+    sliding_window, full_rope_theta, rope_theta and attention_scale.  The fused
+    QKV GEMV and the g_proj GEMV read the same normed x; o_proj reads the
+    gated attention.
+    """
+    w_qkv = bf16_bits_to_f64(w_qkv_bits)
+    w_g = bf16_bits_to_f64(w_g_bits)
+    w_o = bf16_bits_to_f64(w_o_bits)
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    qkv = gemv(w_qkv, x)
+    gl = gemv(w_g, x)
+    st = attention_step(arch, is_full, qkv, gl, seqs)
+    out = gemv(w_o, st.gated)
+    return BlockResult(q_roped=st.q_roped, k16=st.k16, v16=st.v16, slots=st.slots,
+                       windows=st.windows, attn=st.attn, gated=st.gated,
+                       k_caches=st.k_caches, v_caches=st.v_caches, qkv=qkv,
+                       gate_logits=gl, out=out)
 
 
 # ----------------------------------------------------------------------------
