@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode attention block on one MI355X.
+
+One step = one decode step of the whole block (fused qkv+g GEMV, split + RoPE
++ KV-slot write, split-K attention with the headwise gate, o_proj) over one
+batch, with weights and KV cache already resident in HBM.  The default
+workload is the full (causal) layer at 32K context: hidden 2560, position
+32767, 32768-row fp16 cache.  To keep the 256 MiB Infinity Cache from serving
+"HBM" reads, the step rotates over several copies of weights and cache whose
+total exceeds 1 GiB.
+
+Prints ONE JSON line with the throughput (tokens/s), a roofline object for
+the dominant kernel (the attention step: its HBM bytes over its own average
+duration, timed with HIP events around its launches), and the fp64 CPU
+oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn-block tokens/s + achieved HBM GB/s (% peak) at 32K ctx"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "gqa_attention_block_amd", "csrc", "gqa_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workloads():
+    import synth
+    return {
+        "full32k": synth.headline_full_pos32767,
+        "cfg1": synth.cfg1_sliding_pos63,
+        "cfg2": synth.cfg2_full_pos4095,
+        "cfg3": synth.cfg3_sliding_ring_pos32767,
+        "cfg5": synth.cfg5_batched_full,
+    }
+
+
+def attended_rows(case):
+    import oracle
+    n = 0
+    for s in case.seqs:
+        sl, ks, _ = oracle.kv_window(case.is_full, s.position, case.arch.sliding_window,
+                                     s.ring_capacity)
+        n += sl - ks
+    return n
+
+
+def block_bytes(case) -> int:
+    """Algorithmic HBM bytes of one block step: each weight once (bf16), each
+    attended K/V row once (fp16, all KV heads), the slot row written, x in and
+    out as fp32."""
+    a = case.arch
+    h, b = a.hidden, case.batch
+    w = 2 * (a.qkv_rows + a.num_heads) * h + 2 * h * a.q_dim
+    kv_row = 2 * 2 * a.num_kv_heads * a.head_dim          # K and V, fp16
+    return w + kv_row * attended_rows(case) + kv_row * b + 4 * h * b * 2
+
+
+def attention_bytes(case) -> int:
+    """Algorithmic HBM bytes of the attention step: attended K/V rows, the
+    written slot rows, fp32 qkv and gate logits in, gated attention out."""
+    a = case.arch
+    b = case.batch
+    kv_row = 2 * 2 * a.num_kv_heads * a.head_dim
+    return (kv_row * attended_rows(case) + kv_row * b
+            + 4 * b * (a.qkv_rows + a.num_heads + a.q_dim))
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counted_traffic(workload: str):
+    """HBM bytes per attention launch from a committed rocprofv3 PMC summary
+    of the same kernel source, or None."""
+    path = os.path.join(PROFILE_DIR, f"attention_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_digest():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(case, seconds: float):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:                       # pragma: no cover
+        cores = os.cpu_count() or 1
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.block_decode(case.arch, case.is_full, case.w_qkv, case.w_g, case.w_o, case.x,
+                            case.seqs)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    tok = case.batch * runs / el
+    return {"value": tok, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{runs} full fp64 oracle block steps of this workload ({el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="full32k", choices=sorted(workloads()))
+    ap.add_argument("--copies", type=int, default=0, help="weight/cache copies rotated (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle sample length (0 skips the baseline)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the block is a single-GPU decode step and no multi-GPU path exists "
+              "in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gqa_attention_block_amd as gqa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    case = workloads()[args.workload]()
+    a = gqa.Arch(hidden=case.arch.hidden)
+    per_copy = (case.w_qkv.nbytes + case.w_g.nbytes + case.w_o.nbytes
+                + sum(s.k.nbytes + s.v.nbytes for s in case.seqs))
+    copies = args.copies or max(2, min(64, math.ceil((1 << 30) / per_copy)))
+    log(f"workload {case.name}: batch {case.batch}, {per_copy / 1e6:.1f} MB per copy, "
+        f"{copies} copies")
+
+    def up(arr, dt=None):
+        t = torch.from_numpy(arr.view(np.int16) if arr.dtype == np.uint16 else arr)
+        return t.to("cuda:0")
+
+    base = dict(w_qkv=up(case.w_qkv), w_g=up(case.w_g), w_o=up(case.w_o),
+                k=[up(s.k) for s in case.seqs], v=[up(s.v) for s in case.seqs])
+    sets = []
+    for c in range(copies):
+        cl = (lambda t: t) if c == 0 else (lambda t: t.clone())
+        sets.append(dict(w_qkv=cl(base["w_qkv"]), w_g=cl(base["w_g"]), w_o=cl(base["w_o"]),
+                         seqs=[gqa.KvSeq(k=cl(base["k"][i]), v=cl(base["v"][i]),
+                                         position=s.position, ring_capacity=s.ring_capacity)
+                               for i, s in enumerate(case.seqs)]))
+    x = up(case.x)
+    out = torch.empty((case.batch, a.hidden), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(gqa.workspace_size(a, case.batch, max(s.position + 1 for s in case.seqs)),
+                     dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = sets[i % copies]
+        gqa.attention_block_decode(a, s["w_qkv"], s["w_g"], s["w_o"], case.is_full, s["seqs"],
+                                   x, out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert torch.isfinite(out).all(), "non-finite block output"
+    ms_per_step = 1e3 * elapsed / args.steps
+    tokens_per_s = case.batch * args.steps / elapsed
+    bb = block_bytes(case)
+    log(f"block: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.1f} tokens/s, "
+        f"{bb / 1e6:.2f} MB/step -> {bb / (ms_per_step * 1e-3) / 1e9:.1f} GB/s")
+
+    # dominant kernel: the attention step, timed alone with HIP events
+    qkv = torch.empty((case.batch, a.qkv_rows), dtype=torch.float32, device="cuda:0")
+    gl = torch.empty((case.batch, a.num_heads), dtype=torch.float32, device="cuda:0")
+    attn = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda:0")
+    gqa.qkv_gate_gemv(a, sets[0]["w_qkv"], sets[0]["w_g"], x, qkv, gl)
+    n_att = max(args.steps, 20)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_att)]
+    for i in range(args.warmup):
+        gqa.attention_gated(a, case.is_full, sets[i % copies]["seqs"], qkv, gl, attn, ws)
+    for i in range(n_att):
+        evs[i][0].record()
+        gqa.attention_gated(a, case.is_full, sets[i % copies]["seqs"], qkv, gl, attn, ws)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    att_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    att_avg_s = sum(att_ms) / len(att_ms) * 1e-3
+    ab = attention_bytes(case)
+    achieved = ab / att_avg_s / 1e9
+    log(f"attention step: avg {att_avg_s * 1e6:.2f} us (median {att_ms[len(att_ms) // 2] * 1e3:.2f}"
+        f" us), {ab / 1e6:.2f} MB -> {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak")
+
+    traffic = counted_traffic(args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": case.name, "hidden": a.hidden, "batch": case.batch,
+                   "positions": [s.position for s in case.seqs][:4],
+                   "kv_rows_attended": attended_rows(case), "weights": "bf16",
+                   "kv_cache": "fp16", "block_bytes_per_step": bb, "copies_rotated": copies},
+        "block_hbm_gbs": round(bb / (ms_per_step * 1e-3) / 1e9, 1),
+        "block_frac_of_peak": round(bb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,23 @@
+"""MI355X (gfx950) hybrid-window GQA decode attention block.
+
+The compute path is ``libgqa.so`` (hand-written HIP kernels behind the C ABI
+in ``include/gqa.h``); this package is its thin Python binding.  PyTorch only
+provides device memory and streams.
+"""
+from .binding import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    Arch,
+    GqaError,
+    KvSeq,
+    attention_block_decode,
+    attention_gated,
+    kv_slot,
+    kv_window,
+    library_path,
+    o_proj_gemv,
+    qkv_gate_gemv,
+    residual_add,
+    rms_norm_bf16w,
+    rope_params_for,
+    workspace_size,
+)

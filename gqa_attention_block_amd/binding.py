@@ -1,0 +1,322 @@
+"""ctypes binding of libgqa (include/gqa.h).
+
+Argument marshalling only: torch tensors are checked for dtype, device,
+contiguity and shape, turned into raw device pointers, and passed with the
+current HIP stream.  Every step of the block runs in the library's kernels;
+there is no fallback of any kind.  If ``libgqa.so`` has not been built the
+import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
+
+GQA_OK = 0
+_STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARGUMENT", 2: "GQA_ERR_UNSUPPORTED",
+           3: "GQA_ERR_WORKSPACE_TOO_SMALL", 4: "GQA_ERR_GPU"}
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, detail: str, call: str):
+        self.status = status
+        self.status_name = _STATUS.get(status, f"status {status}")
+        super().__init__(f"{call}: {self.status_name}: {detail}")
+
+
+class _Arch(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("full_rotary_dim", ctypes.c_int32), ("sliding_window", ctypes.c_int32),
+                ("full_rope_theta", ctypes.c_double), ("rope_theta", ctypes.c_double),
+                ("attention_scale", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("q_k_v_proj", ctypes.c_void_p), ("g_proj", ctypes.c_void_p),
+                ("o_proj", ctypes.c_void_p)]
+
+
+class _KvSeq(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("ring_capacity", ctypes.c_int32), ("position", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m gqa_attention_block_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, D, F, S = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double,
+                            ctypes.c_float, ctypes.c_size_t)
+    A, W, K = ctypes.POINTER(_Arch), ctypes.POINTER(_Weights), ctypes.POINTER(_KvSeq)
+    sig = {
+        "gqa_rope_params_for": (ctypes.c_int, [ctypes.c_int, I32, I32, D, D, ctypes.POINTER(I32),
+                                               ctypes.POINTER(D)]),
+        "gqa_kv_window": (ctypes.c_int, [ctypes.c_int, I32, I32, I32, ctypes.POINTER(I32),
+                                         ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "gqa_kv_slot": (I32, [I32, I32]),
+        "gqa_workspace_size": (ctypes.c_int, [A, I32, I32, ctypes.POINTER(S)]),
+        "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
+        "gqa_qkv_gate_gemv": (ctypes.c_int, [A, W, I32, P, P, P, P]),
+        "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, S, P]),
+        "gqa_o_proj_gemv": (ctypes.c_int, [A, W, I32, P, P, P]),
+        "gqa_rms_norm_bf16w": (ctypes.c_int, [P, P, P, I32, I32, F, P]),
+        "gqa_residual_add": (ctypes.c_int, [P, P, I64, P]),
+        "gqa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "gqa_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+#: symbols the header declares; tests check the library exports all of them
+EXPORTED_SYMBOLS = (
+    "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size",
+    "gqa_attention_block_decode", "gqa_qkv_gate_gemv", "gqa_attention_gated",
+    "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
+    "gqa_last_error",
+)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _check(status: int, call: str):
+    if status != GQA_OK:
+        raise GqaError(status, _lib.gqa_last_error().decode(), call)
+
+
+# ----------------------------------------------------------------------------
+# plain values
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Arch:
+    """Mirror of gqa_arch.  Defaults are the spark2_5 family's published values."""
+    hidden: int
+    num_heads: int = 16
+    num_kv_heads: int = 4
+    head_dim: int = 256
+    full_rotary_dim: int = 64
+    sliding_window: int = 512
+    full_rope_theta: float = 5.0e6
+    rope_theta: float = 1.0e4
+    attention_scale: float = 0.0625
+    rms_eps: float = 1e-6
+
+    def _c(self) -> _Arch:
+        return _Arch(self.hidden, self.num_heads, self.num_kv_heads, self.head_dim,
+                     self.full_rotary_dim, self.sliding_window, self.full_rope_theta,
+                     self.rope_theta, self.attention_scale, self.rms_eps)
+
+    @property
+    def q_dim(self) -> int:
+        return self.num_heads * self.head_dim
+
+    @property
+    def qkv_rows(self) -> int:
+        return (self.num_heads + 2 * self.num_kv_heads) * self.head_dim
+
+
+@dataclass
+class KvSeq:
+    """One sequence's cache for one layer: fp16 tensors [capacity][Hk][D]."""
+    k: torch.Tensor
+    v: torch.Tensor
+    position: int
+    ring_capacity: int = 0
+
+
+def rope_params_for(is_full: bool, full_rotary_dim: int, head_dim: int, full_theta: float,
+                    sliding_theta: float):
+    r, t = ctypes.c_int32(), ctypes.c_double()
+    _check(_lib.gqa_rope_params_for(int(is_full), full_rotary_dim, head_dim, full_theta,
+                                    sliding_theta, ctypes.byref(r), ctypes.byref(t)),
+           "gqa_rope_params_for")
+    return r.value, t.value
+
+
+def kv_window(is_full: bool, position: int, sliding_window: int, ring_capacity: int):
+    a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.gqa_kv_window(int(is_full), position, sliding_window, ring_capacity,
+                              ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "gqa_kv_window")
+    return a.value, b.value, c.value
+
+
+def kv_slot(position: int, ring_capacity: int) -> int:
+    return int(_lib.gqa_kv_slot(position, ring_capacity))
+
+
+def workspace_size(arch: Arch, batch: int, max_seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    a = arch._c()
+    _check(_lib.gqa_workspace_size(ctypes.byref(a), batch, max_seq_len, ctypes.byref(n)),
+           "gqa_workspace_size")
+    return n.value
+
+
+# ----------------------------------------------------------------------------
+# device calls
+# ----------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str, numel: Optional[int] = None) -> int:
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _wptr(t: Optional[torch.Tensor], name: str, numel: int) -> int:
+    """bf16 weights may be passed as bfloat16 or as raw 16-bit integers."""
+    if t is None:
+        return 0
+    if t.dtype not in _BF16_LIKE:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected bfloat16 (or raw 16-bit bits)")
+    return _ptr(t, t.dtype, name, numel)
+
+
+def _weights(arch: Arch, w_qkv, w_g, w_o) -> _Weights:
+    h = arch.hidden
+    return _Weights(_wptr(w_qkv, "w_qkv", arch.qkv_rows * h),
+                    _wptr(w_g, "w_g", arch.num_heads * h),
+                    _wptr(w_o, "w_o", h * arch.q_dim))
+
+
+def _seqs(arch: Arch, seqs: Sequence[KvSeq]):
+    arr = (_KvSeq * max(1, len(seqs)))()
+    row = arch.num_kv_heads * arch.head_dim
+    for i, s in enumerate(seqs):
+        if s.k.shape != s.v.shape:
+            raise ValueError(f"seqs[{i}]: k and v shapes differ")
+        if s.k.numel() % row != 0:
+            raise ValueError(f"seqs[{i}]: cache size is not a whole number of rows")
+        cap = s.k.numel() // row
+        arr[i] = _KvSeq(_ptr(s.k, torch.float16, f"seqs[{i}].k"),
+                        _ptr(s.v, torch.float16, f"seqs[{i}].v"), cap, int(s.ring_capacity),
+                        int(s.position), 0)
+    return arr
+
+
+def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],
+                           x: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                           stream=None):
+    b = len(seqs)
+    a = arch._c()
+    w = _weights(arch, w_qkv, w_g, w_o)
+    ks = _seqs(arch, seqs)
+    _check(_lib.gqa_attention_block_decode(
+        ctypes.byref(a), ctypes.byref(w), int(is_full), ks, b,
+        _ptr(x, torch.float32, "x", b * arch.hidden),
+        _ptr(out, torch.float32, "out", b * arch.hidden),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+        "gqa_attention_block_decode")
+
+
+def qkv_gate_gemv(arch: Arch, w_qkv, w_g, x: torch.Tensor, qkv: torch.Tensor,
+                  gate_logits: torch.Tensor, stream=None):
+    b = x.shape[0]
+    a = arch._c()
+    w = _weights(arch, w_qkv, w_g, None)
+    _check(_lib.gqa_qkv_gate_gemv(
+        ctypes.byref(a), ctypes.byref(w), b, _ptr(x, torch.float32, "x", b * arch.hidden),
+        _ptr(qkv, torch.float32, "qkv", b * arch.qkv_rows),
+        _ptr(gate_logits, torch.float32, "gate_logits", b * arch.num_heads), _stream(stream)),
+        "gqa_qkv_gate_gemv")
+
+
+def attention_gated(arch: Arch, is_full: bool, seqs: Sequence[KvSeq], qkv: torch.Tensor,
+                    gate_logits: torch.Tensor, attn_gated: torch.Tensor,
+                    workspace: torch.Tensor, stream=None):
+    b = len(seqs)
+    a = arch._c()
+    ks = _seqs(arch, seqs)
+    _check(_lib.gqa_attention_gated(
+        ctypes.byref(a), int(is_full), ks, b,
+        _ptr(qkv, torch.float32, "qkv", b * arch.qkv_rows),
+        _ptr(gate_logits, torch.float32, "gate_logits", b * arch.num_heads),
+        _ptr(attn_gated, torch.float32, "attn_gated", b * arch.q_dim),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+        "gqa_attention_gated")
+
+
+def o_proj_gemv(arch: Arch, w_o, attn_gated: torch.Tensor, out: torch.Tensor, stream=None):
+    b = attn_gated.shape[0]
+    a = arch._c()
+    w = _weights(arch, None, None, w_o)
+    _check(_lib.gqa_o_proj_gemv(
+        ctypes.byref(a), ctypes.byref(w), b,
+        _ptr(attn_gated, torch.float32, "attn_gated", b * arch.q_dim),
+        _ptr(out, torch.float32, "out", b * arch.hidden), _stream(stream)), "gqa_o_proj_gemv")
+
+
+def rms_norm_bf16w(h: torch.Tensor, w, out: torch.Tensor, eps: float, stream=None):
+    rows, hidden = h.shape
+    _check(_lib.gqa_rms_norm_bf16w(
+        _ptr(h, torch.float32, "h"), _wptr(w, "w", hidden),
+        _ptr(out, torch.float32, "out", rows * hidden), rows, hidden, eps, _stream(stream)),
+        "gqa_rms_norm_bf16w")
+
+
+def residual_add(h: torch.Tensor, o: torch.Tensor, stream=None):
+    n = h.numel()
+    _check(_lib.gqa_residual_add(_ptr(h, torch.float32, "h"), _ptr(o, torch.float32, "o", n),
+                                 n, _stream(stream)), "gqa_residual_add")
+
+
+def raw_call(name: str, *args):
+    """Call a library entry point with already-marshalled ctypes arguments and
+    return its raw status (used by the error-path tests)."""
+    return getattr(_lib, name)(*args)
+
+
+def last_error() -> str:
+    return _lib.gqa_last_error().decode()
+
+
+def status_string(status: int) -> str:
+    return _lib.gqa_status_string(status).decode()
+
+
+def c_arch(arch: Arch) -> _Arch:
+    return arch._c()
+
+
+def c_seq_array(n: int):
+    return (_KvSeq * max(1, n))()
+
+
+c_weights = _Weights
+c_kv_seq = _KvSeq

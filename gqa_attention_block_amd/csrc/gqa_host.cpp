@@ -1,0 +1,531 @@
+// Host side of libgqa: argument checks, the window/slot/RoPE-parameter
+// functions, the split-K plan, workspace layout and the extern "C" entry
+// points declared in include/gqa.h.
+//
+// Every entry point validates all of its arguments before the first launch so
+// that an error return means nothing was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "gqa.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+thread_local std::string g_last_error;
+
+gqa_status fail(gqa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gqa_status ok() {
+  g_last_error.clear();
+  return GQA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+constexpr double kLog2e = 1.4426950408889634;
+
+// ---- architecture ---------------------------------------------------------
+
+gqa_status check_arch(const gqa_arch *a) {
+  if (!a) return fail(GQA_ERR_INVALID_ARGUMENT, "arch is null");
+  if (a->hidden < 8 || a->hidden % 8 != 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "hidden=%d must be a positive multiple of 8", a->hidden);
+  if (a->hidden > kMaxHidden)
+    return fail(GQA_ERR_UNSUPPORTED, "hidden=%d exceeds the supported %d", a->hidden, kMaxHidden);
+  if (a->num_kv_heads < 1 || a->num_heads < 1)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (num_heads=%d num_kv_heads=%d)",
+                a->num_heads, a->num_kv_heads);
+  if (a->num_heads % a->num_kv_heads != 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "num_heads=%d is not a multiple of num_kv_heads=%d",
+                a->num_heads, a->num_kv_heads);
+  if (a->num_heads != kGroup * a->num_kv_heads)
+    return fail(GQA_ERR_UNSUPPORTED, "kernels need num_heads == 4 * num_kv_heads (got %d, %d)",
+                a->num_heads, a->num_kv_heads);
+  if (a->head_dim != kHeadDim)
+    return fail(GQA_ERR_UNSUPPORTED, "kernels need head_dim == 256 (got %d)", a->head_dim);
+  if (a->num_heads * a->head_dim > kMaxHidden)
+    return fail(GQA_ERR_UNSUPPORTED, "num_heads*head_dim=%d exceeds %d", a->num_heads * a->head_dim,
+                kMaxHidden);
+  if (a->full_rotary_dim < 2 || a->full_rotary_dim % 2 != 0 || a->full_rotary_dim > a->head_dim)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "full_rotary_dim=%d must be even and in [2, head_dim]",
+                a->full_rotary_dim);
+  if (a->sliding_window < 1)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "sliding_window=%d must be >= 1", a->sliding_window);
+  if (!(a->full_rope_theta > 0.0) || !isfinite(a->full_rope_theta) || !(a->rope_theta > 0.0) ||
+      !isfinite(a->rope_theta))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "rope thetas must be finite and > 0");
+  if (!(a->attention_scale > 0.f) || !isfinite(a->attention_scale))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "attention_scale must be finite and > 0");
+  const size_t qkv_bytes = (size_t)(a->num_heads + 2 * a->num_kv_heads) * a->head_dim * a->hidden * 2u;
+  if (qkv_bytes > kMaxBufferBytes)
+    return fail(GQA_ERR_UNSUPPORTED, "q_k_v_proj of %zu bytes exceeds the supported %u", qkv_bytes,
+                kMaxBufferBytes);
+  return GQA_OK;
+}
+
+gqa_status check_weights(const gqa_layer_weights *w, bool need_qkv, bool need_o) {
+  if (!w) return fail(GQA_ERR_INVALID_ARGUMENT, "weights is null");
+  if (need_qkv) {
+    if (!w->q_k_v_proj || !w->g_proj)
+      return fail(GQA_ERR_INVALID_ARGUMENT, "q_k_v_proj or g_proj is null");
+    if (!aligned16(w->q_k_v_proj) || !aligned16(w->g_proj))
+      return fail(GQA_ERR_INVALID_ARGUMENT, "q_k_v_proj and g_proj must be 16-byte aligned");
+  }
+  if (need_o) {
+    if (!w->o_proj) return fail(GQA_ERR_INVALID_ARGUMENT, "o_proj is null");
+    if (!aligned16(w->o_proj)) return fail(GQA_ERR_INVALID_ARGUMENT, "o_proj must be 16-byte aligned");
+  }
+  return GQA_OK;
+}
+
+gqa_status check_ptr(const void *p, const char *name) {
+  if (!p) return fail(GQA_ERR_INVALID_ARGUMENT, "%s is null", name);
+  if (!aligned16(p)) return fail(GQA_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  return GQA_OK;
+}
+
+// ---- window, slot, RoPE parameters (pure) ---------------------------------
+
+gqa_status window_of(int is_full, int32_t position, int32_t window, int32_t ring, int32_t *seq_len,
+                     int32_t *kv_start, int32_t *active_ring) {
+  if (position < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "position=%d must be >= 0", position);
+  if (position == INT32_MAX) return fail(GQA_ERR_INVALID_ARGUMENT, "position + 1 overflows");
+  if (window < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "sliding_window=%d must be >= 1", window);
+  if (ring < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "ring_capacity=%d must be >= 0", ring);
+  const int32_t sl = position + 1;
+  if (is_full) {
+    *seq_len = sl;
+    *kv_start = 0;
+    *active_ring = 0;
+  } else {
+    *seq_len = sl;
+    *kv_start = sl > window ? sl - window : 0;
+    *active_ring = (ring > 0 && sl > ring) ? ring : 0;
+  }
+  return GQA_OK;
+}
+
+// ---- sequences and the split-K plan ----------------------------------------
+
+struct Plan {
+  int tile = kMaxTile;
+  int chunk = kMaxTile;
+  struct Group {
+    int first = 0, count = 0, total_chunks = 0;
+  };
+  std::vector<Group> groups;
+  size_t max_group_chunks = 0;
+};
+
+int num_cus_of_current_device() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Resolve and check every sequence.  Fills one SeqDesc per sequence (without
+// chunk_begin) and the attended-row counts.
+gqa_status resolve_seqs(const gqa_arch *a, int is_full, const gqa_kv_seq *seqs, int32_t batch,
+                        std::vector<SeqDesc> *out) {
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  if (batch > 0 && !seqs) return fail(GQA_ERR_INVALID_ARGUMENT, "seqs is null");
+  out->resize(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    const gqa_kv_seq &s = seqs[b];
+    gqa_status st;
+    if ((st = check_ptr(s.k, "seqs[].k")) != GQA_OK) return st;
+    if ((st = check_ptr(s.v, "seqs[].v")) != GQA_OK) return st;
+    if (s.reserved != 0) return fail(GQA_ERR_INVALID_ARGUMENT, "seqs[%d].reserved must be 0", b);
+    if (s.capacity < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "seqs[%d].capacity=%d < 1", b, s.capacity);
+    if (s.ring_capacity < 0)
+      return fail(GQA_ERR_INVALID_ARGUMENT, "seqs[%d].ring_capacity=%d < 0", b, s.ring_capacity);
+    if (s.ring_capacity > 0) {
+      if (is_full)
+        return fail(GQA_ERR_INVALID_ARGUMENT,
+                    "seqs[%d]: a full (causal) layer has no ring (ring_capacity=%d)", b, s.ring_capacity);
+      if (s.ring_capacity < a->sliding_window)
+        return fail(GQA_ERR_INVALID_ARGUMENT,
+                    "seqs[%d].ring_capacity=%d < sliding_window=%d would overwrite rows of the window",
+                    b, s.ring_capacity, a->sliding_window);
+      if (s.ring_capacity > s.capacity)
+        return fail(GQA_ERR_INVALID_ARGUMENT, "seqs[%d].ring_capacity=%d > capacity=%d", b,
+                    s.ring_capacity, s.capacity);
+    }
+    int32_t sl, ks, ar;
+    if ((st = window_of(is_full, s.position, a->sliding_window, s.ring_capacity, &sl, &ks, &ar)) != GQA_OK)
+      return st;
+    if (s.ring_capacity == 0 && s.position >= s.capacity)
+      return fail(GQA_ERR_INVALID_ARGUMENT, "seqs[%d].position=%d needs a linear cache of more than %d rows",
+                  b, s.position, s.capacity);
+    const size_t cache_bytes = (size_t)s.capacity * a->num_kv_heads * a->head_dim * 2u;
+    if (cache_bytes > kMaxBufferBytes)
+      return fail(GQA_ERR_UNSUPPORTED, "seqs[%d]: a %zu-byte K/V cache exceeds the supported %u bytes", b,
+                  cache_bytes, kMaxBufferBytes);
+    SeqDesc &d = (*out)[b];
+    d.k = static_cast<_Float16 *>(s.k);
+    d.v = static_cast<_Float16 *>(s.v);
+    d.kv_start = ks;
+    d.n = sl - ks;
+    d.ring = ar;
+    d.slot = s.ring_capacity > 0 ? s.position % s.ring_capacity : s.position;
+    d.position = s.position;
+    d.chunk_begin = 0;
+    d.cache_bytes = (unsigned)cache_bytes;
+  }
+  return GQA_OK;
+}
+
+// Split-K plan.  Workgroups walk their chunk in tiles of kMaxTile rows; the
+// chunk is the largest number of tiles that still gives every CU at least
+// two workgroups, so partials stay few while the chip stays full.  Sequences
+// go in launch groups of up to kMaxSeqPerLaunch.
+Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
+  Plan plan;
+  const long target = 2L * num_cus_of_current_device();
+  auto wgs = [&](int chunk) {
+    long n = 0;
+    for (const SeqDesc &s : seqs) n += (long)ceil_div(s.n, chunk) * num_kv_heads;
+    return n;
+  };
+  const int tile = kMaxTile;
+  int ntiles = 1;
+  while (ntiles < kMaxTilesPerChunk && wgs(tile * (ntiles + 1)) >= target) ++ntiles;
+  plan.tile = tile;
+  plan.chunk = tile * ntiles;
+  for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {
+    Plan::Group g;
+    g.first = first;
+    g.count = std::min<int>(kMaxSeqPerLaunch, (int)seqs.size() - first);
+    int tot = 0;
+    for (int i = 0; i < g.count; ++i) tot += ceil_div(seqs[first + i].n, plan.chunk);
+    g.total_chunks = tot;
+    plan.max_group_chunks = std::max<size_t>(plan.max_group_chunks, (size_t)tot);
+    plan.groups.push_back(g);
+  }
+  return plan;
+}
+
+// ---- workspace layout -----------------------------------------------------
+
+struct Layout {
+  size_t qkv = 0, gate = 0, attn = 0, part_o = 0, part_ml = 0, total = 0;
+};
+
+size_t partial_bytes_o(const gqa_arch *a, size_t chunks) {
+  return round_up(chunks * (size_t)a->num_heads * kHeadDim * sizeof(float), 256);
+}
+size_t partial_bytes_ml(const gqa_arch *a, size_t chunks) {
+  return round_up(chunks * (size_t)a->num_heads * 2 * sizeof(float), 256);
+}
+
+// Block layout: [qkv | gate | attn | part_o | part_ml]; the attention step
+// alone uses [part_o | part_ml] from offset 0.
+Layout block_layout(const gqa_arch *a, int32_t batch, size_t chunks) {
+  Layout L;
+  const size_t qkv_rows = (size_t)(a->num_heads + 2 * a->num_kv_heads) * a->head_dim;
+  L.qkv = 0;
+  L.gate = L.qkv + round_up((size_t)batch * qkv_rows * sizeof(float), 256);
+  L.attn = L.gate + round_up((size_t)batch * a->num_heads * sizeof(float), 256);
+  L.part_o = L.attn + round_up((size_t)batch * a->num_heads * a->head_dim * sizeof(float), 256);
+  L.part_ml = L.part_o + partial_bytes_o(a, chunks);
+  L.total = L.part_ml + partial_bytes_ml(a, chunks);
+  return L;
+}
+
+// ---- launch helpers -------------------------------------------------------
+
+gqa_status gpu_error(hipError_t e, const char *what) {
+  return fail(GQA_ERR_GPU, "%s: %s", what, hipGetErrorString(e));
+}
+
+gqa_status run_qkv_gate(const gqa_arch *a, const gqa_layer_weights *w, int32_t batch, const float *x,
+                        float *qkv, float *gate, hipStream_t stream) {
+  GemvParams p{};
+  p.w0 = static_cast<const uint16_t *>(w->q_k_v_proj);
+  p.w1 = static_cast<const uint16_t *>(w->g_proj);
+  p.rows0 = (a->num_heads + 2 * a->num_kv_heads) * a->head_dim;
+  p.rows1 = a->num_heads;
+  p.cols = a->hidden;
+  p.batch = batch;
+  p.x = x;
+  p.ldx = a->hidden;
+  p.y0 = qkv;
+  p.ldy0 = p.rows0;
+  p.y1 = gate;
+  p.ldy1 = a->num_heads;
+  hipError_t e = launch_gemv(p, stream);
+  return e == hipSuccess ? GQA_OK : gpu_error(e, "qkv/gate GEMV launch");
+}
+
+gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t batch, const float *attn,
+                      float *out, hipStream_t stream) {
+  GemvParams p{};
+  p.w0 = static_cast<const uint16_t *>(w->o_proj);
+  p.w1 = nullptr;
+  p.rows0 = a->hidden;
+  p.rows1 = 0;
+  p.cols = a->num_heads * a->head_dim;
+  p.batch = batch;
+  p.x = attn;
+  p.ldx = p.cols;
+  p.y0 = out;
+  p.ldy0 = a->hidden;
+  p.y1 = nullptr;
+  p.ldy1 = 0;
+  hipError_t e = launch_gemv(p, stream);
+  return e == hipSuccess ? GQA_OK : gpu_error(e, "o_proj GEMV launch");
+}
+
+gqa_status run_attention(const gqa_arch *a, int is_full, const std::vector<SeqDesc> &seqs,
+                         const Plan &plan, const float *qkv, const float *gate, float *attn,
+                         float *part_o, float *part_ml, hipStream_t stream) {
+  int32_t rdim;
+  double theta;
+  gqa_rope_params_for(is_full, a->full_rotary_dim, a->head_dim, a->full_rope_theta, a->rope_theta, &rdim,
+                      &theta);
+  const long qkv_rows = (long)(a->num_heads + 2 * a->num_kv_heads) * a->head_dim;
+  for (const Plan::Group &g : plan.groups) {
+    AttnParams p{};
+    p.qkv = qkv + (size_t)g.first * qkv_rows;
+    p.ld_qkv = qkv_rows;
+    p.gate = gate + (size_t)g.first * a->num_heads;
+    p.ld_gate = a->num_heads;
+    p.out = attn + (size_t)g.first * a->num_heads * a->head_dim;
+    p.ld_out = (long)a->num_heads * a->head_dim;
+    p.part_o = part_o;
+    p.part_ml = part_ml;
+    p.num_kv_heads = a->num_kv_heads;
+    p.rotary_dim = rdim;
+    p.theta = theta;
+    p.qscale = (float)((double)a->attention_scale * kLog2e);
+    p.tile = plan.tile;
+    p.chunk = plan.chunk;
+    p.nseq = g.count;
+    p.total_chunks = g.total_chunks;
+    int cb = 0;
+    for (int i = 0; i < g.count; ++i) {
+      p.seq[i] = seqs[g.first + i];
+      p.seq[i].chunk_begin = cb;
+      cb += ceil_div(p.seq[i].n, plan.chunk);
+    }
+    hipError_t e = launch_attention(p, a->num_heads, stream);
+    if (e != hipSuccess) return gpu_error(e, "attention launch");
+  }
+  return GQA_OK;
+}
+
+}  // namespace
+}  // namespace gqa
+
+using namespace gqa;
+
+extern "C" {
+
+const char *gqa_status_string(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARGUMENT: return "GQA_ERR_INVALID_ARGUMENT";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_WORKSPACE_TOO_SMALL: return "GQA_ERR_WORKSPACE_TOO_SMALL";
+    case GQA_ERR_GPU: return "GQA_ERR_GPU";
+  }
+  return "GQA_ERR_UNKNOWN";
+}
+
+const char *gqa_last_error(void) { return g_last_error.c_str(); }
+
+gqa_status gqa_rope_params_for(int is_full, int32_t full_rotary_dim, int32_t head_dim, double full_theta,
+                               double sliding_theta, int32_t *rotary_dim, double *theta) {
+  if (!rotary_dim || !theta) return fail(GQA_ERR_INVALID_ARGUMENT, "null output pointer");
+  if (head_dim < 2 || head_dim % 2 != 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "head_dim=%d must be even and >= 2", head_dim);
+  if (full_rotary_dim < 2 || full_rotary_dim % 2 != 0 || full_rotary_dim > head_dim)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "full_rotary_dim=%d must be even and in [2, head_dim]",
+                full_rotary_dim);
+  if (!(full_theta > 0.0) || !(sliding_theta > 0.0) || !isfinite(full_theta) || !isfinite(sliding_theta))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "thetas must be finite and > 0");
+  if (is_full) {
+    *rotary_dim = full_rotary_dim;
+    *theta = full_theta;
+  } else {
+    *rotary_dim = head_dim;
+    *theta = sliding_theta;
+  }
+  return ok();
+}
+
+gqa_status gqa_kv_window(int is_full, int32_t position, int32_t sliding_window, int32_t ring_capacity,
+                         int32_t *seq_len, int32_t *kv_start, int32_t *active_ring) {
+  if (!seq_len || !kv_start || !active_ring) return fail(GQA_ERR_INVALID_ARGUMENT, "null output pointer");
+  gqa_status st = window_of(is_full, position, sliding_window, ring_capacity, seq_len, kv_start, active_ring);
+  return st == GQA_OK ? ok() : st;
+}
+
+int32_t gqa_kv_slot(int32_t position, int32_t ring_capacity) {
+  if (position < 0 || ring_capacity < 0) return -1;
+  return ring_capacity > 0 ? position % ring_capacity : position;
+}
+
+gqa_status gqa_workspace_size(const gqa_arch *arch, int32_t batch, int32_t max_seq_len, size_t *bytes) {
+  if (!bytes) return fail(GQA_ERR_INVALID_ARGUMENT, "bytes is null");
+  gqa_status st = check_arch(arch);
+  if (st != GQA_OK) return st;
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  if (max_seq_len < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "max_seq_len=%d must be >= 1", max_seq_len);
+  // Worst case: every sequence split into kMinChunk-row chunks, one launch
+  // group of kMaxSeqPerLaunch sequences live at a time.
+  const size_t per_seq = (size_t)ceil_div(max_seq_len, kMinChunk);
+  const size_t chunks = per_seq * (size_t)std::min<int32_t>(batch, kMaxSeqPerLaunch);
+  *bytes = block_layout(arch, batch, chunks).total;
+  return ok();
+}
+
+gqa_status check_batch(const gqa_arch *a, int32_t batch) {
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  const size_t widest = (size_t)std::max(a->hidden, a->num_heads * a->head_dim);
+  if ((size_t)batch * widest * sizeof(float) > kMaxBufferBytes)
+    return fail(GQA_ERR_UNSUPPORTED, "batch=%d makes an activation larger than %u bytes", batch,
+                kMaxBufferBytes);
+  return GQA_OK;
+}
+
+gqa_status gqa_qkv_gate_gemv(const gqa_arch *arch, const gqa_layer_weights *weights, int32_t batch,
+                             const float *x, float *qkv, float *gate_logits, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_weights(weights, true, false)) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  if (batch == 0) return ok();
+  if ((st = check_ptr(x, "x")) != GQA_OK) return st;
+  if ((st = check_ptr(qkv, "qkv")) != GQA_OK) return st;
+  if ((st = check_ptr(gate_logits, "gate_logits")) != GQA_OK) return st;
+  st = run_qkv_gate(arch, weights, batch, x, qkv, gate_logits, static_cast<hipStream_t>(stream));
+  return st == GQA_OK ? ok() : st;
+}
+
+gqa_status gqa_o_proj_gemv(const gqa_arch *arch, const gqa_layer_weights *weights, int32_t batch,
+                           const float *attn_gated, float *out, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_weights(weights, false, true)) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  if (batch == 0) return ok();
+  if ((st = check_ptr(attn_gated, "attn_gated")) != GQA_OK) return st;
+  if ((st = check_ptr(out, "out")) != GQA_OK) return st;
+  st = run_o_proj(arch, weights, batch, attn_gated, out, static_cast<hipStream_t>(stream));
+  return st == GQA_OK ? ok() : st;
+}
+
+gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs, int32_t batch,
+                               const float *qkv, const float *gate_logits, float *attn_gated,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
+  if (batch == 0) return ok();
+  if ((st = check_ptr(qkv, "qkv")) != GQA_OK) return st;
+  if ((st = check_ptr(gate_logits, "gate_logits")) != GQA_OK) return st;
+  if ((st = check_ptr(attn_gated, "attn_gated")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  const Plan plan = make_plan(descs, arch->num_kv_heads);
+  const size_t need = partial_bytes_o(arch, plan.max_group_chunks) + partial_bytes_ml(arch, plan.max_group_chunks);
+  if (workspace_bytes < need)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the attention needs %zu",
+                workspace_bytes, need);
+  char *ws = static_cast<char *>(workspace);
+  float *part_o = reinterpret_cast<float *>(ws);
+  float *part_ml = reinterpret_cast<float *>(ws + partial_bytes_o(arch, plan.max_group_chunks));
+  st = run_attention(arch, is_full, descs, plan, qkv, gate_logits, attn_gated, part_o, part_ml,
+                     static_cast<hipStream_t>(stream));
+  return st == GQA_OK ? ok() : st;
+}
+
+gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,
+                                      const gqa_kv_seq *seqs, int32_t batch, const float *x_normed,
+                                      float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_weights(weights, true, true)) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
+  if (batch == 0) return ok();
+  if ((st = check_ptr(x_normed, "x_normed")) != GQA_OK) return st;
+  if ((st = check_ptr(out, "out")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  const Plan plan = make_plan(descs, arch->num_kv_heads);
+  const Layout L = block_layout(arch, batch, plan.max_group_chunks);
+  if (workspace_bytes < L.total)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the block needs %zu", workspace_bytes,
+                L.total);
+  char *ws = static_cast<char *>(workspace);
+  float *qkv = reinterpret_cast<float *>(ws + L.qkv);
+  float *gate = reinterpret_cast<float *>(ws + L.gate);
+  float *attn = reinterpret_cast<float *>(ws + L.attn);
+  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
+  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_qkv_gate(arch, weights, batch, x_normed, qkv, gate, s)) != GQA_OK) return st;
+  if ((st = run_attention(arch, is_full, descs, plan, qkv, gate, attn, part_o, part_ml, s)) != GQA_OK)
+    return st;
+  if ((st = run_o_proj(arch, weights, batch, attn, out, s)) != GQA_OK) return st;
+  return ok();
+}
+
+gqa_status gqa_rms_norm_bf16w(const float *h, const void *w, float *out, int32_t rows, int32_t hidden,
+                              float eps, void *stream) {
+  gqa_status st;
+  if (rows < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "rows=%d must be >= 0", rows);
+  if (hidden < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "hidden=%d must be >= 1", hidden);
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(GQA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (rows == 0) return ok();
+  if ((st = check_ptr(h, "h")) != GQA_OK) return st;
+  if ((st = check_ptr(w, "w")) != GQA_OK) return st;
+  if ((st = check_ptr(out, "out")) != GQA_OK) return st;
+  hipError_t e = launch_rms_norm(h, static_cast<const uint16_t *>(w), out, rows, hidden, eps,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : gpu_error(e, "rms_norm launch");
+}
+
+gqa_status gqa_residual_add(float *h, const float *o, int64_t n, void *stream) {
+  gqa_status st;
+  if (n < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "n must be >= 0");
+  if (n == 0) return ok();
+  if ((st = check_ptr(h, "h")) != GQA_OK) return st;
+  if ((st = check_ptr(o, "o")) != GQA_OK) return st;
+  hipError_t e = launch_residual_add(h, o, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : gpu_error(e, "residual_add launch");
+}
+
+}  // extern "C"

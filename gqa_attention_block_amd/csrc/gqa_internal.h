@@ -1,0 +1,77 @@
+// Internal definitions shared by the host side and the kernels of libgqa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gqa.h"
+
+namespace gqa {
+
+constexpr int kHeadDim = 256;        // kernels specialise D = 256
+constexpr int kGroup = 4;            // query heads per KV head
+constexpr int kThreads = 256;        // 4 wave64 per workgroup
+constexpr int kMaxSeqPerLaunch = 32; // sequence descriptors carried in kernel arguments
+constexpr int kMaxTile = 64;         // attention rows per workgroup per step
+constexpr int kMinChunk = 64;        // smallest attention chunk (sizes the workspace)
+constexpr int kMaxTilesPerChunk = 32;
+constexpr unsigned kMaxBufferBytes = 0x7FFFFFFFu;  // buffer loads use 31-bit offsets
+constexpr int kMaxHidden = 8192;     // GEMV keeps up to 16 x 512 columns in registers
+
+// One sequence of one attention launch.  Window and slot are resolved on the
+// host so the kernels only do integer arithmetic that is the same for every row.
+struct SeqDesc {
+  _Float16 *k;        // cache base, [capacity][Hk][D]
+  _Float16 *v;
+  int kv_start;       // first attended logical position
+  int n;              // attended rows: seq_len - kv_start (>= 1)
+  int ring;           // active ring size, 0 = identity addressing
+  int slot;           // physical row that receives this token's k and v
+  int position;       // this token's position (RoPE angle)
+  int chunk_begin;    // first flat chunk index of this sequence in the launch
+  unsigned cache_bytes;  // bytes of each of k and v
+};
+
+struct AttnParams {
+  const float *qkv;   // [nseq][ld_qkv]: q (Hq*D) | k (Hk*D) | v (Hk*D)
+  long ld_qkv;
+  const float *gate;  // [nseq][ld_gate] gate logits
+  long ld_gate;
+  float *out;         // [nseq][ld_out] gated attention, head-major
+  long ld_out;
+  float *part_o;      // [total_chunks][Hq][D]   unnormalised partial outputs
+  float *part_ml;     // [total_chunks][Hq][2]   (running max in log2 units, sum)
+  int num_kv_heads;
+  int rotary_dim;
+  double theta;
+  float qscale;       // attention_scale * log2(e): scores come out in log2 units
+  int tile;           // rows per step (4 waves x tile/4 rows); kernels exist for 64 and 128
+  int chunk;          // rows per workgroup: a multiple of tile
+  int nseq;
+  int total_chunks;
+  SeqDesc seq[kMaxSeqPerLaunch];
+};
+
+struct GemvParams {
+  const uint16_t *w0; // bf16 [rows0][cols]
+  const uint16_t *w1; // bf16 [rows1][cols], rows appended after w0's
+  int rows0;
+  int rows1;
+  int cols;
+  int batch;
+  const float *x;     // [batch][ldx]
+  long ldx;
+  float *y0;          // [batch][ldy0] receives rows of w0
+  long ldy0;
+  float *y1;          // [batch][ldy1] receives rows of w1
+  long ldy1;
+};
+
+// Launchers (gqa_kernels.hip).  They return the hipError_t of the launch.
+hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
+hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
+hipError_t launch_rms_norm(const float *h, const uint16_t *w, float *out, int rows,
+                           int hidden, float eps, hipStream_t stream);
+hipError_t launch_residual_add(float *h, const float *o, int64_t n, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,217 @@
+/*
+ * gqa.h -- C ABI of the MI355X (gfx950) hybrid-window GQA decode attention block.
+ *
+ * The operation is the single-token decode attention block of the spark2_5
+ * family as stated on the docs.rs pages of turbospark-runtime 0.3.0:
+ *   [attn] src/families/spark/attn.rs  -- `encode_attention_block` (its steps,
+ *          in order), `rope_params_for` and its unit test, the module doc;
+ *   [mod]  src/families/spark/mod.rs   -- the module doc's transcription of one
+ *          decoder layer; `produce_real_spark_inner`'s layer loop;
+ *   [kvw]  src/kv_write.rs             -- `kv_write_target`, `encode_attention_any`.
+ *
+ * One call computes, for each of `batch` independent sequences b:
+ *   qkv   = W_qkv x_b              rows q (Hq*D) | k (Hk*D) | v (Hk*D)
+ *   g     = W_g x_b                one logit per query head, same x
+ *   q,k,v = split(qkv); k and v go straight into this token's cache slot
+ *   NeoX RoPE on q and on k (full layers: leading full_rotary_dim dims at
+ *           full_rope_theta; sliding layers: all head_dim dims at rope_theta;
+ *           the frequency divisor is the rotary width)
+ *   a_h   = softmax(scale * K q_h) V over the causal history (full layers) or
+ *           the last sliding_window positions read through a ring (sliding)
+ *   a_h  *= sigmoid(g_h)           headwise, before the output projection
+ *   out_b = W_o a
+ *
+ * Conventions for every entry point
+ *   - Pointers named "device" are device (HBM) addresses; "host" ones are CPU
+ *     addresses read before the call returns.  The caller owns all memory; the
+ *     library allocates nothing and keeps no state except a thread-local error
+ *     string.  Device memory must stay valid until the stream reaches the work.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.  Work
+ *     is enqueued asynchronously: a GQA_OK status says the arguments were valid
+ *     and the launches were accepted, not that the kernels have finished.
+ *   - Every argument is checked on the host BEFORE the first launch, so a call
+ *     that returns an error has enqueued nothing.  The library never aborts.
+ *   - Device pointers must be 16-byte aligned; row counts and sizes are in
+ *     elements unless a name ends in _bytes.
+ *   - Dtypes: weights bf16 (raw uint16 bit patterns), KV cache IEEE fp16,
+ *     activations and every intermediate fp32, accumulation fp32.
+ *   - Kernels specialise head_dim == 256 and num_heads == 4 * num_kv_heads;
+ *     other shapes return GQA_ERR_UNSUPPORTED.
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARGUMENT = 1,   /* a value violates the contract below      */
+  GQA_ERR_UNSUPPORTED = 2,        /* valid, but a shape the kernels lack      */
+  GQA_ERR_WORKSPACE_TOO_SMALL = 3,
+  GQA_ERR_GPU = 4                 /* a HIP call failed; see gqa_last_error()  */
+} gqa_status;
+
+/* Architecture fields the block reads ([attn] `encode_attention_block` reads
+ * hidden size, head counts, head dim, the full-layer mask, both thetas, the
+ * sliding window and the attention scale; `full_rotary_dim` comes from the
+ * family state).  Published values: num_heads 16, num_kv_heads 4, head_dim
+ * 256, full_rotary_dim 64, sliding_window 512, full_rope_theta 5e6,
+ * rope_theta 1e4, attention_scale 256^-0.5, rms_eps 1e-6 ([mod] module doc). */
+typedef struct {
+  int32_t hidden;            /* H: width of x and out                         */
+  int32_t num_heads;         /* Hq                                            */
+  int32_t num_kv_heads;      /* Hk                                            */
+  int32_t head_dim;          /* D                                             */
+  int32_t full_rotary_dim;   /* rotary width on full layers (even, <= D)      */
+  int32_t sliding_window;    /* attended positions on sliding layers (>= 1)   */
+  double full_rope_theta;    /* RoPE base on full layers (> 0)                */
+  double rope_theta;         /* RoPE base on sliding layers (> 0)             */
+  float attention_scale;     /* softmax scale (> 0, finite)                   */
+  float rms_eps;             /* RMSNorm epsilon, used by gqa_rms_norm_bf16w   */
+} gqa_arch;
+
+/* One layer's projection weights, bf16, row-major [out][in] so that y = W x
+ * ([attn] the GEMV calls pass rows = outputs, cols = inputs). Device, read-only. */
+typedef struct {
+  const void *q_k_v_proj;    /* [Hq*D + 2*Hk*D][H], rows q | k | v, head-major */
+  const void *g_proj;        /* [Hq][H]                                        */
+  const void *o_proj;        /* [H][Hq*D]                                      */
+} gqa_layer_weights;
+
+/* One sequence's K/V cache for this layer ([kvw] a slot is one position's row
+ * of Hk*D fp16 values; attention reads the layer buffer from row 0).
+ *   k, v        device fp16 [capacity][Hk][D]; the call WRITES row
+ *               gqa_kv_slot(position, ring_capacity) of both (this token's
+ *               RoPE'd k and its v) and reads only rows of the window.
+ *   capacity    rows allocated (>= 1).
+ *   ring_capacity  0: linear addressing, position < capacity required.
+ *               > 0: ring of that many slots (sliding layers only), with
+ *               sliding_window <= ring_capacity <= capacity.
+ *   position    this token's position (>= 0); seq_len = position + 1.
+ * Sequential positions and cache advancing stay with the caller. */
+typedef struct {
+  void *k;
+  void *v;
+  int32_t capacity;
+  int32_t ring_capacity;
+  int32_t position;
+  int32_t reserved;          /* must be 0 */
+} gqa_kv_seq;
+
+/* ---------------------------------------------------------------------------
+ * Pure host functions (no device access; usable without a GPU).
+ * ------------------------------------------------------------------------- */
+
+/* [attn] `rope_params_for`: full layers rotate the leading full_rotary_dim
+ * dims at full_theta; sliding layers rotate all head_dim dims at
+ * sliding_theta.  Outputs are host pointers; errors: null outputs, head_dim or
+ * full_rotary_dim < 2 or odd, full_rotary_dim > head_dim, a theta <= 0. */
+gqa_status gqa_rope_params_for(int is_full, int32_t full_rotary_dim, int32_t head_dim,
+                               double full_theta, double sliding_theta,
+                               int32_t *rotary_dim, double *theta);
+
+/* [attn] the window/ring step: seq_len = position + 1; full layers read
+ * [0, seq_len) linearly; sliding layers read [max(seq_len - window, 0),
+ * seq_len) and use ring addressing only when ring_capacity > 0 and
+ * seq_len > ring_capacity (active_ring = ring_capacity, else 0).
+ * Errors: null outputs, position < 0, sliding_window < 1, ring_capacity < 0,
+ * position == INT32_MAX. */
+gqa_status gqa_kv_window(int is_full, int32_t position, int32_t sliding_window,
+                         int32_t ring_capacity, int32_t *seq_len,
+                         int32_t *kv_start, int32_t *active_ring);
+
+/* Physical cache row of `position`: position mod ring_capacity on a ring,
+ * position itself when ring_capacity == 0 ([kvw] `kv_write_target` returns
+ * the slot of (layer, position)).  Returns -1 if position < 0 or
+ * ring_capacity < 0. */
+int32_t gqa_kv_slot(int32_t position, int32_t ring_capacity);
+
+/* Bytes of device workspace that gqa_attention_block_decode and
+ * gqa_attention_gated need for `batch` sequences whose seq_len is at most
+ * max_seq_len (an upper bound valid for every layer class). */
+gqa_status gqa_workspace_size(const gqa_arch *arch, int32_t batch, int32_t max_seq_len,
+                              size_t *bytes);
+
+/* ---------------------------------------------------------------------------
+ * The block.
+ * ------------------------------------------------------------------------- */
+
+/* [attn] `encode_attention_block`, for `batch` independent sequences that all
+ * use this layer's weights and class.
+ *   arch, weights   host structs (weights point to device memory)
+ *   is_full         1: full (causal) layer; 0: sliding-window layer
+ *   seqs            host array [batch] of this layer's caches
+ *   x_normed        device fp32 [batch][H]: the already-normed layer input
+ *   out             device fp32 [batch][H]: W_o (sigmoid-gated attention)
+ *   workspace       device, at least gqa_workspace_size(...) bytes for the
+ *                   largest seq_len in `seqs`; contents on entry are ignored
+ * Side effect: each sequence's cache slot row for `position` is written.
+ * x_normed and out must not overlap each other, the workspace or a cache. */
+gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weights *weights,
+                                      int is_full, const gqa_kv_seq *seqs, int32_t batch,
+                                      const float *x_normed, float *out, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Step entry points: the same kernels the block launches, exposed so each
+ * step can be checked and timed on its own.
+ * ------------------------------------------------------------------------- */
+
+/* [attn] the fused q_k_v_proj GEMV and the g_proj GEMV over the same input.
+ *   x       device fp32 [batch][H]
+ *   qkv     device fp32 [batch][Hq*D + 2*Hk*D]
+ *   gate_logits  device fp32 [batch][Hq] (before the sigmoid) */
+gqa_status gqa_qkv_gate_gemv(const gqa_arch *arch, const gqa_layer_weights *weights,
+                             int32_t batch, const float *x, float *qkv, float *gate_logits,
+                             void *stream);
+
+/* [attn] the split into the cache slots, the per-class RoPE of q and of k,
+ * the decode attention over the window, and the headwise sigmoid gate.
+ *   qkv          device fp32 [batch][Hq*D + 2*Hk*D] (projection output)
+ *   gate_logits  device fp32 [batch][Hq]
+ *   attn_gated   device fp32 [batch][Hq*D]: head h at [h*D, (h+1)*D)
+ *   seqs, is_full, workspace as for gqa_attention_block_decode.
+ * Side effect: the cache slot rows, as for the block. */
+gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs,
+                               int32_t batch, const float *qkv, const float *gate_logits,
+                               float *attn_gated, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* [attn] the o_proj GEMV: out[b] = W_o attn_gated[b].
+ *   attn_gated device fp32 [batch][Hq*D]; out device fp32 [batch][H]. */
+gqa_status gqa_o_proj_gemv(const gqa_arch *arch, const gqa_layer_weights *weights,
+                           int32_t batch, const float *attn_gated, float *out, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Layer-loop helpers around the block ([mod] `produce_real_spark_inner`: the
+ * input RMSNorm with a bf16 weight before the block, the raw residual add
+ * after it).
+ * ------------------------------------------------------------------------- */
+
+/* out[r][c] = h[r][c] / sqrt(mean_c(h[r][c]^2) + eps) * w[c], plain w.
+ *   h device fp32 [rows][hidden]; w device bf16 [hidden]; out device fp32
+ *   [rows][hidden] (may equal h).  eps >= 0, finite. */
+gqa_status gqa_rms_norm_bf16w(const float *h, const void *w, float *out, int32_t rows,
+                              int32_t hidden, float eps, void *stream);
+
+/* h[i] += o[i] for i < n (device fp32, n >= 0, no partial overlap). */
+gqa_status gqa_residual_add(float *h, const float *o, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics.
+ * ------------------------------------------------------------------------- */
+const char *gqa_status_string(gqa_status status);
+/* Detail of the last error on this thread ("" if none).  Valid until the next
+ * call into the library from this thread. */
+const char *gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

@@ -1,0 +1,336 @@
+"""HIP path against the fp64 oracle, through the C ABI (needs an MI355X).
+
+Floating point is held to rel-L2 <= 1e-3 and max-abs <= 5e-3 * max|ref|; the
+split, slot and ring/window indexing is held bit-exact (cache rows other than
+the slot are untouched bit for bit; the slot row is this token's k and v; the
+set of rows read is exactly the window).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_block_amd as gqa
+import oracle
+import synth
+from tests.gpu_util import (DevBlock, arch_of, assert_parity, bits_to_dev, check_caches,
+                            f16_to_dev, f32_to_dev, say)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on a CPU host only with -m gpu
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+# ----------------------------------------------------------------------------
+# projections
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hidden,batch", [(1024, 1), (2560, 1), (776, 3), (264, 5), (2560, 32),
+                                          (8192, 1), (4096, 2)])
+def test_qkv_gate_gemv(hidden, batch):
+    say(f"qkv_gate_gemv hidden={hidden} batch={batch}")
+    a = synth.Arch(hidden=hidden)
+    w_qkv = synth.random_bf16((a.qkv_rows, hidden), 0, 10, hidden)
+    w_g = synth.random_bf16((a.num_heads, hidden), 0, 10, hidden + 1)
+    x = synth.random_hidden(hidden, batch, 0, 10)
+    qkv = torch.empty((batch, a.qkv_rows), dtype=torch.float32, device="cuda")
+    gl = torch.empty((batch, a.num_heads), dtype=torch.float32, device="cuda")
+    gqa.qkv_gate_gemv(arch_of(a), bits_to_dev(w_qkv), bits_to_dev(w_g), f32_to_dev(x), qkv, gl)
+    torch.cuda.synchronize()
+    assert_parity(qkv.cpu().numpy(), oracle.gemv(oracle.bf16_bits_to_f64(w_qkv), x), "qkv")
+    assert_parity(gl.cpu().numpy(), oracle.gemv(oracle.bf16_bits_to_f64(w_g), x), "gate logits")
+
+
+@pytest.mark.parametrize("hidden,batch", [(1024, 1), (2560, 1), (776, 3), (2560, 32), (6144, 2)])
+def test_o_proj_gemv(hidden, batch):
+    say(f"o_proj_gemv hidden={hidden} batch={batch}")
+    a = synth.Arch(hidden=hidden)
+    w_o = synth.random_bf16((hidden, a.q_dim), 0, 11, hidden)
+    attn = synth.random_hidden(a.q_dim, batch, 0, 11)
+    out = torch.empty((batch, hidden), dtype=torch.float32, device="cuda")
+    gqa.o_proj_gemv(arch_of(a), bits_to_dev(w_o), f32_to_dev(attn), out)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), oracle.gemv(oracle.bf16_bits_to_f64(w_o), attn), "o_proj")
+
+
+# ----------------------------------------------------------------------------
+# split + RoPE + KV write + attention + gate, from a given qkv
+# ----------------------------------------------------------------------------
+
+# (name, is_full, positions, ring_capacity, capacities or None)
+ATTN_CASES = [
+    ("full_pos0_single_key", True, [0], 0, None),
+    ("full_pos1", True, [1], 0, None),
+    ("full_pos63", True, [63], 0, None),
+    ("full_pos64", True, [64], 0, None),
+    ("full_pos1000_ragged", True, [1000], 0, None),
+    ("full_pos4095", True, [4095], 0, None),
+    ("full_pos20000_multitile", True, [20000], 0, None),
+    ("full_pos32767", True, [32767], 0, None),
+    ("full_cap_larger", True, [700], 0, [2048]),
+    ("sliding_linear_pos63", False, [63], 0, [64]),
+    ("sliding_linear_pos1000", False, [1000], 0, None),
+    ("ring_pos0", False, [0], 512, None),
+    ("ring_pos100", False, [100], 512, None),
+    ("ring_pos510", False, [510], 512, None),
+    ("ring_pos511", False, [511], 512, None),
+    ("ring_pos512", False, [512], 512, None),
+    ("ring_pos513", False, [513], 512, None),
+    ("ring_pos1000", False, [1000], 512, None),
+    ("ring_pos32767", False, [32767], 512, None),
+    ("ring_pos32905", False, [32768 + 137], 512, None),
+    ("ring640_pos2000", False, [2000], 640, None),
+    ("ring_cap_larger", False, [3000], 512, [1024]),
+    ("full_batch_mixed", True, [0, 5, 63, 64, 65, 1000, 4095], 0, None),
+    ("ring_batch_mixed", False, [3, 511, 512, 777, 32767], 512, None),
+    ("full_batch33_two_launches", True, list(range(7, 7 + 33 * 37, 37)), 0, None),
+]
+
+
+def _attn_inputs(name, is_full, positions, ring, caps, case_id):
+    arch = synth.Arch(hidden=1024)
+    seqs = []
+    for i, p in enumerate(positions):
+        cap = caps[i] if caps else (ring if ring else p + 1)
+        seqs.append(synth.make_cache(arch, 0, case_id, 100 + 16 * i, cap, ring, p))
+    case = synth.BlockCase(name=name, arch=arch, is_full=is_full, w_qkv=None, w_g=None,
+                           w_o=None, x=np.zeros((len(positions), 1), np.float32), seqs=seqs)
+    qkv = synth.random_qkv(arch, len(positions), 0, case_id)
+    gl = synth.random_gate_logits(arch, len(positions), 0, case_id)
+    return arch, case, qkv, gl
+
+
+def _run_attention(arch, case, qkv, gl):
+    ga = arch_of(arch)
+    k = [f16_to_dev(s.k) for s in case.seqs]
+    v = [f16_to_dev(s.v) for s in case.seqs]
+    seqs = [gqa.KvSeq(k=k[i], v=v[i], position=s.position, ring_capacity=s.ring_capacity)
+            for i, s in enumerate(case.seqs)]
+    ws = torch.empty(gqa.workspace_size(ga, len(seqs), max(s.position + 1 for s in case.seqs)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((len(seqs), ga.q_dim), dtype=torch.float32, device="cuda")
+    gqa.attention_gated(ga, case.is_full, seqs, f32_to_dev(qkv), f32_to_dev(gl), out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), k, v
+
+
+@pytest.mark.parametrize("name,is_full,positions,ring,caps", ATTN_CASES,
+                         ids=[c[0] for c in ATTN_CASES])
+def test_attention_gated(name, is_full, positions, ring, caps):
+    say(f"attention_gated {name} positions={positions[:8]} ring={ring}")
+    arch, case, qkv, gl = _attn_inputs(name, is_full, positions, ring, caps, 20)
+    got, k, v = _run_attention(arch, case, qkv, gl)
+    ref = oracle.attention_step(arch, is_full, qkv, gl, case.seqs)
+    for b in range(len(positions)):
+        assert_parity(got[b], ref.gated[b], f"{name}[{b}] gated attention")
+    check_caches(case, k, v, ref.k16, ref.v16, ref.slots, name, exact_v=True)
+
+
+# ----------------------------------------------------------------------------
+# bit-exact row set: which rows are read, and how many
+# ----------------------------------------------------------------------------
+
+ROWSET_CASES = [
+    ("full_pos300_cap512", True, 300, 0, 512),
+    ("sliding_linear_pos1000", False, 1000, 0, 1001),
+    ("ring_pos511", False, 511, 512, 512),
+    ("ring_pos512", False, 512, 512, 512),
+    ("ring_pos513", False, 513, 512, 512),
+    ("ring_pos1000", False, 1000, 512, 512),
+    ("ring_pos32905", False, 32768 + 137, 512, 512),
+    ("ring640_pos1500", False, 1500, 640, 640),
+    ("full_pos0", True, 0, 0, 4),
+]
+
+
+def _rowset_inputs(is_full, pos, ring, cap, onehot_row=None):
+    """q = 0, gate logit +30 (sigmoid rounds to 1.0f), V = 1 on every row of the
+    window (or one-hot on one row), NaN on every row outside it."""
+    arch = synth.Arch(hidden=1024)
+    hk, d = arch.num_kv_heads, arch.head_dim
+    sl, ks, ar = oracle.kv_window(is_full, pos, arch.sliding_window, ring)
+    owner = {}
+    for t in range(pos):                       # rows written before this token
+        owner[t % ring if ring else t] = t
+    rng = np.random.default_rng([3, pos, ring, cap])
+    k = rng.standard_normal((cap, hk, d)).astype(np.float16)
+    v = np.ones((cap, hk, d), np.float16)
+    slot = oracle.kv_slot(pos, ring)
+    for r in range(cap):
+        t = owner.get(r, -1)
+        if r != slot and not (ks <= t < sl):
+            k[r] = np.nan
+            v[r] = np.nan
+    qkv = np.zeros((1, arch.qkv_rows), np.float32)
+    qkv[0, arch.q_dim:arch.q_dim + arch.kv_dim] = rng.standard_normal(arch.kv_dim)
+    qkv[0, arch.q_dim + arch.kv_dim:] = 1.0    # this token's v
+    if onehot_row is not None:
+        v[:] = np.where(np.isnan(v), v, np.float16(0))
+        qkv[0, arch.q_dim + arch.kv_dim:] = 0.0
+        if onehot_row == slot:
+            qkv[0, arch.q_dim + arch.kv_dim:] = 1.0
+        else:
+            v[onehot_row] = 1.0
+    gl = np.full((1, arch.num_heads), 30.0, np.float32)
+    seq = synth.SeqCache(k=k, v=v, ring_capacity=ring, position=pos)
+    case = synth.BlockCase(name="rowset", arch=arch, is_full=is_full, w_qkv=None, w_g=None,
+                           w_o=None, x=np.zeros((1, 1), np.float32), seqs=[seq])
+    return arch, case, qkv, gl, sl - ks, owner, (ks, sl)
+
+
+@pytest.mark.parametrize("name,is_full,pos,ring,cap", ROWSET_CASES, ids=[c[0] for c in ROWSET_CASES])
+def test_rows_read_are_exactly_the_window(name, is_full, pos, ring, cap):
+    say(f"rowset {name}")
+    arch, case, qkv, gl, n, owner, (ks, sl) = _rowset_inputs(is_full, pos, ring, cap)
+    got, _, _ = _run_attention(arch, case, qkv, gl)
+    # any row outside the window would bring a NaN in; all in-window rows are 1
+    assert np.array_equal(got[0], np.ones_like(got[0])), f"{name}: {got[0][:4]}"
+    # one-hot V on the oldest in-window row: output 1/n recovers n exactly
+    slot = oracle.kv_slot(pos, ring)
+    oldest = slot if n == 1 else [r for r, t in owner.items() if t == ks][0]
+    arch, case, qkv, gl, n2, _, _ = _rowset_inputs(is_full, pos, ring, cap, onehot_row=oldest)
+    got, _, _ = _run_attention(arch, case, qkv, gl)
+    assert np.all(np.abs(got[0] * n - 1.0) < 4e-7), f"{name}: {got[0][0]} vs 1/{n}"
+    assert int(round(1.0 / float(got[0][0]))) == n
+
+
+@pytest.mark.parametrize("pos", [511, 512, 513, 1000, 32768 + 137])
+def test_ring_equals_linear_bitwise(pos):
+    """The same last-512 rows through a 512-slot ring and through a linear
+    cache give bit-identical results (one reduction order)."""
+    say(f"ring==linear pos={pos}")
+    arch = synth.Arch(hidden=1024)
+    hk, d = arch.num_kv_heads, arch.head_dim
+    rng = np.random.default_rng([4, pos])
+    lo = max(0, pos - 511)
+    lin_k = np.zeros((pos + 1, hk, d), np.float16)
+    lin_v = np.zeros((pos + 1, hk, d), np.float16)
+    lin_k[lo:] = rng.standard_normal((pos + 1 - lo, hk, d))
+    lin_v[lo:] = rng.standard_normal((pos + 1 - lo, hk, d))
+    ring_k = np.zeros((512, hk, d), np.float16)
+    ring_v = np.zeros((512, hk, d), np.float16)
+    for t in range(lo, pos + 1):
+        ring_k[t % 512], ring_v[t % 512] = lin_k[t], lin_v[t]
+    qkv = synth.random_qkv(arch, 1, 0, 30)
+    gl = synth.random_gate_logits(arch, 1, 0, 30)
+    outs = []
+    for k, v, ring in ((lin_k, lin_v, 0), (ring_k, ring_v, 512)):
+        seq = synth.SeqCache(k=k, v=v, ring_capacity=ring, position=pos)
+        case = synth.BlockCase(name="rl", arch=arch, is_full=False, w_qkv=None, w_g=None,
+                               w_o=None, x=np.zeros((1, 1), np.float32), seqs=[seq])
+        outs.append(_run_attention(arch, case, qkv, gl)[0])
+    assert np.array_equal(outs[0].view(np.int32), outs[1].view(np.int32))
+
+
+# ----------------------------------------------------------------------------
+# the whole block on the named workloads
+# ----------------------------------------------------------------------------
+
+BLOCK_CASES = ["cfg1", "cfg2", "cfg3", "cfg5", "full32k"]
+
+
+@pytest.mark.parametrize("name", BLOCK_CASES)
+def test_block_matches_oracle(name):
+    case = synth.NAMED_BLOCK_CASES[name]()
+    say(f"block {case.name} batch={case.batch} positions={[s.position for s in case.seqs][:6]}")
+    dev = DevBlock(case)
+    out = dev.run_block()
+    ref = oracle.block_decode(case.arch, case.is_full, case.w_qkv, case.w_g, case.w_o, case.x,
+                              case.seqs)
+    assert_parity(out, ref.out, f"{name} block output")
+    check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, name)
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3"])
+def test_block_equals_its_steps_bitwise(name):
+    """The block entry point and the three step entry points run the same
+    kernels on the same data: results are bit-identical, and repeatable."""
+    case = synth.NAMED_BLOCK_CASES[name]()
+    say(f"block==steps {case.name}")
+    dev = DevBlock(case)
+    out_block = dev.run_block()
+    dev2 = DevBlock(case)
+    a = dev2.arch
+    b = case.batch
+    qkv = torch.empty((b, a.qkv_rows), dtype=torch.float32, device="cuda")
+    gl = torch.empty((b, a.num_heads), dtype=torch.float32, device="cuda")
+    attn = torch.empty((b, a.q_dim), dtype=torch.float32, device="cuda")
+    out = torch.empty((b, a.hidden), dtype=torch.float32, device="cuda")
+    gqa.qkv_gate_gemv(a, dev2.w_qkv, dev2.w_g, dev2.x, qkv, gl)
+    gqa.attention_gated(a, case.is_full, dev2.seqs(), qkv, gl, attn, dev2.ws)
+    gqa.o_proj_gemv(a, dev2.w_o, attn, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.int32), out_block.view(np.int32))
+    for i in range(b):
+        assert torch.equal(dev.k[i], dev2.k[i]) and torch.equal(dev.v[i], dev2.v[i])
+    out_again = DevBlock(case).run_block()
+    assert np.array_equal(out_again.view(np.int32), out_block.view(np.int32))
+
+
+def test_batch_zero_is_a_no_op():
+    say("batch 0")
+    a = gqa.Arch(hidden=1024)
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    x = torch.full((1, 1024), 7.0, dtype=torch.float32, device="cuda")
+    w_qkv = torch.zeros((a.qkv_rows, 1024), dtype=torch.int16, device="cuda")
+    w_g = torch.zeros((a.num_heads, 1024), dtype=torch.int16, device="cuda")
+    w_o = torch.zeros((1024, a.q_dim), dtype=torch.int16, device="cuda")
+    gqa.attention_block_decode(a, w_qkv, w_g, w_o, True, [], x, x, ws)
+    torch.cuda.synchronize()
+    assert torch.all(x == 7.0)
+
+
+# ----------------------------------------------------------------------------
+# the 36-layer attention-only stack (config 4): compare the residual delta
+# ----------------------------------------------------------------------------
+
+def _run_stack(case: synth.StackCase):
+    a = arch_of(case.arch)
+    hid = a.hidden
+    h = f32_to_dev(case.h)
+    h0 = h.clone()
+    xn = torch.empty_like(h)
+    o = torch.empty_like(h)
+    ws = torch.empty(gqa.workspace_size(a, 1, case.layers[0].cache.position + 1),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for li, L in enumerate(case.layers):
+        k, v = f16_to_dev(L.cache.k), f16_to_dev(L.cache.v)
+        gqa.rms_norm_bf16w(h, bits_to_dev(L.w_norm), xn, a.rms_eps)
+        gqa.attention_block_decode(a, bits_to_dev(L.w_qkv), bits_to_dev(L.w_g), bits_to_dev(L.w_o),
+                                   L.is_full, [gqa.KvSeq(k=k, v=v, position=L.cache.position,
+                                                         ring_capacity=L.cache.ring_capacity)],
+                                   xn, o, ws)
+        outs.append(o.cpu().numpy().copy())
+        gqa.residual_add(h, o)
+    torch.cuda.synchronize()
+    return (h - h0).cpu().numpy(), outs
+
+
+@pytest.mark.parametrize("phase_full_first", [False, True])
+def test_stack_delta_matches_oracle(phase_full_first):
+    case = synth.cfg4_stack(phase_full_first=phase_full_first)
+    say(f"stack {case.name} phase_full_first={phase_full_first}")
+    delta, outs = _run_stack(case)
+    ref = oracle.stack_decode(case.arch, case.h, case.layers)
+    assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "stack residual delta")
+    for li in range(len(case.layers)):
+        assert_parity(outs[li], ref.block_outs[li], f"stack layer {li} block output")
+
+
+def test_rms_norm_and_residual_add():
+    say("rms_norm + residual_add")
+    hidden, rows = 2560, 3
+    h = synth.random_hidden(hidden, rows, 0, 40)
+    w = synth.random_bf16((hidden,), 0, 40, 7, std=0.1, mean=1.0)
+    out = torch.empty((rows, hidden), dtype=torch.float32, device="cuda")
+    hd = f32_to_dev(h)
+    gqa.rms_norm_bf16w(hd, bits_to_dev(w), out, 1e-6)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), oracle.rms_norm(h, w, 1e-6), "rms_norm")
+    o = synth.random_hidden(hidden, rows, 0, 41)
+    gqa.residual_add(hd, f32_to_dev(o))
+    torch.cuda.synchronize()
+    assert np.array_equal(hd.cpu().numpy(), (h + o).astype(np.float32))

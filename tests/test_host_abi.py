@@ -1,0 +1,199 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+symbol include/gqa.h declares, its pure functions agree bit for bit with the
+oracle and the golden fixtures, and every invalid argument is refused before
+anything is launched (a launch here, with no GPU, could only fail as
+GQA_ERR_GPU, so an INVALID/UNSUPPORTED/WORKSPACE status proves the check ran
+first)."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import gqa_attention_block_amd as gqa
+from gqa_attention_block_amd import binding as B
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, GPU = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.library_path())
+    names = declared_functions()
+    assert len(names) >= 12
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(B.EXPORTED_SYMBOLS) == names
+
+
+def test_rope_params_golden():
+    for c in json.load(open(os.path.join(GOLDEN, "rope_params_for.json")))["cases"]:
+        assert gqa.rope_params_for(c["is_full"], c["full_rotary_dim"], c["head_dim"],
+                                   c["full_theta"], c["sliding_theta"]) == (c["rotary_dim"], c["theta"])
+
+
+def test_kv_window_golden():
+    for full, pos, win, ring, sl, ks, ar, slot in json.load(
+            open(os.path.join(GOLDEN, "kv_window_cases.json")))["cases"]:
+        assert gqa.kv_window(full, pos, win, ring) == (sl, ks, ar)
+        assert gqa.kv_slot(pos, 0 if full else ring) == slot
+
+
+def test_kv_window_and_slot_match_oracle_exhaustively():
+    for window, ring in ((512, 512), (512, 0), (512, 640), (6, 6), (1, 1), (7, 30)):
+        for pos in range(0, 2100):
+            for full in (True, False):
+                r = 0 if full else ring
+                assert gqa.kv_window(full, pos, window, r) == oracle.kv_window(full, pos, window, r)
+            assert gqa.kv_slot(pos, ring) == oracle.kv_slot(pos, ring)
+    for pos in (32767, 32768 + 137, 2 ** 31 - 2):
+        assert gqa.kv_window(False, pos, 512, 512) == oracle.kv_window(False, pos, 512, 512)
+
+
+def test_host_function_errors():
+    with pytest.raises(gqa.GqaError):
+        gqa.kv_window(False, -1, 512, 512)
+    with pytest.raises(gqa.GqaError):
+        gqa.kv_window(False, 2 ** 31 - 1, 512, 512)
+    with pytest.raises(gqa.GqaError):
+        gqa.kv_window(False, 5, 0, 512)
+    with pytest.raises(gqa.GqaError):
+        gqa.rope_params_for(True, 63, 256, 5e6, 1e4)
+    with pytest.raises(gqa.GqaError):
+        gqa.rope_params_for(True, 512, 256, 5e6, 1e4)
+    with pytest.raises(gqa.GqaError):
+        gqa.rope_params_for(False, 64, 256, 5e6, -1.0)
+    assert gqa.kv_slot(-1, 512) == -1
+    assert gqa.kv_slot(5, -1) == -1
+
+
+def test_workspace_size_grows_with_batch_and_length():
+    a = gqa.Arch(hidden=2560)
+    s1 = gqa.workspace_size(a, 1, 4096)
+    assert gqa.workspace_size(a, 1, 32768) > s1
+    assert gqa.workspace_size(a, 32, 4096) > s1
+    with pytest.raises(gqa.GqaError):
+        gqa.workspace_size(a, 1, 0)
+    with pytest.raises(gqa.GqaError):
+        gqa.workspace_size(gqa.Arch(hidden=2560, head_dim=128), 1, 10)
+
+
+# ----------------------------------------------------------------------------
+# argument validation of the device entry points, with fake device pointers
+# that are never dereferenced (the checks must fail first)
+# ----------------------------------------------------------------------------
+
+FAKE = 0x7F0000000000          # 16-byte aligned, never touched
+MISALIGNED = FAKE + 8
+
+
+def _call_block(arch=None, is_full=1, seqs=None, batch=1, x=FAKE, out=FAKE + 0x100000,
+                ws=FAKE + 0x200000, ws_bytes=1 << 30, weights=None):
+    a = B.c_arch(arch or gqa.Arch(hidden=1024))
+    w = weights or B.c_weights(FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000)
+    if seqs is None:
+        seqs = [B.c_kv_seq(FAKE + 0x600000, FAKE + 0x700000, 100, 0, 50, 0)]
+    arr = B.c_seq_array(len(seqs))
+    for i, s in enumerate(seqs):
+        arr[i] = s
+    st = B.raw_call("gqa_attention_block_decode", ctypes.byref(a), ctypes.byref(w), is_full, arr,
+                    batch, x, out, ws, ws_bytes, None)
+    return st, B.last_error()
+
+
+def _seq(k=FAKE + 0x600000, v=FAKE + 0x700000, cap=100, ring=0, pos=50, reserved=0):
+    return B.c_kv_seq(k, v, cap, ring, pos, reserved)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(arch=gqa.Arch(hidden=1024, head_dim=128)), UNSUPPORTED),
+    (dict(arch=gqa.Arch(hidden=1024, num_heads=8)), UNSUPPORTED),
+    (dict(arch=gqa.Arch(hidden=1024, num_heads=15)), INVALID),
+    (dict(arch=gqa.Arch(hidden=1020)), INVALID),
+    (dict(arch=gqa.Arch(hidden=16384)), UNSUPPORTED),
+    (dict(arch=gqa.Arch(hidden=1024, full_rotary_dim=63)), INVALID),
+    (dict(arch=gqa.Arch(hidden=1024, full_rotary_dim=512)), INVALID),
+    (dict(arch=gqa.Arch(hidden=1024, sliding_window=0)), INVALID),
+    (dict(arch=gqa.Arch(hidden=1024, rope_theta=0.0)), INVALID),
+    (dict(arch=gqa.Arch(hidden=1024, attention_scale=float("inf"))), INVALID),
+    (dict(batch=-1), INVALID),
+    (dict(x=0), INVALID),
+    (dict(x=MISALIGNED), INVALID),
+    (dict(out=0), INVALID),
+    (dict(ws=0), INVALID),
+    (dict(ws_bytes=1024), WS_SMALL),
+    (dict(weights=B.c_weights(0, FAKE, FAKE)), INVALID),
+    (dict(weights=B.c_weights(FAKE, FAKE, MISALIGNED)), INVALID),
+    (dict(seqs=[_seq(pos=100, cap=100)]), INVALID),            # linear cache too short
+    (dict(seqs=[_seq(pos=-1)]), INVALID),
+    (dict(seqs=[_seq(k=0)]), INVALID),
+    (dict(seqs=[_seq(v=MISALIGNED)]), INVALID),
+    (dict(seqs=[_seq(reserved=1)]), INVALID),
+    (dict(seqs=[_seq(cap=0)]), INVALID),
+    (dict(is_full=1, seqs=[_seq(cap=512, ring=512)]), INVALID),   # full layers have no ring
+    (dict(is_full=0, seqs=[_seq(cap=511, ring=511)]), INVALID),   # ring < window
+    (dict(is_full=0, seqs=[_seq(cap=512, ring=600)]), INVALID),   # ring > capacity
+    (dict(is_full=1, seqs=[_seq(cap=2 ** 20 + 1, pos=5)]), UNSUPPORTED),  # > 2 GiB cache
+    (dict(is_full=1, seqs=[_seq(), _seq(pos=200)]), INVALID),  # second sequence bad
+])
+def test_block_rejects_before_launch(kw, status):
+    batch = len(kw.get("seqs", [None]))
+    if "batch" in kw:
+        batch = kw.pop("batch")
+    st, msg = _call_block(batch=batch, **kw)
+    assert st == status, (st, msg)
+    assert msg, "an error must leave a message"
+
+
+def test_null_seqs_and_null_arch():
+    a = B.c_arch(gqa.Arch(hidden=1024))
+    w = B.c_weights(FAKE, FAKE, FAKE)
+    assert B.raw_call("gqa_attention_block_decode", None, ctypes.byref(w), 1, None, 1, FAKE, FAKE,
+                      FAKE, 1 << 30, None) == INVALID
+    assert B.raw_call("gqa_attention_block_decode", ctypes.byref(a), ctypes.byref(w), 1, None, 1,
+                      FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+
+
+def test_step_entry_points_validate():
+    a = B.c_arch(gqa.Arch(hidden=1024))
+    w = B.c_weights(FAKE, FAKE, FAKE)
+    assert B.raw_call("gqa_qkv_gate_gemv", ctypes.byref(a), ctypes.byref(w), 1, MISALIGNED, FAKE,
+                      FAKE, None) == INVALID
+    assert B.raw_call("gqa_qkv_gate_gemv", ctypes.byref(a), ctypes.byref(w), 0, 0, 0, 0, None) == OK
+    assert B.raw_call("gqa_o_proj_gemv", ctypes.byref(a), ctypes.byref(B.c_weights(FAKE, FAKE, 0)),
+                      1, FAKE, FAKE, None) == INVALID
+    arr = B.c_seq_array(1)
+    arr[0] = _seq(pos=100, cap=100)
+    assert B.raw_call("gqa_attention_gated", ctypes.byref(a), 1, arr, 1, FAKE, FAKE, FAKE, FAKE,
+                      1 << 30, None) == INVALID
+    arr[0] = _seq()
+    assert B.raw_call("gqa_attention_gated", ctypes.byref(a), 1, arr, 1, FAKE, FAKE, FAKE, FAKE,
+                      16, None) == WS_SMALL
+    assert B.raw_call("gqa_rms_norm_bf16w", FAKE, FAKE, FAKE, 1, 0, ctypes.c_float(1e-6),
+                      None) == INVALID
+    assert B.raw_call("gqa_rms_norm_bf16w", FAKE, FAKE, FAKE, 1, 8, ctypes.c_float(-1.0),
+                      None) == INVALID
+    assert B.raw_call("gqa_rms_norm_bf16w", FAKE, FAKE, FAKE, 0, 8, ctypes.c_float(1e-6),
+                      None) == OK
+    assert B.raw_call("gqa_residual_add", FAKE, MISALIGNED, 10, None) == INVALID
+    assert B.raw_call("gqa_residual_add", FAKE, FAKE, -1, None) == INVALID
+    assert B.raw_call("gqa_residual_add", 0, 0, 0, None) == OK
+
+
+def test_status_strings():
+    assert B.status_string(0) == "GQA_OK"
+    assert B.status_string(3) == "GQA_ERR_WORKSPACE_TOO_SMALL"
+    assert B.status_string(99) == "GQA_ERR_UNKNOWN"
