@@ -65,8 +65,12 @@ def assert_parity(got, ref, what: str):
     return r, m
 
 
-def assert_fp16_within_one_ulp(got16: np.ndarray, ref16: np.ndarray, what: str):
-    """Both fp16; equal, or adjacent representable values (one rounding apart)."""
+def assert_fp16_within_one_ulp(got16: np.ndarray, ref16: np.ndarray, what: str,
+                               row_scale: float = 0.0):
+    """Both fp16: equal or one rounding apart.  A value produced by
+    cancellation (k_i cos - k_j sin near 0) may differ by more, up to the fp32
+    evaluation error of its inputs: 2^-18 * row_scale (the row's max |value|)
+    on top of one ulp."""
     g = np.asarray(got16, np.float16)
     r = np.asarray(ref16, np.float16)
     assert g.shape == r.shape, what
@@ -76,7 +80,14 @@ def assert_fp16_within_one_ulp(got16: np.ndarray, ref16: np.ndarray, what: str):
     go = np.where(gi < 0, -(gi & 0x7FFF), gi)
     ro = np.where(ri < 0, -(ri & 0x7FFF), ri)
     d = np.abs(go - ro)
-    assert int(d.max(initial=0)) <= 1, f"{what}: {int((d > 1).sum())} values more than 1 ulp apart"
+    far = d > 1
+    if far.any():
+        ulp = np.spacing(np.abs(r).astype(np.float16)).astype(np.float64)
+        diff = np.abs(g.astype(np.float64) - r.astype(np.float64))
+        ok = diff <= ulp + 2.0 ** -18 * row_scale
+        assert np.all(ok | ~far), (f"{what}: {int((far & ~ok).sum())} values beyond one ulp "
+                                   f"+ 2^-18*{row_scale:.3g}")
+    assert far.sum() <= max(2, 0.01 * far.size), f"{what}: {int(far.sum())} values more than 1 ulp apart"
 
 
 class DevBlock:
@@ -122,9 +133,11 @@ def check_caches(case: synth.BlockCase, k_dev, v_dev, k16_ref, v16_ref, slots, w
             f"{what}[{i}]: K rows other than slot {slot} changed"
         assert np.array_equal(vg[mask].view(np.int16), s.v[mask].view(np.int16)), \
             f"{what}[{i}]: V rows other than slot {slot} changed"
-        assert_fp16_within_one_ulp(kg[slot], k16_ref[i], f"{what}[{i}] K slot row")
+        kscale = float(np.max(np.abs(np.asarray(k16_ref[i], np.float64))))
+        assert_fp16_within_one_ulp(kg[slot], k16_ref[i], f"{what}[{i}] K slot row", kscale)
         if exact_v:
             assert np.array_equal(vg[slot].view(np.int16), np.asarray(v16_ref[i]).view(np.int16)), \
                 f"{what}[{i}] V slot row not bitwise equal"
         else:
-            assert_fp16_within_one_ulp(vg[slot], v16_ref[i], f"{what}[{i}] V slot row")
+            vscale = float(np.max(np.abs(np.asarray(v16_ref[i], np.float64))))
+            assert_fp16_within_one_ulp(vg[slot], v16_ref[i], f"{what}[{i}] V slot row", vscale)
