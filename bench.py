@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight/cache copies rotated (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample length (0 skips the baseline)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per step instead of launching from the host")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -172,39 +174,74 @@ def main():
                      dtype=torch.uint8, device="cuda:0")
     torch.cuda.synchronize()
 
-    def step(i):
-        s = sets[i % copies]
+    def block_step(c):
+        s = sets[c]
         gqa.attention_block_decode(a, s["w_qkv"], s["w_g"], s["w_o"], case.is_full, s["seqs"],
                                    x, out, ws)
 
+    # dominant kernel: the attention step (split/RoPE/slot write, split-K
+    # attention, combine + gate), on a qkv produced once by the GEMV
+    qkv = torch.empty((case.batch, a.qkv_rows), dtype=torch.float32, device="cuda:0")
+    gl = torch.empty((case.batch, a.num_heads), dtype=torch.float32, device="cuda:0")
+    attn = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda:0")
+    gqa.qkv_gate_gemv(a, sets[0]["w_qkv"], sets[0]["w_g"], x, qkv, gl)
+
+    def attn_step(c):
+        gqa.attention_gated(a, case.is_full, sets[c]["seqs"], qkv, gl, attn, ws)
+
+    for c in range(copies):          # eager warm-up of every copy (also caches the CU count)
+        block_step(c)
+        attn_step(c)
+    torch.cuda.synchronize()
+
+    if not args.graph:
+        run_block = block_step
+        run_attn = attn_step
+    else:
+        # one HIP graph per copy: a decode step is replayed the way a serving
+        # loop would replay it, without per-kernel host launch cost
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        gb, ga = [], []
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    block_step(c)
+                gb.append(g)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    attn_step(c)
+                ga.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        run_block = lambda c: gb[c].replay()   # noqa: E731
+        run_attn = lambda c: ga[c].replay()    # noqa: E731
+
     for i in range(args.warmup):
-        step(i)
+        run_block(i % copies)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        run_block(i % copies)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert torch.isfinite(out).all(), "non-finite block output"
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_s = case.batch * args.steps / elapsed
     bb = block_bytes(case)
-    log(f"block: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.1f} tokens/s, "
-        f"{bb / 1e6:.2f} MB/step -> {bb / (ms_per_step * 1e-3) / 1e9:.1f} GB/s")
+    log(f"block ({'graph' if args.graph else 'eager'}): {ms_per_step * 1e3:.2f} us/step, "
+        f"{tokens_per_s:.1f} tokens/s, {bb / 1e6:.2f} MB/step -> "
+        f"{bb / (ms_per_step * 1e-3) / 1e9:.1f} GB/s")
 
-    # dominant kernel: the attention step, timed alone with HIP events
-    qkv = torch.empty((case.batch, a.qkv_rows), dtype=torch.float32, device="cuda:0")
-    gl = torch.empty((case.batch, a.num_heads), dtype=torch.float32, device="cuda:0")
-    attn = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda:0")
-    gqa.qkv_gate_gemv(a, sets[0]["w_qkv"], sets[0]["w_g"], x, qkv, gl)
     n_att = max(args.steps, 20)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_att)]
     for i in range(args.warmup):
-        gqa.attention_gated(a, case.is_full, sets[i % copies]["seqs"], qkv, gl, attn, ws)
+        run_attn(i % copies)
     for i in range(n_att):
         evs[i][0].record()
-        gqa.attention_gated(a, case.is_full, sets[i % copies]["seqs"], qkv, gl, attn, ws)
+        run_attn(i % copies)
         evs[i][1].record()
     torch.cuda.synchronize()
     att_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
@@ -231,7 +268,8 @@ def main():
         "config": {"workload": case.name, "hidden": a.hidden, "batch": case.batch,
                    "positions": [s.position for s in case.seqs][:4],
                    "kv_rows_attended": attended_rows(case), "weights": "bf16",
-                   "kv_cache": "fp16", "block_bytes_per_step": bb, "copies_rotated": copies},
+                   "kv_cache": "fp16", "block_bytes_per_step": bb, "copies_rotated": copies,
+                   "launch": "hip_graph" if args.graph else "eager"},
         "block_hbm_gbs": round(bb / (ms_per_step * 1e-3) / 1e9, 1),
         "block_frac_of_peak": round(bb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,

@@ -325,7 +325,7 @@ gqa_status run_attention(const gqa_arch *a, int is_full, const std::vector<SeqDe
     p.part_ml = part_ml;
     p.num_kv_heads = a->num_kv_heads;
     p.rotary_dim = rdim;
-    p.theta = theta;
+    p.log2_theta = log2(theta);
     p.qscale = (float)((double)a->attention_scale * kLog2e);
     p.tile = plan.tile;
     p.chunk = plan.chunk;

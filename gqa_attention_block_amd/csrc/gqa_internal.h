@@ -43,7 +43,7 @@ struct AttnParams {
   float *part_ml;     // [total_chunks][Hq][2]   (running max in log2 units, sum)
   int num_kv_heads;
   int rotary_dim;
-  double theta;
+  double log2_theta;  // log2 of the RoPE base of this layer class
   float qscale;       // attention_scale * log2(e): scores come out in log2 units
   int tile;           // rows per step (4 waves x tile/4 rows); kernels exist for 64 and 128
   int chunk;          // rows per workgroup: a multiple of tile

@@ -169,31 +169,87 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Batch-1 GEMV.  NIT is exactly ceil(cols/512), so no registers hold loads
+// that would only return zeros; x (the lane's 8*NIT columns) stays in
+// registers for the wave's R rows.  Fewer registers than the batched kernel
+// means more resident waves per CU and more bytes in flight.
+// ---------------------------------------------------------------------------
+template <int R, int NIT>
+__global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int total = p.rows0 + p.rows1;
+  const int row0 = wave * R;
+  if (row0 >= total) return;
+  const unsigned row_bytes = (unsigned)p.cols * 2u;
+  const __amdgpu_buffer_rsrc_t r0 = make_rsrc(p.w0, (unsigned)p.rows0 * row_bytes);
+  const __amdgpu_buffer_rsrc_t r1 = make_rsrc(p.w1, (unsigned)p.rows1 * row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)p.cols * 4u);
+
+  uint4 w[R][NIT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+    const bool first = row < p.rows0;
+    const unsigned base = first ? (unsigned)row * row_bytes : (unsigned)(row - p.rows0) * row_bytes;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int col = (it * 64 + lane) * 8;
+      const unsigned off = (row < total && col < p.cols) ? base + (unsigned)col * 2u : kOutOfRange;
+      w[r][it] = first ? buf_load16(r0, off) : buf_load16(r1, off);
+    }
+  }
+  float4 xa[NIT], xb[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int col = (it * 64 + lane) * 8;
+    const unsigned xo = col < p.cols ? (unsigned)col * 4u : kOutOfRange;
+    xa[it] = __builtin_bit_cast(float4, buf_load16(rx, xo));
+    xb[it] = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float a = 0.f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) a = dot8_bf16(w[r][it], xa[it], xb[it], a);
+    const float s = wave_sum(a);
+    const int row = row0 + r;
+    if (lane == r && row < total) {
+      if (row < p.rows0)
+        p.y0[row] = s;
+      else
+        p.y1[row - p.rows0] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Attention, split-K over the window.
 //
 // Grid (total_chunks, Hk).  Workgroup (chunk c of sequence b, KV head g)
 // owns logical positions [t0, t1) of that sequence and the 4 query heads
 // 4g..4g+3 that read KV head g, so every K/V byte is read from HBM once and
-// used for 4 heads.  The chunk is walked in tiles of 4*rpw rows; wave w owns
-// rows [w*rpw, (w+1)*rpw) of each tile.  K and V are read with buffer loads
-// (32-bit offsets; a row that must not be read gets an offset past the end
-// of the buffer, which the hardware returns as zeros without touching HBM).
+// used for 4 heads.  Each of the 4 waves owns a contiguous quarter of the
+// chunk and runs its own online softmax over it in tiles of RPT rows, with no
+// workgroup barrier in the loop: while a wave computes tile i, the K and V
+// loads of tile i+1 are already in flight (ping-pong register buffers).  K and
+// V are read with buffer loads (32-bit offsets; a row that must not be read
+// gets an offset past the end of the buffer, which returns zeros without an
+// HBM access).
 //
-//   phase 0  RoPE table (fp64 angles), q of the 4 heads rotated and scaled
-//            by scale*log2(e) into LDS.  The chunk that ends at this token
-//            also rotates k, rounds k and v to fp16 once, writes both to the
-//            cache slot, and keeps the rounded row in LDS: the kernel never
-//            reads back what it wrote.
-//   per tile:
-//   scores   16 lanes per row (lane owns dims 8s..8s+7 and 128+8s..+7),
-//            4 rows per load; fp16 K enters v_fma_mix directly; a DPP row
-//            sum reduces.  The V loads of this tile and the K loads of the
-//            next tile are issued before the barrier.
-//   softmax  wave h updates head h's running (max, sum) over the tile and
-//            turns the tile's scores into exp2(s - max).
-//   P.V      lane owns 4 dims of a whole row (512 B per load); the running
-//            accumulators are rescaled once per tile.
-//   end      cross-wave sum, write (max, sum, acc[256]) per head.
+//   prologue  RoPE table (fp64 angle reduction), q of the 4 heads rotated and
+//             scaled by scale*log2(e) into LDS.  The chunk that ends at this
+//             token also rotates k, rounds k and v to fp16 once, writes both
+//             to the cache slot, keeps the rounded row in LDS and scores it:
+//             the kernel never reads back what it wrote.
+//   per tile  scores: 16 lanes per row (lane owns dims 8s..8s+7 and
+//             128+8s..+7), 4 rows per load, fp16 K straight into v_fma_mix,
+//             DPP row sum.  Softmax: one (row, head) score per lane, per-head
+//             max and sum by DPP/shuffles, one exp2 per lane.  P.V: lane owns
+//             4 dims of a whole row (512 B per load), probabilities read back
+//             from a wave-private LDS slot.
+//   end       the 4 waves' (max, sum, acc) are merged in LDS and written as
+//             this chunk's partial per head.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   int s = 0;
@@ -202,21 +258,36 @@ __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   return s;
 }
 
-// RPW: rows per wave per tile (tile = 4 * RPW rows).
-template <int RPW>
+// max / sum over the lanes that hold the same head (same lane & 3)
+__device__ __forceinline__ float head_max(float v) {
+  v = fmaxf(v, dpp<0x124>(v));   // row_ror:4
+  v = fmaxf(v, dpp<0x128>(v));   // row_ror:8
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float head_sum(float v) {
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int RPT>
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
-  constexpr int kTile = 4 * RPW;
-  constexpr int kQuads = RPW / 4;
+  static_assert(RPT % 4 == 0 && RPT <= 16, "a tile is 1..4 groups of 4 rows");
+  constexpr int kQuads = RPT / 4;
   __shared__ float s_cos[kHeadDim / 2];
   __shared__ float s_sin[kHeadDim / 2];
   __shared__ float s_q[kGroup][kHeadDim];
   __shared__ float s_kcur[kHeadDim];
   __shared__ float s_vcur[kHeadDim];
-  __shared__ float4 s_p[2][kTile];             // [buffer][row] x 4 heads
-  __shared__ float4 s_red[4][kGroup][kHeadDim / 4];
-  __shared__ float s_m[kGroup];
-  __shared__ float s_l[kGroup];
-  __shared__ float s_alpha[kGroup];
+  __shared__ float s_cur[kGroup];                 // scores of this token's own row
+  __shared__ float4 s_pw[4][RPT];                 // per-wave probabilities [row] x 4 heads
+  __shared__ float4 s_acc[4][kGroup][kHeadDim / 4];
+  __shared__ float s_mw[4][kGroup];
+  __shared__ float s_lw[4][kGroup];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -236,10 +307,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
   const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
   const int ring = sd.ring;
   const int p0 = ring ? (t0 % ring) : t0;        // physical row of t0; a chunk wraps at most once
-  const int tile = kTile;
-  const int rpw = RPW;
-  const int wr0 = w * rpw;
-  const int ntiles = (nrows + tile - 1) / tile;
+  const int per_wave = p.chunk >> 2;
+  const int wr0 = w * per_wave;                  // first row of this wave, relative to t0
+  const int wrows = max(0, min(per_wave, nrows - wr0));
+  const int ntiles = (wrows + RPT - 1) / RPT;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(sd.k, sd.cache_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(sd.v, sd.cache_bytes);
   const unsigned head_off = (unsigned)g * kHeadDim * 2u;
@@ -247,43 +318,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
   // byte offset of row `rel` (relative to t0) of this KV head, or out of range
   // (this token's own row is never read back: it is taken from LDS)
   auto row_off = [&](int rel) -> unsigned {
-    if (rel >= nrows || (has_cur && rel == cur_rel)) return kOutOfRange;
+    if (rel >= nrows || rel >= wr0 + wrows || (has_cur && rel == cur_rel)) return kOutOfRange;
     int ph = p0 + rel;
     if (ring && ph >= ring) ph -= ring;
     return (unsigned)ph * row_bytes + head_off;
   };
-  const unsigned k_lane_off = (unsigned)(lane & 15) * 16u;   // lane's 16 bytes in each half row
-  const unsigned v_lane_off = (unsigned)lane * 8u;           // lane's 8 bytes of a row
-
   const int sub = lane & 15;
   const int quad = lane >> 4;
-  uint4 kr[kQuads][2];
-  auto load_k = [&](int trow0) {
+  const unsigned k_lane_off = (unsigned)sub * 16u;   // lane's 16 bytes in each half row
+  const unsigned v_lane_off = (unsigned)lane * 8u;   // lane's 8 bytes of a row
+
+  uint4 kA[kQuads][2], kB[kQuads][2];
+  uint2 vA[RPT], vB[RPT];
+  auto load_tile = [&](uint4 (&kb)[kQuads][2], uint2 (&vb)[RPT], int it) {
+    const int r0 = wr0 + it * RPT;
 #pragma unroll
     for (int qi = 0; qi < kQuads; ++qi) {
-      const unsigned off = row_off(trow0 + wr0 + qi * 4 + quad) + k_lane_off;
-      kr[qi][0] = buf_load16(krs, off);
-      kr[qi][1] = buf_load16(krs, off + kHeadDim);
+      const unsigned off = row_off(r0 + qi * 4 + quad) + k_lane_off;
+      kb[qi][0] = buf_load16(krs, off);
+      kb[qi][1] = buf_load16(krs, off + kHeadDim);
     }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) vb[j] = buf_load8(vrs, row_off(r0 + j) + v_lane_off);
   };
-  load_k(0);   // HBM traffic starts before the prologue
+  if (ntiles > 0) load_tile(kA, vA, 0);   // HBM traffic starts before the prologue
 
-  // ---- phase 0: RoPE table, q, and this token's k/v ----
+  // ---- prologue: RoPE table, q, and this token's k/v ----
   const int rdim = p.rotary_dim;
   const int rhalf = rdim >> 1;
   if (tid < rhalf) {
-    // angle = position * theta^(-2i/r), formed in fp64 so that positions in
-    // the tens of thousands keep a small absolute angle error.
-    const double inv = pow(p.theta, -2.0 * (double)tid / (double)rdim);
+    // angle = position * theta^(-2i/r), formed and reduced mod 2*pi in fp64
+    // (an fp32 angle at position 32767 would be off by ~4e-3 rad); the
+    // reduced angle is in [-pi, pi], where fp32 sin/cos are accurate.
+    const double inv = exp2(-(2.0 * (double)tid / (double)rdim) * p.log2_theta);
     const double ang = (double)sd.position * inv;
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    s_cos[tid] = (float)cs;
-    s_sin[tid] = (float)sn;
-  }
-  if (tid < kGroup) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.f;
+    const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
+    double red = fma(-k, 6.283185307179586, ang);               // 2 pi, high part
+    red = fma(-k, 2.4492935982947064e-16, red);                 // 2 pi, low part
+    float sn, cs;
+    sincosf((float)red, &sn, &cs);
+    s_cos[tid] = cs;
+    s_sin[tid] = sn;
   }
   __syncthreads();
 
@@ -322,16 +397,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
     }
   }
   __syncthreads();
-
-  // score of this token's own row for head w (kept in a register of wave w)
-  float my_cur = 0.f;
-  if (has_cur) {
+  if (has_cur) {   // wave w scores this token's row for head w
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) s = fmaf(s_q[w][lane * 4 + e], s_kcur[lane * 4 + e], s);
-    my_cur = wave_sum(s);
+    s = wave_sum(s);
+    if (lane == 0) s_cur[w] = s;
   }
-
   float qreg[kGroup][16];
 #pragma unroll
   for (int i = 0; i < kGroup; ++i)
@@ -340,145 +412,152 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
       qreg[i][e] = s_q[i][sub * 8 + e];
       qreg[i][8 + e] = s_q[i][kHeadDim / 2 + sub * 8 + e];
     }
+  __syncthreads();
 
+  // ---- per-wave online softmax over this wave's rows ----
+  const int h_l = lane & 3;               // head of the score this lane holds
+  const int q_l = (lane >> 2) & 3;        // row group of the score this lane holds
+  const int r_l = 4 * q_l + quad;         // row (within the tile) of that score
+  float m_run = -INFINITY;                // per head h_l
+  float l_run = 0.f;
   float acc[kGroup][4];
 #pragma unroll
   for (int i = 0; i < kGroup; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+  float4 *pw = s_pw[w];
+  float *pwf = reinterpret_cast<float *>(pw);
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int trow0 = it * tile;
-    const int trows = min(tile, nrows - trow0);
-
-    // scores of this tile
+  auto process = [&](const uint4 (&kb)[kQuads][2], const uint2 (&vb)[RPT], int it) {
+    const int r0 = wr0 + it * RPT;
+    float my_s = -INFINITY;
 #pragma unroll
     for (int qi = 0; qi < kQuads; ++qi) {
-      {
-        const _Float16 *k0 = reinterpret_cast<const _Float16 *>(&kr[qi][0]);
-        const _Float16 *k1 = reinterpret_cast<const _Float16 *>(&kr[qi][1]);
-        float a[kGroup] = {0.f, 0.f, 0.f, 0.f};
+      const _Float16 *k0 = reinterpret_cast<const _Float16 *>(&kb[qi][0]);
+      const _Float16 *k1 = reinterpret_cast<const _Float16 *>(&kb[qi][1]);
+      float a[kGroup] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float ka = (float)k0[e];
-          const float kb = (float)k1[e];
+      for (int e = 0; e < 8; ++e) {
+        const float ka = (float)k0[e];
+        const float kc = (float)k1[e];
 #pragma unroll
-          for (int i = 0; i < kGroup; ++i) {
-            a[i] = fmaf(ka, qreg[i][e], a[i]);
-            a[i] = fmaf(kb, qreg[i][8 + e], a[i]);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) a[i] = row_sum16(a[i]);
-        const int rt = wr0 + qi * 4 + quad;
-        if (sub == 0 && rt < trows) s_p[buf][rt] = make_float4(a[0], a[1], a[2], a[3]);
-      }
-    }
-
-    // V loads of this tile, K loads of the next one
-    uint2 vr[RPW];
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      vr[j] = buf_load8(vrs, row_off(trow0 + wr0 + j) + v_lane_off);
-    }
-    if (it + 1 < ntiles) load_k(trow0 + tile);
-    __syncthreads();
-
-    // running softmax statistics of head w
-    {
-      float *sp = reinterpret_cast<float *>(s_p[buf]);
-      const int cur_t = has_cur ? cur_rel - trow0 : -1;   // this token's row in the tile, if any
-      float tmax = -INFINITY;
-      for (int r = lane; r < trows; r += 64) tmax = fmaxf(tmax, r == cur_t ? my_cur : sp[r * 4 + w]);
-      tmax = wave_max(tmax);
-      const float m_old = s_m[w];
-      const float m_new = fmaxf(m_old, tmax);
-      const float alpha = exp2f(m_old - m_new);
-      float tsum = 0.f;
-      for (int r = lane; r < trows; r += 64) {
-        const float e = exp2f((r == cur_t ? my_cur : sp[r * 4 + w]) - m_new);
-        sp[r * 4 + w] = e;
-        tsum += e;
-      }
-      tsum = wave_sum(tsum);
-      if (lane == 0) {
-        s_m[w] = m_new;
-        s_l[w] = fmaf(s_l[w], alpha, tsum);
-        s_alpha[w] = alpha;
-      }
-    }
-    __syncthreads();
-
-    // P.V of this tile
-    {
-      const float al[kGroup] = {s_alpha[0], s_alpha[1], s_alpha[2], s_alpha[3]};
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][e] *= al[i];
-#pragma unroll
-      for (int j = 0; j < RPW; ++j) {
-        if (wr0 + j < trows) {
-          const float4 pp = s_p[buf][wr0 + j];
-          const _Float16 *vh = reinterpret_cast<const _Float16 *>(&vr[j]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float vv = (float)vh[e];
-            acc[0][e] = fmaf(vv, pp.x, acc[0][e]);
-            acc[1][e] = fmaf(vv, pp.y, acc[1][e]);
-            acc[2][e] = fmaf(vv, pp.z, acc[2][e]);
-            acc[3][e] = fmaf(vv, pp.w, acc[3][e]);
-          }
+        for (int i = 0; i < kGroup; ++i) {
+          a[i] = fmaf(ka, qreg[i][e], a[i]);
+          a[i] = fmaf(kc, qreg[i][8 + e], a[i]);
         }
       }
-      const int cur_t = has_cur ? cur_rel - trow0 : -1;
-      if (cur_t >= wr0 && cur_t < wr0 + rpw && cur_t < trows) {
-        const float4 pp = s_p[buf][cur_t];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float vv = s_vcur[lane * 4 + e];
-          acc[0][e] = fmaf(vv, pp.x, acc[0][e]);
-          acc[1][e] = fmaf(vv, pp.y, acc[1][e]);
-          acc[2][e] = fmaf(vv, pp.z, acc[2][e]);
-          acc[3][e] = fmaf(vv, pp.w, acc[3][e]);
-        }
+      for (int i = 0; i < kGroup; ++i) a[i] = row_sum16(a[i]);
+      const float sel = h_l == 0 ? a[0] : h_l == 1 ? a[1] : h_l == 2 ? a[2] : a[3];
+      if (q_l == qi) my_s = sel;
+    }
+    const int rel = r0 + r_l;
+    const bool cur_here = has_cur && rel == cur_rel;
+    if (cur_here) my_s = s_cur[h_l];
+    if (q_l >= kQuads || rel >= wr0 + wrows) my_s = -INFINITY;
+
+    const float m_new = fmaxf(m_run, head_max(my_s));
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    const float pr = my_s == -INFINITY ? 0.f : exp2f(my_s - m_new);
+    l_run = fmaf(l_run, alpha, head_sum(pr));
+    m_run = m_new;
+    if (q_l < kQuads) pwf[r_l * 4 + h_l] = pr;
+    float al[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) al[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] *= al[i];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const float4 pp = pw[j];
+      const _Float16 *vh = reinterpret_cast<const _Float16 *>(&vb[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float vv = (float)vh[e];
+        acc[0][e] = fmaf(vv, pp.x, acc[0][e]);
+        acc[1][e] = fmaf(vv, pp.y, acc[1][e]);
+        acc[2][e] = fmaf(vv, pp.z, acc[2][e]);
+        acc[3][e] = fmaf(vv, pp.w, acc[3][e]);
       }
     }
+    const int jc = cur_rel - r0;   // this token's row: its V comes from LDS
+    if (has_cur && jc >= 0 && jc < RPT) {
+      const float4 pp = pw[jc];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float vv = s_vcur[lane * 4 + e];
+        acc[0][e] = fmaf(vv, pp.x, acc[0][e]);
+        acc[1][e] = fmaf(vv, pp.y, acc[1][e]);
+        acc[2][e] = fmaf(vv, pp.z, acc[2][e]);
+        acc[3][e] = fmaf(vv, pp.w, acc[3][e]);
+      }
+    }
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    if (it + 1 < ntiles) load_tile(kB, vB, it + 1);
+    process(kA, vA, it);
+    if (it + 1 >= ntiles) break;
+    if (it + 2 < ntiles) load_tile(kA, vA, it + 2);
+    process(kB, vB, it + 1);
   }
 
-  // ---- sum the 4 waves, write this chunk's partials ----
+  // ---- merge the 4 waves, write this chunk's partials ----
+  if (lane < kGroup) {
+    s_mw[w][lane] = m_run;
+    s_lw[w][lane] = l_run;
+  }
 #pragma unroll
   for (int i = 0; i < kGroup; ++i)
-    s_red[w][i][lane] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    s_acc[w][i][lane] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
   __syncthreads();
   {
-    const float *red = reinterpret_cast<const float *>(s_red);
+    const float *red = reinterpret_cast<const float *>(s_acc);
     const int d = tid;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
-      float o = 0.f;
+      float M = -INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) o += red[(ww * kGroup + i) * kHeadDim + d];
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_mw[ww][i]);
+      float o = 0.f, L = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = s_mw[ww][i];
+        const float wgt = mw == -INFINITY ? 0.f : exp2f(mw - M);
+        o = fmaf(wgt, red[(ww * kGroup + i) * kHeadDim + d], o);
+        L = fmaf(wgt, s_lw[ww][i], L);
+      }
       p.part_o[((size_t)cid * Hq + g * kGroup + i) * kHeadDim + d] = o;
-    }
-    if (tid < kGroup) {
-      float *ml = p.part_ml + ((size_t)cid * Hq + g * kGroup + tid) * 2;
-      ml[0] = s_m[tid];
-      ml[1] = s_l[tid];
+      if (d == 0) {
+        float *ml = p.part_ml + ((size_t)cid * Hq + g * kGroup + i) * 2;
+        ml[0] = M;
+        ml[1] = L;
+      }
     }
   }
 }
 
-// Grid (Hq, nseq).  Thread (cg, dq): chunk group cg = tid/64 walks chunks
-// cg, cg+4, ...; dq = tid%64 owns dims 4dq..4dq+3.
+// Merge of the split-K partials and the headwise gate.
+// Grid (Hq * kCombineSplit, nseq).  Workgroup (h, part) owns head h and dims
+// [part*64, part*64 + 64).  Thread (cg, dq): dq = tid % 16 owns 4 dims, chunk
+// group cg = tid / 16 takes chunks cg, cg + 16, ...; each thread issues all
+// of its loads (up to 8 at a time) before using any.
+constexpr int kCombineSplit = 4;
+constexpr int kCombineDims = kHeadDim / kCombineSplit;   // 64
+constexpr int kCombineQuads = kCombineDims / 4;           // 16 threads per chunk row
+constexpr int kCombineGroups = kThreads / kCombineQuads;  // 16 chunk groups
+constexpr int kCombineBatch = 8;
+
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams p) {
-  __shared__ float s_red[4];
-  __shared__ float4 s_acc[4][kHeadDim / 4];
-  __shared__ float s_lsum[4];
+  __shared__ float s_red[kThreads / 64];
+  __shared__ float4 s_acc[kCombineGroups][kCombineQuads];
+  __shared__ float s_lsum[kCombineGroups];
 
   const int tid = threadIdx.x;
-  const int h = blockIdx.x;
+  const int h = blockIdx.x / kCombineSplit;
+  const int part = blockIdx.x % kCombineSplit;
   const int b = blockIdx.y;
   const SeqDesc sd = p.seq[b];
   const int Hq = p.num_kv_heads * kGroup;
@@ -494,36 +573,51 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
   __syncthreads();
   const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
-  const int cg = tid >> 6;
-  const int dq = tid & 63;
+  const int cg = tid / kCombineQuads;
+  const int dq = tid % kCombineQuads;
+  const int dim0 = part * kCombineDims + dq * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.f;
-#pragma unroll 8
-  for (int c = cg; c < nchunks; c += 4) {
-    const size_t base = (size_t)(f0 + c) * Hq + h;
-    const float2 ml = *reinterpret_cast<const float2 *>(p.part_ml + base * 2);
-    const float4 o = *reinterpret_cast<const float4 *>(p.part_o + base * kHeadDim + dq * 4);
-    const float wgt = exp2f(ml.x - M);
-    lsum = fmaf(wgt, ml.y, lsum);
-    acc.x = fmaf(wgt, o.x, acc.x);
-    acc.y = fmaf(wgt, o.y, acc.y);
-    acc.z = fmaf(wgt, o.z, acc.z);
-    acc.w = fmaf(wgt, o.w, acc.w);
+  for (int c0 = cg; c0 < nchunks; c0 += kCombineGroups * kCombineBatch) {
+    float4 o[kCombineBatch];
+    float2 ml[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int c = c0 + u * kCombineGroups;
+      if (c < nchunks) {
+        const size_t base = (size_t)(f0 + c) * Hq + h;
+        ml[u] = *reinterpret_cast<const float2 *>(p.part_ml + base * 2);
+        o[u] = *reinterpret_cast<const float4 *>(p.part_o + base * kHeadDim + dim0);
+      } else {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float wgt = exp2f(ml[u].x - M);   // 0 for padding entries
+      lsum = fmaf(wgt, ml[u].y, lsum);
+      acc.x = fmaf(wgt, o[u].x, acc.x);
+      acc.y = fmaf(wgt, o[u].y, acc.y);
+      acc.z = fmaf(wgt, o[u].z, acc.z);
+      acc.w = fmaf(wgt, o[u].w, acc.w);
+    }
   }
   s_acc[cg][dq] = acc;
   if (dq == 0) s_lsum[cg] = lsum;
   __syncthreads();
-  if (tid < kHeadDim / 4) {
+  if (tid < kCombineQuads) {
     float4 t = s_acc[0][tid];
+    float L = s_lsum[0];
 #pragma unroll
-    for (int k = 1; k < 4; ++k) {
+    for (int k = 1; k < kCombineGroups; ++k) {
       const float4 u = s_acc[k][tid];
       t.x += u.x;
       t.y += u.y;
       t.z += u.z;
       t.w += u.w;
+      L += s_lsum[k];
     }
-    const float L = (s_lsum[0] + s_lsum[1]) + (s_lsum[2] + s_lsum[3]);
     const float gl = p.gate[(size_t)b * p.ld_gate + h];
     const float gate = 1.0f / (1.0f + expf(-gl));
     const float sc = gate / L;
@@ -532,7 +626,8 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
     r.y = t.y * sc;
     r.z = t.z * sc;
     r.w = t.w * sc;
-    *reinterpret_cast<float4 *>(p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim + tid * 4) = r;
+    *reinterpret_cast<float4 *>(p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim + part * kCombineDims +
+                                tid * 4) = r;
   }
 }
 
@@ -564,10 +659,7 @@ __global__ __launch_bounds__(kThreads) void residual_add_kernel(float *h, const 
 template <int R, int NIT>
 hipError_t gemv_dispatch_mb(const GemvParams &p, int waves, hipStream_t stream) {
   const int blocks = (waves + 3) / 4;
-  if (p.batch == 1)
-    hipLaunchKernelGGL((gemv_bf16_kernel<R, NIT, 1>), dim3(blocks), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemv_bf16_kernel<R, NIT, 4>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((gemv_bf16_kernel<R, NIT, 4>), dim3(blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -580,12 +672,42 @@ hipError_t gemv_dispatch_nit(const GemvParams &p, int waves, hipStream_t stream)
   return gemv_dispatch_mb<R, 16>(p, waves, stream);
 }
 
+template <int R, int NIT>
+hipError_t gemv1_launch(const GemvParams &p, hipStream_t stream) {
+  const int rows = p.rows0 + p.rows1;
+  const int waves = (rows + R - 1) / R;
+  hipLaunchKernelGGL((gemv1_bf16_kernel<R, NIT>), dim3((waves + 3) / 4), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Two rows per wave while that still gives >= 2048 waves, else one.
+template <int NIT>
+hipError_t gemv1_rows(const GemvParams &p, hipStream_t stream) {
+  if (p.rows0 + p.rows1 >= 4096) return gemv1_launch<2, NIT>(p, stream);
+  return gemv1_launch<1, NIT>(p, stream);
+}
+
+hipError_t gemv1_dispatch(const GemvParams &p, hipStream_t stream) {
+  switch ((p.cols + 511) / 512) {
+    case 1: return gemv1_rows<1>(p, stream);
+    case 2: return gemv1_rows<2>(p, stream);
+    case 3: return gemv1_rows<3>(p, stream);
+    case 4: return gemv1_rows<4>(p, stream);
+    case 5: return gemv1_rows<5>(p, stream);
+    case 6: return gemv1_rows<6>(p, stream);
+    case 7: return gemv1_rows<7>(p, stream);
+    case 8: return gemv1_rows<8>(p, stream);
+    case 9: case 10: return gemv1_rows<10>(p, stream);
+    case 11: case 12: return gemv1_rows<12>(p, stream);
+    default: return gemv1_rows<16>(p, stream);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream) {
+  if (p.batch == 1) return gemv1_dispatch(p, stream);
   const int rows = p.rows0 + p.rows1;
-  // Enough waves to cover all CUs several times over, as few rows per wave
-  // as that allows (more rows per wave = more bytes in flight per wave).
   if (rows >= 4 * 1024) return gemv_dispatch_nit<4>(p, (rows + 3) / 4, stream);
   if (rows >= 2 * 1024) return gemv_dispatch_nit<2>(p, (rows + 1) / 2, stream);
   return gemv_dispatch_nit<1>(p, rows, stream);
@@ -593,13 +715,11 @@ hipError_t launch_gemv(const GemvParams &p, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
   const dim3 grid(p.total_chunks, p.num_kv_heads);
-  if (p.tile == 128)
-    hipLaunchKernelGGL(attn_partial_kernel<32>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_partial_kernel<16>, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(attn_partial_kernel<8>, grid, dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads, p.nseq), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
