@@ -71,13 +71,12 @@ def block_bytes(case) -> int:
 
 
 def attention_bytes(case) -> int:
-    """Algorithmic HBM bytes of the attention step: attended K/V rows, the
-    written slot rows, fp32 qkv and gate logits in, gated attention out."""
+    """Algorithmic HBM bytes of the attention step: attended K/V rows (fp16,
+    all KV heads), fp32 q and gate logits in, gated attention out."""
     a = case.arch
     b = case.batch
     kv_row = 2 * 2 * a.num_kv_heads * a.head_dim
-    return (kv_row * attended_rows(case) + kv_row * b
-            + 4 * b * (a.qkv_rows + a.num_heads + a.q_dim))
+    return kv_row * attended_rows(case) + 4 * b * (a.q_dim + a.num_heads + a.q_dim)
 
 
 def source_digest() -> str:
@@ -179,15 +178,15 @@ def main():
         gqa.attention_block_decode(a, s["w_qkv"], s["w_g"], s["w_o"], case.is_full, s["seqs"],
                                    x, out, ws)
 
-    # dominant kernel: the attention step (split/RoPE/slot write, split-K
-    # attention, combine + gate), on a qkv produced once by the GEMV
-    qkv = torch.empty((case.batch, a.qkv_rows), dtype=torch.float32, device="cuda:0")
+    # dominant kernel: the attention step (split-K attention over the window,
+    # combine + gate), on a q produced once by the projection step
+    q = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda:0")
     gl = torch.empty((case.batch, a.num_heads), dtype=torch.float32, device="cuda:0")
     attn = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda:0")
-    gqa.qkv_gate_gemv(a, sets[0]["w_qkv"], sets[0]["w_g"], x, qkv, gl)
+    gqa.qkv_rope_kv(a, sets[0]["w_qkv"], sets[0]["w_g"], case.is_full, sets[0]["seqs"], x, q, gl)
 
     def attn_step(c):
-        gqa.attention_gated(a, case.is_full, sets[c]["seqs"], qkv, gl, attn, ws)
+        gqa.attention_gated(a, case.is_full, sets[c]["seqs"], q, gl, attn, ws)
 
     for c in range(copies):          # eager warm-up of every copy (also caches the CU count)
         block_step(c)

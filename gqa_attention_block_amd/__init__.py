@@ -15,7 +15,7 @@ from .binding import (  # noqa: F401
     kv_window,
     library_path,
     o_proj_gemv,
-    qkv_gate_gemv,
+    qkv_rope_kv,
     residual_add,
     rms_norm_bf16w,
     rope_params_for,

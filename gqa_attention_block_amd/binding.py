@@ -51,7 +51,7 @@ class _KvSeq(ctypes.Structure):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
-                          "`python -m gqa_attention_block_amd.build` (or __graft_entry__.build())")
+                          "`python gqa_attention_block_amd/build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I32, I64, D, F, S = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double,
                             ctypes.c_float, ctypes.c_size_t)
@@ -64,7 +64,7 @@ def _load():
         "gqa_kv_slot": (I32, [I32, I32]),
         "gqa_workspace_size": (ctypes.c_int, [A, I32, I32, ctypes.POINTER(S)]),
         "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
-        "gqa_qkv_gate_gemv": (ctypes.c_int, [A, W, I32, P, P, P, P]),
+        "gqa_qkv_rope_kv": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, P]),
         "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, S, P]),
         "gqa_o_proj_gemv": (ctypes.c_int, [A, W, I32, P, P, P]),
         "gqa_rms_norm_bf16w": (ctypes.c_int, [P, P, P, I32, I32, F, P]),
@@ -84,7 +84,7 @@ _lib = _load()
 #: symbols the header declares; tests check the library exports all of them
 EXPORTED_SYMBOLS = (
     "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size",
-    "gqa_attention_block_decode", "gqa_qkv_gate_gemv", "gqa_attention_gated",
+    "gqa_attention_block_decode", "gqa_qkv_rope_kv", "gqa_attention_gated",
     "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
     "gqa_last_error",
 )
@@ -245,27 +245,31 @@ def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Seq
         "gqa_attention_block_decode")
 
 
-def qkv_gate_gemv(arch: Arch, w_qkv, w_g, x: torch.Tensor, qkv: torch.Tensor,
-                  gate_logits: torch.Tensor, stream=None):
-    b = x.shape[0]
+def qkv_rope_kv(arch: Arch, w_qkv, w_g, is_full: bool, seqs: Sequence[KvSeq], x: torch.Tensor,
+                q_roped: torch.Tensor, gate_logits: torch.Tensor, stream=None):
+    """The projections, split, RoPE and KV-slot write; writes each cache's slot row."""
+    b = len(seqs)
     a = arch._c()
     w = _weights(arch, w_qkv, w_g, None)
-    _check(_lib.gqa_qkv_gate_gemv(
-        ctypes.byref(a), ctypes.byref(w), b, _ptr(x, torch.float32, "x", b * arch.hidden),
-        _ptr(qkv, torch.float32, "qkv", b * arch.qkv_rows),
+    ks = _seqs(arch, seqs)
+    _check(_lib.gqa_qkv_rope_kv(
+        ctypes.byref(a), ctypes.byref(w), int(is_full), ks, b,
+        _ptr(x, torch.float32, "x", b * arch.hidden),
+        _ptr(q_roped, torch.float32, "q_roped", b * arch.q_dim),
         _ptr(gate_logits, torch.float32, "gate_logits", b * arch.num_heads), _stream(stream)),
-        "gqa_qkv_gate_gemv")
+        "gqa_qkv_rope_kv")
 
 
-def attention_gated(arch: Arch, is_full: bool, seqs: Sequence[KvSeq], qkv: torch.Tensor,
+def attention_gated(arch: Arch, is_full: bool, seqs: Sequence[KvSeq], q_roped: torch.Tensor,
                     gate_logits: torch.Tensor, attn_gated: torch.Tensor,
                     workspace: torch.Tensor, stream=None):
+    """Attention over each cache window and the headwise gate (reads the caches only)."""
     b = len(seqs)
     a = arch._c()
     ks = _seqs(arch, seqs)
     _check(_lib.gqa_attention_gated(
         ctypes.byref(a), int(is_full), ks, b,
-        _ptr(qkv, torch.float32, "qkv", b * arch.qkv_rows),
+        _ptr(q_roped, torch.float32, "q_roped", b * arch.q_dim),
         _ptr(gate_logits, torch.float32, "gate_logits", b * arch.num_heads),
         _ptr(attn_gated, torch.float32, "attn_gated", b * arch.q_dim),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),

@@ -1,6 +1,7 @@
 """Build libgqa.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: ``python -m gqa_attention_block_amd.build`` or ``build_library()``.
+Usage: ``python gqa_attention_block_amd/build.py`` (runs without importing the
+package, which would load the library being rebuilt) or ``build_library()``.
 """
 from __future__ import annotations
 

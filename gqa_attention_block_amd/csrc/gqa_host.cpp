@@ -130,8 +130,9 @@ gqa_status window_of(int is_full, int32_t position, int32_t window, int32_t ring
 // ---- sequences and the split-K plan ----------------------------------------
 
 struct Plan {
-  int tile = kMaxTile;
-  int chunk = kMaxTile;
+  int hpg = 4;
+  int tile = kMinChunk;
+  int chunk = kMinChunk;
   struct Group {
     int first = 0, count = 0, total_chunks = 0;
   };
@@ -204,23 +205,32 @@ gqa_status resolve_seqs(const gqa_arch *a, int is_full, const gqa_kv_seq *seqs, 
   return GQA_OK;
 }
 
-// Split-K plan.  Workgroups walk their chunk in tiles of kMaxTile rows; the
-// chunk is the largest number of tiles that still gives every CU at least
-// two workgroups, so partials stay few while the chip stays full.  Sequences
-// go in launch groups of up to kMaxSeqPerLaunch.
+// Split-K plan.  An attention workgroup covers a chunk of rows for hpg KV
+// heads (hpg = 4 when Hk is a multiple of 4, one wave per head).  The chunk is
+// the largest multiple of kMinChunk rows (up to what a wave keeps scores for)
+// that still gives every CU two workgroups, so partials stay few while the
+// chip stays full.  Sequences go in launch groups of up to kMaxSeqPerLaunch.
+int heads_per_group(int num_kv_heads) {
+  if (num_kv_heads % 4 == 0) return 4;
+  if (num_kv_heads % 2 == 0) return 2;
+  return 1;
+}
+
 Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
   Plan plan;
+  plan.hpg = heads_per_group(num_kv_heads);
   const long target = 2L * num_cus_of_current_device();
+  const int groups = num_kv_heads / plan.hpg;
   auto wgs = [&](int chunk) {
     long n = 0;
-    for (const SeqDesc &s : seqs) n += (long)ceil_div(s.n, chunk) * num_kv_heads;
+    for (const SeqDesc &s : seqs) n += (long)ceil_div(s.n, chunk) * groups;
     return n;
   };
-  const int tile = kMaxTile;
-  int ntiles = 1;
-  while (ntiles < kMaxTilesPerChunk && wgs(tile * (ntiles + 1)) >= target) ++ntiles;
-  plan.tile = tile;
-  plan.chunk = tile * ntiles;
+  const int max_chunk = kMaxWaveRows * (4 / plan.hpg);   // a wave keeps <= kMaxWaveRows scores
+  int chunk = kMinChunk;
+  while (chunk + kMinChunk <= max_chunk && wgs(chunk + kMinChunk) >= target) chunk += kMinChunk;
+  plan.tile = kMinChunk;
+  plan.chunk = chunk;
   for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {
     Plan::Group g;
     g.first = first;
@@ -237,7 +247,7 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
 // ---- workspace layout -----------------------------------------------------
 
 struct Layout {
-  size_t qkv = 0, gate = 0, attn = 0, part_o = 0, part_ml = 0, total = 0;
+  size_t q = 0, gate = 0, attn = 0, part_o = 0, part_ml = 0, total = 0;
 };
 
 size_t partial_bytes_o(const gqa_arch *a, size_t chunks) {
@@ -247,13 +257,13 @@ size_t partial_bytes_ml(const gqa_arch *a, size_t chunks) {
   return round_up(chunks * (size_t)a->num_heads * 2 * sizeof(float), 256);
 }
 
-// Block layout: [qkv | gate | attn | part_o | part_ml]; the attention step
+// Block layout: [q | gate | attn | part_o | part_ml]; the attention step
 // alone uses [part_o | part_ml] from offset 0.
 Layout block_layout(const gqa_arch *a, int32_t batch, size_t chunks) {
   Layout L;
-  const size_t qkv_rows = (size_t)(a->num_heads + 2 * a->num_kv_heads) * a->head_dim;
-  L.qkv = 0;
-  L.gate = L.qkv + round_up((size_t)batch * qkv_rows * sizeof(float), 256);
+  const size_t q_dim = (size_t)a->num_heads * a->head_dim;
+  L.q = 0;
+  L.gate = L.q + round_up((size_t)batch * q_dim * sizeof(float), 256);
   L.attn = L.gate + round_up((size_t)batch * a->num_heads * sizeof(float), 256);
   L.part_o = L.attn + round_up((size_t)batch * a->num_heads * a->head_dim * sizeof(float), 256);
   L.part_ml = L.part_o + partial_bytes_o(a, chunks);
@@ -267,23 +277,37 @@ gqa_status gpu_error(hipError_t e, const char *what) {
   return fail(GQA_ERR_GPU, "%s: %s", what, hipGetErrorString(e));
 }
 
-gqa_status run_qkv_gate(const gqa_arch *a, const gqa_layer_weights *w, int32_t batch, const float *x,
-                        float *qkv, float *gate, hipStream_t stream) {
-  GemvParams p{};
-  p.w0 = static_cast<const uint16_t *>(w->q_k_v_proj);
-  p.w1 = static_cast<const uint16_t *>(w->g_proj);
-  p.rows0 = (a->num_heads + 2 * a->num_kv_heads) * a->head_dim;
-  p.rows1 = a->num_heads;
-  p.cols = a->hidden;
-  p.batch = batch;
-  p.x = x;
-  p.ldx = a->hidden;
-  p.y0 = qkv;
-  p.ldy0 = p.rows0;
-  p.y1 = gate;
-  p.ldy1 = a->num_heads;
-  hipError_t e = launch_gemv(p, stream);
-  return e == hipSuccess ? GQA_OK : gpu_error(e, "qkv/gate GEMV launch");
+// The fused projection step for every sequence, in launch groups of up to
+// kMaxSeqPerLaunch batch rows.
+gqa_status run_qkv_rope(const gqa_arch *a, const gqa_layer_weights *w, int is_full,
+                        const std::vector<SeqDesc> &seqs, const float *x, float *q, float *gate,
+                        hipStream_t stream) {
+  int32_t rdim;
+  double theta;
+  gqa_rope_params_for(is_full, a->full_rotary_dim, a->head_dim, a->full_rope_theta, a->rope_theta, &rdim,
+                      &theta);
+  const long q_dim = (long)a->num_heads * a->head_dim;
+  for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {
+    QkvParams p{};
+    p.w_qkv = static_cast<const uint16_t *>(w->q_k_v_proj);
+    p.w_g = static_cast<const uint16_t *>(w->g_proj);
+    p.hidden = a->hidden;
+    p.batch = std::min<int>(kMaxSeqPerLaunch, (int)seqs.size() - first);
+    p.x = x + (size_t)first * a->hidden;
+    p.ldx = a->hidden;
+    p.q_out = q + (size_t)first * q_dim;
+    p.ld_q = q_dim;
+    p.gate_out = gate + (size_t)first * a->num_heads;
+    p.ld_gate = a->num_heads;
+    p.num_heads = a->num_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.rotary_dim = rdim;
+    p.log2_theta = log2(theta);
+    for (int i = 0; i < p.batch; ++i) p.seq[i] = seqs[first + i];
+    hipError_t e = launch_qkv_rope(p, stream);
+    if (e != hipSuccess) return gpu_error(e, "qkv/RoPE/KV-write launch");
+  }
+  return GQA_OK;
 }
 
 gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t batch, const float *attn,
@@ -305,29 +329,24 @@ gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t bat
   return e == hipSuccess ? GQA_OK : gpu_error(e, "o_proj GEMV launch");
 }
 
-gqa_status run_attention(const gqa_arch *a, int is_full, const std::vector<SeqDesc> &seqs,
-                         const Plan &plan, const float *qkv, const float *gate, float *attn,
-                         float *part_o, float *part_ml, hipStream_t stream) {
-  int32_t rdim;
-  double theta;
-  gqa_rope_params_for(is_full, a->full_rotary_dim, a->head_dim, a->full_rope_theta, a->rope_theta, &rdim,
-                      &theta);
-  const long qkv_rows = (long)(a->num_heads + 2 * a->num_kv_heads) * a->head_dim;
+gqa_status run_attention(const gqa_arch *a, const std::vector<SeqDesc> &seqs, const Plan &plan,
+                         const float *q, const float *gate, float *attn, float *part_o, float *part_ml,
+                         hipStream_t stream) {
+  const long q_dim = (long)a->num_heads * a->head_dim;
   for (const Plan::Group &g : plan.groups) {
     AttnParams p{};
-    p.qkv = qkv + (size_t)g.first * qkv_rows;
-    p.ld_qkv = qkv_rows;
+    p.q = q + (size_t)g.first * q_dim;
+    p.ld_q = q_dim;
     p.gate = gate + (size_t)g.first * a->num_heads;
     p.ld_gate = a->num_heads;
-    p.out = attn + (size_t)g.first * a->num_heads * a->head_dim;
-    p.ld_out = (long)a->num_heads * a->head_dim;
+    p.out = attn + (size_t)g.first * q_dim;
+    p.ld_out = q_dim;
     p.part_o = part_o;
     p.part_ml = part_ml;
     p.num_kv_heads = a->num_kv_heads;
-    p.rotary_dim = rdim;
-    p.log2_theta = log2(theta);
     p.qscale = (float)((double)a->attention_scale * kLog2e);
     p.tile = plan.tile;
+    p.hpg = plan.hpg;
     p.chunk = plan.chunk;
     p.nseq = g.count;
     p.total_chunks = g.total_chunks;
@@ -418,17 +437,20 @@ gqa_status check_batch(const gqa_arch *a, int32_t batch) {
   return GQA_OK;
 }
 
-gqa_status gqa_qkv_gate_gemv(const gqa_arch *arch, const gqa_layer_weights *weights, int32_t batch,
-                             const float *x, float *qkv, float *gate_logits, void *stream) {
+gqa_status gqa_qkv_rope_kv(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,
+                           const gqa_kv_seq *seqs, int32_t batch, const float *x, float *q_roped,
+                           float *gate_logits, void *stream) {
   gqa_status st;
   if ((st = check_arch(arch)) != GQA_OK) return st;
   if ((st = check_weights(weights, true, false)) != GQA_OK) return st;
   if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
   if (batch == 0) return ok();
   if ((st = check_ptr(x, "x")) != GQA_OK) return st;
-  if ((st = check_ptr(qkv, "qkv")) != GQA_OK) return st;
+  if ((st = check_ptr(q_roped, "q_roped")) != GQA_OK) return st;
   if ((st = check_ptr(gate_logits, "gate_logits")) != GQA_OK) return st;
-  st = run_qkv_gate(arch, weights, batch, x, qkv, gate_logits, static_cast<hipStream_t>(stream));
+  st = run_qkv_rope(arch, weights, is_full, descs, x, q_roped, gate_logits, static_cast<hipStream_t>(stream));
   return st == GQA_OK ? ok() : st;
 }
 
@@ -446,7 +468,7 @@ gqa_status gqa_o_proj_gemv(const gqa_arch *arch, const gqa_layer_weights *weight
 }
 
 gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs, int32_t batch,
-                               const float *qkv, const float *gate_logits, float *attn_gated,
+                               const float *q_roped, const float *gate_logits, float *attn_gated,
                                void *workspace, size_t workspace_bytes, void *stream) {
   gqa_status st;
   if ((st = check_arch(arch)) != GQA_OK) return st;
@@ -454,7 +476,7 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
   std::vector<SeqDesc> descs;
   if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
   if (batch == 0) return ok();
-  if ((st = check_ptr(qkv, "qkv")) != GQA_OK) return st;
+  if ((st = check_ptr(q_roped, "q_roped")) != GQA_OK) return st;
   if ((st = check_ptr(gate_logits, "gate_logits")) != GQA_OK) return st;
   if ((st = check_ptr(attn_gated, "attn_gated")) != GQA_OK) return st;
   if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
@@ -466,7 +488,7 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
   char *ws = static_cast<char *>(workspace);
   float *part_o = reinterpret_cast<float *>(ws);
   float *part_ml = reinterpret_cast<float *>(ws + partial_bytes_o(arch, plan.max_group_chunks));
-  st = run_attention(arch, is_full, descs, plan, qkv, gate_logits, attn_gated, part_o, part_ml,
+  st = run_attention(arch, descs, plan, q_roped, gate_logits, attn_gated, part_o, part_ml,
                      static_cast<hipStream_t>(stream));
   return st == GQA_OK ? ok() : st;
 }
@@ -490,15 +512,14 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the block needs %zu", workspace_bytes,
                 L.total);
   char *ws = static_cast<char *>(workspace);
-  float *qkv = reinterpret_cast<float *>(ws + L.qkv);
+  float *q = reinterpret_cast<float *>(ws + L.q);
   float *gate = reinterpret_cast<float *>(ws + L.gate);
   float *attn = reinterpret_cast<float *>(ws + L.attn);
   float *part_o = reinterpret_cast<float *>(ws + L.part_o);
   float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_qkv_gate(arch, weights, batch, x_normed, qkv, gate, s)) != GQA_OK) return st;
-  if ((st = run_attention(arch, is_full, descs, plan, qkv, gate, attn, part_o, part_ml, s)) != GQA_OK)
-    return st;
+  if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
+  if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
   if ((st = run_o_proj(arch, weights, batch, attn, out, s)) != GQA_OK) return st;
   return ok();
 }

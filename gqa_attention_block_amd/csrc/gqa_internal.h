@@ -12,9 +12,8 @@ constexpr int kHeadDim = 256;        // kernels specialise D = 256
 constexpr int kGroup = 4;            // query heads per KV head
 constexpr int kThreads = 256;        // 4 wave64 per workgroup
 constexpr int kMaxSeqPerLaunch = 32; // sequence descriptors carried in kernel arguments
-constexpr int kMaxTile = 64;         // attention rows per workgroup per step
 constexpr int kMinChunk = 64;        // smallest attention chunk (sizes the workspace)
-constexpr int kMaxTilesPerChunk = 32;
+constexpr int kMaxWaveRows = 256;    // attention rows one wave keeps scores for
 constexpr unsigned kMaxBufferBytes = 0x7FFFFFFFu;  // buffer loads use 31-bit offsets
 constexpr int kMaxHidden = 8192;     // GEMV keeps up to 16 x 512 columns in registers
 
@@ -33,8 +32,8 @@ struct SeqDesc {
 };
 
 struct AttnParams {
-  const float *qkv;   // [nseq][ld_qkv]: q (Hq*D) | k (Hk*D) | v (Hk*D)
-  long ld_qkv;
+  const float *q;     // [nseq][ld_q] RoPE'd query heads, head-major
+  long ld_q;
   const float *gate;  // [nseq][ld_gate] gate logits
   long ld_gate;
   float *out;         // [nseq][ld_out] gated attention, head-major
@@ -42,13 +41,32 @@ struct AttnParams {
   float *part_o;      // [total_chunks][Hq][D]   unnormalised partial outputs
   float *part_ml;     // [total_chunks][Hq][2]   (running max in log2 units, sum)
   int num_kv_heads;
-  int rotary_dim;
-  double log2_theta;  // log2 of the RoPE base of this layer class
   float qscale;       // attention_scale * log2(e): scores come out in log2 units
-  int tile;           // rows per step (4 waves x tile/4 rows); kernels exist for 64 and 128
+  int tile;           // rows per step of the split plan
+  int hpg;            // KV heads per attention workgroup: 1, 2 or 4 (one wave each if 4)
   int chunk;          // rows per workgroup: a multiple of tile
   int nseq;
   int total_chunks;
+  SeqDesc seq[kMaxSeqPerLaunch];
+};
+
+// The fused projection step: q_k_v_proj and g_proj over the same x, then the
+// split, RoPE and the fp16 KV-slot write (uses seq[].k, .v, .slot, .position).
+struct QkvParams {
+  const uint16_t *w_qkv;  // bf16 [(Hq + 2 Hk) * D][hidden]
+  const uint16_t *w_g;    // bf16 [Hq][hidden]
+  int hidden;
+  int batch;              // <= kMaxSeqPerLaunch
+  const float *x;         // [batch][ldx]
+  long ldx;
+  float *q_out;           // [batch][ld_q] RoPE'd q
+  long ld_q;
+  float *gate_out;        // [batch][ld_gate] gate logits
+  long ld_gate;
+  int num_heads;
+  int num_kv_heads;
+  int rotary_dim;
+  double log2_theta;
   SeqDesc seq[kMaxSeqPerLaunch];
 };
 
@@ -69,6 +87,7 @@ struct GemvParams {
 
 // Launchers (gqa_kernels.hip).  They return the hipError_t of the launch.
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
+hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
 hipError_t launch_rms_norm(const float *h, const uint16_t *w, float *out, int rows,
                            int hidden, float eps, hipStream_t stream);

@@ -1,16 +1,19 @@
 // HIP kernels of the decode attention block for CDNA4 (gfx950), wave64.
 //
 // Steps and their source (docs.rs turbospark-runtime 0.3.0):
-//   gemv_bf16_kernel     -- the fused q_k_v_proj GEMV with the g_proj rows
-//                           appended, and the o_proj GEMV
-//                           ([attn.rs] `encode_attention_block`, GEMV steps)
-//   attn_partial_kernel  -- the split into the cache slot, per-class NeoX RoPE
-//                           of q and k, and split-K decode attention over the
-//                           window/ring ([attn.rs] split, RoPE, window and
-//                           attention steps; [kv_write.rs] `kv_write_target`,
-//                           `encode_attention_any`)
+//   qkv_rope_kernel      -- the fused q_k_v_proj GEMV and the g_proj GEMV over
+//                           the same input, with the split, the per-class
+//                           NeoX RoPE of q and k, and the fp16 write of k and
+//                           v into this token's cache slot done in the
+//                           epilogue ([attn.rs] `encode_attention_block`:
+//                           GEMV, split, RoPE steps; [kv_write.rs]
+//                           `kv_write_target`)
+//   attn_partial_kernel  -- split-K decode attention over the window/ring
+//                           ([attn.rs] window and attention steps;
+//                           [kv_write.rs] `encode_attention_any`)
 //   attn_combine_kernel  -- merge of the split-K partials and the headwise
 //                           sigmoid gate ([attn.rs] gate step, before o_proj)
+//   gemv1/gemv kernels   -- the o_proj GEMV ([attn.rs] last GEMV)
 //   rms_norm_kernel, residual_add_kernel -- the layer loop around the block
 //                           ([mod.rs] `produce_real_spark_inner`)
 //
@@ -61,6 +64,20 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+
+// fp16 -> fp32 of the low / high half of a dword, one full-rate VALU op each.
+// Written out so the compiler keeps one conversion feeding several plain
+// FMAs instead of fusing it into a (half-rate) mixed-precision FMA per use.
+__device__ __forceinline__ float h2f_lo(uint32_t w) {
+  float f;
+  asm("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(w));
+  return f;
+}
+__device__ __forceinline__ float h2f_hi(uint32_t w) {
+  float f;
+  asm("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(f) : "v"(w));
+  return f;
+}
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------
@@ -224,33 +241,158 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
 }
 
 // ---------------------------------------------------------------------------
-// Attention, split-K over the window.
+// Fused q_k_v_proj + g_proj GEMV with the split, RoPE and KV-slot write in the
+// epilogue.
 //
-// Grid (total_chunks, Hk).  Workgroup (chunk c of sequence b, KV head g)
-// owns logical positions [t0, t1) of that sequence and the 4 query heads
-// 4g..4g+3 that read KV head g, so every K/V byte is read from HBM once and
-// used for 4 heads.  Each of the 4 waves owns a contiguous quarter of the
-// chunk and runs its own online softmax over it in tiles of RPT rows, with no
-// workgroup barrier in the loop: while a wave computes tile i, the K and V
-// loads of tile i+1 are already in flight (ping-pong register buffers).  K and
-// V are read with buffer loads (32-bit offsets; a row that must not be read
-// gets an offset past the end of the buffer, which returns zeros without an
-// HBM access).
-//
-//   prologue  RoPE table (fp64 angle reduction), q of the 4 heads rotated and
-//             scaled by scale*log2(e) into LDS.  The chunk that ends at this
-//             token also rotates k, rounds k and v to fp16 once, writes both
-//             to the cache slot, keeps the rounded row in LDS and scores it:
-//             the kernel never reads back what it wrote.
-//   per tile  scores: 16 lanes per row (lane owns dims 8s..8s+7 and
-//             128+8s..+7), 4 rows per load, fp16 K straight into v_fma_mix,
-//             DPP row sum.  Softmax: one (row, head) score per lane, per-head
-//             max and sum by DPP/shuffles, one exp2 per lane.  P.V: lane owns
-//             4 dims of a whole row (512 B per load), probabilities read back
-//             from a wave-private LDS slot.
-//   end       the 4 waves' (max, sum, acc) are merged in LDS and written as
-//             this chunk's partial per head.
+// Wave P computes TWO output rows that RoPE pairs: inside a q or k head with
+// rotary width r, pair i < r/2 is rows (i, i + r/2), which turn together by
+// the angle position * theta^(-2i/r); pairs i >= r/2, all v pairs and all
+// gate pairs are rows (2i, 2i+1), left as they are.  Sections in pair order:
+// q heads (128 pairs each), k heads, v heads, then Hq/2 gate pairs.  The dot
+// products run like the GEMV below (16-byte loads, all issued up front); then
+// lane m (batch row b0 + m) forms its sequence's angle in fp64, rotates the
+// pair in fp32 and writes: q -> q_out (fp32), k and v -> fp16, rounded once,
+// straight into the cache slot of this position; gate logits -> gate_out.
 // ---------------------------------------------------------------------------
+template <int NIT, int MB>
+__global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
+  const int lane = threadIdx.x & 63;
+  const int P = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int Hq = p.num_heads, Hk = p.num_kv_heads;
+  constexpr int kPairs = kHeadDim / 2;
+  const int nq = Hq * kPairs, nk = Hk * kPairs, nv = Hk * kPairs;
+  if (P >= nq + nk + nv + Hq / 2) return;
+  int sec, head, pi;
+  if (P < nq) {
+    sec = 0; head = P / kPairs; pi = P % kPairs;
+  } else if (P < nq + nk) {
+    sec = 1; head = (P - nq) / kPairs; pi = (P - nq) % kPairs;
+  } else if (P < nq + nk + nv) {
+    sec = 2; head = (P - nq - nk) / kPairs; pi = (P - nq - nk) % kPairs;
+  } else {
+    sec = 3; head = 0; pi = P - nq - nk - nv;
+  }
+  const int rhalf = p.rotary_dim >> 1;
+  const bool rotate = sec <= 1 && pi < rhalf;
+  const int dA = rotate ? pi : 2 * pi;
+  const int dB = rotate ? pi + rhalf : 2 * pi + 1;
+  // rows in the weight matrices
+  const int base_row = sec == 0 ? head * kHeadDim
+                     : sec == 1 ? (Hq + head) * kHeadDim
+                     : sec == 2 ? (Hq + Hk + head) * kHeadDim : 0;
+  const unsigned row_bytes = (unsigned)p.hidden * 2u;
+  const int qkv_rows = (Hq + 2 * Hk) * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rw = sec < 3 ? make_rsrc(p.w_qkv, (unsigned)qkv_rows * row_bytes)
+                                            : make_rsrc(p.w_g, (unsigned)Hq * row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)((size_t)p.batch * p.ldx * 4u));
+
+  uint4 wa[NIT], wb[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int col = (it * 64 + lane) * 8;
+    const bool ok = col < p.hidden;
+    wa[it] = buf_load16(rw, ok ? (unsigned)(base_row + dA) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+    wb[it] = buf_load16(rw, ok ? (unsigned)(base_row + dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+  }
+
+  for (int b0 = 0; b0 < p.batch; b0 += MB) {
+    float sa[MB], sb[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int col = (it * 64 + lane) * 8;
+        const unsigned xo = (col < p.hidden && b0 + m < p.batch)
+                                ? (unsigned)(((size_t)(b0 + m) * p.ldx + col) * 4u)
+                                : kOutOfRange;
+        const float4 xa = __builtin_bit_cast(float4, buf_load16(rx, xo));
+        const float4 xb = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
+        a = dot8_bf16(wa[it], xa, xb, a);
+        c = dot8_bf16(wb[it], xa, xb, c);
+      }
+      sa[m] = wave_sum(a);
+      sb[m] = wave_sum(c);
+    }
+    // epilogue: lane m handles batch row b0 + m
+    float ya = 0.f, yb = 0.f;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      if (lane == m) {
+        ya = sa[m];
+        yb = sb[m];
+      }
+    const int b = b0 + lane;
+    if (lane < MB && b < p.batch) {
+      const SeqDesc &sd = p.seq[b];
+      if (rotate) {
+        // angle = position * theta^(-2i/r), formed and reduced mod 2*pi in
+        // fp64 (an fp32 angle at position 32767 would be off by ~4e-3 rad);
+        // the reduced angle is in [-pi, pi], where fp32 sin/cos are accurate.
+        const double inv = exp2(-(2.0 * (double)pi / (double)p.rotary_dim) * p.log2_theta);
+        const double ang = (double)sd.position * inv;
+        const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
+        double red = fma(-k, 6.283185307179586, ang);               // 2 pi, high part
+        red = fma(-k, 2.4492935982947064e-16, red);                 // 2 pi, low part
+        float sn, cs;
+        sincosf((float)red, &sn, &cs);
+        const float ra = ya * cs - yb * sn;
+        const float rb = yb * cs + ya * sn;
+        ya = ra;
+        yb = rb;
+      }
+      if (sec == 0) {
+        float *q = p.q_out + (size_t)b * p.ld_q + (size_t)head * kHeadDim;
+        q[dA] = ya;
+        q[dB] = yb;
+      } else if (sec == 3) {
+        float *gl = p.gate_out + (size_t)b * p.ld_gate;
+        gl[dA] = ya;
+        gl[dB] = yb;
+      } else {
+        _Float16 *dst = (sec == 1 ? sd.k : sd.v) + (size_t)sd.slot * Hk * kHeadDim + (size_t)head * kHeadDim;
+        dst[dA] = (_Float16)ya;
+        dst[dB] = (_Float16)yb;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention, split-K over the window, on the matrix cores.
+//
+// Grid (total_chunks, Hk / hpg).  Workgroup (chunk c of sequence b, head
+// group y) owns logical positions [t0, t1) of that sequence for hpg KV heads
+// (hpg = 4 when Hk is a multiple of 4): wave w works on KV head
+// y*hpg + w / wph and on part w % wph of the rows (wph = 4 / hpg waves per
+// head).  Each KV head's K/V bytes are read from HBM once and serve its 4
+// query heads.  This token's k and v are already in the cache (the qkv kernel
+// wrote them), so every row of the window is read the same way.
+//
+// Both products are small dense contractions per 16-row tile -- S = K q for
+// 4 query heads and O += P V -- and on VALU they cost ~65 instructions per
+// row, more than the HBM stream leaves room for; on MFMA they cost ~2.
+//   pass 1  S^T[16 rows x 16] = K[16 x 256] * Qf[256 x 16] with
+//           v_mfma_f32_16x16x32_f16: the K fragments come straight from HBM
+//           (lane l: row l%16, 8 dims), Qf's columns 0-3 hold the fp16 high
+//           part of the 4 query heads (pre-scaled by scale*log2(e)) and 4-7
+//           the fp16 low part (q - hi), so S = hi + lo keeps fp32 accuracy.
+//           Scores go to LDS; each wave tracks its max.
+//   pass 2  O[16 x 256] += P[16 x 16 rows] * V[16 rows x 256] with
+//           v_mfma_f32_16x16x16_f16: P's rows 0-3 are the fp16 high part of
+//           exp2(s - max) for the 4 heads, rows 4-7 the low part; V is staged
+//           through LDS and read back transposed (ds_read_b64_tr_b16) into
+//           the B-operand layout.
+// Two passes need no online rescaling.  K/V are read with buffer loads whose
+// out-of-range offsets return zeros without an HBM access; two tiles are in
+// flight per wave (ping-pong registers).  At the end the waves of each KV head
+// merge (max, sum, acc) in LDS and write this chunk's partial per query head.
+// ---------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   int s = 0;
   for (int i = 1; i < p.nseq; ++i)
@@ -258,282 +400,216 @@ __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   return s;
 }
 
-// max / sum over the lanes that hold the same head (same lane & 3)
-__device__ __forceinline__ float head_max(float v) {
-  v = fmaxf(v, dpp<0x124>(v));   // row_ror:4
-  v = fmaxf(v, dpp<0x128>(v));   // row_ror:8
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
-__device__ __forceinline__ float head_sum(float v) {
-  v += dpp<0x124>(v);
-  v += dpp<0x128>(v);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
+constexpr int kTileRows = 16;                      // rows per MFMA tile
+constexpr int kVStride = kHeadDim + 16;            // halves per staged V row (32 B pad)
 
-template <int RPT>
+template <int TPW>   // max 16-row tiles per wave
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
-  static_assert(RPT % 4 == 0 && RPT <= 16, "a tile is 1..4 groups of 4 rows");
-  constexpr int kQuads = RPT / 4;
-  __shared__ float s_cos[kHeadDim / 2];
-  __shared__ float s_sin[kHeadDim / 2];
-  __shared__ float s_q[kGroup][kHeadDim];
-  __shared__ float s_kcur[kHeadDim];
-  __shared__ float s_vcur[kHeadDim];
-  __shared__ float s_cur[kGroup];                 // scores of this token's own row
-  __shared__ float4 s_pw[4][RPT];                 // per-wave probabilities [row] x 4 heads
-  __shared__ float4 s_acc[4][kGroup][kHeadDim / 4];
+  __shared__ float4 s_sc4[4][kGroup][TPW * kTileRows / 4];   // scores [wave][head][row]
+  __shared__ _Float16 s_v[4][kTileRows * kVStride];          // staged V tile per wave
+  __shared__ float4 s_acc[4][kGroup][kHeadDim / 4];          // per-wave O [head][lane n][c]
   __shared__ float s_mw[4][kGroup];
   __shared__ float s_lw[4][kGroup];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
-  const int g = blockIdx.y;
+  const int hpg = p.hpg;                         // KV heads per workgroup: 1, 2 or 4
+  const int wph = 4 / hpg;                       // waves per KV head
+  const int g0 = blockIdx.y * hpg;               // first KV head of the workgroup
+  const int g = g0 + w / wph;                    // this wave's KV head
   const int cid = blockIdx.x;
   const int b = find_seq(p, cid);
   const SeqDesc sd = p.seq[b];
   const int Hk = p.num_kv_heads;
   const int Hq = Hk * kGroup;
   const int t0 = sd.kv_start + (cid - sd.chunk_begin) * p.chunk;
-  const int seq_len = sd.kv_start + sd.n;
-  const int t1 = min(t0 + p.chunk, seq_len);
-  const int nrows = t1 - t0;
-  const bool has_cur = (t1 == seq_len);
-  const int cur_rel = seq_len - 1 - t0;          // meaningful when has_cur
+  const int nrows = min(p.chunk, sd.kv_start + sd.n - t0);
   const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
   const int ring = sd.ring;
   const int p0 = ring ? (t0 % ring) : t0;        // physical row of t0; a chunk wraps at most once
-  const int per_wave = p.chunk >> 2;
-  const int wr0 = w * per_wave;                  // first row of this wave, relative to t0
-  const int wrows = max(0, min(per_wave, nrows - wr0));
-  const int ntiles = (wrows + RPT - 1) / RPT;
+  const int per_wave = p.chunk / wph;
+  const int wr0 = (w % wph) * per_wave;          // first row of this wave, relative to t0
+  const int wend = min(nrows, wr0 + per_wave);   // one past its last row
+  const int ntiles = max(0, (wend - wr0 + kTileRows - 1) / kTileRows);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(sd.k, sd.cache_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(sd.v, sd.cache_bytes);
   const unsigned head_off = (unsigned)g * kHeadDim * 2u;
+  const int G = lane >> 4;                       // lane group (MFMA k-slot group / D row group)
+  const int n = lane & 15;                       // lane within the group (MFMA row / column)
 
   // byte offset of row `rel` (relative to t0) of this KV head, or out of range
-  // (this token's own row is never read back: it is taken from LDS)
   auto row_off = [&](int rel) -> unsigned {
-    if (rel >= nrows || rel >= wr0 + wrows || (has_cur && rel == cur_rel)) return kOutOfRange;
+    if (rel >= wend) return kOutOfRange;
     int ph = p0 + rel;
     if (ring && ph >= ring) ph -= ring;
     return (unsigned)ph * row_bytes + head_off;
   };
-  const int sub = lane & 15;
-  const int quad = lane >> 4;
-  const unsigned k_lane_off = (unsigned)sub * 16u;   // lane's 16 bytes in each half row
-  const unsigned v_lane_off = (unsigned)lane * 8u;   // lane's 8 bytes of a row
 
-  uint4 kA[kQuads][2], kB[kQuads][2];
-  uint2 vA[RPT], vB[RPT];
-  auto load_tile = [&](uint4 (&kb)[kQuads][2], uint2 (&vb)[RPT], int it) {
-    const int r0 = wr0 + it * RPT;
+  // K A-fragments of tile t: lane (G, n) holds row 16t + n, dims 32s + 8G .. +8
+  auto load_k = [&](half8_t (&kf)[8], int t) {
+    const unsigned off = row_off(wr0 + t * kTileRows + n) + (unsigned)G * 16u;
 #pragma unroll
-    for (int qi = 0; qi < kQuads; ++qi) {
-      const unsigned off = row_off(r0 + qi * 4 + quad) + k_lane_off;
-      kb[qi][0] = buf_load16(krs, off);
-      kb[qi][1] = buf_load16(krs, off + kHeadDim);
-    }
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) vb[j] = buf_load8(vrs, row_off(r0 + j) + v_lane_off);
+    for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(half8_t, buf_load16(krs, off + (unsigned)s * 64u));
   };
-  if (ntiles > 0) load_tile(kA, vA, 0);   // HBM traffic starts before the prologue
+  // V tile t, row-major: lane l holds 16 B of row 16t + 2j + l/32 at dims 8(l%32)
+  auto load_v = [&](uint4 (&vr)[8], int t) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vr[j] = buf_load16(vrs, row_off(wr0 + t * kTileRows + 2 * j + (lane >> 5)) + (unsigned)(lane & 31) * 16u);
+  };
 
-  // ---- prologue: RoPE table, q, and this token's k/v ----
-  const int rdim = p.rotary_dim;
-  const int rhalf = rdim >> 1;
-  if (tid < rhalf) {
-    // angle = position * theta^(-2i/r), formed and reduced mod 2*pi in fp64
-    // (an fp32 angle at position 32767 would be off by ~4e-3 rad); the
-    // reduced angle is in [-pi, pi], where fp32 sin/cos are accurate.
-    const double inv = exp2(-(2.0 * (double)tid / (double)rdim) * p.log2_theta);
-    const double ang = (double)sd.position * inv;
-    const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
-    double red = fma(-k, 6.283185307179586, ang);               // 2 pi, high part
-    red = fma(-k, 2.4492935982947064e-16, red);                 // 2 pi, low part
-    float sn, cs;
-    sincosf((float)red, &sn, &cs);
-    s_cos[tid] = cs;
-    s_sin[tid] = sn;
-  }
-  __syncthreads();
+  half8_t kA[8], kB[8];
+  if (ntiles > 0) load_k(kA, 0);
+  if (ntiles > 1) load_k(kB, 1);
 
-  const float *row_in = p.qkv + (size_t)b * p.ld_qkv;
+  // Qf B-fragments: lane (G, n) holds column n, dims 32s + 8G .. +8 of
+  // n < 4: hi(q_n); 4 <= n < 8: lo(q_{n-4}); else 0   (q pre-scaled)
+  half8_t qf[8];
   {
-    const int d = tid;   // one dim of each of the 4 heads
+    const float *qh = p.q + (size_t)b * p.ld_q + (size_t)(g * kGroup + (n & 3)) * kHeadDim + G * 8;
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      const float *qh = row_in + (size_t)(g * kGroup + i) * kHeadDim;
-      float val = qh[d];
-      if (d < rdim) {
-        const bool lo = d < rhalf;
-        const int j = lo ? d : d - rhalf;
-        const float other = lo ? qh[d + rhalf] : qh[d - rhalf];
-        val = lo ? val * s_cos[j] - other * s_sin[j] : val * s_cos[j] + other * s_sin[j];
+    for (int s = 0; s < 8; ++s) {
+      const float4 x0 = *reinterpret_cast<const float4 *>(qh + s * 32);
+      const float4 x1 = *reinterpret_cast<const float4 *>(qh + s * 32 + 4);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xs = x[i] * p.qscale;
+        const _Float16 hi = (_Float16)xs;
+        const _Float16 lo = (_Float16)(xs - (float)hi);
+        qf[s][i] = n < 4 ? hi : (n < 8 ? lo : (_Float16)0.f);
       }
-      s_q[i][d] = val * p.qscale;
-    }
-    if (has_cur) {
-      const float *kh = row_in + (size_t)Hq * kHeadDim + (size_t)g * kHeadDim;
-      const float *vh = row_in + (size_t)(Hq + Hk) * kHeadDim + (size_t)g * kHeadDim;
-      float kv = kh[d];
-      if (d < rdim) {
-        const bool lo = d < rhalf;
-        const int j = lo ? d : d - rhalf;
-        const float other = lo ? kh[d + rhalf] : kh[d - rhalf];
-        kv = lo ? kv * s_cos[j] - other * s_sin[j] : kv * s_cos[j] + other * s_sin[j];
-      }
-      const _Float16 k16 = (_Float16)kv;
-      const _Float16 v16 = (_Float16)vh[d];
-      const size_t off = (size_t)sd.slot * Hk * kHeadDim + (size_t)g * kHeadDim + d;
-      sd.k[off] = k16;
-      sd.v[off] = v16;
-      s_kcur[d] = (float)k16;
-      s_vcur[d] = (float)v16;
     }
   }
-  __syncthreads();
-  if (has_cur) {   // wave w scores this token's row for head w
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s = fmaf(s_q[w][lane * 4 + e], s_kcur[lane * 4 + e], s);
-    s = wave_sum(s);
-    if (lane == 0) s_cur[w] = s;
-  }
-  float qreg[kGroup][16];
-#pragma unroll
-  for (int i = 0; i < kGroup; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qreg[i][e] = s_q[i][sub * 8 + e];
-      qreg[i][8 + e] = s_q[i][kHeadDim / 2 + sub * 8 + e];
-    }
-  __syncthreads();
 
-  // ---- per-wave online softmax over this wave's rows ----
-  const int h_l = lane & 3;               // head of the score this lane holds
-  const int q_l = (lane >> 2) & 3;        // row group of the score this lane holds
-  const int r_l = 4 * q_l + quad;         // row (within the tile) of that score
-  float m_run = -INFINITY;                // per head h_l
-  float l_run = 0.f;
-  float acc[kGroup][4];
+  // ---- pass 1: scores and their max ----
+  float4 *sc4 = &s_sc4[w][0][0];
+  float *scf = reinterpret_cast<float *>(sc4);
+  constexpr int kScStride = TPW * kTileRows;     // floats per head in s_sc4[w]
+  float mloc = -INFINITY;
+  auto scores = [&](const half8_t (&kf)[8], int t) {
+    floatx4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < kGroup; ++i)
+    for (int s = 0; s < 8; ++s) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], d, 0, 0, 0);
+    // d[i] = S[row 4G+i][column n]; add the low-part column n+4 to column n
+    float sv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
-  float4 *pw = s_pw[w];
-  float *pwf = reinterpret_cast<float *>(pw);
-
-  auto process = [&](const uint4 (&kb)[kQuads][2], const uint2 (&vb)[RPT], int it) {
-    const int r0 = wr0 + it * RPT;
-    float my_s = -INFINITY;
-#pragma unroll
-    for (int qi = 0; qi < kQuads; ++qi) {
-      const _Float16 *k0 = reinterpret_cast<const _Float16 *>(&kb[qi][0]);
-      const _Float16 *k1 = reinterpret_cast<const _Float16 *>(&kb[qi][1]);
-      float a[kGroup] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ka = (float)k0[e];
-        const float kc = (float)k1[e];
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-          a[i] = fmaf(ka, qreg[i][e], a[i]);
-          a[i] = fmaf(kc, qreg[i][8 + e], a[i]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) a[i] = row_sum16(a[i]);
-      const float sel = h_l == 0 ? a[0] : h_l == 1 ? a[1] : h_l == 2 ? a[2] : a[3];
-      if (q_l == qi) my_s = sel;
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = d[i] + dpp<0x104>(d[i]);             // row_shl:4 -> value of lane n+4
+      if (wr0 + t * kTileRows + 4 * G + i >= wend) sv[i] = -INFINITY;
     }
-    const int rel = r0 + r_l;
-    const bool cur_here = has_cur && rel == cur_rel;
-    if (cur_here) my_s = s_cur[h_l];
-    if (q_l >= kQuads || rel >= wr0 + wrows) my_s = -INFINITY;
-
-    const float m_new = fmaxf(m_run, head_max(my_s));
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-    const float pr = my_s == -INFINITY ? 0.f : exp2f(my_s - m_new);
-    l_run = fmaf(l_run, alpha, head_sum(pr));
-    m_run = m_new;
-    if (q_l < kQuads) pwf[r_l * 4 + h_l] = pr;
-    float al[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) al[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][e] *= al[i];
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const float4 pp = pw[j];
-      const _Float16 *vh = reinterpret_cast<const _Float16 *>(&vb[j]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float vv = (float)vh[e];
-        acc[0][e] = fmaf(vv, pp.x, acc[0][e]);
-        acc[1][e] = fmaf(vv, pp.y, acc[1][e]);
-        acc[2][e] = fmaf(vv, pp.z, acc[2][e]);
-        acc[3][e] = fmaf(vv, pp.w, acc[3][e]);
-      }
-    }
-    const int jc = cur_rel - r0;   // this token's row: its V comes from LDS
-    if (has_cur && jc >= 0 && jc < RPT) {
-      const float4 pp = pw[jc];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float vv = s_vcur[lane * 4 + e];
-        acc[0][e] = fmaf(vv, pp.x, acc[0][e]);
-        acc[1][e] = fmaf(vv, pp.y, acc[1][e]);
-        acc[2][e] = fmaf(vv, pp.z, acc[2][e]);
-        acc[3][e] = fmaf(vv, pp.w, acc[3][e]);
-      }
+    if (n < kGroup) {
+      sc4[n * (kScStride / 4) + t * 4 + G] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+      mloc = fmaxf(mloc, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     }
   };
-
-  for (int it = 0; it < ntiles; it += 2) {
-    if (it + 1 < ntiles) load_tile(kB, vB, it + 1);
-    process(kA, vA, it);
-    if (it + 1 >= ntiles) break;
-    if (it + 2 < ntiles) load_tile(kA, vA, it + 2);
-    process(kB, vB, it + 1);
+  for (int t = 0; t < ntiles; t += 2) {
+    scores(kA, t);
+    if (t + 2 < ntiles) load_k(kA, t + 2);
+    if (t + 1 >= ntiles) break;
+    scores(kB, t + 1);
+    if (t + 3 < ntiles) load_k(kB, t + 3);
   }
+  uint4 vA[8], vB[8];
+  if (ntiles > 0) load_v(vA, 0);
+  if (ntiles > 1) load_v(vB, 1);
+  // per-head max over the wave's rows: lanes (G, n < 4) -> all lanes of column n; lanes n = 4..7 take head n-4
+  float mh = mloc;
+  mh = fmaxf(mh, __shfl_xor(mh, 16));
+  mh = fmaxf(mh, __shfl_xor(mh, 32));
+  const float m_lo = dpp<0x114>(mh);               // row_shr:4 -> value of lane n-4
+  const float m_row = n < 4 ? mh : m_lo;           // max of the head this lane's P row uses
 
-  // ---- merge the 4 waves, write this chunk's partials ----
-  if (lane < kGroup) {
-    s_mw[w][lane] = m_run;
-    s_lw[w][lane] = l_run;
-  }
+  // ---- pass 2: P V ----
+  floatx4_t acc[16];
 #pragma unroll
-  for (int i = 0; i < kGroup; ++i)
-    s_acc[w][i][lane] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  for (int c = 0; c < 16; ++c) acc[c] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  _Float16 *sv = s_v[w];
+  const int ph_head = n & 3;
+  auto pv = [&](const uint4 (&vr)[8], int t) {
+    // stage the V tile (row-major, padded rows)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4 *>(sv + (2 * j + (lane >> 5)) * kVStride + (lane & 31) * 8) = vr[j];
+    // P A-fragment: lane (G, n) holds P[row n][k = rows 4G..4G+3]
+    half4_t pf = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+    if (n < 8) {
+      const float4 s4 = sc4[ph_head * (kScStride / 4) + t * 4 + G];
+      const float sx[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pr = sx[i] == -INFINITY ? 0.f : exp2f(sx[i] - m_row);
+        const _Float16 hi = (_Float16)pr;
+        pf[i] = n < 4 ? hi : (_Float16)(pr - (float)hi);
+        if (n < 4) lsum += pr;
+      }
+    }
+    // B fragments by transposed LDS reads: source lane (G, n) points at
+    // row 4G + n/4, dims 16c + 4(n%4) .. +4
+    const int vrow = 4 * G + (n >> 2);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const short4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4_t *)(sv + vrow * kVStride + 16 * c + 4 * (n & 3)));
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pf, __builtin_bit_cast(half4_t, vt), acc[c], 0, 0, 0);
+    }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    pv(vA, t);
+    if (t + 2 < ntiles) load_v(vA, t + 2);
+    if (t + 1 >= ntiles) break;
+    pv(vB, t + 1);
+    if (t + 3 < ntiles) load_v(vB, t + 3);
+  }
+
+  // ---- combine hi + lo rows, merge the waves of each KV head ----
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  // acc[c][i] at lane (G, n) = O_part[row 4G + i][dim 16c + n]; rows 0-3 (G = 0)
+  // are the high parts of heads 0-3, rows 4-7 (G = 1) the low parts.
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[c][i] += __shfl_xor(acc[c][i], 16);
+  if (G == 0) {
+    float *oa = reinterpret_cast<float *>(&s_acc[w][0][0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+        *reinterpret_cast<float4 *>(oa + i * kHeadDim + n * 16 + c4 * 4) =
+            make_float4(acc[c4 * 4][i], acc[c4 * 4 + 1][i], acc[c4 * 4 + 2][i], acc[c4 * 4 + 3][i]);
+  }
+  if (lane < kGroup) {
+    s_mw[w][lane] = ntiles > 0 ? mh : -INFINITY;
+    s_lw[w][lane] = lsum;
+  }
   __syncthreads();
   {
     const float *red = reinterpret_cast<const float *>(s_acc);
     const int d = tid;
+    const int ridx = (d % 16) * 16 + d / 16;       // where dim d sits in a wave's [n][c] layout
+    for (int hh = 0; hh < hpg; ++hh) {
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_mw[ww][i]);
-      float o = 0.f, L = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        const float mw = s_mw[ww][i];
-        const float wgt = mw == -INFINITY ? 0.f : exp2f(mw - M);
-        o = fmaf(wgt, red[(ww * kGroup + i) * kHeadDim + d], o);
-        L = fmaf(wgt, s_lw[ww][i], L);
-      }
-      p.part_o[((size_t)cid * Hq + g * kGroup + i) * kHeadDim + d] = o;
-      if (d == 0) {
-        float *ml = p.part_ml + ((size_t)cid * Hq + g * kGroup + i) * 2;
-        ml[0] = M;
-        ml[1] = L;
+      for (int i = 0; i < kGroup; ++i) {
+        float M = -INFINITY;
+        for (int ww = hh * wph; ww < (hh + 1) * wph; ++ww) M = fmaxf(M, s_mw[ww][i]);
+        float o = 0.f, L = 0.f;
+        for (int ww = hh * wph; ww < (hh + 1) * wph; ++ww) {
+          const float mw = s_mw[ww][i];
+          const float wgt = mw == -INFINITY ? 0.f : exp2f(mw - M);
+          o = fmaf(wgt, red[(ww * kGroup + i) * kHeadDim + ridx], o);
+          L = fmaf(wgt, s_lw[ww][i], L);
+        }
+        const int qh = (g0 + hh) * kGroup + i;
+        p.part_o[((size_t)cid * Hq + qh) * kHeadDim + d] = o;
+        if (d == 0) {
+          float *ml = p.part_ml + ((size_t)cid * Hq + qh) * 2;
+          ml[0] = M;
+          ml[1] = L;
+        }
       }
     }
   }
@@ -541,13 +617,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
 
 // Merge of the split-K partials and the headwise gate.
 // Grid (Hq * kCombineSplit, nseq).  Workgroup (h, part) owns head h and dims
-// [part*64, part*64 + 64).  Thread (cg, dq): dq = tid % 16 owns 4 dims, chunk
-// group cg = tid / 16 takes chunks cg, cg + 16, ...; each thread issues all
-// of its loads (up to 8 at a time) before using any.
-constexpr int kCombineSplit = 4;
-constexpr int kCombineDims = kHeadDim / kCombineSplit;   // 64
-constexpr int kCombineQuads = kCombineDims / 4;           // 16 threads per chunk row
-constexpr int kCombineGroups = kThreads / kCombineQuads;  // 16 chunk groups
+// [part*32, part*32 + 32).  Thread (cg, dq): dq = tid % 8 owns 4 dims, chunk
+// group cg = tid / 8 takes chunks cg, cg + 32, ...; each thread issues all of
+// its loads (up to 8 at a time) before using any.
+constexpr int kCombineSplit = 8;
+constexpr int kCombineDims = kHeadDim / kCombineSplit;   // 32
+constexpr int kCombineQuads = kCombineDims / 4;           // 8 threads per chunk row
+constexpr int kCombineGroups = kThreads / kCombineQuads;  // 32 chunk groups
 constexpr int kCombineBatch = 8;
 
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams p) {
@@ -703,6 +779,17 @@ hipError_t gemv1_dispatch(const GemvParams &p, hipStream_t stream) {
   }
 }
 
+template <int NIT>
+hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
+  const int pairs = (p.num_heads + 2 * p.num_kv_heads) * (kHeadDim / 2) + p.num_heads / 2;
+  const dim3 grid((pairs + 3) / 4);
+  if (p.batch == 1)
+    hipLaunchKernelGGL((qkv_rope_kernel<NIT, 1>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((qkv_rope_kernel<NIT, 4>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream) {
@@ -713,9 +800,25 @@ hipError_t launch_gemv(const GemvParams &p, hipStream_t stream) {
   return gemv_dispatch_nit<1>(p, rows, stream);
 }
 
+hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {
+  switch ((p.hidden + 511) / 512) {
+    case 1: return qkv_launch<1>(p, stream);
+    case 2: return qkv_launch<2>(p, stream);
+    case 3: return qkv_launch<3>(p, stream);
+    case 4: return qkv_launch<4>(p, stream);
+    case 5: return qkv_launch<5>(p, stream);
+    case 6: return qkv_launch<6>(p, stream);
+    case 7: return qkv_launch<7>(p, stream);
+    case 8: return qkv_launch<8>(p, stream);
+    case 9: case 10: return qkv_launch<10>(p, stream);
+    case 11: case 12: return qkv_launch<12>(p, stream);
+    default: return qkv_launch<16>(p, stream);
+  }
+}
+
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
-  const dim3 grid(p.total_chunks, p.num_kv_heads);
-  hipLaunchKernelGGL(attn_partial_kernel<8>, grid, dim3(kThreads), 0, stream, p);
+  const dim3 grid(p.total_chunks, p.num_kv_heads / p.hpg);
+  hipLaunchKernelGGL(attn_partial_kernel<kMaxWaveRows / kTileRows>, grid, dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,

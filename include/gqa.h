@@ -85,7 +85,7 @@ typedef struct {
 
 /* One sequence's K/V cache for this layer ([kvw] a slot is one position's row
  * of Hk*D fp16 values; attention reads the layer buffer from row 0).
- *   k, v        device fp16 [capacity][Hk][D]; the call WRITES row
+ *   k, v        device fp16 [capacity][Hk][D]; the block WRITES row
  *               gqa_kv_slot(position, ring_capacity) of both (this token's
  *               RoPE'd k and its v) and reads only rows of the window.
  *   capacity    rows allocated (>= 1).
@@ -162,23 +162,30 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
  * step can be checked and timed on its own.
  * ------------------------------------------------------------------------- */
 
-/* [attn] the fused q_k_v_proj GEMV and the g_proj GEMV over the same input.
- *   x       device fp32 [batch][H]
- *   qkv     device fp32 [batch][Hq*D + 2*Hk*D]
- *   gate_logits  device fp32 [batch][Hq] (before the sigmoid) */
-gqa_status gqa_qkv_gate_gemv(const gqa_arch *arch, const gqa_layer_weights *weights,
-                             int32_t batch, const float *x, float *qkv, float *gate_logits,
-                             void *stream);
+/* [attn] the fused q_k_v_proj GEMV and the g_proj GEMV over the same input,
+ * the split, the per-class NeoX RoPE of q and k, and the write of k and v
+ * into this position's cache slot ([attn] GEMV, split and RoPE steps; [kvw]
+ * `kv_write_target`).  k and v are rounded to fp16 once, after RoPE.
+ *   x            device fp32 [batch][H]
+ *   q_roped      device fp32 [batch][Hq*D]: RoPE'd q, head h at [h*D, (h+1)*D)
+ *   gate_logits  device fp32 [batch][Hq] (before the sigmoid)
+ *   seqs, is_full as for gqa_attention_block_decode (only the slot is used).
+ * Side effect: each sequence's cache slot row for `position` is written. */
+gqa_status gqa_qkv_rope_kv(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,
+                           const gqa_kv_seq *seqs, int32_t batch, const float *x, float *q_roped,
+                           float *gate_logits, void *stream);
 
-/* [attn] the split into the cache slots, the per-class RoPE of q and of k,
- * the decode attention over the window, and the headwise sigmoid gate.
- *   qkv          device fp32 [batch][Hq*D + 2*Hk*D] (projection output)
+/* [attn] the decode attention over the window (full layers: causal over
+ * [0, seq_len); sliding layers: the last sliding_window positions, read
+ * through the ring once it has wrapped) and the headwise sigmoid gate.  The
+ * cache must already hold this token's row (gqa_qkv_rope_kv writes it).
+ *   q_roped      device fp32 [batch][Hq*D]
  *   gate_logits  device fp32 [batch][Hq]
  *   attn_gated   device fp32 [batch][Hq*D]: head h at [h*D, (h+1)*D)
  *   seqs, is_full, workspace as for gqa_attention_block_decode.
- * Side effect: the cache slot rows, as for the block. */
+ * Reads the caches only. */
 gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs,
-                               int32_t batch, const float *qkv, const float *gate_logits,
+                               int32_t batch, const float *q_roped, const float *gate_logits,
                                float *attn_gated, void *workspace, size_t workspace_bytes,
                                void *stream);
 

@@ -27,20 +27,34 @@ if not torch.cuda.is_available():  # collected on a CPU host only with -m gpu
 # projections
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("hidden,batch", [(1024, 1), (2560, 1), (776, 3), (264, 5), (2560, 32),
-                                          (8192, 1), (4096, 2)])
-def test_qkv_gate_gemv(hidden, batch):
-    say(f"qkv_gate_gemv hidden={hidden} batch={batch}")
-    a = synth.Arch(hidden=hidden)
-    w_qkv = synth.random_bf16((a.qkv_rows, hidden), 0, 10, hidden)
-    w_g = synth.random_bf16((a.num_heads, hidden), 0, 10, hidden + 1)
-    x = synth.random_hidden(hidden, batch, 0, 10)
-    qkv = torch.empty((batch, a.qkv_rows), dtype=torch.float32, device="cuda")
-    gl = torch.empty((batch, a.num_heads), dtype=torch.float32, device="cuda")
-    gqa.qkv_gate_gemv(arch_of(a), bits_to_dev(w_qkv), bits_to_dev(w_g), f32_to_dev(x), qkv, gl)
+# (hidden, is_full, positions, ring_capacity)
+QKV_CASES = [
+    (1024, False, [63], 0), (2560, True, [4095], 0), (1024, False, [32767], 512),
+    (776, True, [5, 900, 17], 0), (264, False, [0, 511, 512, 513, 2000], 512),
+    (2560, True, [int(n) - 1 for n in synth.cfg5_lengths()], 0), (8192, True, [100], 0),
+    (4096, False, [1000, 31], 0), (2560, True, list(range(3, 3 + 40 * 5, 5)), 0),
+]
+
+
+@pytest.mark.parametrize("hidden,is_full,positions,ring", QKV_CASES,
+                         ids=[f"h{c[0]}_{'full' if c[1] else 'sliding'}_b{len(c[2])}" for c in QKV_CASES])
+def test_qkv_rope_kv(hidden, is_full, positions, ring):
+    """Projections + split + RoPE + fp16 KV-slot write against the oracle."""
+    say(f"qkv_rope_kv hidden={hidden} full={is_full} batch={len(positions)} ring={ring}")
+    case = synth.block_case("qkv", hidden, is_full, positions, ring_capacity=ring, seed=0,
+                            case_id=12)
+    dev = DevBlock(case)
+    a = dev.arch
+    b = case.batch
+    q = torch.empty((b, a.q_dim), dtype=torch.float32, device="cuda")
+    gl = torch.empty((b, a.num_heads), dtype=torch.float32, device="cuda")
+    gqa.qkv_rope_kv(a, dev.w_qkv, dev.w_g, is_full, dev.seqs(), dev.x, q, gl)
     torch.cuda.synchronize()
-    assert_parity(qkv.cpu().numpy(), oracle.gemv(oracle.bf16_bits_to_f64(w_qkv), x), "qkv")
-    assert_parity(gl.cpu().numpy(), oracle.gemv(oracle.bf16_bits_to_f64(w_g), x), "gate logits")
+    ref = oracle.block_decode(case.arch, is_full, case.w_qkv, case.w_g, case.w_o, case.x,
+                              case.seqs)
+    assert_parity(q.cpu().numpy(), ref.q_roped.reshape(b, -1), "RoPE'd q")
+    assert_parity(gl.cpu().numpy(), ref.gate_logits, "gate logits")
+    check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, "qkv_rope_kv")
 
 
 @pytest.mark.parametrize("hidden,batch", [(1024, 1), (2560, 1), (776, 3), (2560, 32), (6144, 2)])
@@ -56,7 +70,7 @@ def test_o_proj_gemv(hidden, batch):
 
 
 # ----------------------------------------------------------------------------
-# split + RoPE + KV write + attention + gate, from a given qkv
+# attention + gate over the cache window, from a given RoPE'd q
 # ----------------------------------------------------------------------------
 
 # (name, is_full, positions, ring_capacity, capacities or None)
@@ -69,6 +83,7 @@ ATTN_CASES = [
     ("full_pos4095", True, [4095], 0, None),
     ("full_pos20000_multitile", True, [20000], 0, None),
     ("full_pos32767", True, [32767], 0, None),
+    ("full_pos100000", True, [100000], 0, None),
     ("full_cap_larger", True, [700], 0, [2048]),
     ("sliding_linear_pos63", False, [63], 0, [64]),
     ("sliding_linear_pos1000", False, [1000], 0, None),
@@ -97,12 +112,24 @@ def _attn_inputs(name, is_full, positions, ring, caps, case_id):
         seqs.append(synth.make_cache(arch, 0, case_id, 100 + 16 * i, cap, ring, p))
     case = synth.BlockCase(name=name, arch=arch, is_full=is_full, w_qkv=None, w_g=None,
                            w_o=None, x=np.zeros((len(positions), 1), np.float32), seqs=seqs)
-    qkv = synth.random_qkv(arch, len(positions), 0, case_id)
+    q = synth.random_hidden(arch.q_dim, len(positions), 0, case_id, tensor_id=903)
     gl = synth.random_gate_logits(arch, len(positions), 0, case_id)
-    return arch, case, qkv, gl
+    return arch, case, q, gl
 
 
-def _run_attention(arch, case, qkv, gl):
+def _oracle_attention(arch, case, q, gl):
+    """Attention over each cache as it is (the slot row already written) + gate."""
+    out = []
+    for i, s in enumerate(case.seqs):
+        sl, ks, ar = oracle.kv_window(case.is_full, s.position, arch.sliding_window,
+                                      s.ring_capacity)
+        att = oracle.attention_decode(np.asarray(q[i], np.float64).reshape(arch.num_heads, -1),
+                                      s.k, s.v, sl, ks, ar, arch.attention_scale)
+        out.append(oracle.head_gate(att, gl[i]).reshape(-1))
+    return np.stack(out)
+
+
+def _run_attention(arch, case, q, gl):
     ga = arch_of(arch)
     k = [f16_to_dev(s.k) for s in case.seqs]
     v = [f16_to_dev(s.v) for s in case.seqs]
@@ -111,7 +138,7 @@ def _run_attention(arch, case, qkv, gl):
     ws = torch.empty(gqa.workspace_size(ga, len(seqs), max(s.position + 1 for s in case.seqs)),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((len(seqs), ga.q_dim), dtype=torch.float32, device="cuda")
-    gqa.attention_gated(ga, case.is_full, seqs, f32_to_dev(qkv), f32_to_dev(gl), out, ws)
+    gqa.attention_gated(ga, case.is_full, seqs, f32_to_dev(q), f32_to_dev(gl), out, ws)
     torch.cuda.synchronize()
     return out.cpu().numpy(), k, v
 
@@ -120,12 +147,14 @@ def _run_attention(arch, case, qkv, gl):
                          ids=[c[0] for c in ATTN_CASES])
 def test_attention_gated(name, is_full, positions, ring, caps):
     say(f"attention_gated {name} positions={positions[:8]} ring={ring}")
-    arch, case, qkv, gl = _attn_inputs(name, is_full, positions, ring, caps, 20)
-    got, k, v = _run_attention(arch, case, qkv, gl)
-    ref = oracle.attention_step(arch, is_full, qkv, gl, case.seqs)
+    arch, case, q, gl = _attn_inputs(name, is_full, positions, ring, caps, 20)
+    got, k, v = _run_attention(arch, case, q, gl)
+    ref = _oracle_attention(arch, case, q, gl)
     for b in range(len(positions)):
-        assert_parity(got[b], ref.gated[b], f"{name}[{b}] gated attention")
-    check_caches(case, k, v, ref.k16, ref.v16, ref.slots, name, exact_v=True)
+        assert_parity(got[b], ref[b], f"{name}[{b}] gated attention")
+    for i, s in enumerate(case.seqs):   # the attention step only reads the caches
+        assert np.array_equal(k[i].cpu().numpy().view(np.int16), s.k.view(np.int16))
+        assert np.array_equal(v[i].cpu().numpy().view(np.int16), s.v.view(np.int16))
 
 
 # ----------------------------------------------------------------------------
@@ -134,6 +163,7 @@ def test_attention_gated(name, is_full, positions, ring, caps):
 
 ROWSET_CASES = [
     ("full_pos300_cap512", True, 300, 0, 512),
+    ("full_pos5000", True, 5000, 0, 5001),
     ("sliding_linear_pos1000", False, 1000, 0, 1001),
     ("ring_pos511", False, 511, 512, 512),
     ("ring_pos512", False, 512, 512, 512),
@@ -152,46 +182,38 @@ def _rowset_inputs(is_full, pos, ring, cap, onehot_row=None):
     hk, d = arch.num_kv_heads, arch.head_dim
     sl, ks, ar = oracle.kv_window(is_full, pos, arch.sliding_window, ring)
     owner = {}
-    for t in range(pos):                       # rows written before this token
+    for t in range(pos + 1):                   # rows written up to this token
         owner[t % ring if ring else t] = t
     rng = np.random.default_rng([3, pos, ring, cap])
     k = rng.standard_normal((cap, hk, d)).astype(np.float16)
     v = np.ones((cap, hk, d), np.float16)
-    slot = oracle.kv_slot(pos, ring)
     for r in range(cap):
         t = owner.get(r, -1)
-        if r != slot and not (ks <= t < sl):
+        if not (ks <= t < sl):
             k[r] = np.nan
             v[r] = np.nan
-    qkv = np.zeros((1, arch.qkv_rows), np.float32)
-    qkv[0, arch.q_dim:arch.q_dim + arch.kv_dim] = rng.standard_normal(arch.kv_dim)
-    qkv[0, arch.q_dim + arch.kv_dim:] = 1.0    # this token's v
     if onehot_row is not None:
         v[:] = np.where(np.isnan(v), v, np.float16(0))
-        qkv[0, arch.q_dim + arch.kv_dim:] = 0.0
-        if onehot_row == slot:
-            qkv[0, arch.q_dim + arch.kv_dim:] = 1.0
-        else:
-            v[onehot_row] = 1.0
+        v[onehot_row] = 1.0
+    q = np.zeros((1, arch.q_dim), np.float32)
     gl = np.full((1, arch.num_heads), 30.0, np.float32)
     seq = synth.SeqCache(k=k, v=v, ring_capacity=ring, position=pos)
     case = synth.BlockCase(name="rowset", arch=arch, is_full=is_full, w_qkv=None, w_g=None,
                            w_o=None, x=np.zeros((1, 1), np.float32), seqs=[seq])
-    return arch, case, qkv, gl, sl - ks, owner, (ks, sl)
+    return arch, case, q, gl, sl - ks, owner, (ks, sl)
 
 
 @pytest.mark.parametrize("name,is_full,pos,ring,cap", ROWSET_CASES, ids=[c[0] for c in ROWSET_CASES])
 def test_rows_read_are_exactly_the_window(name, is_full, pos, ring, cap):
     say(f"rowset {name}")
-    arch, case, qkv, gl, n, owner, (ks, sl) = _rowset_inputs(is_full, pos, ring, cap)
-    got, _, _ = _run_attention(arch, case, qkv, gl)
+    arch, case, q, gl, n, owner, (ks, sl) = _rowset_inputs(is_full, pos, ring, cap)
+    got, _, _ = _run_attention(arch, case, q, gl)
     # any row outside the window would bring a NaN in; all in-window rows are 1
     assert np.array_equal(got[0], np.ones_like(got[0])), f"{name}: {got[0][:4]}"
-    # one-hot V on the oldest in-window row: output 1/n recovers n exactly
-    slot = oracle.kv_slot(pos, ring)
-    oldest = slot if n == 1 else [r for r, t in owner.items() if t == ks][0]
-    arch, case, qkv, gl, n2, _, _ = _rowset_inputs(is_full, pos, ring, cap, onehot_row=oldest)
-    got, _, _ = _run_attention(arch, case, qkv, gl)
+    # one-hot V on the oldest in-window row: the output 1/n recovers n exactly
+    oldest = [r for r, t in owner.items() if t == ks][0]
+    arch, case, q, gl, n2, _, _ = _rowset_inputs(is_full, pos, ring, cap, onehot_row=oldest)
+    got, _, _ = _run_attention(arch, case, q, gl)
     assert np.all(np.abs(got[0] * n - 1.0) < 4e-7), f"{name}: {got[0][0]} vs 1/{n}"
     assert int(round(1.0 / float(got[0][0]))) == n
 
@@ -213,14 +235,14 @@ def test_ring_equals_linear_bitwise(pos):
     ring_v = np.zeros((512, hk, d), np.float16)
     for t in range(lo, pos + 1):
         ring_k[t % 512], ring_v[t % 512] = lin_k[t], lin_v[t]
-    qkv = synth.random_qkv(arch, 1, 0, 30)
+    q = synth.random_hidden(arch.q_dim, 1, 0, 30, tensor_id=903)
     gl = synth.random_gate_logits(arch, 1, 0, 30)
     outs = []
     for k, v, ring in ((lin_k, lin_v, 0), (ring_k, ring_v, 512)):
         seq = synth.SeqCache(k=k, v=v, ring_capacity=ring, position=pos)
         case = synth.BlockCase(name="rl", arch=arch, is_full=False, w_qkv=None, w_g=None,
                                w_o=None, x=np.zeros((1, 1), np.float32), seqs=[seq])
-        outs.append(_run_attention(arch, case, qkv, gl)[0])
+        outs.append(_run_attention(arch, case, q, gl)[0])
     assert np.array_equal(outs[0].view(np.int32), outs[1].view(np.int32))
 
 
@@ -254,12 +276,12 @@ def test_block_equals_its_steps_bitwise(name):
     dev2 = DevBlock(case)
     a = dev2.arch
     b = case.batch
-    qkv = torch.empty((b, a.qkv_rows), dtype=torch.float32, device="cuda")
+    q = torch.empty((b, a.q_dim), dtype=torch.float32, device="cuda")
     gl = torch.empty((b, a.num_heads), dtype=torch.float32, device="cuda")
     attn = torch.empty((b, a.q_dim), dtype=torch.float32, device="cuda")
     out = torch.empty((b, a.hidden), dtype=torch.float32, device="cuda")
-    gqa.qkv_gate_gemv(a, dev2.w_qkv, dev2.w_g, dev2.x, qkv, gl)
-    gqa.attention_gated(a, case.is_full, dev2.seqs(), qkv, gl, attn, dev2.ws)
+    gqa.qkv_rope_kv(a, dev2.w_qkv, dev2.w_g, case.is_full, dev2.seqs(), dev2.x, q, gl)
+    gqa.attention_gated(a, case.is_full, dev2.seqs(), q, gl, attn, dev2.ws)
     gqa.o_proj_gemv(a, dev2.w_o, attn, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.int32), out_block.view(np.int32))

@@ -170,9 +170,15 @@ def test_null_seqs_and_null_arch():
 def test_step_entry_points_validate():
     a = B.c_arch(gqa.Arch(hidden=1024))
     w = B.c_weights(FAKE, FAKE, FAKE)
-    assert B.raw_call("gqa_qkv_gate_gemv", ctypes.byref(a), ctypes.byref(w), 1, MISALIGNED, FAKE,
-                      FAKE, None) == INVALID
-    assert B.raw_call("gqa_qkv_gate_gemv", ctypes.byref(a), ctypes.byref(w), 0, 0, 0, 0, None) == OK
+    arr = B.c_seq_array(1)
+    arr[0] = _seq()
+    assert B.raw_call("gqa_qkv_rope_kv", ctypes.byref(a), ctypes.byref(w), 1, arr, 1, MISALIGNED,
+                      FAKE, FAKE, None) == INVALID
+    arr[0] = _seq(pos=100, cap=100)
+    assert B.raw_call("gqa_qkv_rope_kv", ctypes.byref(a), ctypes.byref(w), 1, arr, 1, FAKE,
+                      FAKE, FAKE, None) == INVALID
+    assert B.raw_call("gqa_qkv_rope_kv", ctypes.byref(a), ctypes.byref(w), 1, None, 0, 0, 0, 0,
+                      None) == OK
     assert B.raw_call("gqa_o_proj_gemv", ctypes.byref(a), ctypes.byref(B.c_weights(FAKE, FAKE, 0)),
                       1, FAKE, FAKE, None) == INVALID
     arr = B.c_seq_array(1)
