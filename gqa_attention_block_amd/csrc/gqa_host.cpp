@@ -130,28 +130,13 @@ gqa_status window_of(int is_full, int32_t position, int32_t window, int32_t ring
 // ---- sequences and the split-K plan ----------------------------------------
 
 struct Plan {
-  int hpg = 4;
-  int tile = kMinChunk;
-  int chunk = kMinChunk;
+  int chunk = kTileRows;
   struct Group {
     int first = 0, count = 0, total_chunks = 0;
   };
   std::vector<Group> groups;
   size_t max_group_chunks = 0;
 };
-
-int num_cus_of_current_device() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 // Resolve and check every sequence.  Fills one SeqDesc per sequence (without
 // chunk_begin) and the attended-row counts.
@@ -205,31 +190,24 @@ gqa_status resolve_seqs(const gqa_arch *a, int is_full, const gqa_kv_seq *seqs, 
   return GQA_OK;
 }
 
-// Split-K plan.  An attention workgroup covers a chunk of rows for hpg KV
-// heads (hpg = 4 when Hk is a multiple of 4, one wave per head).  The chunk is
-// the largest multiple of kMinChunk rows (up to what a wave keeps scores for)
-// that still gives every CU two workgroups, so partials stay few while the
-// chip stays full.  Sequences go in launch groups of up to kMaxSeqPerLaunch.
-int heads_per_group(int num_kv_heads) {
-  if (num_kv_heads % 4 == 0) return 4;
-  if (num_kv_heads % 2 == 0) return 2;
-  return 1;
-}
-
+// Split-K plan.  One attention wave covers a chunk of rows for one KV head.
+// The chunk is the largest multiple of kTileRows that still gives every
+// launch about kAttnTargetWaves waves (longer chunks spend less on each
+// wave's set-up and on the partials; fewer waves than the chip holds leave
+// HBM bandwidth unused).  With C(c) chunks at chunk size c this keeps
+// C <= 2 * kAttnTargetWaves / Hk + sequences (see max_chunks).
 Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
   Plan plan;
-  plan.hpg = heads_per_group(num_kv_heads);
-  const long target = 2L * num_cus_of_current_device();
-  const int groups = num_kv_heads / plan.hpg;
-  auto wgs = [&](int chunk) {
+  auto waves = [&](int chunk) {
     long n = 0;
-    for (const SeqDesc &s : seqs) n += (long)ceil_div(s.n, chunk) * groups;
+    for (const SeqDesc &s : seqs) n += (long)ceil_div(s.n, chunk) * num_kv_heads;
     return n;
   };
-  const int max_chunk = kMaxWaveRows * (4 / plan.hpg);   // a wave keeps <= kMaxWaveRows scores
-  int chunk = kMinChunk;
-  while (chunk + kMinChunk <= max_chunk && wgs(chunk + kMinChunk) >= target) chunk += kMinChunk;
-  plan.tile = kMinChunk;
+  int longest = 1;
+  for (const SeqDesc &s : seqs) longest = std::max(longest, s.n);
+  const int cap = ceil_div(longest, kTileRows) * kTileRows;
+  int chunk = kTileRows;
+  while (chunk + kTileRows <= cap && waves(chunk + kTileRows) >= kAttnTargetWaves) chunk += kTileRows;
   plan.chunk = chunk;
   for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {
     Plan::Group g;
@@ -242,6 +220,17 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
     plan.groups.push_back(g);
   }
   return plan;
+}
+
+// Upper bound of Plan::max_group_chunks for `batch` sequences of at most
+// max_seq_len attended rows.  If the plan stops at chunk c > kTileRows because
+// C(c + kTileRows) * Hk < target, then C(c) <= N / c + B <= 2 C(c + kTileRows) + B;
+// at c = kTileRows, C(16) <= 2 C(32) likewise; at the cap C = B.
+size_t max_chunks(int num_kv_heads, int32_t batch, int32_t max_seq_len) {
+  const size_t seqs = (size_t)std::min<int32_t>(batch, kMaxSeqPerLaunch);
+  const size_t finest = (size_t)ceil_div(max_seq_len, kTileRows) * seqs;
+  const size_t bound = 2 * (size_t)ceil_div(kAttnTargetWaves, num_kv_heads) + seqs;
+  return std::min(finest, bound);
 }
 
 // ---- workspace layout -----------------------------------------------------
@@ -345,8 +334,6 @@ gqa_status run_attention(const gqa_arch *a, const std::vector<SeqDesc> &seqs, co
     p.part_ml = part_ml;
     p.num_kv_heads = a->num_kv_heads;
     p.qscale = (float)((double)a->attention_scale * kLog2e);
-    p.tile = plan.tile;
-    p.hpg = plan.hpg;
     p.chunk = plan.chunk;
     p.nseq = g.count;
     p.total_chunks = g.total_chunks;
@@ -420,11 +407,8 @@ gqa_status gqa_workspace_size(const gqa_arch *arch, int32_t batch, int32_t max_s
   if (st != GQA_OK) return st;
   if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
   if (max_seq_len < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "max_seq_len=%d must be >= 1", max_seq_len);
-  // Worst case: every sequence split into kMinChunk-row chunks, one launch
-  // group of kMaxSeqPerLaunch sequences live at a time.
-  const size_t per_seq = (size_t)ceil_div(max_seq_len, kMinChunk);
-  const size_t chunks = per_seq * (size_t)std::min<int32_t>(batch, kMaxSeqPerLaunch);
-  *bytes = block_layout(arch, batch, chunks).total;
+  // one launch group of kMaxSeqPerLaunch sequences is live at a time
+  *bytes = block_layout(arch, batch, max_chunks(arch->num_kv_heads, batch, max_seq_len)).total;
   return ok();
 }
 

@@ -46,21 +46,37 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row_sum16(v);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// v_permlane16_swap / v_permlane32_swap (VALU, no LDS traffic): every lane
+// gets, in .x and .y, the values of its lane in the two rows of its row pair
+// (16-lane rows 0/1 and 2/3), resp. of its lane in the two 32-lane halves.
+__device__ __forceinline__ float2 pair16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float2 pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum / max over lanes l, l^16, l^32, l^48.
+__device__ __forceinline__ float sum_across_rows(float v) {
+  float2 a = pair16(v);
+  a = pair32(a.x + a.y);
+  return a.x + a.y;
+}
+__device__ __forceinline__ float max_across_rows(float v) {
+  float2 a = pair16(v);
+  a = pair32(fmaxf(a.x, a.y));
+  return fmaxf(a.x, a.y);
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return sum_across_rows(row_sum16(v)); }
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0xB1>(v));
   v = fmaxf(v, dpp<0x4E>(v));
   v = fmaxf(v, dpp<0x141>(v));
   v = fmaxf(v, dpp<0x140>(v));
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  return max_across_rows(v);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -361,37 +377,41 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
 // ---------------------------------------------------------------------------
 // Attention, split-K over the window, on the matrix cores.
 //
-// Grid (total_chunks, Hk / hpg).  Workgroup (chunk c of sequence b, head
-// group y) owns logical positions [t0, t1) of that sequence for hpg KV heads
-// (hpg = 4 when Hk is a multiple of 4): wave w works on KV head
-// y*hpg + w / wph and on part w % wph of the rows (wph = 4 / hpg waves per
-// head).  Each KV head's K/V bytes are read from HBM once and serve its 4
-// query heads.  This token's k and v are already in the cache (the qkv kernel
-// wrote them), so every row of the window is read the same way.
+// Every wave is independent: wave id = 4 * blockIdx.x + w owns chunk
+// cid = id / Hk (logical positions [t0, t0 + chunk) of one sequence) for KV
+// head g = id % Hk, and serves that head's 4 query heads, so each KV byte is
+// read from HBM once.  The 4 waves of a workgroup are the 4 heads of one chunk
+// when Hk is a multiple of 4 (neighbouring bytes of the same rows).  This
+// token's k and v are already in the cache (the qkv kernel wrote them), so
+// every row of the window is read the same way.
 //
 // Both products are small dense contractions per 16-row tile -- S = K q for
 // 4 query heads and O += P V -- and on VALU they cost ~65 instructions per
 // row, more than the HBM stream leaves room for; on MFMA they cost ~2.
-//   pass 1  S^T[16 rows x 16] = K[16 x 256] * Qf[256 x 16] with
+// Per 16-row tile:
+//   S^T[16 rows x 16] = K[16 x 256] * Qf[256 x 16] with
 //           v_mfma_f32_16x16x32_f16: the K fragments come straight from HBM
-//           (lane l: row l%16, 8 dims), Qf's columns 0-3 hold the fp16 high
-//           part of the 4 query heads (pre-scaled by scale*log2(e)) and 4-7
-//           the fp16 low part (q - hi), so S = hi + lo keeps fp32 accuracy.
-//           Scores go to LDS; each wave tracks its max.
-//   pass 2  O[16 x 256] += P[16 x 16 rows] * V[16 rows x 256] with
+//           into registers (lane l: row l%16, 8 dims), Qf's columns 0-3 hold
+//           the fp16 high part of the 4 query heads (pre-scaled by
+//           scale*log2(e)) and 4-7 the fp16 low part (q - hi), so
+//           S = hi + lo keeps fp32 accuracy.
+//   online softmax with a lazily moved reference max (see kRescaleSlack).
+//   O[16 x 256] += P[16 x 16 rows] * V[16 rows x 256] with
 //           v_mfma_f32_16x16x16_f16: P's rows 0-3 are the fp16 high part of
-//           exp2(s - max) for the 4 heads, rows 4-7 the low part; V is staged
-//           through LDS and read back transposed (ds_read_b64_tr_b16) into
-//           the B-operand layout.
-// Two passes need no online rescaling.  K/V are read with buffer loads whose
-// out-of-range offsets return zeros without an HBM access; two tiles are in
-// flight per wave (ping-pong registers).  At the end the waves of each KV head
-// merge (max, sum, acc) in LDS and write this chunk's partial per query head.
+//           exp2(s - m) for the 4 heads, rows 4-7 the low part; V goes from
+//           HBM straight into LDS (buffer_load ... lds) and is read back
+//           transposed (ds_read_b64_tr_b16) into the B-operand layout.
+// K and V of the next tile are in flight while a tile is computed (K in
+// ping-pong registers, V in two LDS buffers).  Buffer loads whose offsets are
+// out of range return zeros without an HBM access, which pads the last tile.
+// Each wave writes its own partial (m, l, O) per query head.
 // ---------------------------------------------------------------------------
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   int s = 0;
@@ -400,38 +420,45 @@ __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   return s;
 }
 
-constexpr int kTileRows = 16;                      // rows per MFMA tile
-constexpr int kVStride = kHeadDim + 16;            // halves per staged V row (32 B pad)
+constexpr int kTileHalves = kTileRows * kHeadDim;   // one staged V tile: 8 KB
 
-template <int TPW>   // max 16-row tiles per wave
-__global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
-  __shared__ float4 s_sc4[4][kGroup][TPW * kTileRows / 4];   // scores [wave][head][row]
-  __shared__ _Float16 s_v[4][kTileRows * kVStride];          // staged V tile per wave
-  __shared__ float4 s_acc[4][kGroup][kHeadDim / 4];          // per-wave O [head][lane n][c]
-  __shared__ float s_mw[4][kGroup];
-  __shared__ float s_lw[4][kGroup];
+// One column block J of a staged V tile: 64 lanes x 16 B from HBM into LDS
+// at sv + J KB + 16 B * lane.  The block's 64 B of each row is selected with
+// the scalar offset J * 64, which moves only the global address (the
+// instruction's immediate offset would move the LDS address as well).
+template <int J>
+__device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 *sv, unsigned off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sv + J * 512), 16, off, J * 64, 0, 0);
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
-  const int hpg = p.hpg;                         // KV heads per workgroup: 1, 2 or 4
-  const int wph = 4 / hpg;                       // waves per KV head
-  const int g0 = blockIdx.y * hpg;               // first KV head of the workgroup
-  const int g = g0 + w / wph;                    // this wave's KV head
-  const int cid = blockIdx.x;
-  const int b = find_seq(p, cid);
-  const SeqDesc sd = p.seq[b];
+// Staged V tile in LDS: eight 1 KB column blocks j (dims 32j .. 32j+31), each
+// with the 16 rows at 64 B per row; rows r with bit 2 set keep their two 32 B
+// halves swapped.  A transposed read of a 16-dim slice then lands 8 rows x
+// 32 B on distinct banks in each half wave, with the slice's offset an
+// immediate.  One buffer_load ... lds writes 1 KB (64 lanes x 16 B) = one
+// column block: lane l brings row l/4, quarter l%4 of that row's 64 B.
+// One wave's work.  sv0 / sv1 are this wave's two staged V buffers; passing
+// them as restrict parameters gives their accesses alias scopes, so the
+// compiler waits for a buffer's LDS-bound loads only before reading that
+// buffer (not for the other buffer's loads, which are still in flight).
+__device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _Float16 *__restrict__ sv0,
+                                                  _Float16 *__restrict__ sv1) {
+  const int lane = threadIdx.x & 63;
   const int Hk = p.num_kv_heads;
   const int Hq = Hk * kGroup;
+  const int id = blockIdx.x * 4 + w;
+  if (id >= p.total_chunks * Hk) return;         // whole wave; the kernel has no barrier
+  const int cid = id / Hk;
+  const int g = id - cid * Hk;
+  const int b = find_seq(p, cid);
+  const SeqDesc sd = p.seq[b];
   const int t0 = sd.kv_start + (cid - sd.chunk_begin) * p.chunk;
   const int nrows = min(p.chunk, sd.kv_start + sd.n - t0);
+  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
   const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
   const int ring = sd.ring;
   const int p0 = ring ? (t0 % ring) : t0;        // physical row of t0; a chunk wraps at most once
-  const int per_wave = p.chunk / wph;
-  const int wr0 = (w % wph) * per_wave;          // first row of this wave, relative to t0
-  const int wend = min(nrows, wr0 + per_wave);   // one past its last row
-  const int ntiles = max(0, (wend - wr0 + kTileRows - 1) / kTileRows);
+  const int ring_end = ring ? ring : 0x7FFFFFFF;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(sd.k, sd.cache_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(sd.v, sd.cache_bytes);
   const unsigned head_off = (unsigned)g * kHeadDim * 2u;
@@ -440,38 +467,61 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
 
   // byte offset of row `rel` (relative to t0) of this KV head, or out of range
   auto row_off = [&](int rel) -> unsigned {
-    if (rel >= wend) return kOutOfRange;
     int ph = p0 + rel;
-    if (ring && ph >= ring) ph -= ring;
-    return (unsigned)ph * row_bytes + head_off;
+    ph -= ph >= ring_end ? ring : 0;
+    const unsigned off = __umul24((unsigned)ph, row_bytes) + head_off;   // ph, row_bytes < 2^24
+    return rel < nrows ? off : kOutOfRange;
   };
-
   // K A-fragments of tile t: lane (G, n) holds row 16t + n, dims 32s + 8G .. +8
   auto load_k = [&](half8_t (&kf)[8], int t) {
-    const unsigned off = row_off(wr0 + t * kTileRows + n) + (unsigned)G * 16u;
+    const unsigned off = row_off(t * kTileRows + n) + (unsigned)G * 16u;
 #pragma unroll
     for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(half8_t, buf_load16(krs, off + (unsigned)s * 64u));
   };
-  // V tile t, row-major: lane l holds 16 B of row 16t + 2j + l/32 at dims 8(l%32)
-  auto load_v = [&](uint4 (&vr)[8], int t) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      vr[j] = buf_load16(vrs, row_off(wr0 + t * kTileRows + 2 * j + (lane >> 5)) + (unsigned)(lane & 31) * 16u);
+  // V tile t into a staged buffer (layout above)
+  auto load_v = [&](_Float16 *sv, int t) {
+    const int r = lane >> 2;
+    const int q = lane & 3;
+    const unsigned off = row_off(t * kTileRows + r) + 32u * (unsigned)(((q >> 1) ^ (r >> 2)) & 1) +
+                         16u * (unsigned)(q & 1);
+    vload_block<0>(vrs, sv, off);
+    vload_block<1>(vrs, sv, off);
+    vload_block<2>(vrs, sv, off);
+    vload_block<3>(vrs, sv, off);
+    vload_block<4>(vrs, sv, off);
+    vload_block<5>(vrs, sv, off);
+    vload_block<6>(vrs, sv, off);
+    vload_block<7>(vrs, sv, off);
   };
 
+  // q first: its wait then does not include the tile loads issued after it
+  float4 qx[16];
+  {
+    const float *qh = p.q + (size_t)b * p.ld_q + (size_t)(g * kGroup + (n & 3)) * kHeadDim + G * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qx[2 * s] = *reinterpret_cast<const float4 *>(qh + s * 32);
+      qx[2 * s + 1] = *reinterpret_cast<const float4 *>(qh + s * 32 + 4);
+    }
+  }
+  // An even number of tiles (a padding tile is fully masked and its loads
+  // are out of range: no HBM traffic), so that the steady-state loop below has
+  // no conditional loads and the compiler's waits stay exact.
+  const int ne = (ntiles + 1) & ~1;
   half8_t kA[8], kB[8];
-  if (ntiles > 0) load_k(kA, 0);
-  if (ntiles > 1) load_k(kB, 1);
+  load_k(kA, 0);
+  load_v(sv0, 0);
+  load_k(kB, 1);
+  load_v(sv1, 1);
 
   // Qf B-fragments: lane (G, n) holds column n, dims 32s + 8G .. +8 of
   // n < 4: hi(q_n); 4 <= n < 8: lo(q_{n-4}); else 0   (q pre-scaled)
   half8_t qf[8];
   {
-    const float *qh = p.q + (size_t)b * p.ld_q + (size_t)(g * kGroup + (n & 3)) * kHeadDim + G * 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const float4 x0 = *reinterpret_cast<const float4 *>(qh + s * 32);
-      const float4 x1 = *reinterpret_cast<const float4 *>(qh + s * 32 + 4);
+      const float4 x0 = qx[2 * s];
+      const float4 x1 = qx[2 * s + 1];
       const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -483,136 +533,120 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
     }
   }
 
-  // ---- pass 1: scores and their max ----
-  float4 *sc4 = &s_sc4[w][0][0];
-  float *scf = reinterpret_cast<float *>(sc4);
-  constexpr int kScStride = TPW * kTileRows;     // floats per head in s_sc4[w]
-  float mloc = -INFINITY;
-  auto scores = [&](const half8_t (&kf)[8], int t) {
-    floatx4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], d, 0, 0, 0);
-    // d[i] = S[row 4G+i][column n]; add the low-part column n+4 to column n
-    float sv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = d[i] + dpp<0x104>(d[i]);             // row_shl:4 -> value of lane n+4
-      if (wr0 + t * kTileRows + 4 * G + i >= wend) sv[i] = -INFINITY;
-    }
-    if (n < kGroup) {
-      sc4[n * (kScStride / 4) + t * 4 + G] = make_float4(sv[0], sv[1], sv[2], sv[3]);
-      mloc = fmaxf(mloc, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-    }
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    scores(kA, t);
-    if (t + 2 < ntiles) load_k(kA, t + 2);
-    if (t + 1 >= ntiles) break;
-    scores(kB, t + 1);
-    if (t + 3 < ntiles) load_k(kB, t + 3);
-  }
-  uint4 vA[8], vB[8];
-  if (ntiles > 0) load_v(vA, 0);
-  if (ntiles > 1) load_v(vB, 1);
-  // per-head max over the wave's rows: lanes (G, n < 4) -> all lanes of column n; lanes n = 4..7 take head n-4
-  float mh = mloc;
-  mh = fmaxf(mh, __shfl_xor(mh, 16));
-  mh = fmaxf(mh, __shfl_xor(mh, 32));
-  const float m_lo = dpp<0x114>(mh);               // row_shr:4 -> value of lane n-4
-  const float m_row = n < 4 ? mh : m_lo;           // max of the head this lane's P row uses
-
-  // ---- pass 2: P V ----
+  // acc[c][i] at lane (G, n): row 4G + i, dim 16c + n of O, i.e. head i
+  // (G = 0 high part, G = 1 low part; rows 8-15 stay zero)
   floatx4_t acc[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) acc[c] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  _Float16 *sv = s_v[w];
-  const int ph_head = n & 3;
-  auto pv = [&](const uint4 (&vr)[8], int t) {
-    // stage the V tile (row-major, padded rows)
+  float m_run = -INFINITY;   // lanes (G, n < 4): reference max of head n (log2 units)
+  float l_run = 0.f;         // lanes (G, n < 4): this lane group's share of head n's sum
+  // transposed-read source of this lane: row 4G + n/4, 8 B at 8 (n % 4) within
+  // the 32 B of a slice; even slices sit in half (G & 1), odd ones in the other
+  const int vrow = 4 * G + (n >> 2);
+  const int rd_even = vrow * 64 + (G & 1) * 32 + (n & 3) * 8;   // bytes
+  const int rd_odd = vrow * 64 + ((G & 1) ^ 1) * 32 + (n & 3) * 8;
+
+  auto process = [&](const half8_t (&kf)[8], const _Float16 *sv, int t) {
+    // S^T = K Qf: d[i] = S[row 4G+i][column n]; column n+4 holds the low part
+    floatx4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint4 *>(sv + (2 * j + (lane >> 5)) * kVStride + (lane & 31) * 8) = vr[j];
-    // P A-fragment: lane (G, n) holds P[row n][k = rows 4G..4G+3]
-    half4_t pf = {(_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
-    if (n < 8) {
-      const float4 s4 = sc4[ph_head * (kScStride / 4) + t * 4 + G];
-      const float sx[4] = {s4.x, s4.y, s4.z, s4.w};
+    for (int s = 0; s < 8; ++s) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], d, 0, 0, 0);
+    float sc[4];
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pr = sx[i] == -INFINITY ? 0.f : exp2f(sx[i] - m_row);
-        const _Float16 hi = (_Float16)pr;
-        pf[i] = n < 4 ? hi : (_Float16)(pr - (float)hi);
-        if (n < 4) lsum += pr;
-      }
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = d[i] + dpp<0x104>(d[i]);             // row_shl:4 -> value of lane n+4
+      if (n >= kGroup || t * kTileRows + 4 * G + i >= nrows) sc[i] = -INFINITY;
+      tmax = fmaxf(tmax, sc[i]);
     }
-    // B fragments by transposed LDS reads: source lane (G, n) points at
-    // row 4G + n/4, dims 16c + 4(n%4) .. +4
-    const int vrow = 4 * G + (n >> 2);
+    tmax = max_across_rows(tmax);
+    // Lazy rescaling: the reference max m_run moves only when a score exceeds
+    // it by more than kRescaleSlack (log2 units), so P = exp2(s - m_run) stays
+    // <= 2^kRescaleSlack (exact in fp16 hi + lo) and the 64 accumulators are
+    // rescaled only on the rare tiles where the max jumps.
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      float al[kGroup];
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) al[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] *= al[i];
+    }
+    float pr[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = sc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - m_run);
+      psum += pr[i];
+    }
+    l_run += psum;
+    // P A-fragment: lane (G, m) holds P[row m][k = rows 4G..4G+3]; rows 0-3 the
+    // high fp16 part of head m, rows 4-7 the low part of head m-4 (from lane m-4)
+    half4_t pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = n < 4 ? pr[i] : dpp<0x114>(pr[i]);   // row_shr:4 -> value of lane n-4
+      const _Float16 hi = (_Float16)pv;
+      pf[i] = n < 4 ? hi : (n < 8 ? (_Float16)(pv - (float)hi) : (_Float16)0.f);
+    }
+    // O += P V; B fragments by transposed reads of the staged tile
+    const char *base = reinterpret_cast<const char *>(sv);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const short4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4_t *)(sv + vrow * kVStride + 16 * c + 4 * (n & 3)));
+          (lds_short4_t *)(base + (c & 1 ? rd_odd : rd_even) + (c >> 1) * 1024));
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pf, __builtin_bit_cast(half4_t, vt), acc[c], 0, 0, 0);
     }
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    pv(vA, t);
-    if (t + 2 < ntiles) load_v(vA, t + 2);
-    if (t + 1 >= ntiles) break;
-    pv(vB, t + 1);
-    if (t + 3 < ntiles) load_v(vB, t + 3);
+  // sched_barrier: the refill of a buffer stays behind the reads of it
+  for (int t = 0; t + 2 < ne; t += 2) {
+    process(kA, sv0, t);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kA, t + 2);
+    load_v(sv0, t + 2);
+    process(kB, sv1, t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kB, t + 3);
+    load_v(sv1, t + 3);
   }
+  process(kA, sv0, ne - 2);
+  process(kB, sv1, ne - 1);
 
-  // ---- combine hi + lo rows, merge the waves of each KV head ----
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  // acc[c][i] at lane (G, n) = O_part[row 4G + i][dim 16c + n]; rows 0-3 (G = 0)
-  // are the high parts of heads 0-3, rows 4-7 (G = 1) the low parts.
+  // ---- this wave's partial: add the high and low rows, write (m, l, O) ----
+  l_run = sum_across_rows(l_run);
 #pragma unroll
   for (int c = 0; c < 16; ++c)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[c][i] += __shfl_xor(acc[c][i], 16);
+    for (int i = 0; i < 4; ++i) {
+      const float2 hl = pair16(acc[c][i]);
+      acc[c][i] = hl.x + hl.y;
+    }
+  // partial layout per query head: element n * 16 + c holds dim 16c + n,
+  // so lane n of group 0 writes 16 consecutive floats per head
   if (G == 0) {
-    float *oa = reinterpret_cast<float *>(&s_acc[w][0][0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kGroup; ++i) {
+      float *o = p.part_o + ((size_t)cid * Hq + g * kGroup + i) * kHeadDim + n * 16;
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
-        *reinterpret_cast<float4 *>(oa + i * kHeadDim + n * 16 + c4 * 4) =
+        *reinterpret_cast<float4 *>(o + c4 * 4) =
             make_float4(acc[c4 * 4][i], acc[c4 * 4 + 1][i], acc[c4 * 4 + 2][i], acc[c4 * 4 + 3][i]);
-  }
-  if (lane < kGroup) {
-    s_mw[w][lane] = ntiles > 0 ? mh : -INFINITY;
-    s_lw[w][lane] = lsum;
-  }
-  __syncthreads();
-  {
-    const float *red = reinterpret_cast<const float *>(s_acc);
-    const int d = tid;
-    const int ridx = (d % 16) * 16 + d / 16;       // where dim d sits in a wave's [n][c] layout
-    for (int hh = 0; hh < hpg; ++hh) {
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        float M = -INFINITY;
-        for (int ww = hh * wph; ww < (hh + 1) * wph; ++ww) M = fmaxf(M, s_mw[ww][i]);
-        float o = 0.f, L = 0.f;
-        for (int ww = hh * wph; ww < (hh + 1) * wph; ++ww) {
-          const float mw = s_mw[ww][i];
-          const float wgt = mw == -INFINITY ? 0.f : exp2f(mw - M);
-          o = fmaf(wgt, red[(ww * kGroup + i) * kHeadDim + ridx], o);
-          L = fmaf(wgt, s_lw[ww][i], L);
-        }
-        const int qh = (g0 + hh) * kGroup + i;
-        p.part_o[((size_t)cid * Hq + qh) * kHeadDim + d] = o;
-        if (d == 0) {
-          float *ml = p.part_ml + ((size_t)cid * Hq + qh) * 2;
-          ml[0] = M;
-          ml[1] = L;
-        }
-      }
     }
+    if (n < kGroup)
+      *reinterpret_cast<float2 *>(p.part_ml + ((size_t)cid * Hq + g * kGroup + n) * 2) = make_float2(m_run, l_run);
   }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v0[4][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v1[4][kTileHalves];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
+  attn_partial_wave(p, w, s_v0[w], s_v1[w]);
 }
 
 // Merge of the split-K partials and the headwise gate.
@@ -702,8 +736,14 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
     r.y = t.y * sc;
     r.z = t.z * sc;
     r.w = t.w * sc;
-    *reinterpret_cast<float4 *>(p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim + part * kCombineDims +
-                                tid * 4) = r;
+    // stored element e = n * 16 + c holds dim 16c + n (partial layout)
+    const int e = part * kCombineDims + tid * 4;
+    float *dst = p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim + (e >> 4);
+    const int c0 = e & 15;
+    dst[16 * c0] = r.x;
+    dst[16 * (c0 + 1)] = r.y;
+    dst[16 * (c0 + 2)] = r.z;
+    dst[16 * (c0 + 3)] = r.w;
   }
 }
 
@@ -817,8 +857,8 @@ hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
-  const dim3 grid(p.total_chunks, p.num_kv_heads / p.hpg);
-  hipLaunchKernelGGL(attn_partial_kernel<kMaxWaveRows / kTileRows>, grid, dim3(kThreads), 0, stream, p);
+  const int waves = p.total_chunks * p.num_kv_heads;
+  hipLaunchKernelGGL(attn_partial_kernel, dim3((waves + 3) / 4), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,
