@@ -130,7 +130,7 @@ gqa_status window_of(int is_full, int32_t position, int32_t window, int32_t ring
 // ---- sequences and the split-K plan ----------------------------------------
 
 struct Plan {
-  int chunk = kTileRows;
+  int chunk = kChunkQuantum;
   struct Group {
     int first = 0, count = 0, total_chunks = 0;
   };
@@ -190,24 +190,25 @@ gqa_status resolve_seqs(const gqa_arch *a, int is_full, const gqa_kv_seq *seqs, 
   return GQA_OK;
 }
 
-// Split-K plan.  One attention wave covers a chunk of rows for one KV head.
-// The chunk is the largest multiple of kTileRows that still gives every
-// launch about kAttnTargetWaves waves (longer chunks spend less on each
-// wave's set-up and on the partials; fewer waves than the chip holds leave
-// HBM bandwidth unused).  With C(c) chunks at chunk size c this keeps
-// C <= 2 * kAttnTargetWaves / Hk + sequences (see max_chunks).
+// Split-K plan.  One attention workgroup covers a chunk of rows for one KV
+// head (a quarter of the rows per wave).  The chunk is the largest multiple
+// of kChunkQuantum that still gives every launch about kAttnTargetWgs
+// workgroups (longer chunks spend less on each wave's set-up and on the
+// partials; fewer workgroups than the chip holds leave HBM bandwidth unused).
+// With C(c) chunks at chunk size c this keeps C <= 2 * kAttnTargetWgs / Hk +
+// sequences (see max_chunks).
 Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
   Plan plan;
-  auto waves = [&](int chunk) {
+  auto wgs = [&](int chunk) {
     long n = 0;
     for (const SeqDesc &s : seqs) n += (long)ceil_div(s.n, chunk) * num_kv_heads;
     return n;
   };
   int longest = 1;
   for (const SeqDesc &s : seqs) longest = std::max(longest, s.n);
-  const int cap = ceil_div(longest, kTileRows) * kTileRows;
-  int chunk = kTileRows;
-  while (chunk + kTileRows <= cap && waves(chunk + kTileRows) >= kAttnTargetWaves) chunk += kTileRows;
+  const int cap = ceil_div(longest, kChunkQuantum) * kChunkQuantum;
+  int chunk = kChunkQuantum;
+  while (chunk + kChunkQuantum <= cap && wgs(chunk + kChunkQuantum) >= kAttnTargetWgs) chunk += kChunkQuantum;
   plan.chunk = chunk;
   for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {
     Plan::Group g;
@@ -223,13 +224,13 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
 }
 
 // Upper bound of Plan::max_group_chunks for `batch` sequences of at most
-// max_seq_len attended rows.  If the plan stops at chunk c > kTileRows because
-// C(c + kTileRows) * Hk < target, then C(c) <= N / c + B <= 2 C(c + kTileRows) + B;
-// at c = kTileRows, C(16) <= 2 C(32) likewise; at the cap C = B.
+// max_seq_len attended rows.  If the plan stops at chunk c > q (q =
+// kChunkQuantum) because C(c + q) * Hk < target, then C(c) <= N / c + B <=
+// 2 C(c + q) + B; at c = q, C(q) <= 2 C(2q) likewise; at the cap C = B.
 size_t max_chunks(int num_kv_heads, int32_t batch, int32_t max_seq_len) {
   const size_t seqs = (size_t)std::min<int32_t>(batch, kMaxSeqPerLaunch);
-  const size_t finest = (size_t)ceil_div(max_seq_len, kTileRows) * seqs;
-  const size_t bound = 2 * (size_t)ceil_div(kAttnTargetWaves, num_kv_heads) + seqs;
+  const size_t finest = (size_t)ceil_div(max_seq_len, kChunkQuantum) * seqs;
+  const size_t bound = 2 * (size_t)ceil_div(kAttnTargetWgs, num_kv_heads) + seqs;
   return std::min(finest, bound);
 }
 

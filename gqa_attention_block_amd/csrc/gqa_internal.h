@@ -12,14 +12,16 @@ constexpr int kHeadDim = 256;        // kernels specialise D = 256
 constexpr int kGroup = 4;            // query heads per KV head
 constexpr int kThreads = 256;        // 4 wave64 per workgroup
 constexpr int kMaxSeqPerLaunch = 32; // sequence descriptors carried in kernel arguments
-constexpr int kTileRows = 16;        // attention rows per MFMA tile; chunks are multiples
-// Attention waves a launch aims for: one per SIMD of MI355X (256 CUs x 4).
-// Measured on a 32K-row window: 1024 waves of 8 tiles finish together, while
-// 2048 waves of 4 tiles (the two that fit per SIMD) spread their end times
-// over ~10 us as HBM serves their first tiles in arbitrary order.  A constant
-// (not the device's CU count) so the split plan, and the workspace bound
-// derived from it, are the same everywhere.
-constexpr int kAttnTargetWaves = 1024;
+constexpr int kTileRows = 16;        // attention rows per MFMA tile
+constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles for each of 4 waves
+// Attention workgroups a launch aims for: one wave per SIMD of MI355X
+// (256 CUs x 4 SIMDs, 4 waves per workgroup).  Measured on a 32K-row window:
+// 1024 waves of 8 tiles finish together, while 2048 waves of 4 tiles (the two
+// that fit per SIMD) spread their end times over ~10 us as HBM serves their
+// first tiles in arbitrary order.  A constant (not the device's CU count) so
+// the split plan, and the workspace bound derived from it, are the same
+// everywhere.
+constexpr int kAttnTargetWgs = 256;
 constexpr float kRescaleSlack = 8.f; // log2 headroom before the softmax reference moves
 constexpr unsigned kMaxBufferBytes = 0x7FFFFFFFu;  // buffer loads use 31-bit offsets
 constexpr int kMaxHidden = 8192;     // GEMV keeps up to 16 x 512 columns in registers
@@ -50,7 +52,8 @@ struct AttnParams {
   float *part_ml;     // [total_chunks][Hq][2]   (reference max in log2 units, sum)
   int num_kv_heads;
   float qscale;       // attention_scale * log2(e): scores come out in log2 units
-  int chunk;          // rows per chunk (one wave per chunk and KV head): a multiple of kTileRows
+  int chunk;          // rows per chunk (one workgroup per chunk and KV head, a quarter
+                      // per wave): a multiple of kChunkQuantum
   int nseq;
   int total_chunks;
   SeqDesc seq[kMaxSeqPerLaunch];

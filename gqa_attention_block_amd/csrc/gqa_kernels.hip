@@ -442,19 +442,19 @@ __device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 
 // compiler waits for a buffer's LDS-bound loads only before reading that
 // buffer (not for the other buffer's loads, which are still in flight).
 __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _Float16 *__restrict__ sv0,
-                                                  _Float16 *__restrict__ sv1) {
+                                                  _Float16 *__restrict__ sv1, float &m_out, float &l_out) {
   const int lane = threadIdx.x & 63;
   const int Hk = p.num_kv_heads;
-  const int Hq = Hk * kGroup;
-  const int id = blockIdx.x * 4 + w;
-  if (id >= p.total_chunks * Hk) return;         // whole wave; the kernel has no barrier
-  const int cid = id / Hk;
-  const int g = id - cid * Hk;
+  const int cid = blockIdx.x / Hk;
+  const int g = blockIdx.x - cid * Hk;
   const int b = find_seq(p, cid);
   const SeqDesc sd = p.seq[b];
   const int t0 = sd.kv_start + (cid - sd.chunk_begin) * p.chunk;
   const int nrows = min(p.chunk, sd.kv_start + sd.n - t0);
-  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
+  const int cw = p.chunk / 4;                    // rows per wave
+  const int wr0 = w * cw;                        // this wave's rows: [wr0, wend) relative to t0
+  const int wend = min(nrows, wr0 + cw);
+  const int ntiles = wend > wr0 ? (wend - wr0 + kTileRows - 1) / kTileRows : 0;
   const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
   const int ring = sd.ring;
   const int p0 = ring ? (t0 % ring) : t0;        // physical row of t0; a chunk wraps at most once
@@ -470,11 +470,11 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     int ph = p0 + rel;
     ph -= ph >= ring_end ? ring : 0;
     const unsigned off = __umul24((unsigned)ph, row_bytes) + head_off;   // ph, row_bytes < 2^24
-    return rel < nrows ? off : kOutOfRange;
+    return rel < wend ? off : kOutOfRange;
   };
   // K A-fragments of tile t: lane (G, n) holds row 16t + n, dims 32s + 8G .. +8
   auto load_k = [&](half8_t (&kf)[8], int t) {
-    const unsigned off = row_off(t * kTileRows + n) + (unsigned)G * 16u;
+    const unsigned off = row_off(wr0 + t * kTileRows + n) + (unsigned)G * 16u;
 #pragma unroll
     for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(half8_t, buf_load16(krs, off + (unsigned)s * 64u));
   };
@@ -482,7 +482,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   auto load_v = [&](_Float16 *sv, int t) {
     const int r = lane >> 2;
     const int q = lane & 3;
-    const unsigned off = row_off(t * kTileRows + r) + 32u * (unsigned)(((q >> 1) ^ (r >> 2)) & 1) +
+    const unsigned off = row_off(wr0 + t * kTileRows + r) + 32u * (unsigned)(((q >> 1) ^ (r >> 2)) & 1) +
                          16u * (unsigned)(q & 1);
     vload_block<0>(vrs, sv, off);
     vload_block<1>(vrs, sv, off);
@@ -505,9 +505,11 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     }
   }
   // An even number of tiles (a padding tile is fully masked and its loads
-  // are out of range: no HBM traffic), so that the steady-state loop below has
-  // no conditional loads and the compiler's waits stay exact.
-  const int ne = (ntiles + 1) & ~1;
+  // are out of range: no HBM traffic), so that no load below is conditional
+  // and the compiler's waits stay exact.
+  // A wave without rows (a short chunk) runs two fully masked tiles: its
+  // loads are out of range and it contributes m = -inf, l = 0, O = 0.
+  const int ne = ntiles > 2 ? (ntiles + 1) & ~1 : 2;
   half8_t kA[8], kB[8];
   load_k(kA, 0);
   load_v(sv0, 0);
@@ -556,7 +558,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[i] = d[i] + dpp<0x104>(d[i]);             // row_shl:4 -> value of lane n+4
-      if (n >= kGroup || t * kTileRows + 4 * G + i >= nrows) sc[i] = -INFINITY;
+      if (n >= kGroup || wr0 + t * kTileRows + 4 * G + i >= wend) sc[i] = -INFINITY;
       tmax = fmaxf(tmax, sc[i]);
     }
     tmax = max_across_rows(tmax);
@@ -617,7 +619,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   process(kA, sv0, ne - 2);
   process(kB, sv1, ne - 1);
 
-  // ---- this wave's partial: add the high and low rows, write (m, l, O) ----
+  // ---- this wave's partial: add the high and low rows, stage (m, l, O) ----
   l_run = sum_across_rows(l_run);
 #pragma unroll
   for (int c = 0; c < 16; ++c)
@@ -626,44 +628,81 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
       const float2 hl = pair16(acc[c][i]);
       acc[c][i] = hl.x + hl.y;
     }
-  // partial layout per query head: element n * 16 + c holds dim 16c + n,
-  // so lane n of group 0 writes 16 consecutive floats per head
+  // staged per query head i in the first 4 KB of sv0 (idle now): element
+  // n * 16 + c holds dim 16c + n, the layout of the partials
   if (G == 0) {
+    float *st = reinterpret_cast<float *>(sv0);
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      float *o = p.part_o + ((size_t)cid * Hq + g * kGroup + i) * kHeadDim + n * 16;
+    for (int i = 0; i < kGroup; ++i)
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
-        *reinterpret_cast<float4 *>(o + c4 * 4) =
+        *reinterpret_cast<float4 *>(st + i * kHeadDim + n * 16 + c4 * 4) =
             make_float4(acc[c4 * 4][i], acc[c4 * 4 + 1][i], acc[c4 * 4 + 2][i], acc[c4 * 4 + 3][i]);
-    }
-    if (n < kGroup)
-      *reinterpret_cast<float2 *>(p.part_ml + ((size_t)cid * Hq + g * kGroup + n) * 2) = make_float2(m_run, l_run);
   }
+  m_out = m_run;
+  l_out = l_run;
 }
 
+// Workgroup = (chunk cid, KV head g); its 4 waves split the chunk's rows and
+// then merge in LDS, so one partial per (chunk, query head) is written.
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) _Float16 s_v0[4][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_v1[4][kTileHalves];
+  __shared__ float s_m[4][kGroup];
+  __shared__ float s_l[4][kGroup];
+  const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
-  attn_partial_wave(p, w, s_v0[w], s_v1[w]);
+  float m_run, l_run;
+  attn_partial_wave(p, w, s_v0[w], s_v1[w], m_run, l_run);
+  if (lane < kGroup) {
+    s_m[w][lane] = m_run;
+    s_l[w][lane] = l_run;
+  }
+  __syncthreads();
+  // wave w merges query head i = w of this KV head: lane l owns elements 4l .. 4l+3
+  const int Hk = p.num_kv_heads;
+  const int Hq = Hk * kGroup;
+  const int cid = blockIdx.x / Hk;
+  const int g = blockIdx.x - cid * Hk;
+  const int i = w;
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_m[ww][i]);
+  float L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const float mw = s_m[ww][i];
+    const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);   // a wave without rows
+    L = fmaf(wt, s_l[ww][i], L);
+    const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(s_v0[ww]) +
+                                                       i * kHeadDim + lane * 4);
+    o.x = fmaf(wt, v.x, o.x);
+    o.y = fmaf(wt, v.y, o.y);
+    o.z = fmaf(wt, v.z, o.z);
+    o.w = fmaf(wt, v.w, o.w);
+  }
+  const size_t row = (size_t)cid * Hq + g * kGroup + i;
+  *reinterpret_cast<float4 *>(p.part_o + row * kHeadDim + lane * 4) = o;
+  if (lane == 0) *reinterpret_cast<float2 *>(p.part_ml + row * 2) = make_float2(M, L);
 }
 
 // Merge of the split-K partials and the headwise gate.
-// Grid (Hq * kCombineSplit, nseq).  Workgroup (h, part) owns head h and dims
-// [part*32, part*32 + 32).  Thread (cg, dq): dq = tid % 8 owns 4 dims, chunk
-// group cg = tid / 8 takes chunks cg, cg + 32, ...; each thread issues all of
-// its loads (up to 8 at a time) before using any.
-constexpr int kCombineSplit = 8;
-constexpr int kCombineDims = kHeadDim / kCombineSplit;   // 32
-constexpr int kCombineQuads = kCombineDims / 4;           // 8 threads per chunk row
-constexpr int kCombineGroups = kThreads / kCombineQuads;  // 32 chunk groups
-constexpr int kCombineBatch = 8;
+// Grid (Hq * kCombineSplit, nseq).  Workgroup (h, part) owns query head h and
+// the 16 stored elements [part*16, part*16 + 16) of its partials (stored
+// element n * 16 + c holds dim 16c + n).  Thread (cg, dq): dq = tid % 4 owns
+// 4 elements, chunk group cg = tid / 4 takes chunks cg, cg + 64, ... and
+// merges them online (running max, sum, acc), four chunks' loads at a time;
+// then wave dq merges the 64 groups of its 4 elements across its lanes.
+constexpr int kCombineSplit = 16;
+constexpr int kCombineElems = kHeadDim / kCombineSplit;   // 16
+constexpr int kCombineQuads = kCombineElems / 4;          // 4 threads per chunk row
+constexpr int kCombineGroups = kThreads / kCombineQuads;  // 64 chunk groups
+constexpr int kCombineBatch = 4;
 
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams p) {
-  __shared__ float s_red[kThreads / 64];
-  __shared__ float4 s_acc[kCombineGroups][kCombineQuads];
-  __shared__ float s_lsum[kCombineGroups];
+  __shared__ float4 s_o[kCombineGroups][kCombineQuads];
+  __shared__ float2 s_ml[kCombineGroups];
 
   const int tid = threadIdx.x;
   const int h = blockIdx.x / kCombineSplit;
@@ -673,21 +712,12 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
   const int Hq = p.num_kv_heads * kGroup;
   const int nchunks = (sd.n + p.chunk - 1) / p.chunk;
   const int f0 = sd.chunk_begin;
-
-  // global max of the chunk maxima
-  float m = -INFINITY;
-  for (int c = tid; c < nchunks; c += kThreads)
-    m = fmaxf(m, p.part_ml[((size_t)(f0 + c) * Hq + h) * 2]);
-  m = wave_max(m);
-  if ((tid & 63) == 0) s_red[tid >> 6] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
   const int cg = tid / kCombineQuads;
   const int dq = tid % kCombineQuads;
-  const int dim0 = part * kCombineDims + dq * 4;
+  const int e0 = part * kCombineElems + dq * 4;
+
+  float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lsum = 0.f;
   for (int c0 = cg; c0 < nchunks; c0 += kCombineGroups * kCombineBatch) {
     float4 o[kCombineBatch];
     float2 ml[kCombineBatch];
@@ -695,9 +725,9 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
     for (int u = 0; u < kCombineBatch; ++u) {
       const int c = c0 + u * kCombineGroups;
       if (c < nchunks) {
-        const size_t base = (size_t)(f0 + c) * Hq + h;
-        ml[u] = *reinterpret_cast<const float2 *>(p.part_ml + base * 2);
-        o[u] = *reinterpret_cast<const float4 *>(p.part_o + base * kHeadDim + dim0);
+        const size_t row = (size_t)(f0 + c) * Hq + h;
+        ml[u] = *reinterpret_cast<const float2 *>(p.part_ml + row * 2);
+        o[u] = *reinterpret_cast<const float4 *>(p.part_o + row * kHeadDim + e0);
       } else {
         ml[u] = make_float2(-INFINITY, 0.f);
         o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -705,45 +735,45 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
     }
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
-      const float wgt = exp2f(ml[u].x - M);   // 0 for padding entries
-      lsum = fmaf(wgt, ml[u].y, lsum);
-      acc.x = fmaf(wgt, o[u].x, acc.x);
-      acc.y = fmaf(wgt, o[u].y, acc.y);
-      acc.z = fmaf(wgt, o[u].z, acc.z);
-      acc.w = fmaf(wgt, o[u].w, acc.w);
+      if (ml[u].x == -INFINITY) continue;   // padding entry (a chunk always has rows)
+      const float mn = fmaxf(m, ml[u].x);
+      const float a = __builtin_amdgcn_exp2f(m - mn);       // 0 while m is -inf
+      const float c = __builtin_amdgcn_exp2f(ml[u].x - mn);
+      l = fmaf(l, a, ml[u].y * c);
+      acc.x = fmaf(acc.x, a, o[u].x * c);
+      acc.y = fmaf(acc.y, a, o[u].y * c);
+      acc.z = fmaf(acc.z, a, o[u].z * c);
+      acc.w = fmaf(acc.w, a, o[u].w * c);
+      m = mn;
     }
   }
-  s_acc[cg][dq] = acc;
-  if (dq == 0) s_lsum[cg] = lsum;
+  s_o[cg][dq] = acc;
+  if (dq == 0) s_ml[cg] = make_float2(m, l);
   __syncthreads();
-  if (tid < kCombineQuads) {
-    float4 t = s_acc[0][tid];
-    float L = s_lsum[0];
-#pragma unroll
-    for (int k = 1; k < kCombineGroups; ++k) {
-      const float4 u = s_acc[k][tid];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-      L += s_lsum[k];
-    }
+  // wave q merges element quad q: lane k holds chunk group k
+  const int lane = tid & 63;
+  const int q = tid >> 6;
+  const float2 mlk = s_ml[lane];
+  const float M = wave_max(mlk.x);
+  const float wt = mlk.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mlk.x - M);
+  const float L = wave_sum(wt * mlk.y);
+  const float4 ok = s_o[lane][q];
+  const float ox = wave_sum(wt * ok.x);
+  const float oy = wave_sum(wt * ok.y);
+  const float oz = wave_sum(wt * ok.z);
+  const float ow = wave_sum(wt * ok.w);
+  if (lane == 0) {
     const float gl = p.gate[(size_t)b * p.ld_gate + h];
     const float gate = 1.0f / (1.0f + expf(-gl));
     const float sc = gate / L;
-    float4 r;
-    r.x = t.x * sc;
-    r.y = t.y * sc;
-    r.z = t.z * sc;
-    r.w = t.w * sc;
-    // stored element e = n * 16 + c holds dim 16c + n (partial layout)
-    const int e = part * kCombineDims + tid * 4;
+    // element e = n * 16 + c holds dim 16c + n
+    const int e = part * kCombineElems + q * 4;
     float *dst = p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim + (e >> 4);
     const int c0 = e & 15;
-    dst[16 * c0] = r.x;
-    dst[16 * (c0 + 1)] = r.y;
-    dst[16 * (c0 + 2)] = r.z;
-    dst[16 * (c0 + 3)] = r.w;
+    dst[16 * c0] = ox * sc;
+    dst[16 * (c0 + 1)] = oy * sc;
+    dst[16 * (c0 + 2)] = oz * sc;
+    dst[16 * (c0 + 3)] = ow * sc;
   }
 }
 
@@ -857,8 +887,7 @@ hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
-  const int waves = p.total_chunks * p.num_kv_heads;
-  hipLaunchKernelGGL(attn_partial_kernel, dim3((waves + 3) / 4), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,
