@@ -10,9 +10,11 @@ workload is the full (causal) layer at 32K context: hidden 2560, position
 total exceeds 1 GiB.
 
 Prints ONE JSON line with the throughput (tokens/s), a roofline object for
-the dominant kernel (the attention step: its HBM bytes over its own average
-duration, timed with HIP events around its launches), and the fp64 CPU
-oracle timed on the host as a baseline.
+the dominant kernel (attn_partial_kernel, the split-K pass: its algorithmic
+HBM bytes over its average duration, timed with HIP events around a run of
+back-to-back launches on the stream it is launched on), and the fp64 CPU
+oracle timed on the host as a baseline.  `--calibrate-copy MIB` only runs a
+plain device copy of known size, to scale rocprofv3's HBM byte counters.
 """
 from __future__ import annotations
 
@@ -79,15 +81,25 @@ def attention_bytes(case) -> int:
     return kv_row * attended_rows(case) + 4 * b * (a.q_dim + a.num_heads + a.q_dim)
 
 
+def partial_bytes(case, chunks: int) -> int:
+    """HBM bytes the split-K pass (the dominant kernel) must move: attended K/V
+    rows (fp16, all KV heads) and fp32 q in, one fp32 (O, m, l) partial per
+    chunk and query head out."""
+    a = case.arch
+    kv_row = 2 * 2 * a.num_kv_heads * a.head_dim
+    return (kv_row * attended_rows(case) + 4 * case.batch * a.q_dim
+            + 4 * chunks * a.num_heads * (a.head_dim + 2))
+
+
 def source_digest() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def counted_traffic(workload: str):
-    """HBM bytes per attention launch from a committed rocprofv3 PMC summary
-    of the same kernel source, or None."""
-    path = os.path.join(PROFILE_DIR, f"attention_{workload}_hbm_counters.md")
+    """HBM bytes per launch of attn_partial_kernel from a committed rocprofv3
+    PMC summary of the same kernel source, or None."""
+    path = os.path.join(PROFILE_DIR, f"attn_partial_kernel_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -119,6 +131,20 @@ def cpu_baseline(case, seconds: float):
             "sample": f"{runs} full fp64 oracle block steps of this workload ({el:.1f} s)"}
 
 
+def calibrate_copy(mib: int, reps: int):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) read by rocprofv3 --pmc."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,13 +156,18 @@ def main():
                     help="CPU oracle sample length (0 skips the baseline)")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per step instead of launching from the host")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 5)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}); the block is a single-GPU decode step and no multi-GPU path exists "
-              "in this build", file=sys.stderr)
+              f"{world}); the block is a single-GPU decode step and sharding it across GPUs "
+              "is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -233,27 +264,44 @@ def main():
         f"{tokens_per_s:.1f} tokens/s, {bb / 1e6:.2f} MB/step -> "
         f"{bb / (ms_per_step * 1e-3) / 1e9:.1f} GB/s")
 
-    n_att = max(args.steps, 20)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_att)]
-    for i in range(args.warmup):
-        run_attn(i % copies)
-    for i in range(n_att):
-        evs[i][0].record()
-        run_attn(i % copies)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    att_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-    att_avg_s = sum(att_ms) / len(att_ms) * 1e-3
+    # dominant kernel: the split-K pass alone, launched back to back over the
+    # copies; one event pair around the whole run gives its average duration
+    part_o = torch.empty((1024, a.num_heads, a.head_dim), dtype=torch.float32, device="cuda:0")
+    part_ml = torch.empty((part_o.shape[0], a.num_heads, 2), dtype=torch.float32, device="cuda:0")
+
+    def part_step(c):
+        return gqa.attention_partials(a, case.is_full, sets[c]["seqs"], q, part_o, part_ml)
+
+    chunk_rows, begin = part_step(0)
+    n_runs = max(args.steps, 20)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i % copies)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_runs):
+            fn(i % copies)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n_runs
+
+    part_s = timed(part_step)
+    pb = partial_bytes(case, begin[-1])
+    achieved = pb / part_s / 1e9
+    log(f"attn_partial_kernel: {part_s * 1e6:.2f} us avg over {n_runs} back-to-back launches, "
+        f"{begin[-1]} chunks of {chunk_rows} rows, {pb / 1e6:.2f} MB -> {achieved:.1f} GB/s = "
+        f"{achieved / HBM_PEAK_GBS:.3f} of peak")
+    att_s = timed(attn_step)
     ab = attention_bytes(case)
-    achieved = ab / att_avg_s / 1e9
-    log(f"attention step: avg {att_avg_s * 1e6:.2f} us (median {att_ms[len(att_ms) // 2] * 1e3:.2f}"
-        f" us), {ab / 1e6:.2f} MB -> {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBS:.3f} of peak")
+    log(f"attention step (partials + combine): {att_s * 1e6:.2f} us avg, {ab / 1e6:.2f} MB -> "
+        f"{ab / att_s / 1e9:.1f} GB/s")
 
     traffic = counted_traffic(args.workload)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic}
+    roofline = {"kernel": "attn_partial_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "us_per_launch": round(part_s * 1e6, 3),
+                "algorithmic_bytes_per_launch": pb}
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(case, args.cpu_seconds)
@@ -268,7 +316,9 @@ def main():
                    "positions": [s.position for s in case.seqs][:4],
                    "kv_rows_attended": attended_rows(case), "weights": "bf16",
                    "kv_cache": "fp16", "block_bytes_per_step": bb, "copies_rotated": copies,
-                   "launch": "hip_graph" if args.graph else "eager"},
+                   "launch": "hip_graph" if args.graph else "eager",
+                   "attention_chunk_rows": chunk_rows},
+        "attention_step_us": round(att_s * 1e6, 3),
         "block_hbm_gbs": round(bb / (ms_per_step * 1e-3) / 1e9, 1),
         "block_frac_of_peak": round(bb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,

@@ -66,6 +66,8 @@ def _load():
         "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_qkv_rope_kv": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, P]),
         "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, S, P]),
+        "gqa_attention_partials": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, I32,
+                                                  ctypes.POINTER(I32), ctypes.POINTER(I32), P]),
         "gqa_o_proj_gemv": (ctypes.c_int, [A, W, I32, P, P, P]),
         "gqa_rms_norm_bf16w": (ctypes.c_int, [P, P, P, I32, I32, F, P]),
         "gqa_residual_add": (ctypes.c_int, [P, P, I64, P]),
@@ -85,7 +87,7 @@ _lib = _load()
 EXPORTED_SYMBOLS = (
     "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size",
     "gqa_attention_block_decode", "gqa_qkv_rope_kv", "gqa_attention_gated",
-    "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
+    "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
     "gqa_last_error",
 )
 
@@ -274,6 +276,30 @@ def attention_gated(arch: Arch, is_full: bool, seqs: Sequence[KvSeq], q_roped: t
         _ptr(attn_gated, torch.float32, "attn_gated", b * arch.q_dim),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
         "gqa_attention_gated")
+
+
+def attention_partials(arch: Arch, is_full: bool, seqs: Sequence[KvSeq], q_roped: torch.Tensor,
+                       part_o: torch.Tensor, part_ml: torch.Tensor, stream=None):
+    """The split-K pass alone: per chunk and query head the unnormalised
+    partial (m, l, O) in log2 units; part_o is [max_chunks, Hq, D] and part_ml
+    [max_chunks, Hq, 2], fp32.  Returns (chunk_rows, chunk_begin) where
+    chunk_begin has len(seqs) + 1 entries (the last is the chunk count)."""
+    b = len(seqs)
+    a = arch._c()
+    ks = _seqs(arch, seqs)
+    per_chunk = arch.num_heads * arch.head_dim
+    if part_o.dim() == 0 or part_o.numel() % per_chunk != 0:
+        raise ValueError("part_o: must hold whole [Hq, D] chunks")
+    max_chunks = part_o.numel() // per_chunk
+    rows = ctypes.c_int32(0)
+    begin = (ctypes.c_int32 * (b + 1))()
+    _check(_lib.gqa_attention_partials(
+        ctypes.byref(a), int(is_full), ks, b,
+        _ptr(q_roped, torch.float32, "q_roped", b * arch.q_dim),
+        _ptr(part_o, torch.float32, "part_o"),
+        _ptr(part_ml, torch.float32, "part_ml", max_chunks * arch.num_heads * 2), max_chunks,
+        ctypes.byref(rows), begin, _stream(stream)), "gqa_attention_partials")
+    return rows.value, [int(begin[i]) for i in range(b + 1)] if b else [0]
 
 
 def o_proj_gemv(arch: Arch, w_o, attn_gated: torch.Tensor, out: torch.Tensor, stream=None):

@@ -319,31 +319,40 @@ gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t bat
   return e == hipSuccess ? GQA_OK : gpu_error(e, "o_proj GEMV launch");
 }
 
+// Kernel arguments of one launch group.  q, gate and attn point at row 0 of
+// the whole batch; gate and attn may be null (the partial pass alone).
+AttnParams attn_params(const gqa_arch *a, const std::vector<SeqDesc> &seqs, const Plan &plan,
+                       const Plan::Group &g, const float *q, const float *gate, float *attn, float *part_o,
+                       float *part_ml) {
+  const long q_dim = (long)a->num_heads * a->head_dim;
+  AttnParams p{};
+  p.q = q + (size_t)g.first * q_dim;
+  p.ld_q = q_dim;
+  p.gate = gate ? gate + (size_t)g.first * a->num_heads : nullptr;
+  p.ld_gate = a->num_heads;
+  p.out = attn ? attn + (size_t)g.first * q_dim : nullptr;
+  p.ld_out = q_dim;
+  p.part_o = part_o;
+  p.part_ml = part_ml;
+  p.num_kv_heads = a->num_kv_heads;
+  p.qscale = (float)((double)a->attention_scale * kLog2e);
+  p.chunk = plan.chunk;
+  p.nseq = g.count;
+  p.total_chunks = g.total_chunks;
+  int cb = 0;
+  for (int i = 0; i < g.count; ++i) {
+    p.seq[i] = seqs[g.first + i];
+    p.seq[i].chunk_begin = cb;
+    cb += ceil_div(p.seq[i].n, plan.chunk);
+  }
+  return p;
+}
+
 gqa_status run_attention(const gqa_arch *a, const std::vector<SeqDesc> &seqs, const Plan &plan,
                          const float *q, const float *gate, float *attn, float *part_o, float *part_ml,
                          hipStream_t stream) {
-  const long q_dim = (long)a->num_heads * a->head_dim;
   for (const Plan::Group &g : plan.groups) {
-    AttnParams p{};
-    p.q = q + (size_t)g.first * q_dim;
-    p.ld_q = q_dim;
-    p.gate = gate + (size_t)g.first * a->num_heads;
-    p.ld_gate = a->num_heads;
-    p.out = attn + (size_t)g.first * q_dim;
-    p.ld_out = q_dim;
-    p.part_o = part_o;
-    p.part_ml = part_ml;
-    p.num_kv_heads = a->num_kv_heads;
-    p.qscale = (float)((double)a->attention_scale * kLog2e);
-    p.chunk = plan.chunk;
-    p.nseq = g.count;
-    p.total_chunks = g.total_chunks;
-    int cb = 0;
-    for (int i = 0; i < g.count; ++i) {
-      p.seq[i] = seqs[g.first + i];
-      p.seq[i].chunk_begin = cb;
-      cb += ceil_div(p.seq[i].n, plan.chunk);
-    }
+    const AttnParams p = attn_params(a, seqs, plan, g, q, gate, attn, part_o, part_ml);
     hipError_t e = launch_attention(p, a->num_heads, stream);
     if (e != hipSuccess) return gpu_error(e, "attention launch");
   }
@@ -476,6 +485,37 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
   st = run_attention(arch, descs, plan, q_roped, gate_logits, attn_gated, part_o, part_ml,
                      static_cast<hipStream_t>(stream));
   return st == GQA_OK ? ok() : st;
+}
+
+gqa_status gqa_attention_partials(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs, int32_t batch,
+                                  const float *q_roped, float *part_o, float *part_ml, int32_t max_chunks,
+                                  int32_t *chunk_rows, int32_t *chunk_begin, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  if (batch > kMaxSeqPerLaunch)
+    return fail(GQA_ERR_UNSUPPORTED, "batch=%d: the partial pass runs one launch group of at most %d sequences",
+                batch, kMaxSeqPerLaunch);
+  if (!chunk_rows) return fail(GQA_ERR_INVALID_ARGUMENT, "chunk_rows is null");
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
+  if (batch == 0) return ok();
+  if (!chunk_begin) return fail(GQA_ERR_INVALID_ARGUMENT, "chunk_begin is null");
+  if ((st = check_ptr(q_roped, "q_roped")) != GQA_OK) return st;
+  if ((st = check_ptr(part_o, "part_o")) != GQA_OK) return st;
+  if ((st = check_ptr(part_ml, "part_ml")) != GQA_OK) return st;
+  const Plan plan = make_plan(descs, arch->num_kv_heads);
+  const Plan::Group &g = plan.groups[0];
+  if (g.total_chunks > max_chunks)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "the partial pass writes %d chunks, max_chunks is %d", g.total_chunks,
+                max_chunks);
+  const AttnParams p = attn_params(arch, descs, plan, g, q_roped, nullptr, nullptr, part_o, part_ml);
+  *chunk_rows = plan.chunk;
+  for (int i = 0; i < batch; ++i) chunk_begin[i] = p.seq[i].chunk_begin;
+  chunk_begin[batch] = g.total_chunks;
+  hipError_t e = launch_attention_partials(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return gpu_error(e, "attention partial launch");
+  return ok();
 }
 
 gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,

@@ -98,6 +98,7 @@ struct GemvParams {
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
+hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
 hipError_t launch_rms_norm(const float *h, const uint16_t *w, float *out, int rows,
                            int hidden, float eps, hipStream_t stream);
 hipError_t launch_residual_add(float *h, const float *o, int64_t n, hipStream_t stream);

@@ -886,6 +886,11 @@ hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {
   }
 }
 
+hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
   hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();

@@ -189,6 +189,32 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
                                float *attn_gated, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* The split-K pass of gqa_attention_gated alone (the dominant kernel of the
+ * block), for one launch group of at most 32 sequences; exposed so the pass
+ * can be checked and timed by itself.  The attended rows of sequence i are
+ * cut into chunks of *chunk_rows rows (the plan the block uses); chunk j of
+ * sequence i is flat chunk chunk_begin[i] + j.  For every flat chunk c and
+ * query head h it writes the chunk's unnormalised softmax partial, scores in
+ * log2 units (s_r = attention_scale * log2(e) * q_h . k_r over the chunk's
+ * rows r, [attn] attention step):
+ *   part_ml[c][h] = (m, l)  with  l * 2^m = sum_r 2^s_r  (m is a reference
+ *                   point within 8 of the chunk's largest s_r)
+ *   part_o[c][h][e] = (sum_r 2^(s_r - m) v_r)[16 * (e % 16) + e / 16]
+ * so that part_o / l is the attention of q_h over the chunk's rows.
+ *   q_roped      device fp32 [batch][Hq*D]
+ *   part_o       device fp32 [max_chunks][Hq][D]
+ *   part_ml      device fp32 [max_chunks][Hq][2]
+ *   chunk_rows   host out: rows per chunk (a multiple of 64)
+ *   chunk_begin  host out [batch + 1]: first flat chunk of each sequence, then
+ *                the total
+ * Errors: batch > 32 (UNSUPPORTED), more chunks than max_chunks
+ * (WORKSPACE_TOO_SMALL), and the checks of gqa_attention_gated.
+ * Reads the caches only. */
+gqa_status gqa_attention_partials(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs,
+                                  int32_t batch, const float *q_roped, float *part_o,
+                                  float *part_ml, int32_t max_chunks, int32_t *chunk_rows,
+                                  int32_t *chunk_begin, void *stream);
+
 /* [attn] the o_proj GEMV: out[b] = W_o attn_gated[b].
  *   attn_gated device fp32 [batch][Hq*D]; out device fp32 [batch][H]. */
 gqa_status gqa_o_proj_gemv(const gqa_arch *arch, const gqa_layer_weights *weights,

@@ -158,6 +158,76 @@ def test_attention_gated(name, is_full, positions, ring, caps):
 
 
 # ----------------------------------------------------------------------------
+# the split-K pass alone: every chunk's partial against the oracle's attention
+# over that chunk's rows, and its partition function
+# ----------------------------------------------------------------------------
+
+PARTIAL_CASES = ["full_pos0_single_key", "full_pos1000_ragged", "full_pos32767", "ring_pos513",
+                 "ring_pos32905", "full_batch_mixed", "ring_batch_mixed"]
+# stored element e of a partial holds dim 16 * (e % 16) + e // 16
+_PERM = np.array([16 * (e % 16) + e // 16 for e in range(256)])
+
+
+@pytest.mark.parametrize("name", PARTIAL_CASES)
+def test_attention_partials_per_chunk(name):
+    _, is_full, positions, ring, caps = next(c for c in ATTN_CASES if c[0] == name)
+    say(f"attention_partials {name} positions={positions[:8]} ring={ring}")
+    arch, case, q, _ = _attn_inputs(name, is_full, positions, ring, caps, 21)
+    ga = arch_of(arch)
+    k = [f16_to_dev(s.k) for s in case.seqs]
+    v = [f16_to_dev(s.v) for s in case.seqs]
+    seqs = [gqa.KvSeq(k=k[i], v=v[i], position=s.position, ring_capacity=s.ring_capacity)
+            for i, s in enumerate(case.seqs)]
+    max_chunks = 1024
+    part_o = torch.full((max_chunks, ga.num_heads, ga.head_dim), float("nan"), device="cuda")
+    part_ml = torch.full((max_chunks, ga.num_heads, 2), float("nan"), device="cuda")
+    rows, begin = gqa.attention_partials(ga, is_full, seqs, f32_to_dev(q), part_o, part_ml)
+    torch.cuda.synchronize()
+    assert rows % 64 == 0 and begin[0] == 0 and begin[-1] <= max_chunks
+    po, pml = part_o.cpu().numpy().astype(np.float64), part_ml.cpu().numpy().astype(np.float64)
+    log2e = 1.0 / np.log(2.0)
+    group = arch.num_heads // arch.num_kv_heads
+    for i, s in enumerate(case.seqs):
+        sl, ks, ar = oracle.kv_window(is_full, s.position, arch.sliding_window, s.ring_capacity)
+        qi = np.asarray(q[i], np.float64).reshape(arch.num_heads, -1)
+        nch = begin[i + 1] - begin[i]
+        assert nch == -(-(sl - ks) // rows)
+        for j in range(nch):
+            c0, c1 = ks + j * rows, min(ks + (j + 1) * rows, sl)
+            ref = oracle.attention_decode(qi, s.k, s.v, c1, c0, ar, arch.attention_scale)
+            phys = oracle.physical_rows(c1, c0, ar)
+            c = begin[i] + j
+            for h in range(arch.num_heads):
+                m, l = pml[c, h]
+                o = np.empty(256)
+                o[_PERM] = po[c, h]
+                assert_parity(o / l, ref[h], f"{name}[{i}] chunk {j} head {h}")
+                # l * 2^m is the chunk's partition function in log2 units
+                sc = arch.attention_scale * log2e * (s.k[phys, h // group].astype(np.float64) @ qi[h])
+                z = sc.max() + np.log2(np.sum(np.exp2(sc - sc.max())))
+                assert abs(np.log2(l) + m - z) <= 1e-4, (name, i, j, h, np.log2(l) + m, z)
+                assert sc.max() - 8 - 1e-3 <= m <= sc.max() + 1e-3, (name, i, j, h, m, sc.max())
+    assert np.all(np.isnan(pml[begin[-1]:])), "wrote past the last chunk"
+
+
+def test_attention_partials_rejects_two_launch_groups():
+    arch = synth.Arch(hidden=1024)
+    ga = arch_of(arch)
+    cap = 8
+    k = torch.zeros((cap, arch.num_kv_heads, arch.head_dim), dtype=torch.float16, device="cuda")
+    seqs = [gqa.KvSeq(k=k, v=k, position=3, ring_capacity=0)] * 33
+    q = torch.zeros((33, ga.q_dim), device="cuda")
+    part_o = torch.empty((64, ga.num_heads, ga.head_dim), device="cuda")
+    part_ml = torch.empty((64, ga.num_heads, 2), device="cuda")
+    with pytest.raises(gqa.GqaError) as e:
+        gqa.attention_partials(ga, True, seqs, q, part_o, part_ml)
+    assert e.value.status == 2
+    with pytest.raises(gqa.GqaError) as e:
+        gqa.attention_partials(ga, True, seqs[:32], q, part_o[:16], part_ml)
+    assert e.value.status == 3
+
+
+# ----------------------------------------------------------------------------
 # bit-exact row set: which rows are read, and how many
 # ----------------------------------------------------------------------------
 

@@ -199,6 +199,25 @@ def test_step_entry_points_validate():
     assert B.raw_call("gqa_residual_add", 0, 0, 0, None) == OK
 
 
+def test_partials_entry_validates():
+    a = B.c_arch(gqa.Arch(hidden=1024))
+    arr = B.c_seq_array(33)
+    for i in range(33):
+        arr[i] = _seq()
+    rows = ctypes.c_int32(0)
+    begin = (ctypes.c_int32 * 34)()
+    call = lambda batch, rows_p, begin_p, q=FAKE, mc=1024: B.raw_call(  # noqa: E731
+        "gqa_attention_partials", ctypes.byref(a), 1, arr, batch, q, FAKE, FAKE, mc, rows_p, begin_p, None)
+    assert call(33, ctypes.byref(rows), begin) == UNSUPPORTED       # one launch group only
+    assert call(1, None, begin) == INVALID                           # chunk_rows is null
+    assert call(1, ctypes.byref(rows), None) == INVALID              # chunk_begin is null
+    assert call(1, ctypes.byref(rows), begin, q=MISALIGNED) == INVALID
+    assert call(1, ctypes.byref(rows), begin, mc=0) == WS_SMALL
+    assert call(0, ctypes.byref(rows), None) == OK                  # nothing to do
+    arr[0] = _seq(pos=100, cap=100)
+    assert call(1, ctypes.byref(rows), begin) == INVALID             # linear cache too short
+
+
 def test_status_strings():
     assert B.status_string(0) == "GQA_OK"
     assert B.status_string(3) == "GQA_ERR_WORKSPACE_TOO_SMALL"
