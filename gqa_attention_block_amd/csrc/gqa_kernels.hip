@@ -377,13 +377,13 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
 // ---------------------------------------------------------------------------
 // Attention, split-K over the window, on the matrix cores.
 //
-// Every wave is independent: wave id = 4 * blockIdx.x + w owns chunk
-// cid = id / Hk (logical positions [t0, t0 + chunk) of one sequence) for KV
-// head g = id % Hk, and serves that head's 4 query heads, so each KV byte is
-// read from HBM once.  The 4 waves of a workgroup are the 4 heads of one chunk
-// when Hk is a multiple of 4 (neighbouring bytes of the same rows).  This
-// token's k and v are already in the cache (the qkv kernel wrote them), so
-// every row of the window is read the same way.
+// Workgroup blockIdx.x = cid * Hk + g owns chunk cid (logical positions
+// [t0, t0 + chunk) of one sequence) for KV head g and serves that head's 4
+// query heads, so each KV byte is read from HBM once; consecutive workgroups
+// are the KV heads of one chunk (neighbouring bytes of the same rows).  Wave w
+// takes the w-th quarter of the chunk's rows.  This token's k and v are
+// already in the cache (the qkv kernel wrote them), so every row of the window
+// is read the same way.
 //
 // Both products are small dense contractions per 16-row tile -- S = K q for
 // 4 query heads and O += P V -- and on VALU they cost ~65 instructions per
@@ -404,7 +404,8 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
 // K and V of the next tile are in flight while a tile is computed (K in
 // ping-pong registers, V in two LDS buffers).  Buffer loads whose offsets are
 // out of range return zeros without an HBM access, which pads the last tile.
-// Each wave writes its own partial (m, l, O) per query head.
+// The 4 waves then merge their (m, l, O) in LDS and the workgroup writes one
+// partial per query head; attn_combine_kernel merges the chunks.
 // ---------------------------------------------------------------------------
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));

@@ -15,7 +15,7 @@ pages of the crate turbospark-runtime 0.3.0, cited below as:
   [kvw]   src/kv_write.rs             (`kv_write_target`, `encode_kv_commit`,
           `encode_attention_any`)
 
-Readings where the pages leave a step open (numbered as in the design notes):
+Readings where the pages leave a step open (numbered O1..O20 throughout):
   O1 weights are row-major [out][in] and y = W x; O2 head h of a section is the
   contiguous block [256h, 256h+256); O3 query head h reads KV head
   h // (num_heads / num_kv_heads); O4 NeoX pairs (i, i + r/2) over the leading r
