@@ -254,12 +254,15 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         run_block(i % copies)
+    submitted = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert torch.isfinite(out).all(), "non-finite block output"
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_s = case.batch * args.steps / elapsed
     bb = block_bytes(case)
+    log(f"host submit time {submitted / args.steps * 1e6:.2f} us/step (the GPU is the bound "
+        f"while this stays below the step time)")
     log(f"block ({'graph' if args.graph else 'eager'}): {ms_per_step * 1e3:.2f} us/step, "
         f"{tokens_per_s:.1f} tokens/s, {bb / 1e6:.2f} MB/step -> "
         f"{bb / (ms_per_step * 1e-3) / 1e9:.1f} GB/s")
@@ -319,6 +322,7 @@ def main():
                    "launch": "hip_graph" if args.graph else "eager",
                    "attention_chunk_rows": chunk_rows},
         "attention_step_us": round(att_s * 1e6, 3),
+        "host_submit_us_per_step": round(submitted / args.steps * 1e6, 3),
         "block_hbm_gbs": round(bb / (ms_per_step * 1e-3) / 1e9, 1),
         "block_frac_of_peak": round(bb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,

@@ -442,8 +442,10 @@ __device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 
 // them as restrict parameters gives their accesses alias scopes, so the
 // compiler waits for a buffer's LDS-bound loads only before reading that
 // buffer (not for the other buffer's loads, which are still in flight).
+// sq is this wave's 4 KB staging area for its query fragments.
 __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _Float16 *__restrict__ sv0,
-                                                  _Float16 *__restrict__ sv1, float &m_out, float &l_out) {
+                                                  _Float16 *__restrict__ sv1, _Float16 *__restrict__ sq,
+                                                  float &m_out, float &l_out) {
   const int lane = threadIdx.x & 63;
   const int Hk = p.num_kv_heads;
   const int cid = blockIdx.x / Hk;
@@ -495,15 +497,13 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     vload_block<7>(vrs, sv, off);
   };
 
-  // q first: its wait then does not include the tile loads issued after it
-  float4 qx[16];
+  // q first (its wait then does not include the tile loads): lane l takes
+  // dims 4l .. 4l+3 of the KV head's 4 query heads
+  float4 qv[kGroup];
   {
-    const float *qh = p.q + (size_t)b * p.ld_q + (size_t)(g * kGroup + (n & 3)) * kHeadDim + G * 8;
+    const float *qh = p.q + (size_t)b * p.ld_q + (size_t)g * kGroup * kHeadDim + lane * 4;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      qx[2 * s] = *reinterpret_cast<const float4 *>(qh + s * 32);
-      qx[2 * s + 1] = *reinterpret_cast<const float4 *>(qh + s * 32 + 4);
-    }
+    for (int i = 0; i < kGroup; ++i) qv[i] = *reinterpret_cast<const float4 *>(qh + i * kHeadDim);
   }
   // An even number of tiles (a padding tile is fully masked and its loads
   // are out of range: no HBM traffic), so that no load below is conditional
@@ -517,22 +517,30 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   load_k(kB, 1);
   load_v(sv1, 1);
 
+  // Query fragments, built while the first tiles are in flight: each lane
+  // splits its dims (pre-scaled by scale * log2(e)) into fp16 high and low
+  // parts in the wave's staging area sq = [hi, lo][query head][dim]; then the
   // Qf B-fragments: lane (G, n) holds column n, dims 32s + 8G .. +8 of
-  // n < 4: hi(q_n); 4 <= n < 8: lo(q_{n-4}); else 0   (q pre-scaled)
+  // n < 4: hi(q_n); 4 <= n < 8: lo(q_{n-4}); else 0.
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    const float x[4] = {qv[i].x * p.qscale, qv[i].y * p.qscale, qv[i].z * p.qscale, qv[i].w * p.qscale};
+    half4_t hi, lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hi[j] = (_Float16)x[j];
+      lo[j] = (_Float16)(x[j] - (float)hi[j]);
+    }
+    *reinterpret_cast<half4_t *>(sq + i * kHeadDim + lane * 4) = hi;
+    *reinterpret_cast<half4_t *>(sq + (kGroup + i) * kHeadDim + lane * 4) = lo;
+  }
   half8_t qf[8];
   {
+    const _Float16 *src = sq + (((n >> 2) & 1) * kGroup + (n & 3)) * kHeadDim + G * 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const float4 x0 = qx[2 * s];
-      const float4 x1 = qx[2 * s + 1];
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float xs = x[i] * p.qscale;
-        const _Float16 hi = (_Float16)xs;
-        const _Float16 lo = (_Float16)(xs - (float)hi);
-        qf[s][i] = n < 4 ? hi : (n < 8 ? lo : (_Float16)0.f);
-      }
+      const half8_t v = *reinterpret_cast<const half8_t *>(src + s * 32);
+      qf[s] = n < 8 ? v : (half8_t){};
     }
   }
 
@@ -649,15 +657,16 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) _Float16 s_v0[4][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_v1[4][kTileHalves];
-  __shared__ float s_m[4][kGroup];
-  __shared__ float s_l[4][kGroup];
+  // per wave: its query fragments during the loop, then its (m, l) per query head
+  __shared__ __attribute__((aligned(16))) _Float16 s_q[4][2 * kGroup * kHeadDim];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
   float m_run, l_run;
-  attn_partial_wave(p, w, s_v0[w], s_v1[w], m_run, l_run);
+  attn_partial_wave(p, w, s_v0[w], s_v1[w], s_q[w], m_run, l_run);
   if (lane < kGroup) {
-    s_m[w][lane] = m_run;
-    s_l[w][lane] = l_run;
+    float *ml = reinterpret_cast<float *>(s_q[w]);
+    ml[lane] = m_run;
+    ml[kGroup + lane] = l_run;
   }
   __syncthreads();
   // wave w merges query head i = w of this KV head: lane l owns elements 4l .. 4l+3
@@ -666,16 +675,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
   const int cid = blockIdx.x / Hk;
   const int g = blockIdx.x - cid * Hk;
   const int i = w;
+  auto m_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[i]; };
+  auto l_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[kGroup + i]; };
   float M = -INFINITY;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_m[ww][i]);
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, m_of(ww));
   float L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) {
-    const float mw = s_m[ww][i];
+    const float mw = m_of(ww);
     const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);   // a wave without rows
-    L = fmaf(wt, s_l[ww][i], L);
+    L = fmaf(wt, l_of(ww), L);
     const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(s_v0[ww]) +
                                                        i * kHeadDim + lane * 4);
     o.x = fmaf(wt, v.x, o.x);

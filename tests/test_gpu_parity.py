@@ -210,6 +210,24 @@ def test_attention_partials_per_chunk(name):
     assert np.all(np.isnan(pml[begin[-1]:])), "wrote past the last chunk"
 
 
+@pytest.mark.parametrize("num_kv_heads,positions", [(1, [700]), (2, [3000, 64]), (3, [1000, 130]),
+                                                    (5, [2047]), (8, [500])])
+def test_attention_other_kv_head_counts(num_kv_heads, positions):
+    """Head counts other than the spark2_5 family's 4 (one attention
+    workgroup per chunk and KV head, whatever their number)."""
+    say(f"attention_gated num_kv_heads={num_kv_heads} positions={positions}")
+    arch = synth.Arch(hidden=1024, num_heads=4 * num_kv_heads, num_kv_heads=num_kv_heads)
+    seqs = [synth.make_cache(arch, 0, 22, 100 + 16 * i, p + 1, 0, p) for i, p in enumerate(positions)]
+    case = synth.BlockCase(name="kv_heads", arch=arch, is_full=True, w_qkv=None, w_g=None, w_o=None,
+                           x=np.zeros((len(positions), 1), np.float32), seqs=seqs)
+    q = synth.random_hidden(arch.q_dim, len(positions), 0, 22, tensor_id=903)
+    gl = synth.random_gate_logits(arch, len(positions), 0, 22)
+    got, _, _ = _run_attention(arch, case, q, gl)
+    ref = _oracle_attention(arch, case, q, gl)
+    for b in range(len(positions)):
+        assert_parity(got[b], ref[b], f"Hk={num_kv_heads}[{b}] gated attention")
+
+
 def test_attention_partials_rejects_two_launch_groups():
     arch = synth.Arch(hidden=1024)
     ga = arch_of(arch)
