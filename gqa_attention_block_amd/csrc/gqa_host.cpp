@@ -294,7 +294,10 @@ gqa_status run_qkv_rope(const gqa_arch *a, const gqa_layer_weights *w, int is_fu
     p.rotary_dim = rdim;
     p.log2_theta = log2(theta);
     for (int i = 0; i < p.batch; ++i) p.seq[i] = seqs[first + i];
-    hipError_t e = launch_qkv_rope(p, stream);
+    // batched: MFMA (its units pair RoPE tiles, so the rotated width must be
+    // whole 32-row tile pairs); batch 1-3: the fused VALU kernel
+    const bool mfma = p.batch >= kMfmaMinBatch && rdim % 32 == 0;
+    hipError_t e = mfma ? launch_qkv_mfma(p, stream) : launch_qkv_rope(p, stream);
     if (e != hipSuccess) return gpu_error(e, "qkv/RoPE/KV-write launch");
   }
   return GQA_OK;
@@ -302,6 +305,24 @@ gqa_status run_qkv_rope(const gqa_arch *a, const gqa_layer_weights *w, int is_fu
 
 gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t batch, const float *attn,
                       float *out, hipStream_t stream) {
+  const int cols = a->num_heads * a->head_dim;
+  if (batch >= kMfmaMinBatch) {
+    // groups of <= 32 batch rows on MFMA (a small last group on the VALU GEMV)
+    for (int first = 0; first < batch; first += 32) {
+      GemvParams p{};
+      p.w0 = static_cast<const uint16_t *>(w->o_proj);
+      p.rows0 = a->hidden;
+      p.cols = cols;
+      p.batch = std::min(32, batch - first);
+      p.x = attn + (size_t)first * cols;
+      p.ldx = cols;
+      p.y0 = out + (size_t)first * a->hidden;
+      p.ldy0 = a->hidden;
+      hipError_t e = p.batch >= kMfmaMinBatch ? launch_proj_mfma(p, stream) : launch_gemv(p, stream);
+      if (e != hipSuccess) return gpu_error(e, "o_proj launch");
+    }
+    return GQA_OK;
+  }
   GemvParams p{};
   p.w0 = static_cast<const uint16_t *>(w->o_proj);
   p.w1 = nullptr;

@@ -22,6 +22,7 @@ constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles f
 // the split plan, and the workspace bound derived from it, are the same
 // everywhere.
 constexpr int kAttnTargetWgs = 256;
+constexpr int kMfmaMinBatch = 4;     // projections run on MFMA from this batch on
 constexpr float kRescaleSlack = 8.f; // log2 headroom before the softmax reference moves
 constexpr unsigned kMaxBufferBytes = 0x7FFFFFFFu;  // buffer loads use 31-bit offsets
 constexpr int kMaxHidden = 8192;     // GEMV keeps up to 16 x 512 columns in registers
@@ -99,6 +100,9 @@ hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
+// Batched projections on MFMA (batch <= 32 per launch; see kMfmaMinBatch).
+hipError_t launch_proj_mfma(const GemvParams &p, hipStream_t stream);
+hipError_t launch_qkv_mfma(const QkvParams &p, hipStream_t stream);
 hipError_t launch_rms_norm(const float *h, const uint16_t *w, float *out, int rows,
                            int hidden, float eps, hipStream_t stream);
 hipError_t launch_residual_add(float *h, const float *o, int64_t n, hipStream_t stream);

@@ -32,6 +32,15 @@ namespace {
 // wave-level helpers
 // ---------------------------------------------------------------------------
 
+// MFMA operand and LDS pointer types
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -270,6 +279,25 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
 // pair in fp32 and writes: q -> q_out (fp32), k and v -> fp16, rounded once,
 // straight into the cache slot of this position; gate logits -> gate_out.
 // ---------------------------------------------------------------------------
+// NeoX rotation of the pair (x_i, x_{i + r/2}) by angle position * theta^(-2i/r).
+// The angle is formed and reduced mod 2*pi in fp64 (an fp32 angle at position
+// 32767 would be off by ~4e-3 rad); the reduced angle is in [-pi, pi], where
+// fp32 sin/cos are accurate.
+__device__ __forceinline__ void rope_rotate(int position, int i, int rotary_dim, double log2_theta, float &ya,
+                                            float &yb) {
+  const double inv = exp2(-(2.0 * (double)i / (double)rotary_dim) * log2_theta);
+  const double ang = (double)position * inv;
+  const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
+  double red = fma(-k, 6.283185307179586, ang);               // 2 pi, high part
+  red = fma(-k, 2.4492935982947064e-16, red);                 // 2 pi, low part
+  float sn, cs;
+  sincosf((float)red, &sn, &cs);
+  const float ra = ya * cs - yb * sn;
+  const float rb = yb * cs + ya * sn;
+  ya = ra;
+  yb = rb;
+}
+
 template <int NIT, int MB>
 __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
   const int lane = threadIdx.x & 63;
@@ -341,22 +369,7 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
     const int b = b0 + lane;
     if (lane < MB && b < p.batch) {
       const SeqDesc &sd = p.seq[b];
-      if (rotate) {
-        // angle = position * theta^(-2i/r), formed and reduced mod 2*pi in
-        // fp64 (an fp32 angle at position 32767 would be off by ~4e-3 rad);
-        // the reduced angle is in [-pi, pi], where fp32 sin/cos are accurate.
-        const double inv = exp2(-(2.0 * (double)pi / (double)p.rotary_dim) * p.log2_theta);
-        const double ang = (double)sd.position * inv;
-        const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
-        double red = fma(-k, 6.283185307179586, ang);               // 2 pi, high part
-        red = fma(-k, 2.4492935982947064e-16, red);                 // 2 pi, low part
-        float sn, cs;
-        sincosf((float)red, &sn, &cs);
-        const float ra = ya * cs - yb * sn;
-        const float rb = yb * cs + ya * sn;
-        ya = ra;
-        yb = rb;
-      }
+      if (rotate) rope_rotate(sd.position, pi, p.rotary_dim, p.log2_theta, ya, yb);
       if (sec == 0) {
         float *q = p.q_out + (size_t)b * p.ld_q + (size_t)head * kHeadDim;
         q[dA] = ya;
@@ -370,6 +383,226 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
         dst[dA] = (_Float16)ya;
         dst[dB] = (_Float16)yb;
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Batched projections on the matrix cores.
+//
+// At batch B >= kMfmaMinBatch a projection y[b][r] = sum_c W[r][c] x[b][c] is
+// a [rows x C] x [C x B] product with enough columns for MFMA: the fp32 VALU
+// GEMV needs one FMA per weight and batch row, and at B = 32 that is the bound,
+// not HBM.  v_mfma_f32_16x16x32_bf16 takes W (bf16) as the A operand straight
+// from HBM (lane (G, n): row n, 8 columns = 16 B) and x (fp32) split into bf16
+// high and low parts, x = hi + lo up to 2^-16 |x|, as two B operands, so the
+// product keeps fp32 accuracy.
+//
+// A workgroup owns a unit of two 16-row tiles for <= 32 batch rows; its
+// kProjSplit waves split the columns and add their partial sums in LDS in a
+// fixed order (the result does not depend on timing).  For q_k_v_proj the two
+// tiles of a unit are RoPE partners inside a head (rows i and i + r/2), so the
+// epilogue rotates, splits and writes q, k, v and the gate logits as the fused
+// batch-1 kernel does.
+// ---------------------------------------------------------------------------
+constexpr int kProjSplit = 8;                 // waves (column splits) per workgroup
+constexpr int kProjThreads = 64 * kProjSplit;
+constexpr int kProjSet = 2;                   // k-steps (32 columns each) per load set
+
+// Which two 16-row tiles a unit covers.  Plain: tiles 2u, 2u+1 of the
+// concatenated rows.  q_k_v_proj + g_proj: per head (q, k, v sections) 8
+// units; with rt = rotary_dim / 16 rotated tiles, unit j < rt/2 pairs tiles
+// (j, j + rt/2), the others pair the remaining tiles in order; the last unit
+// is the gate rows (W_g).
+struct ProjUnit {
+  int sec;        // 0 q, 1 k, 2 v, 3 gate (qkv mode); 0 plain
+  int head;
+  int ta, tb;     // tile index inside the head (qkv) or global tile (plain)
+  bool rotate;
+};
+
+__device__ __forceinline__ ProjUnit qkv_unit(const QkvParams &p, int u) {
+  ProjUnit U{};
+  const int nheads = p.num_heads + 2 * p.num_kv_heads;
+  if (u >= 8 * nheads) {
+    U.sec = 3; U.head = 0; U.ta = 0; U.tb = 1; U.rotate = false;
+    return U;
+  }
+  const int h = u >> 3, uh = u & 7;
+  U.sec = h < p.num_heads ? 0 : (h < p.num_heads + p.num_kv_heads ? 1 : 2);
+  U.head = U.sec == 0 ? h : (U.sec == 1 ? h - p.num_heads : h - p.num_heads - p.num_kv_heads);
+  const int rt = U.sec == 2 ? 0 : p.rotary_dim / 16;
+  if (uh < rt / 2) {
+    U.ta = uh; U.tb = uh + rt / 2; U.rotate = true;
+  } else {
+    U.ta = rt + 2 * (uh - rt / 2); U.tb = U.ta + 1; U.rotate = false;
+  }
+  return U;
+}
+
+__device__ __forceinline__ void proj_to_bf16(const float4 x0, const float4 x1, bf16x8_t &hi, bf16x8_t &lo) {
+  const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hi[i] = (__bf16)v[i];
+    lo[i] = (__bf16)(v[i] - (float)hi[i]);
+  }
+}
+
+// MODE 0: plain product into y0 / y1 (GemvParams); MODE 1: q_k_v_proj +
+// g_proj with the RoPE / KV-slot epilogue (QkvParams).  MB batch tiles of 16.
+template <int MODE, int MB, typename Params>
+__global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p) {
+  __shared__ float4 s_red[kProjSplit][2][32][4];   // [wave][tile][batch][rows 4k..4k+3] per 16-row tile
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = lane >> 4, n = lane & 15;
+  const int u = blockIdx.x;
+
+  // rows of the two tiles, their matrix and its row count
+  const uint16_t *wmat;
+  int wrows, rowA, rowB, cols, batch;
+  ProjUnit U{};
+  const float *x;
+  long ldx;
+  bool first = true;   // plain mode: the unit's rows are in w0 (else w1)
+  if constexpr (MODE == 0) {
+    // plain: units over w0's rows, then units over w1's rows
+    const int u0 = (p.rows0 + 31) / 32;
+    first = u < u0;
+    if (first) {
+      wmat = p.w0; wrows = p.rows0; rowA = u * 32;
+    } else {
+      wmat = p.w1; wrows = p.rows1; rowA = (u - u0) * 32;
+    }
+    rowB = rowA + 16;
+    cols = p.cols; batch = p.batch; x = p.x; ldx = p.ldx;
+  } else {
+    U = qkv_unit(p, u);
+    if (U.sec == 3) {
+      wmat = p.w_g; wrows = p.num_heads; rowA = 0; rowB = 16;
+    } else {
+      const int hrow = (U.sec == 0 ? U.head : U.sec == 1 ? p.num_heads + U.head
+                                                         : p.num_heads + p.num_kv_heads + U.head) * kHeadDim;
+      wmat = p.w_qkv; wrows = (p.num_heads + 2 * p.num_kv_heads) * kHeadDim;
+      rowA = hrow + U.ta * 16; rowB = hrow + U.tb * 16;
+    }
+    cols = p.hidden; batch = p.batch; x = p.x; ldx = p.ldx;
+  }
+  const unsigned row_bytes = (unsigned)cols * 2u;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wmat, (unsigned)wrows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (unsigned)((size_t)batch * ldx * 4u));
+  const unsigned offA = rowA + n < wrows ? (unsigned)(rowA + n) * row_bytes : kOutOfRange;
+  const unsigned offB = rowB + n < wrows ? (unsigned)(rowB + n) * row_bytes : kOutOfRange;
+  unsigned offX[MB];
+#pragma unroll
+  for (int bt = 0; bt < MB; ++bt)
+    offX[bt] = bt * 16 + n < batch ? (unsigned)((size_t)(bt * 16 + n) * ldx * 4u) : kOutOfRange;
+
+  // this wave's k-steps: [s0, s0 + spw), spw a multiple of 2 * kProjSet
+  const int nsteps = (cols + 31) / 32;
+  int spw = (nsteps + kProjSplit - 1) / kProjSplit;
+  spw = (spw + 2 * kProjSet - 1) / (2 * kProjSet) * (2 * kProjSet);
+  const int s0 = w * spw;
+
+  struct Set {
+    uint4 wa[kProjSet], wb[kProjSet];
+    float4 xv[kProjSet][MB][2];
+  };
+  auto load = [&](Set &S, int set) {
+#pragma unroll
+    for (int j = 0; j < kProjSet; ++j) {
+      const int col = (s0 + set * kProjSet + j) * 32 + G * 8;
+      const bool ok = col < cols;
+      S.wa[j] = buf_load16(rw, ok ? offA + (unsigned)col * 2u : kOutOfRange);
+      S.wb[j] = buf_load16(rw, ok ? offB + (unsigned)col * 2u : kOutOfRange);
+#pragma unroll
+      for (int bt = 0; bt < MB; ++bt) {
+        const unsigned xo = ok ? offX[bt] + (unsigned)col * 4u : kOutOfRange;
+        S.xv[j][bt][0] = __builtin_bit_cast(float4, buf_load16(rx, xo));
+        S.xv[j][bt][1] = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
+      }
+    }
+  };
+  floatx4_t accA[MB], accB[MB];
+#pragma unroll
+  for (int bt = 0; bt < MB; ++bt) {
+    accA[bt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+    accB[bt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+  }
+  auto compute = [&](const Set &S) {
+#pragma unroll
+    for (int j = 0; j < kProjSet; ++j) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, S.wa[j]);
+      const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, S.wb[j]);
+#pragma unroll
+      for (int bt = 0; bt < MB; ++bt) {
+        bf16x8_t hi, lo;
+        proj_to_bf16(S.xv[j][bt][0], S.xv[j][bt][1], hi, lo);
+        accA[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, accA[bt], 0, 0, 0);
+        accA[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, accA[bt], 0, 0, 0);
+        accB[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b2, hi, accB[bt], 0, 0, 0);
+        accB[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b2, lo, accB[bt], 0, 0, 0);
+      }
+    }
+  };
+  // two load sets in flight; no load is conditional (steps past the end
+  // are out of range: zeros without HBM traffic), so the waits stay exact
+  const int nsets = spw / kProjSet;
+  Set SA, SB;
+  load(SA, 0);
+  load(SB, 1);
+  for (int set = 0; set + 2 < nsets; set += 2) {
+    compute(SA);
+    load(SA, set + 2);
+    compute(SB);
+    load(SB, set + 3);
+  }
+  compute(SA);
+  compute(SB);
+
+  // partial sums: lane (G, n) holds rows 4G..4G+3 of batch column n
+#pragma unroll
+  for (int bt = 0; bt < MB; ++bt) {
+    s_red[w][0][bt * 16 + n][G] = make_float4(accA[bt][0], accA[bt][1], accA[bt][2], accA[bt][3]);
+    s_red[w][1][bt * 16 + n][G] = make_float4(accB[bt][0], accB[bt][1], accB[bt][2], accB[bt][3]);
+  }
+  __syncthreads();
+  // thread t: batch row b = t / 16, row xr = t % 16 of both tiles
+  const int t = threadIdx.x;
+  const int b = t >> 4, xr = t & 15;
+  if (b >= MB * 16 || b >= batch) return;
+  float ya = 0.f, yb = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < kProjSplit; ++ww) {
+    ya += reinterpret_cast<const float *>(&s_red[ww][0][b][0])[xr];
+    yb += reinterpret_cast<const float *>(&s_red[ww][1][b][0])[xr];
+  }
+  if constexpr (MODE == 0) {
+    float *y = first ? p.y0 : p.y1;
+    const long ldy = first ? p.ldy0 : p.ldy1;
+    if (rowA + xr < wrows) y[(size_t)b * ldy + rowA + xr] = ya;
+    if (rowB + xr < wrows) y[(size_t)b * ldy + rowB + xr] = yb;
+  } else {
+    if (U.sec == 3) {
+      float *gl = p.gate_out + (size_t)b * p.ld_gate;
+      if (xr < p.num_heads) gl[xr] = ya;
+      if (16 + xr < p.num_heads) gl[16 + xr] = yb;
+      return;
+    }
+    const SeqDesc &sd = p.seq[b];
+    const int dA = U.ta * 16 + xr, dB = U.tb * 16 + xr;
+    if (U.rotate) rope_rotate(sd.position, dA, p.rotary_dim, p.log2_theta, ya, yb);
+    if (U.sec == 0) {
+      float *q = p.q_out + (size_t)b * p.ld_q + (size_t)U.head * kHeadDim;
+      q[dA] = ya;
+      q[dB] = yb;
+    } else {
+      _Float16 *dst = (U.sec == 1 ? sd.k : sd.v) + (size_t)sd.slot * p.num_kv_heads * kHeadDim +
+                      (size_t)U.head * kHeadDim;
+      dst[dA] = (_Float16)ya;
+      dst[dB] = (_Float16)yb;
     }
   }
 }
@@ -407,12 +640,6 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
 // The 4 waves then merge their (m, l, O) in LDS and the workgroup writes one
 // partial per query head; attn_combine_kernel merges the chunks.
 // ---------------------------------------------------------------------------
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   int s = 0;
@@ -873,6 +1100,24 @@ hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_proj_mfma(const GemvParams &p, hipStream_t stream) {
+  const int units = (p.rows0 + 31) / 32 + (p.rows1 + 31) / 32;
+  if (p.batch > 16)
+    hipLaunchKernelGGL((proj_mfma_kernel<0, 2, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((proj_mfma_kernel<0, 1, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_mfma(const QkvParams &p, hipStream_t stream) {
+  const int units = 8 * (p.num_heads + 2 * p.num_kv_heads) + 1;
+  if (p.batch > 16)
+    hipLaunchKernelGGL((proj_mfma_kernel<1, 2, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((proj_mfma_kernel<1, 1, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream) {
   if (p.batch == 1) return gemv1_dispatch(p, stream);

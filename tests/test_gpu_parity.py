@@ -33,6 +33,9 @@ QKV_CASES = [
     (776, True, [5, 900, 17], 0), (264, False, [0, 511, 512, 513, 2000], 512),
     (2560, True, [int(n) - 1 for n in synth.cfg5_lengths()], 0), (8192, True, [100], 0),
     (4096, False, [1000, 31], 0), (2560, True, list(range(3, 3 + 40 * 5, 5)), 0),
+    # batched (MFMA) edges: 4 rows, 17 rows (second batch tile), a tiny hidden
+    (1024, True, [7, 63, 64, 3000], 0), (2560, False, list(range(100, 100 + 17 * 61, 61)), 512),
+    (8, True, [1, 2, 3, 4, 5], 0),
 ]
 
 
@@ -57,7 +60,8 @@ def test_qkv_rope_kv(hidden, is_full, positions, ring):
     check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, "qkv_rope_kv")
 
 
-@pytest.mark.parametrize("hidden,batch", [(1024, 1), (2560, 1), (776, 3), (2560, 32), (6144, 2)])
+@pytest.mark.parametrize("hidden,batch", [(1024, 1), (2560, 1), (776, 3), (2560, 32), (6144, 2),
+                                          (776, 5), (1024, 17), (2560, 33), (8, 4)])
 def test_o_proj_gemv(hidden, batch):
     say(f"o_proj_gemv hidden={hidden} batch={batch}")
     a = synth.Arch(hidden=hidden)
