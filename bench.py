@@ -145,12 +145,115 @@ def calibrate_copy(mib: int, reps: int):
                       "reps": reps}), flush=True)
 
 
+def stack_bytes(st) -> int:
+    """Algorithmic HBM bytes of one token through the stack: per layer the
+    block's bytes (block_bytes) plus the RMSNorm (h in, x out, bf16 w) and the
+    residual add (h and o in, h out), fp32 [1][hidden]."""
+    import numpy as np
+    import synth
+    total = 0
+    h = st.arch.hidden
+    for L in st.layers:
+        c = synth.BlockCase(name="layer", arch=st.arch, is_full=L.is_full, w_qkv=L.w_qkv, w_g=L.w_g,
+                            w_o=L.w_o, x=np.zeros((1, h), np.float32), seqs=[L.cache])
+        total += block_bytes(c) + (4 * h * 2 + 2 * h) + 4 * h * 3
+    return total
+
+
+def bench_stack(args):
+    """The 36-layer stack (RMSNorm -> block -> residual add per layer, no MLP)
+    at position 8191: 9 full layers over 8192 rows, 27 sliding layers over a
+    wrapped 512-slot ring.  One step = one token through all 36 layers."""
+    import numpy as np
+    import torch
+    import gqa_attention_block_amd as gqa
+    import synth
+    st = synth.cfg4_stack()
+    a = gqa.Arch(hidden=st.arch.hidden)
+    up = lambda arr: torch.from_numpy(arr.view(np.int16) if arr.dtype == np.uint16 else arr).to("cuda:0")  # noqa: E731
+    layers = [dict(w_norm=up(L.w_norm), w_qkv=up(L.w_qkv), w_g=up(L.w_g), w_o=up(L.w_o),
+                   seq=gqa.KvSeq(k=up(L.cache.k), v=up(L.cache.v), position=L.cache.position,
+                                 ring_capacity=L.cache.ring_capacity), full=L.is_full)
+              for L in st.layers]
+    h0 = up(st.h)
+    h = h0.clone()
+    xn = torch.empty_like(h)
+    o = torch.empty_like(h)
+    ws = torch.empty(gqa.workspace_size(a, 1, st.layers[0].cache.position + 1), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def step():
+        for L in layers:
+            gqa.rms_norm_bf16w(h, L["w_norm"], xn, a.rms_eps)
+            gqa.attention_block_decode(a, L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], xn, o, ws)
+            gqa.residual_add(h, o)
+
+    run = step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        run = g.replay
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    submitted = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert torch.isfinite(h).all(), "non-finite residual stream"
+    ms = 1e3 * elapsed / args.steps
+    sb = stack_bytes(st)
+    log(f"stack ({'graph' if args.graph else 'eager'}): {ms * 1e3:.1f} us/token, host submit "
+        f"{submitted / args.steps * 1e6:.1f} us/token, {sb / 1e9:.3f} GB/token -> "
+        f"{sb / (ms * 1e-3) / 1e9:.1f} GB/s")
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        # bounded sample: the fp64 oracle over the first layers, scaled to 36
+        done, t0 = 0, time.perf_counter()
+        while done < len(st.layers) and time.perf_counter() - t0 < args.cpu_seconds:
+            oracle.stack_decode(st.arch, st.h, st.layers[done:done + 1])
+            done += 1
+        el = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:                   # pragma: no cover
+            cores = os.cpu_count() or 1
+        cpu = {"value": 1.0 / (el / done * len(st.layers)), "unit": "tokens/s", "cores": int(cores),
+               "kind": "oracle", "sample": f"{done} of {len(st.layers)} layers in {el:.1f} s, scaled to 36"}
+    line = {
+        "metric": METRIC, "value": round(1e3 / ms, 3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": st.name, "hidden": a.hidden, "batch": 1, "layers": len(st.layers),
+                   "positions": [st.layers[0].cache.position], "weights": "bf16", "kv_cache": "fp16",
+                   "stack_bytes_per_token": sb, "launch": "hip_graph" if args.graph else "eager"},
+        "block_hbm_gbs": round(sb / (ms * 1e-3) / 1e9, 1),
+        "block_frac_of_peak": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "host_submit_us_per_step": round(submitted / args.steps * 1e6, 3),
+        "roofline": None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="full32k", choices=sorted(workloads()))
+    ap.add_argument("--workload", default="full32k", choices=sorted(list(workloads()) + ["cfg4"]),
+                    help="cfg4 is the 36-layer stack at position 8191 (no dominant-kernel roofline)")
     ap.add_argument("--copies", type=int, default=0, help="weight/cache copies rotated (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample length (0 skips the baseline)")
@@ -177,6 +280,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.workload == "cfg4":
+        bench_stack(args)
+        return
     case = workloads()[args.workload]()
     a = gqa.Arch(hidden=case.arch.hidden)
     per_copy = (case.w_qkv.nbytes + case.w_g.nbytes + case.w_o.nbytes
