@@ -131,6 +131,7 @@ gqa_status window_of(int is_full, int32_t position, int32_t window, int32_t ring
 
 struct Plan {
   int chunk = kChunkQuantum;
+  bool direct = false;   // one chunk per sequence, finished by the partial kernel
   struct Group {
     int first = 0, count = 0, total_chunks = 0;
   };
@@ -197,7 +198,7 @@ gqa_status resolve_seqs(const gqa_arch *a, int is_full, const gqa_kv_seq *seqs, 
 // partials; fewer workgroups than the chip holds leave HBM bandwidth unused).
 // With C(c) chunks at chunk size c this keeps C <= 2 * kAttnTargetWgs / Hk +
 // sequences (see max_chunks).
-Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
+Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads, bool allow_direct) {
   Plan plan;
   auto wgs = [&](int chunk) {
     long n = 0;
@@ -208,7 +209,12 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads) {
   for (const SeqDesc &s : seqs) longest = std::max(longest, s.n);
   const int cap = ceil_div(longest, kChunkQuantum) * kChunkQuantum;
   int chunk = kChunkQuantum;
-  while (chunk + kChunkQuantum <= cap && wgs(chunk + kChunkQuantum) >= kAttnTargetWgs) chunk += kChunkQuantum;
+  if (allow_direct && longest <= kDirectMaxRows) {
+    chunk = cap;
+    plan.direct = true;
+  } else {
+    while (chunk + kChunkQuantum <= cap && wgs(chunk + kChunkQuantum) >= kAttnTargetWgs) chunk += kChunkQuantum;
+  }
   plan.chunk = chunk;
   for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {
     Plan::Group g;
@@ -358,6 +364,7 @@ AttnParams attn_params(const gqa_arch *a, const std::vector<SeqDesc> &seqs, cons
   p.num_kv_heads = a->num_kv_heads;
   p.qscale = (float)((double)a->attention_scale * kLog2e);
   p.chunk = plan.chunk;
+  p.direct = plan.direct ? 1 : 0;
   p.nseq = g.count;
   p.total_chunks = g.total_chunks;
   int cb = 0;
@@ -495,7 +502,7 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
   if ((st = check_ptr(gate_logits, "gate_logits")) != GQA_OK) return st;
   if ((st = check_ptr(attn_gated, "attn_gated")) != GQA_OK) return st;
   if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
-  const Plan plan = make_plan(descs, arch->num_kv_heads);
+  const Plan plan = make_plan(descs, arch->num_kv_heads, true);
   const size_t need = partial_bytes_o(arch, plan.max_group_chunks) + partial_bytes_ml(arch, plan.max_group_chunks);
   if (workspace_bytes < need)
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the attention needs %zu",
@@ -525,7 +532,7 @@ gqa_status gqa_attention_partials(const gqa_arch *arch, int is_full, const gqa_k
   if ((st = check_ptr(q_roped, "q_roped")) != GQA_OK) return st;
   if ((st = check_ptr(part_o, "part_o")) != GQA_OK) return st;
   if ((st = check_ptr(part_ml, "part_ml")) != GQA_OK) return st;
-  const Plan plan = make_plan(descs, arch->num_kv_heads);
+  const Plan plan = make_plan(descs, arch->num_kv_heads, false);
   const Plan::Group &g = plan.groups[0];
   if (g.total_chunks > max_chunks)
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "the partial pass writes %d chunks, max_chunks is %d", g.total_chunks,
@@ -552,7 +559,7 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
   if ((st = check_ptr(x_normed, "x_normed")) != GQA_OK) return st;
   if ((st = check_ptr(out, "out")) != GQA_OK) return st;
   if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
-  const Plan plan = make_plan(descs, arch->num_kv_heads);
+  const Plan plan = make_plan(descs, arch->num_kv_heads, true);
   const Layout L = block_layout(arch, batch, plan.max_group_chunks);
   if (workspace_bytes < L.total)
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the block needs %zu", workspace_bytes,

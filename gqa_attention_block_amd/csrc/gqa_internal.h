@@ -22,6 +22,12 @@ constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles f
 // the split plan, and the workspace bound derived from it, are the same
 // everywhere.
 constexpr int kAttnTargetWgs = 256;
+// Windows of at most this many rows run as one chunk per sequence and KV
+// head, finished inside the partial kernel (no combine launch).  Measured:
+// at 64 rows this saves the combine (~3.4 us); at 512 rows the 16 waves of
+// a one-chunk plan walk 8 tiles each in sequence (~14 us), slower than 8
+// chunks plus the combine (~10 us).
+constexpr int kDirectMaxRows = 128;
 constexpr int kMfmaMinBatch = 4;     // projections run on MFMA from this batch on
 constexpr float kRescaleSlack = 8.f; // log2 headroom before the softmax reference moves
 constexpr unsigned kMaxBufferBytes = 0x7FFFFFFFu;  // buffer loads use 31-bit offsets
@@ -55,6 +61,8 @@ struct AttnParams {
   float qscale;       // attention_scale * log2(e): scores come out in log2 units
   int chunk;          // rows per chunk (one workgroup per chunk and KV head, a quarter
                       // per wave): a multiple of kChunkQuantum
+  int direct;         // 1: every sequence is one chunk and the partial kernel writes
+                      // the gated output itself (no partials, no combine)
   int nseq;
   int total_chunks;
   SeqDesc seq[kMaxSeqPerLaunch];

@@ -921,6 +921,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
     o.z = fmaf(wt, v.z, o.z);
     o.w = fmaf(wt, v.w, o.w);
   }
+  if (p.direct) {
+    // the chunk is the whole window of sequence cid: normalise, gate, write
+    const int qh = g * kGroup + i;
+    const float gl = p.gate[(size_t)cid * p.ld_gate + qh];
+    const float sc = (1.0f / (1.0f + expf(-gl))) / L;
+    float *dst = p.out + (size_t)cid * p.ld_out + (size_t)qh * kHeadDim;
+    const float v[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane * 4 + j;                  // element e holds dim 16 (e % 16) + e / 16
+      dst[16 * (e & 15) + (e >> 4)] = v[j] * sc;
+    }
+    return;
+  }
   const size_t row = (size_t)cid * Hq + g * kGroup + i;
   *reinterpret_cast<float4 *>(p.part_o + row * kHeadDim + lane * 4) = o;
   if (lane == 0) *reinterpret_cast<float2 *>(p.part_ml + row * 2) = make_float2(M, L);
@@ -1151,7 +1165,7 @@ hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream) {
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
   hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.direct) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();
