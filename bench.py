@@ -161,7 +161,8 @@ def stack_bytes(st) -> int:
 
 
 def bench_stack(args):
-    """The 36-layer stack (RMSNorm -> block -> residual add per layer, no MLP)
+    """The 36-layer stack (RMSNorm -> block -> residual add per layer, no MLP,
+    each layer one gqa_attention_layer_decode call)
     at position 8191: 9 full layers over 8192 rows, 27 sliding layers over a
     wrapped 512-slot ring.  One step = one token through all 36 layers."""
     import numpy as np
@@ -177,16 +178,12 @@ def bench_stack(args):
               for L in st.layers]
     h0 = up(st.h)
     h = h0.clone()
-    xn = torch.empty_like(h)
-    o = torch.empty_like(h)
     ws = torch.empty(gqa.workspace_size(a, 1, st.layers[0].cache.position + 1), dtype=torch.uint8,
                      device="cuda:0")
 
-    def step():
+    def step():   # one gqa_attention_layer_decode per layer: h += block(RMSNorm(h) * w)
         for L in layers:
-            gqa.rms_norm_bf16w(h, L["w_norm"], xn, a.rms_eps)
-            gqa.attention_block_decode(a, L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], xn, o, ws)
-            gqa.residual_add(h, o)
+            gqa.attention_layer_decode(a, L["w_norm"], L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], h, ws)
 
     run = step
     if args.graph:

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     KvSeq,
     attention_block_decode,
     attention_gated,
+    attention_layer_decode,
     attention_partials,
     kv_slot,
     kv_window,

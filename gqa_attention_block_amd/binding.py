@@ -64,6 +64,7 @@ def _load():
         "gqa_kv_slot": (I32, [I32, I32]),
         "gqa_workspace_size": (ctypes.c_int, [A, I32, I32, ctypes.POINTER(S)]),
         "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
+        "gqa_attention_layer_decode": (ctypes.c_int, [A, W, P, ctypes.c_int, K, I32, P, P, S, P]),
         "gqa_qkv_rope_kv": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, P]),
         "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, S, P]),
         "gqa_attention_partials": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, I32,
@@ -86,7 +87,7 @@ _lib = _load()
 #: symbols the header declares; tests check the library exports all of them
 EXPORTED_SYMBOLS = (
     "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size",
-    "gqa_attention_block_decode", "gqa_qkv_rope_kv", "gqa_attention_gated",
+    "gqa_attention_block_decode", "gqa_attention_layer_decode", "gqa_qkv_rope_kv", "gqa_attention_gated",
     "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
     "gqa_last_error",
 )
@@ -245,6 +246,20 @@ def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Seq
         _ptr(out, torch.float32, "out", b * arch.hidden),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
         "gqa_attention_block_decode")
+
+
+def attention_layer_decode(arch: Arch, w_norm, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],
+                           h: torch.Tensor, workspace: torch.Tensor, stream=None):
+    """h += block(RMSNorm(h) * w_norm), in place (the attention half of a decoder layer)."""
+    b = len(seqs)
+    a = arch._c()
+    w = _weights(arch, w_qkv, w_g, w_o)
+    ks = _seqs(arch, seqs)
+    _check(_lib.gqa_attention_layer_decode(
+        ctypes.byref(a), ctypes.byref(w), _wptr(w_norm, "w_norm", arch.hidden), int(is_full), ks, b,
+        _ptr(h, torch.float32, "h", b * arch.hidden),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+        "gqa_attention_layer_decode")
 
 
 def qkv_rope_kv(arch: Arch, w_qkv, w_g, is_full: bool, seqs: Sequence[KvSeq], x: torch.Tensor,

@@ -275,9 +275,11 @@ gqa_status gpu_error(hipError_t e, const char *what) {
 
 // The fused projection step for every sequence, in launch groups of up to
 // kMaxSeqPerLaunch batch rows.
+// x is the normed input, or (w_norm set) the raw residual stream h, normed
+// on the fly with w_norm.
 gqa_status run_qkv_rope(const gqa_arch *a, const gqa_layer_weights *w, int is_full,
                         const std::vector<SeqDesc> &seqs, const float *x, float *q, float *gate,
-                        hipStream_t stream) {
+                        hipStream_t stream, const uint16_t *w_norm = nullptr) {
   int32_t rdim;
   double theta;
   gqa_rope_params_for(is_full, a->full_rotary_dim, a->head_dim, a->full_rope_theta, a->rope_theta, &rdim,
@@ -299,6 +301,8 @@ gqa_status run_qkv_rope(const gqa_arch *a, const gqa_layer_weights *w, int is_fu
     p.num_kv_heads = a->num_kv_heads;
     p.rotary_dim = rdim;
     p.log2_theta = log2(theta);
+    p.w_norm = w_norm;
+    p.rms_eps = a->rms_eps;
     for (int i = 0; i < p.batch; ++i) p.seq[i] = seqs[first + i];
     // batched: MFMA (its units pair RoPE tiles, so the rotated width must be
     // whole 32-row tile pairs); batch 1-3: the fused VALU kernel
@@ -309,8 +313,9 @@ gqa_status run_qkv_rope(const gqa_arch *a, const gqa_layer_weights *w, int is_fu
   return GQA_OK;
 }
 
+// accumulate: out += W_o attn (the residual add) instead of out = W_o attn
 gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t batch, const float *attn,
-                      float *out, hipStream_t stream) {
+                      float *out, hipStream_t stream, bool accumulate = false) {
   const int cols = a->num_heads * a->head_dim;
   if (batch >= kMfmaMinBatch) {
     // groups of <= 32 batch rows on MFMA (a small last group on the VALU GEMV)
@@ -324,6 +329,7 @@ gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t bat
       p.ldx = cols;
       p.y0 = out + (size_t)first * a->hidden;
       p.ldy0 = a->hidden;
+      p.accumulate = accumulate ? 1 : 0;
       hipError_t e = p.batch >= kMfmaMinBatch ? launch_proj_mfma(p, stream) : launch_gemv(p, stream);
       if (e != hipSuccess) return gpu_error(e, "o_proj launch");
     }
@@ -342,6 +348,7 @@ gqa_status run_o_proj(const gqa_arch *a, const gqa_layer_weights *w, int32_t bat
   p.ldy0 = a->hidden;
   p.y1 = nullptr;
   p.ldy1 = 0;
+  p.accumulate = accumulate ? 1 : 0;
   hipError_t e = launch_gemv(p, stream);
   return e == hipSuccess ? GQA_OK : gpu_error(e, "o_proj GEMV launch");
 }
@@ -574,6 +581,41 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
   if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
   if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
   if ((st = run_o_proj(arch, weights, batch, attn, out, s)) != GQA_OK) return st;
+  return ok();
+}
+
+gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weights *weights, const void *w_norm,
+                                      int is_full, const gqa_kv_seq *seqs, int32_t batch, float *h, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_weights(weights, true, true)) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  if (!(arch->rms_eps >= 0.f) || !isfinite(arch->rms_eps))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
+  if (batch == 0) return ok();
+  if ((st = check_ptr(w_norm, "w_norm")) != GQA_OK) return st;
+  if ((st = check_ptr(h, "h")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  const Plan plan = make_plan(descs, arch->num_kv_heads, true);
+  const Layout L = block_layout(arch, batch, plan.max_group_chunks);
+  if (workspace_bytes < L.total)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the layer needs %zu", workspace_bytes,
+                L.total);
+  char *ws = static_cast<char *>(workspace);
+  float *q = reinterpret_cast<float *>(ws + L.q);
+  float *gate = reinterpret_cast<float *>(ws + L.gate);
+  float *attn = reinterpret_cast<float *>(ws + L.attn);
+  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
+  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_qkv_rope(arch, weights, is_full, descs, h, q, gate, s, static_cast<const uint16_t *>(w_norm))) !=
+      GQA_OK)
+    return st;
+  if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
+  if ((st = run_o_proj(arch, weights, batch, attn, h, s, true)) != GQA_OK) return st;
   return ok();
 }
 

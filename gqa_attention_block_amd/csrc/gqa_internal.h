@@ -85,6 +85,9 @@ struct QkvParams {
   int num_kv_heads;
   int rotary_dim;
   double log2_theta;
+  const uint16_t *w_norm; // bf16 [hidden] or null: x is then the raw residual stream h and
+                          // the projections see RMSNorm(h) * w_norm (eps rms_eps)
+  float rms_eps;
   SeqDesc seq[kMaxSeqPerLaunch];
 };
 
@@ -101,6 +104,7 @@ struct GemvParams {
   long ldy0;
   float *y1;          // [batch][ldy1] receives rows of w1
   long ldy1;
+  int accumulate;     // 1: y += W x (the residual add of the layer loop), else y = W x
 };
 
 // Launchers (gqa_kernels.hip).  They return the hipError_t of the launch.

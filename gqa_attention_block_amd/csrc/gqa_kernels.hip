@@ -200,10 +200,9 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p)
       for (int m = 0; m < MB; ++m) {
         const float s = wave_sum(acc[r][m]);
         if (lane == r * MB + m && row < total && b0 + m < p.batch) {
-          if (row < p.rows0)
-            p.y0[(size_t)(b0 + m) * p.ldy0 + row] = s;
-          else
-            p.y1[(size_t)(b0 + m) * p.ldy1 + (row - p.rows0)] = s;
+          float *y = row < p.rows0 ? p.y0 + (size_t)(b0 + m) * p.ldy0 + row
+                                   : p.y1 + (size_t)(b0 + m) * p.ldy1 + (row - p.rows0);
+          *y = p.accumulate ? *y + s : s;
         }
       }
     }
@@ -257,10 +256,8 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
     const float s = wave_sum(a);
     const int row = row0 + r;
     if (lane == r && row < total) {
-      if (row < p.rows0)
-        p.y0[row] = s;
-      else
-        p.y1[row - p.rows0] = s;
+      float *y = row < p.rows0 ? p.y0 + row : p.y1 + (row - p.rows0);
+      *y = p.accumulate ? *y + s : s;
     }
   }
 }
@@ -298,7 +295,9 @@ __device__ __forceinline__ void rope_rotate(int position, int i, int rotary_dim,
   yb = rb;
 }
 
-template <int NIT, int MB>
+// NORM: x is the raw residual stream h and each projection is
+// inv_rms(h) * W (h * w_norm), the sum of squares taken over the same loads.
+template <int NIT, int MB, bool NORM>
 __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
   const int lane = threadIdx.x & 63;
   const int P = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -339,24 +338,47 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
     wb[it] = buf_load16(rw, ok ? (unsigned)(base_row + dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
   }
 
+  uint4 wn[NORM ? NIT : 1];
+  if constexpr (NORM) {
+    const __amdgpu_buffer_rsrc_t rn = make_rsrc(p.w_norm, (unsigned)p.hidden * 2u);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int col = (it * 64 + lane) * 8;
+      wn[it] = buf_load16(rn, col < p.hidden ? (unsigned)col * 2u : kOutOfRange);
+    }
+  }
+
   for (int b0 = 0; b0 < p.batch; b0 += MB) {
     float sa[MB], sb[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      float a = 0.f, c = 0.f;
+      float a = 0.f, c = 0.f, ss = 0.f;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int col = (it * 64 + lane) * 8;
         const unsigned xo = (col < p.hidden && b0 + m < p.batch)
                                 ? (unsigned)(((size_t)(b0 + m) * p.ldx + col) * 4u)
                                 : kOutOfRange;
-        const float4 xa = __builtin_bit_cast(float4, buf_load16(rx, xo));
-        const float4 xb = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
+        float4 xa = __builtin_bit_cast(float4, buf_load16(rx, xo));
+        float4 xb = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
+        if constexpr (NORM) {
+          ss = fmaf(xa.x, xa.x, fmaf(xa.y, xa.y, fmaf(xa.z, xa.z, fmaf(xa.w, xa.w, ss))));
+          ss = fmaf(xb.x, xb.x, fmaf(xb.y, xb.y, fmaf(xb.z, xb.z, fmaf(xb.w, xb.w, ss))));
+          xa = make_float4(xa.x * bf16_lo(wn[it].x), xa.y * bf16_hi(wn[it].x), xa.z * bf16_lo(wn[it].y),
+                           xa.w * bf16_hi(wn[it].y));
+          xb = make_float4(xb.x * bf16_lo(wn[it].z), xb.y * bf16_hi(wn[it].z), xb.z * bf16_lo(wn[it].w),
+                           xb.w * bf16_hi(wn[it].w));
+        }
         a = dot8_bf16(wa[it], xa, xb, a);
         c = dot8_bf16(wb[it], xa, xb, c);
       }
       sa[m] = wave_sum(a);
       sb[m] = wave_sum(c);
+      if constexpr (NORM) {
+        const float inv = rsqrtf(wave_sum(ss) / (float)p.hidden + p.rms_eps);
+        sa[m] *= inv;
+        sb[m] *= inv;
+      }
     }
     // epilogue: lane m handles batch row b0 + m
     float ya = 0.f, yb = 0.f;
@@ -449,11 +471,18 @@ __device__ __forceinline__ void proj_to_bf16(const float4 x0, const float4 x1, b
   }
 }
 
+__device__ __forceinline__ const uint16_t *norm_weights(const QkvParams &p) { return p.w_norm; }
+__device__ __forceinline__ const uint16_t *norm_weights(const GemvParams &) { return nullptr; }
+
 // MODE 0: plain product into y0 / y1 (GemvParams); MODE 1: q_k_v_proj +
 // g_proj with the RoPE / KV-slot epilogue (QkvParams).  MB batch tiles of 16.
-template <int MODE, int MB, typename Params>
+// NORM (MODE 1): x is the raw residual stream h; the product takes h * w_norm
+// and the epilogue scales by inv_rms(h), whose sum of squares the waves
+// gather over their columns and add in LDS.
+template <int MODE, int MB, bool NORM, typename Params>
 __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p) {
   __shared__ float4 s_red[kProjSplit][2][32][4];   // [wave][tile][batch][rows 4k..4k+3] per 16-row tile
+  __shared__ float s_ss[kProjSplit][32];           // NORM: [wave][batch] partial sums of squares
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -509,7 +538,11 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
   struct Set {
     uint4 wa[kProjSet], wb[kProjSet];
     float4 xv[kProjSet][MB][2];
+    uint4 wn[NORM ? kProjSet : 1];
   };
+  // NORM: the w_norm resource (a zero-size resource otherwise, never read)
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(NORM ? (const void *)norm_weights(p) : nullptr,
+                                              NORM ? (unsigned)cols * 2u : 0u);
   auto load = [&](Set &S, int set) {
 #pragma unroll
     for (int j = 0; j < kProjSet; ++j) {
@@ -523,8 +556,12 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
         S.xv[j][bt][0] = __builtin_bit_cast(float4, buf_load16(rx, xo));
         S.xv[j][bt][1] = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
       }
+      if constexpr (NORM) S.wn[j] = buf_load16(rn, ok ? (unsigned)col * 2u : kOutOfRange);
     }
   };
+  float ssp[MB];   // NORM: this lane's sum of squares per batch tile
+#pragma unroll
+  for (int bt = 0; bt < MB; ++bt) ssp[bt] = 0.f;
   floatx4_t accA[MB], accB[MB];
 #pragma unroll
   for (int bt = 0; bt < MB; ++bt) {
@@ -538,8 +575,18 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
       const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, S.wb[j]);
 #pragma unroll
       for (int bt = 0; bt < MB; ++bt) {
+        float4 x0 = S.xv[j][bt][0], x1 = S.xv[j][bt][1];
+        if constexpr (NORM) {
+          float q = ssp[bt];
+          q = fmaf(x0.x, x0.x, fmaf(x0.y, x0.y, fmaf(x0.z, x0.z, fmaf(x0.w, x0.w, q))));
+          q = fmaf(x1.x, x1.x, fmaf(x1.y, x1.y, fmaf(x1.z, x1.z, fmaf(x1.w, x1.w, q))));
+          ssp[bt] = q;
+          const uint4 wv = S.wn[j];
+          x0 = make_float4(x0.x * bf16_lo(wv.x), x0.y * bf16_hi(wv.x), x0.z * bf16_lo(wv.y), x0.w * bf16_hi(wv.y));
+          x1 = make_float4(x1.x * bf16_lo(wv.z), x1.y * bf16_hi(wv.z), x1.z * bf16_lo(wv.w), x1.w * bf16_hi(wv.w));
+        }
         bf16x8_t hi, lo;
-        proj_to_bf16(S.xv[j][bt][0], S.xv[j][bt][1], hi, lo);
+        proj_to_bf16(x0, x1, hi, lo);
         accA[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, accA[bt], 0, 0, 0);
         accA[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, accA[bt], 0, 0, 0);
         accB[bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b2, hi, accB[bt], 0, 0, 0);
@@ -568,6 +615,13 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
     s_red[w][0][bt * 16 + n][G] = make_float4(accA[bt][0], accA[bt][1], accA[bt][2], accA[bt][3]);
     s_red[w][1][bt * 16 + n][G] = make_float4(accB[bt][0], accB[bt][1], accB[bt][2], accB[bt][3]);
   }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int bt = 0; bt < MB; ++bt) {
+      const float q = sum_across_rows(ssp[bt]);   // the 4 lane groups of batch column n
+      if (G == 0) s_ss[w][bt * 16 + n] = q;
+    }
+  }
   __syncthreads();
   // thread t: batch row b = t / 16, row xr = t % 16 of both tiles
   const int t = threadIdx.x;
@@ -582,9 +636,23 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
   if constexpr (MODE == 0) {
     float *y = first ? p.y0 : p.y1;
     const long ldy = first ? p.ldy0 : p.ldy1;
-    if (rowA + xr < wrows) y[(size_t)b * ldy + rowA + xr] = ya;
-    if (rowB + xr < wrows) y[(size_t)b * ldy + rowB + xr] = yb;
+    if (rowA + xr < wrows) {
+      float *d = y + (size_t)b * ldy + rowA + xr;
+      *d = p.accumulate ? *d + ya : ya;
+    }
+    if (rowB + xr < wrows) {
+      float *d = y + (size_t)b * ldy + rowB + xr;
+      *d = p.accumulate ? *d + yb : yb;
+    }
   } else {
+    if constexpr (NORM) {
+      float q = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kProjSplit; ++ww) q += s_ss[ww][b];
+      const float inv = rsqrtf(q / (float)cols + p.rms_eps);
+      ya *= inv;
+      yb *= inv;
+    }
     if (U.sec == 3) {
       float *gl = p.gate_out + (size_t)b * p.ld_gate;
       if (xr < p.num_heads) gl[xr] = ya;
@@ -1106,10 +1174,18 @@ template <int NIT>
 hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
   const int pairs = (p.num_heads + 2 * p.num_kv_heads) * (kHeadDim / 2) + p.num_heads / 2;
   const dim3 grid((pairs + 3) / 4);
-  if (p.batch == 1)
-    hipLaunchKernelGGL((qkv_rope_kernel<NIT, 1>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((qkv_rope_kernel<NIT, 4>), grid, dim3(kThreads), 0, stream, p);
+  const bool norm = p.w_norm != nullptr;
+  if (p.batch == 1) {
+    if (norm)
+      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 1, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 1, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (norm)
+      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 4, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 4, false>), grid, dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -1118,18 +1194,26 @@ hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
 hipError_t launch_proj_mfma(const GemvParams &p, hipStream_t stream) {
   const int units = (p.rows0 + 31) / 32 + (p.rows1 + 31) / 32;
   if (p.batch > 16)
-    hipLaunchKernelGGL((proj_mfma_kernel<0, 2, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+    hipLaunchKernelGGL((proj_mfma_kernel<0, 2, false, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((proj_mfma_kernel<0, 1, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+    hipLaunchKernelGGL((proj_mfma_kernel<0, 1, false, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_mfma(const QkvParams &p, hipStream_t stream) {
   const int units = 8 * (p.num_heads + 2 * p.num_kv_heads) + 1;
-  if (p.batch > 16)
-    hipLaunchKernelGGL((proj_mfma_kernel<1, 2, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((proj_mfma_kernel<1, 1, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  const bool norm = p.w_norm != nullptr;
+  if (p.batch > 16) {
+    if (norm)
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 2, true, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 2, false, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  } else {
+    if (norm)
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 1, true, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 1, false, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

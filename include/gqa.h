@@ -157,6 +157,24 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
                                       const float *x_normed, float *out, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* The attention half of one decoder layer, in place on the residual stream
+ * ([mod] `produce_real_spark_inner`: input RMSNorm with a plain bf16 weight,
+ * the block, the raw residual add):
+ *   h[b] += block(RMSNorm(h[b]) * w_norm)
+ * with RMSNorm(h) = h / sqrt(mean(h^2) + arch->rms_eps).  The norm is folded
+ * into the projections (inv_rms(h) * W (h * w_norm)) and the residual add into
+ * the o_proj epilogue, so a layer is the block's launches and nothing more.
+ *   w_norm     device bf16 [H]
+ *   h          device fp32 [batch][H], read and updated in place
+ *   weights, is_full, seqs, workspace as for gqa_attention_block_decode (the
+ *   workspace size is the block's).
+ * Side effect: each sequence's cache slot row for `position` is written.
+ * Errors: those of gqa_attention_block_decode, and rms_eps < 0 or not finite. */
+gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weights *weights,
+                                      const void *w_norm, int is_full, const gqa_kv_seq *seqs,
+                                      int32_t batch, float *h, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Step entry points: the same kernels the block launches, exposed so each
  * step can be checked and timed on its own.

@@ -434,6 +434,57 @@ def test_stack_delta_matches_oracle(phase_full_first):
         assert_parity(outs[li], ref.block_outs[li], f"stack layer {li} block output")
 
 
+# ----------------------------------------------------------------------------
+# the fused layer entry: h += block(RMSNorm(h) * w_norm)
+# ----------------------------------------------------------------------------
+
+LAYER_CASES = [
+    ("full_h2560_pos4095_b1", 2560, True, [4095], 0),
+    ("ring_h1024_pos1000_b1", 1024, False, [1000], 512),
+    ("full_h1024_b2", 1024, True, [63, 700], 0),
+    ("full_h1024_b5", 1024, True, [7, 63, 200, 1000, 4095], 0),
+    ("ring_h2560_b17", 2560, False, list(range(300, 300 + 17 * 97, 97)), 512),
+]
+
+
+@pytest.mark.parametrize("name,hidden,is_full,positions,ring", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_decode_matches_oracle(name, hidden, is_full, positions, ring):
+    say(f"attention_layer_decode {name}")
+    case = synth.block_case(name, hidden, is_full, positions, ring_capacity=ring, seed=0, case_id=30)
+    w_norm = synth.random_bf16((hidden,), 0, 30, 77, std=0.1, mean=1.0)
+    h0 = synth.random_hidden(hidden, case.batch, 0, 30, tensor_id=78)
+    dev = DevBlock(case)
+    h = f32_to_dev(h0)
+    gqa.attention_layer_decode(dev.arch, bits_to_dev(w_norm), dev.w_qkv, dev.w_g, dev.w_o, is_full,
+                               dev.seqs(), h, dev.ws)
+    torch.cuda.synchronize()
+    delta = h.cpu().numpy().astype(np.float64) - h0.astype(np.float64)
+    xn = oracle.rms_norm(h0, w_norm, case.arch.rms_eps)
+    ref = oracle.block_decode(case.arch, is_full, case.w_qkv, case.w_g, case.w_o, xn, case.seqs)
+    assert_parity(delta, ref.out, f"{name} residual delta")
+    check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, name)
+
+
+@pytest.mark.parametrize("phase_full_first", [False, True])
+def test_stack_of_fused_layers_matches_oracle(phase_full_first):
+    case = synth.cfg4_stack(num_layers=8, position=1000, phase_full_first=phase_full_first)
+    say(f"fused-layer stack {case.name} phase_full_first={phase_full_first}")
+    a = arch_of(case.arch)
+    h = f32_to_dev(case.h)
+    ws = torch.empty(gqa.workspace_size(a, 1, case.layers[0].cache.position + 1), dtype=torch.uint8,
+                     device="cuda")
+    for L in case.layers:
+        k, v = f16_to_dev(L.cache.k), f16_to_dev(L.cache.v)
+        gqa.attention_layer_decode(a, bits_to_dev(L.w_norm), bits_to_dev(L.w_qkv), bits_to_dev(L.w_g),
+                                   bits_to_dev(L.w_o), L.is_full,
+                                   [gqa.KvSeq(k=k, v=v, position=L.cache.position,
+                                              ring_capacity=L.cache.ring_capacity)], h, ws)
+    torch.cuda.synchronize()
+    ref = oracle.stack_decode(case.arch, case.h, case.layers)
+    delta = h.cpu().numpy().astype(np.float64) - np.asarray(case.h, np.float64)
+    assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "fused-layer stack residual delta")
+
+
 def test_rms_norm_and_residual_add():
     say("rms_norm + residual_add")
     hidden, rows = 2560, 3

@@ -218,6 +218,24 @@ def test_partials_entry_validates():
     assert call(1, ctypes.byref(rows), begin) == INVALID             # linear cache too short
 
 
+def test_layer_entry_validates():
+    a = B.c_arch(gqa.Arch(hidden=1024))
+    w = B.c_weights(FAKE, FAKE, FAKE)
+    arr = B.c_seq_array(1)
+    arr[0] = _seq()
+    call = lambda arch, wn, h: B.raw_call("gqa_attention_layer_decode", ctypes.byref(arch),  # noqa: E731
+                                          ctypes.byref(w), wn, 1, arr, 1, h, FAKE, 1 << 30, None)
+    assert call(a, 0, FAKE) == INVALID                 # w_norm is null
+    assert call(a, MISALIGNED, FAKE) == INVALID
+    assert call(a, FAKE, MISALIGNED) == INVALID        # h misaligned
+    assert call(B.c_arch(gqa.Arch(hidden=1024, rms_eps=-1.0)), FAKE, FAKE) == INVALID
+    assert call(B.c_arch(gqa.Arch(hidden=1024, rms_eps=float("nan"))), FAKE, FAKE) == INVALID
+    assert B.raw_call("gqa_attention_layer_decode", ctypes.byref(a), ctypes.byref(w), FAKE, 1, arr, 1,
+                      FAKE, FAKE, 1024, None) == WS_SMALL
+    assert B.raw_call("gqa_attention_layer_decode", ctypes.byref(a), ctypes.byref(w), 0, 1, None, 0,
+                      0, 0, 0, None) == OK                  # batch 0: nothing to do
+
+
 def test_status_strings():
     assert B.status_string(0) == "GQA_OK"
     assert B.status_string(3) == "GQA_ERR_WORKSPACE_TOO_SMALL"
