@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kProjSplit = 8;                 // waves (column splits) per workgroup
 constexpr int kProjThreads = 64 * kProjSplit;
-constexpr int kProjSet = 2;                   // k-steps (32 columns each) per load set
+constexpr int kProjSet = 3;                   // k-steps (32 columns each) per load set
 
 // Which two 16-row tiles a unit covers.  Plain: tiles 2u, 2u+1 of the
 // concatenated rows.  q_k_v_proj + g_proj: per head (q, k, v sections) 8
@@ -1098,6 +1098,56 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
   }
 }
 
+// The merge for plans with at most kCombineSmallChunks chunks per sequence
+// (short windows, many sequences): one wave per (query head, sequence), lane
+// l owns elements 4l .. 4l+3 and loads every chunk's partial at once.
+constexpr int kCombineSmallChunks = 8;
+
+__global__ __launch_bounds__(64) void attn_combine_small_kernel(const AttnParams p) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const SeqDesc sd = p.seq[b];
+  const int Hq = p.num_kv_heads * kGroup;
+  const int nchunks = (sd.n + p.chunk - 1) / p.chunk;
+  float2 ml[kCombineSmallChunks];
+  float4 o[kCombineSmallChunks];
+#pragma unroll
+  for (int u = 0; u < kCombineSmallChunks; ++u) {
+    if (u < nchunks) {
+      const size_t row = (size_t)(sd.chunk_begin + u) * Hq + h;
+      ml[u] = *reinterpret_cast<const float2 *>(p.part_ml + row * 2);
+      o[u] = *reinterpret_cast<const float4 *>(p.part_o + row * kHeadDim + lane * 4);
+    } else {
+      ml[u] = make_float2(-INFINITY, 0.f);
+      o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kCombineSmallChunks; ++u) M = fmaxf(M, ml[u].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < kCombineSmallChunks; ++u) {
+    const float wt = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - M);
+    L = fmaf(wt, ml[u].y, L);
+    acc.x = fmaf(wt, o[u].x, acc.x);
+    acc.y = fmaf(wt, o[u].y, acc.y);
+    acc.z = fmaf(wt, o[u].z, acc.z);
+    acc.w = fmaf(wt, o[u].w, acc.w);
+  }
+  const float gl = p.gate[(size_t)b * p.ld_gate + h];
+  const float sc = (1.0f / (1.0f + expf(-gl))) / L;
+  float *dst = p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim;
+  const float v[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane * 4 + j;                    // element e holds dim 16 (e % 16) + e / 16
+    dst[16 * (e & 15) + (e >> 4)] = v[j] * sc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // RMSNorm with a bf16 weight: one workgroup per row.
 // ---------------------------------------------------------------------------
@@ -1250,8 +1300,13 @@ hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stre
   hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.direct) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,
-                     stream, p);
+  int most = 0;
+  for (int i = 0; i < p.nseq; ++i) most = std::max(most, (p.seq[i].n + p.chunk - 1) / p.chunk);
+  if (most <= kCombineSmallChunks)
+    hipLaunchKernelGGL(attn_combine_small_kernel, dim3(num_heads, p.nseq), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
