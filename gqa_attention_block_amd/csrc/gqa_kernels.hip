@@ -148,7 +148,8 @@ __device__ __forceinline__ float dot8_bf16(uint4 q, float4 xa, float4 xb, float 
 template <int R, int NIT, int MB>
 __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p) {
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  // wave index kept scalar: row-dependent choices (which weight buffer) stay uniform
+  const int wave = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int total = p.rows0 + p.rows1;
   const int row0 = wave * R;
   if (row0 >= total) return;
@@ -210,23 +211,78 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p)
 }
 
 // ---------------------------------------------------------------------------
+// x staged once per workgroup in LDS for the batch-1 kernels.
+//
+// Lane l of a wave reads columns (it*64 + l)*8 .. +8 of its rows, so it needs
+// x at the same columns in every wave of the workgroup; loaded per wave, x
+// (fp32: twice the bytes of a bf16 row) would pass through the CU's L1 once
+// per wave.  Here the workgroup loads it once: thread t holds float4s
+// t, t + 256, ... (columns 4f .. 4f+3), issued before the weight loads so that
+// the wait for them does not include the weights, and writes them to LDS as
+// two arrays, s[0][j] = columns 8j .. 8j+3 and s[1][j] = 8j+4 .. 8j+7, so a
+// wave's 16-byte reads of either are contiguous.  NORM also multiplies by a
+// bf16 weight and keeps the thread's sum of squares of x.
+// ---------------------------------------------------------------------------
+template <int NIT>
+struct StagedX {
+  static constexpr int kGroups = NIT * 64;                           // 8-column groups read
+  static constexpr int kPer = (2 * kGroups + kThreads - 1) / kThreads;  // float4s per thread
+  static constexpr int kSlots = kPer * kThreads / 2;                 // >= kGroups: every store in bounds
+  float4 v[kPer];
+  uint2 wn[kPer];
+
+  // x row at byte `base` of rx.  No load or store is conditional (a
+  // conditional store lets the compiler sink its load behind the weight
+  // loads): float4s past the row read as zeros from the resource bound and
+  // land in the slots past kGroups, which are never read.
+  template <bool NORM>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rx, unsigned base, __amdgpu_buffer_rsrc_t rn) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const unsigned f = threadIdx.x + k * kThreads;
+      v[k] = __builtin_bit_cast(float4, buf_load16(rx, base + f * 16u));
+      if constexpr (NORM) wn[k] = buf_load8(rn, f * 8u);
+    }
+  }
+  // writes LDS; returns this thread's sum of squares of x (NORM) or 0
+  template <bool NORM>
+  __device__ __forceinline__ float store(float4 (*s)[kSlots]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const unsigned f = threadIdx.x + k * kThreads;
+      float4 x = v[k];
+      if constexpr (NORM) {
+        ss = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, ss))));
+        x = make_float4(x.x * bf16_lo(wn[k].x), x.y * bf16_hi(wn[k].x), x.z * bf16_lo(wn[k].y),
+                        x.w * bf16_hi(wn[k].y));
+      }
+      s[f & 1][f >> 1] = x;
+    }
+    return ss;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Batch-1 GEMV.  NIT is exactly ceil(cols/512), so no registers hold loads
-// that would only return zeros; x (the lane's 8*NIT columns) stays in
-// registers for the wave's R rows.  Fewer registers than the batched kernel
-// means more resident waves per CU and more bytes in flight.
+// that would only return zeros; x comes from LDS (StagedX).  Waves past the
+// last row still take part in the barrier; their loads are out of range.
 // ---------------------------------------------------------------------------
 template <int R, int NIT>
 __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p) {
+  __shared__ float4 s_x[2][StagedX<NIT>::kSlots];
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  // wave index kept scalar: row-dependent choices (which weight buffer) stay uniform
+  const int wave = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int total = p.rows0 + p.rows1;
   const int row0 = wave * R;
-  if (row0 >= total) return;
   const unsigned row_bytes = (unsigned)p.cols * 2u;
   const __amdgpu_buffer_rsrc_t r0 = make_rsrc(p.w0, (unsigned)p.rows0 * row_bytes);
   const __amdgpu_buffer_rsrc_t r1 = make_rsrc(p.w1, (unsigned)p.rows1 * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)p.cols * 4u);
 
+  StagedX<NIT> xs;
+  xs.template issue<false>(rx, 0u, rx);
   uint4 w[R][NIT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -240,19 +296,13 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
       w[r][it] = first ? buf_load16(r0, off) : buf_load16(r1, off);
     }
   }
-  float4 xa[NIT], xb[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int col = (it * 64 + lane) * 8;
-    const unsigned xo = col < p.cols ? (unsigned)col * 4u : kOutOfRange;
-    xa[it] = __builtin_bit_cast(float4, buf_load16(rx, xo));
-    xb[it] = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
-  }
+  xs.template store<false>(s_x);
+  __syncthreads();
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float a = 0.f;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) a = dot8_bf16(w[r][it], xa[it], xb[it], a);
+    for (int it = 0; it < NIT; ++it) a = dot8_bf16(w[r][it], s_x[0][it * 64 + lane], s_x[1][it * 64 + lane], a);
     const float s = wave_sum(a);
     const int row = row0 + r;
     if (lane == r && row < total) {
@@ -280,31 +330,68 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
 // The angle is formed and reduced mod 2*pi in fp64 (an fp32 angle at position
 // 32767 would be off by ~4e-3 rad); the reduced angle is in [-pi, pi], where
 // fp32 sin/cos are accurate.
-__device__ __forceinline__ void rope_rotate(int position, int i, int rotary_dim, double log2_theta, float &ya,
-                                            float &yb) {
+__device__ __forceinline__ void rope_sincos(int position, int i, int rotary_dim, double log2_theta, float &sn,
+                                            float &cs) {
   const double inv = exp2(-(2.0 * (double)i / (double)rotary_dim) * log2_theta);
   const double ang = (double)position * inv;
   const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
   double red = fma(-k, 6.283185307179586, ang);               // 2 pi, high part
   red = fma(-k, 2.4492935982947064e-16, red);                 // 2 pi, low part
-  float sn, cs;
   sincosf((float)red, &sn, &cs);
+}
+
+__device__ __forceinline__ void rope_apply(float sn, float cs, float &ya, float &yb) {
   const float ra = ya * cs - yb * sn;
   const float rb = yb * cs + ya * sn;
   ya = ra;
   yb = rb;
 }
 
+__device__ __forceinline__ void rope_rotate(int position, int i, int rotary_dim, double log2_theta, float &ya,
+                                            float &yb) {
+  float sn, cs;
+  rope_sincos(position, i, rotary_dim, log2_theta, sn, cs);
+  rope_apply(sn, cs, ya, yb);
+}
+
+// Epilogue of one output pair (rows dA, dB of section sec, head `head`) for
+// batch row b: RoPE, then q -> q_out (fp32), k and v -> fp16 into the cache
+// slot of this position, gate logits -> gate_out.
+__device__ __forceinline__ void qkv_write(const QkvParams &p, int sec, int head, bool rotate, float sn, float cs,
+                                          int dA, int dB, int b, float ya, float yb) {
+  const SeqDesc &sd = p.seq[b];
+  if (rotate) rope_apply(sn, cs, ya, yb);
+  if (sec == 0) {
+    float *q = p.q_out + (size_t)b * p.ld_q + (size_t)head * kHeadDim;
+    q[dA] = ya;
+    q[dB] = yb;
+  } else if (sec == 3) {
+    float *gl = p.gate_out + (size_t)b * p.ld_gate;
+    gl[dA] = ya;
+    gl[dB] = yb;
+  } else {
+    _Float16 *dst = (sec == 1 ? sd.k : sd.v) + (size_t)sd.slot * p.num_kv_heads * kHeadDim + (size_t)head * kHeadDim;
+    dst[dA] = (_Float16)ya;
+    dst[dB] = (_Float16)yb;
+  }
+}
+
 // NORM: x is the raw residual stream h and each projection is
 // inv_rms(h) * W (h * w_norm), the sum of squares taken over the same loads.
+// MB == 1 (batch 1) stages x in LDS (StagedX); then waves past the last pair
+// still take part in the barrier, with out-of-range loads and no writes.
 template <int NIT, int MB, bool NORM>
 __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
+  constexpr bool kStaged = MB == 1;
+  __shared__ float4 s_x[kStaged ? 2 : 1][kStaged ? StagedX<NIT>::kSlots : 1];
+  __shared__ float s_ss[kThreads / 64];
   const int lane = threadIdx.x & 63;
-  const int P = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int P = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar
   const int Hq = p.num_heads, Hk = p.num_kv_heads;
   constexpr int kPairs = kHeadDim / 2;
   const int nq = Hq * kPairs, nk = Hk * kPairs, nv = Hk * kPairs;
-  if (P >= nq + nk + nv + Hq / 2) return;
+  const bool active = P < nq + nk + nv + Hq / 2;
+  if (!kStaged && !active) return;
   int sec, head, pi;
   if (P < nq) {
     sec = 0; head = P / kPairs; pi = P % kPairs;
@@ -329,81 +416,95 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
                                             : make_rsrc(p.w_g, (unsigned)Hq * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)((size_t)p.batch * p.ldx * 4u));
 
+  StagedX<NIT> xs;
+  if constexpr (kStaged)   // row 0 of x only, bounded at hidden (ldx may be larger)
+    xs.template issue<NORM>(make_rsrc(p.x, (unsigned)p.hidden * 4u), 0u,
+                            make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u));
   uint4 wa[NIT], wb[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int col = (it * 64 + lane) * 8;
-    const bool ok = col < p.hidden;
+    const bool ok = active && col < p.hidden;
     wa[it] = buf_load16(rw, ok ? (unsigned)(base_row + dA) * row_bytes + (unsigned)col * 2u : kOutOfRange);
     wb[it] = buf_load16(rw, ok ? (unsigned)(base_row + dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
   }
 
-  uint4 wn[NORM ? NIT : 1];
-  if constexpr (NORM) {
-    const __amdgpu_buffer_rsrc_t rn = make_rsrc(p.w_norm, (unsigned)p.hidden * 2u);
+  if constexpr (kStaged) {
+    // the rotation does not depend on the loads: formed while they are in flight
+    float sn = 0.f, cs = 1.f;
+    if (rotate) rope_sincos(p.seq[0].position, pi, p.rotary_dim, p.log2_theta, sn, cs);
+    const float ss = wave_sum(xs.template store<NORM>(s_x));
+    if (NORM && lane == 0) s_ss[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float a = 0.f, c = 0.f;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int col = (it * 64 + lane) * 8;
-      wn[it] = buf_load16(rn, col < p.hidden ? (unsigned)col * 2u : kOutOfRange);
+      a = dot8_bf16(wa[it], s_x[0][it * 64 + lane], s_x[1][it * 64 + lane], a);
+      c = dot8_bf16(wb[it], s_x[0][it * 64 + lane], s_x[1][it * 64 + lane], c);
     }
-  }
-
-  for (int b0 = 0; b0 < p.batch; b0 += MB) {
-    float sa[MB], sb[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      float a = 0.f, c = 0.f, ss = 0.f;
+    float ya = wave_sum(a), yb = wave_sum(c);
+    if constexpr (NORM) {
+      const float inv = rsqrtf((s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3]) / (float)p.hidden + p.rms_eps);
+      ya *= inv;
+      yb *= inv;
+    }
+    if (lane == 0 && active) qkv_write(p, sec, head, rotate, sn, cs, dA, dB, 0, ya, yb);
+  } else {
+    uint4 wn[NORM ? NIT : 1];
+    if constexpr (NORM) {
+      const __amdgpu_buffer_rsrc_t rn = make_rsrc(p.w_norm, (unsigned)p.hidden * 2u);
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int col = (it * 64 + lane) * 8;
-        const unsigned xo = (col < p.hidden && b0 + m < p.batch)
-                                ? (unsigned)(((size_t)(b0 + m) * p.ldx + col) * 4u)
-                                : kOutOfRange;
-        float4 xa = __builtin_bit_cast(float4, buf_load16(rx, xo));
-        float4 xb = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
-        if constexpr (NORM) {
-          ss = fmaf(xa.x, xa.x, fmaf(xa.y, xa.y, fmaf(xa.z, xa.z, fmaf(xa.w, xa.w, ss))));
-          ss = fmaf(xb.x, xb.x, fmaf(xb.y, xb.y, fmaf(xb.z, xb.z, fmaf(xb.w, xb.w, ss))));
-          xa = make_float4(xa.x * bf16_lo(wn[it].x), xa.y * bf16_hi(wn[it].x), xa.z * bf16_lo(wn[it].y),
-                           xa.w * bf16_hi(wn[it].y));
-          xb = make_float4(xb.x * bf16_lo(wn[it].z), xb.y * bf16_hi(wn[it].z), xb.z * bf16_lo(wn[it].w),
-                           xb.w * bf16_hi(wn[it].w));
-        }
-        a = dot8_bf16(wa[it], xa, xb, a);
-        c = dot8_bf16(wb[it], xa, xb, c);
-      }
-      sa[m] = wave_sum(a);
-      sb[m] = wave_sum(c);
-      if constexpr (NORM) {
-        const float inv = rsqrtf(wave_sum(ss) / (float)p.hidden + p.rms_eps);
-        sa[m] *= inv;
-        sb[m] *= inv;
+        wn[it] = buf_load16(rn, col < p.hidden ? (unsigned)col * 2u : kOutOfRange);
       }
     }
-    // epilogue: lane m handles batch row b0 + m
-    float ya = 0.f, yb = 0.f;
+
+    for (int b0 = 0; b0 < p.batch; b0 += MB) {
+      float sa[MB], sb[MB];
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
-      if (lane == m) {
-        ya = sa[m];
-        yb = sb[m];
+      for (int m = 0; m < MB; ++m) {
+        float a = 0.f, c = 0.f, ss = 0.f;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int col = (it * 64 + lane) * 8;
+          const unsigned xo = (col < p.hidden && b0 + m < p.batch)
+                                  ? (unsigned)(((size_t)(b0 + m) * p.ldx + col) * 4u)
+                                  : kOutOfRange;
+          float4 xa = __builtin_bit_cast(float4, buf_load16(rx, xo));
+          float4 xb = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
+          if constexpr (NORM) {
+            ss = fmaf(xa.x, xa.x, fmaf(xa.y, xa.y, fmaf(xa.z, xa.z, fmaf(xa.w, xa.w, ss))));
+            ss = fmaf(xb.x, xb.x, fmaf(xb.y, xb.y, fmaf(xb.z, xb.z, fmaf(xb.w, xb.w, ss))));
+            xa = make_float4(xa.x * bf16_lo(wn[it].x), xa.y * bf16_hi(wn[it].x), xa.z * bf16_lo(wn[it].y),
+                             xa.w * bf16_hi(wn[it].y));
+            xb = make_float4(xb.x * bf16_lo(wn[it].z), xb.y * bf16_hi(wn[it].z), xb.z * bf16_lo(wn[it].w),
+                             xb.w * bf16_hi(wn[it].w));
+          }
+          a = dot8_bf16(wa[it], xa, xb, a);
+          c = dot8_bf16(wb[it], xa, xb, c);
+        }
+        sa[m] = wave_sum(a);
+        sb[m] = wave_sum(c);
+        if constexpr (NORM) {
+          const float inv = rsqrtf(wave_sum(ss) / (float)p.hidden + p.rms_eps);
+          sa[m] *= inv;
+          sb[m] *= inv;
+        }
       }
-    const int b = b0 + lane;
-    if (lane < MB && b < p.batch) {
-      const SeqDesc &sd = p.seq[b];
-      if (rotate) rope_rotate(sd.position, pi, p.rotary_dim, p.log2_theta, ya, yb);
-      if (sec == 0) {
-        float *q = p.q_out + (size_t)b * p.ld_q + (size_t)head * kHeadDim;
-        q[dA] = ya;
-        q[dB] = yb;
-      } else if (sec == 3) {
-        float *gl = p.gate_out + (size_t)b * p.ld_gate;
-        gl[dA] = ya;
-        gl[dB] = yb;
-      } else {
-        _Float16 *dst = (sec == 1 ? sd.k : sd.v) + (size_t)sd.slot * Hk * kHeadDim + (size_t)head * kHeadDim;
-        dst[dA] = (_Float16)ya;
-        dst[dB] = (_Float16)yb;
+      // epilogue: lane m handles batch row b0 + m
+      float ya = 0.f, yb = 0.f;
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        if (lane == m) {
+          ya = sa[m];
+          yb = sb[m];
+        }
+      const int b = b0 + lane;
+      if (lane < MB && b < p.batch) {
+        float sn = 0.f, cs = 1.f;
+        if (rotate) rope_sincos(p.seq[b].position, pi, p.rotary_dim, p.log2_theta, sn, cs);
+        qkv_write(p, sec, head, rotate, sn, cs, dA, dB, b, ya, yb);
       }
     }
   }
