@@ -394,6 +394,38 @@ gqa_status run_attention(const gqa_arch *a, const std::vector<SeqDesc> &seqs, co
   return GQA_OK;
 }
 
+// One sequence whose window needs more than one chunk: the partial pass, then
+// the merge, gate and o_proj in one launch (combine_oproj_kernel), which adds
+// into y.  accumulate: y += W_o attn (the residual add) instead of y = W_o attn
+// (the partial kernel then zeroes y first).
+bool fused_tail(const Plan &plan, int32_t batch) {
+  return batch == 1 && !plan.direct && plan.groups.size() == 1;
+}
+
+gqa_status run_attention_oproj(const gqa_arch *a, const gqa_layer_weights *w, const std::vector<SeqDesc> &seqs,
+                               const Plan &plan, const float *q, const float *gate, float *part_o,
+                               float *part_ml, float *y, bool accumulate, hipStream_t stream) {
+  const Plan::Group &g = plan.groups[0];
+  AttnParams p = attn_params(a, seqs, plan, g, q, gate, nullptr, part_o, part_ml);
+  if (!accumulate) {
+    p.zero_out = y;
+    p.zero_n = a->hidden;
+  }
+  hipError_t e = launch_attention_partials(p, stream);
+  if (e != hipSuccess) return gpu_error(e, "attention partial launch");
+  OprojParams op{};
+  op.part_o = part_o;
+  op.part_ml = part_ml;
+  op.gate = gate;
+  op.nchunks = g.total_chunks;
+  op.num_heads = a->num_heads;
+  op.w_o = static_cast<const uint16_t *>(w->o_proj);
+  op.hidden = a->hidden;
+  op.y = y;
+  e = launch_combine_oproj(op, stream);
+  return e == hipSuccess ? GQA_OK : gpu_error(e, "combine + o_proj launch");
+}
+
 }  // namespace
 }  // namespace gqa
 
@@ -579,6 +611,10 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
   float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
+  if (fused_tail(plan, batch)) {
+    st = run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, out, false, s);
+    return st == GQA_OK ? ok() : st;
+  }
   if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
   if ((st = run_o_proj(arch, weights, batch, attn, out, s)) != GQA_OK) return st;
   return ok();
@@ -614,6 +650,10 @@ gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weig
   if ((st = run_qkv_rope(arch, weights, is_full, descs, h, q, gate, s, static_cast<const uint16_t *>(w_norm))) !=
       GQA_OK)
     return st;
+  if (fused_tail(plan, batch)) {
+    st = run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, h, true, s);
+    return st == GQA_OK ? ok() : st;
+  }
   if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
   if ((st = run_o_proj(arch, weights, batch, attn, h, s, true)) != GQA_OK) return st;
   return ok();

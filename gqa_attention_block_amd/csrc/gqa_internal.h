@@ -65,7 +65,22 @@ struct AttnParams {
                       // the gated output itself (no partials, no combine)
   int nseq;
   int total_chunks;
+  float *zero_out;    // or null: workgroup 0 also writes zero_n zeros here (the output that
+  int zero_n;         // combine_oproj_kernel then adds into with atomics)
   SeqDesc seq[kMaxSeqPerLaunch];
+};
+
+// Merge of one sequence's split-K partials, the gate and o_proj in one launch
+// (combine_oproj_kernel): y[r] += sum_h W_o[r][h*D .. h*D + D) a_h.
+struct OprojParams {
+  const float *part_o;   // as AttnParams, chunks [0, nchunks) of the sequence
+  const float *part_ml;
+  const float *gate;     // [Hq] gate logits
+  int nchunks;
+  int num_heads;         // Hq
+  const uint16_t *w_o;   // bf16 [hidden][Hq * D]
+  int hidden;
+  float *y;              // [hidden]: zeros (plain product) or the residual stream (layer)
 };
 
 // The fused projection step: q_k_v_proj and g_proj over the same x, then the
@@ -112,6 +127,8 @@ hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
+// One sequence, any number of chunks.
+hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream);
 // Batched projections on MFMA (batch <= 32 per launch; see kMfmaMinBatch).
 hipError_t launch_proj_mfma(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_mfma(const QkvParams &p, hipStream_t stream);

@@ -1107,6 +1107,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
   const size_t row = (size_t)cid * Hq + g * kGroup + i;
   *reinterpret_cast<float4 *>(p.part_o + row * kHeadDim + lane * 4) = o;
   if (lane == 0) *reinterpret_cast<float2 *>(p.part_ml + row * 2) = make_float2(M, L);
+  if (blockIdx.x == 0 && p.zero_out)
+    for (int k = threadIdx.x; k < p.zero_n; k += kThreads) p.zero_out[k] = 0.f;
 }
 
 // Merge of the split-K partials and the headwise gate.
@@ -1250,6 +1252,126 @@ __global__ __launch_bounds__(64) void attn_combine_small_kernel(const AttnParams
 }
 
 // ---------------------------------------------------------------------------
+// Merge of one sequence's split-K partials, the headwise gate and o_proj in
+// one launch.
+//
+// o_proj is linear in the gated attention output, y = sum_h W_o[:, h] a_h
+// (W_o's column block h: head h's 256 dims), so the product splits over
+// query heads.  Workgroup (h, s) merges head h's chunk partials into a_h,
+// multiplies it into rows [s * kOprojRows, +kOprojRows) of column block h and
+// adds the result into y with fp32 atomics.  Every wave forms the chunk
+// weights itself (lane c holds chunk c's), wave w sums chunk group w of the
+// partials (chunks w, w + 4, ...), and one barrier joins the four groups in
+// LDS.  Vector-memory loads return in issue order, so the loads are issued
+// as: (m, l) of chunks 0..63, the O values of the first kOprojBatch chunks of
+// each group, then the weights; the merge waits only for what it reads while
+// the weight bytes stream.  (Chunks past those are loaded after the weights
+// and wait for them.)
+// The sum over the Hq heads happens in the order the atomics land: y can
+// differ between runs by rounding, by at most the fp32 error of an Hq-term
+// sum.  y must hold zeros (plain product: the partial kernel writes them) or
+// the residual stream (layer) before the launch.
+// ---------------------------------------------------------------------------
+constexpr int kOprojPairs = 10;                                // row pairs per wave
+constexpr int kOprojRows = 2 * kOprojPairs * (kThreads / 64);  // 80 rows per workgroup
+constexpr int kOprojBatch = 16;                                // chunks per thread loaded up front
+
+__global__ __launch_bounds__(kThreads) void combine_oproj_kernel(const OprojParams p) {
+  __shared__ float4 s_acc[kThreads / 64][64];  // per chunk group: elements 4q .. 4q+3
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x;
+  const int Hq = p.num_heads;
+  const int nch = p.nchunks;
+  const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)nch * Hq * 8u);
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)nch * Hq * kHeadDim * 4u);
+
+  // (m, l) of chunk `lane`; O of chunks w + 4j (j < kOprojBatch), elements 4 lane .. +3
+  const float2 ml0 = __builtin_bit_cast(float2, buf_load8(rml, ((unsigned)lane * Hq + h) * 8u));
+  float4 o[kOprojBatch];
+#pragma unroll
+  for (int j = 0; j < kOprojBatch; ++j) {
+    const unsigned c = (unsigned)(w + 4 * j);
+    o[j] = __builtin_bit_cast(float4, buf_load16(rpo, ((c * Hq + h) * kHeadDim + 4u * lane) * 4u));
+  }
+  // weights: lane (half, cg) holds rows rbase + 2i, columns h*256 + 8cg .. +8
+  const int half = lane >> 5, cg = lane & 31;
+  const unsigned row_bytes = (unsigned)Hq * kHeadDim * 2u;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_o, (unsigned)p.hidden * row_bytes);
+  const int rbase = blockIdx.y * kOprojRows + w * 2 * kOprojPairs + half;
+  uint4 wv[kOprojPairs];
+#pragma unroll
+  for (int i = 0; i < kOprojPairs; ++i) {
+    const int r = rbase + 2 * i;
+    wv[i] = buf_load16(rw, r < p.hidden ? (unsigned)r * row_bytes + (unsigned)(h * kHeadDim + cg * 8) * 2u
+                                        : kOutOfRange);
+  }
+
+  // ---- merge, per wave (no barrier): M = max_c m_c, w_c = exp2(m_c - M),
+  // L = sum_c w_c l_c; lane c < 64 keeps w_c ----
+  auto ml_of = [&](int c) { return *reinterpret_cast<const float2 *>(p.part_ml + ((size_t)c * Hq + h) * 2); };
+  const float m0 = lane < nch ? ml0.x : -INFINITY;
+  float m = m0;
+  for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, ml_of(c).x);
+  const float M = wave_max(m);
+  const float wt = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+  float lsum = wt * ml0.y;
+  for (int c = lane + 64; c < nch; c += 64) {
+    const float2 ml = ml_of(c);
+    lsum = fmaf(ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M), ml.y, lsum);
+  }
+  const float L = wave_sum(lsum);
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kOprojBatch; ++j) {
+    const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), w + 4 * j));   // 0 past nch
+    acc.x = fmaf(wc, o[j].x, acc.x);
+    acc.y = fmaf(wc, o[j].y, acc.y);
+    acc.z = fmaf(wc, o[j].z, acc.z);
+    acc.w = fmaf(wc, o[j].w, acc.w);
+  }
+  for (int c = w + 4 * kOprojBatch; c < nch; c += 4) {
+    const float mc = ml_of(c).x;
+    const float wc = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+    const float4 v = *reinterpret_cast<const float4 *>(p.part_o + ((size_t)c * Hq + h) * kHeadDim + 4 * lane);
+    acc.x = fmaf(wc, v.x, acc.x);
+    acc.y = fmaf(wc, v.y, acc.y);
+    acc.z = fmaf(wc, v.z, acc.z);
+    acc.w = fmaf(wc, v.w, acc.w);
+  }
+  s_acc[w][lane] = acc;
+  __syncthreads();
+
+  // ---- a_h at this lane's 8 dims 8cg .. 8cg+7: element e = n * 16 + c holds
+  // dim 16c + n, so dim 8cg + k is element (8 (cg & 1) + k) * 16 + cg / 2 ----
+  const float sc = (1.0f / (1.0f + expf(-p.gate[h]))) / L;
+  const float *sa = reinterpret_cast<const float *>(s_acc);
+  float xv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int e = (8 * (cg & 1) + k) * 16 + (cg >> 1);
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < kThreads / 64; ++g) v += sa[g * kHeadDim + e];
+    xv[k] = v * sc;
+  }
+  const float4 xa = make_float4(xv[0], xv[1], xv[2], xv[3]);
+  const float4 xb = make_float4(xv[4], xv[5], xv[6], xv[7]);
+
+  // ---- rows: dot with a_h, sum over the 32 lanes of each half, add into y ----
+  float mine = 0.f;
+#pragma unroll
+  for (int i = 0; i < kOprojPairs; ++i) {
+    const float2 t = pair16(row_sum16(dot8_bf16(wv[i], xa, xb, 0.f)));
+    if (cg == i) mine = t.x + t.y;
+  }
+  const int r = rbase + 2 * cg;
+  if (cg < kOprojPairs && r < p.hidden) unsafeAtomicAdd(p.y + r, mine);
+}
+
+// ---------------------------------------------------------------------------
 // RMSNorm with a bf16 weight: one workgroup per row.
 // ---------------------------------------------------------------------------
 // `out` may equal `h`: each thread reads h[c] before it writes out[c].
@@ -1390,6 +1512,12 @@ hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {
     case 11: case 12: return qkv_launch<12>(p, stream);
     default: return qkv_launch<16>(p, stream);
   }
+}
+
+hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream) {
+  const dim3 grid(p.num_heads, (p.hidden + kOprojRows - 1) / kOprojRows);
+  hipLaunchKernelGGL(combine_oproj_kernel, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream) {

@@ -175,12 +175,15 @@ def make_cache(arch: Arch, seed: int, case_id: int, tensor_base: int,
 
 def block_case(name: str, hidden: int, is_full: bool, positions, *,
                capacities=None, ring_capacity: int = 0, seed: int = 0,
-               case_id: int = 0) -> BlockCase:
+               case_id: int = 0, arch: "Arch | None" = None) -> BlockCase:
     """General single-layer case: one cache per entry of ``positions``.
 
     ``capacities`` defaults to ``position + 1`` (linear) or ``ring_capacity``.
+    ``arch`` (its hidden must equal ``hidden``) replaces the family's head counts.
     """
-    arch = Arch(hidden=hidden)
+    if arch is None:
+        arch = Arch(hidden=hidden)
+    assert arch.hidden == hidden
     positions = [int(p) for p in positions]
     w_qkv, w_g, w_o = _weights(arch, seed, case_id, 0)
     x = _normal(seed, case_id, _T_X, (len(positions), hidden))
