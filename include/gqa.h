@@ -151,7 +151,12 @@ gqa_status gqa_workspace_size(const gqa_arch *arch, int32_t batch, int32_t max_s
  *   workspace       device, at least gqa_workspace_size(...) bytes for the
  *                   largest seq_len in `seqs`; contents on entry are ignored
  * Side effect: each sequence's cache slot row for `position` is written.
- * x_normed and out must not overlap each other, the workspace or a cache. */
+ * x_normed and out must not overlap each other, the workspace or a cache.
+ * Determinism: with batch 1 and a window of more than 128 rows, the split-K
+ * merge, the gate and W_o run in one launch that sums the query heads' parts
+ * of `out` with fp32 atomics, so `out` can differ between runs by fp32
+ * rounding of that sum; `out` must then be ordinary (coarse-grained) device
+ * memory.  Every other case, and the cache rows always, are bit-reproducible. */
 gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weights *weights,
                                       int is_full, const gqa_kv_seq *seqs, int32_t batch,
                                       const float *x_normed, float *out, void *workspace,
@@ -169,6 +174,7 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
  *   weights, is_full, seqs, workspace as for gqa_attention_block_decode (the
  *   workspace size is the block's).
  * Side effect: each sequence's cache slot row for `position` is written.
+ * Determinism as for gqa_attention_block_decode (h takes the atomic adds).
  * Errors: those of gqa_attention_block_decode, and rms_eps < 0 or not finite. */
 gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weights *weights,
                                       const void *w_norm, int is_full, const gqa_kv_seq *seqs,
@@ -176,8 +182,11 @@ gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weig
                                       size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
- * Step entry points: the same kernels the block launches, exposed so each
- * step can be checked and timed on its own.
+ * Step entry points: the block's steps one launch each, exposed so each
+ * step can be checked and timed on its own.  They are the kernels the block
+ * launches, except that for one sequence with a window over 128 rows the
+ * block merges, gates and projects in a single launch instead of
+ * gqa_attention_gated's merge plus gqa_o_proj_gemv.
  * ------------------------------------------------------------------------- */
 
 /* [attn] the fused q_k_v_proj GEMV and the g_proj GEMV over the same input,
