@@ -13,7 +13,12 @@
 //                           [kv_write.rs] `encode_attention_any`)
 //   attn_combine_kernel  -- merge of the split-K partials and the headwise
 //                           sigmoid gate ([attn.rs] gate step, before o_proj)
-//   gemv1/gemv kernels   -- the o_proj GEMV ([attn.rs] last GEMV)
+//   combine_oproj_kernel -- for one sequence: that merge, the gate and the
+//                           o_proj GEMV in one launch ([attn.rs] gate step
+//                           and last GEMV)
+//   gemv_bf16_kernel     -- the o_proj GEMV below the MFMA batch
+//                           ([attn.rs] last GEMV)
+//   proj_mfma_kernel     -- both projections on the matrix cores for batches
 //   rms_norm_kernel, residual_add_kernel -- the layer loop around the block
 //                           ([mod.rs] `produce_real_spark_inner`)
 //
@@ -137,91 +142,17 @@ __device__ __forceinline__ float dot8_bf16(uint4 q, float4 xa, float4 xb, float 
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: y[b][r] = sum_c W[r][c] x[b][c], bf16 W, fp32 x/y/accumulation.
+// Rows of x staged in LDS for the VALU projections.
 //
-// One wave owns R consecutive rows.  Lane l reads columns
-// [(it*64 + l)*8, +8) for it < NIT, so each 16-byte load instruction covers
-// 1 KiB of one row contiguously; all R*NIT loads are issued before the first
-// FMA so a wave keeps R*NIT KiB in flight.  The weights stay in registers
-// while the batch is walked MB rows at a time, so W is read once per call.
-// ---------------------------------------------------------------------------
-template <int R, int NIT, int MB>
-__global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p) {
-  const int lane = threadIdx.x & 63;
-  // wave index kept scalar: row-dependent choices (which weight buffer) stay uniform
-  const int wave = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int total = p.rows0 + p.rows1;
-  const int row0 = wave * R;
-  if (row0 >= total) return;
-  const unsigned row_bytes = (unsigned)p.cols * 2u;
-  const __amdgpu_buffer_rsrc_t r0 = make_rsrc(p.w0, (unsigned)p.rows0 * row_bytes);
-  const __amdgpu_buffer_rsrc_t r1 = make_rsrc(p.w1, (unsigned)p.rows1 * row_bytes);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)((size_t)p.batch * p.ldx * 4u));
-
-  uint4 w[R][NIT];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int row = row0 + r;
-    const bool first = row < p.rows0;
-    const unsigned base = first ? (unsigned)row * row_bytes : (unsigned)(row - p.rows0) * row_bytes;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int col = (it * 64 + lane) * 8;
-      const unsigned off = (row < total && col < p.cols) ? base + (unsigned)col * 2u : kOutOfRange;
-      w[r][it] = first ? buf_load16(r0, off) : buf_load16(r1, off);
-    }
-  }
-
-  for (int b0 = 0; b0 < p.batch; b0 += MB) {
-    float acc[R][MB];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int m = 0; m < MB; ++m) acc[r][m] = 0.f;
-
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int col = (it * 64 + lane) * 8;
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const unsigned xo = (col < p.cols && b0 + m < p.batch)
-                                ? (unsigned)(((size_t)(b0 + m) * p.ldx + col) * 4u)
-                                : kOutOfRange;
-        const float4 xa = __builtin_bit_cast(float4, buf_load16(rx, xo));
-        const float4 xb = __builtin_bit_cast(float4, buf_load16(rx, xo == kOutOfRange ? xo : xo + 16u));
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][m] = dot8_bf16(w[r][it], xa, xb, acc[r][m]);
-      }
-    }
-
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = row0 + r;
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const float s = wave_sum(acc[r][m]);
-        if (lane == r * MB + m && row < total && b0 + m < p.batch) {
-          float *y = row < p.rows0 ? p.y0 + (size_t)(b0 + m) * p.ldy0 + row
-                                   : p.y1 + (size_t)(b0 + m) * p.ldy1 + (row - p.rows0);
-          *y = p.accumulate ? *y + s : s;
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// x staged once per workgroup in LDS for the batch-1 kernels.
-//
-// Lane l of a wave reads columns (it*64 + l)*8 .. +8 of its rows, so it needs
-// x at the same columns in every wave of the workgroup; loaded per wave, x
-// (fp32: twice the bytes of a bf16 row) would pass through the CU's L1 once
-// per wave.  Here the workgroup loads it once: thread t holds float4s
-// t, t + 256, ... (columns 4f .. 4f+3), issued before the weight loads so that
-// the wait for them does not include the weights, and writes them to LDS as
-// two arrays, s[0][j] = columns 8j .. 8j+3 and s[1][j] = 8j+4 .. 8j+7, so a
-// wave's 16-byte reads of either are contiguous.  NORM also multiplies by a
-// bf16 weight and keeps the thread's sum of squares of x.
+// Lane l of a wave reads columns (it*64 + l)*8 .. +8 of its weight rows, so it
+// needs x at the same columns in every wave of the workgroup; loaded per wave,
+// x (fp32: twice the bytes of a bf16 row) would pass through the CU's L1 once
+// per wave.  Here the workgroup loads each x row once: thread t holds float4s
+// t, t + 256, ... (columns 4f .. 4f+3) and writes them to LDS as two arrays,
+// s[0][j] = columns 8j .. 8j+3 and s[1][j] = 8j+4 .. 8j+7, so a wave's 16-byte
+// reads of either are contiguous.  The first rows' loads are issued before
+// the weight loads, so the wait for them does not include the weights.  NORM
+// also multiplies by a bf16 weight and keeps the thread's sum of squares.
 // ---------------------------------------------------------------------------
 template <int NIT>
 struct StagedX {
@@ -264,13 +195,22 @@ struct StagedX {
 };
 
 // ---------------------------------------------------------------------------
-// Batch-1 GEMV.  NIT is exactly ceil(cols/512), so no registers hold loads
-// that would only return zeros; x comes from LDS (StagedX).  Waves past the
-// last row still take part in the barrier; their loads are out of range.
+// GEMV: y[b][r] = sum_c W[r][c] x[b][c], bf16 W, fp32 x/y/accumulation, for
+// the batches below the MFMA path (and the last rows of a batched o_proj).
+//
+// One wave owns R consecutive rows.  Lane l reads columns
+// [(it*64 + l)*8, +8) for it < NIT (NIT = ceil(cols / 512)), so each 16-byte
+// load instruction covers 1 KiB of one row; all R*NIT loads are issued before
+// the first FMA and the weights stay in registers while the batch is walked
+// RB rows at a time, x staged in LDS (StagedX), the next rows' x loads in
+// flight during each pass.  ONE (batch 1) is the same without the loop, which
+// keeps the x loads ahead of the weight loads in the compiled order.  Waves
+// past the last row still take part in the barriers; their loads are out of
+// range.  With accumulate the kernel adds into y (the layer's residual add).
 // ---------------------------------------------------------------------------
-template <int R, int NIT>
-__global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p) {
-  __shared__ float4 s_x[2][StagedX<NIT>::kSlots];
+template <int R, int NIT, int RB, bool ONE>
+__global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p) {
+  __shared__ float4 s_x[RB][2][StagedX<NIT>::kSlots];
   const int lane = threadIdx.x & 63;
   // wave index kept scalar: row-dependent choices (which weight buffer) stay uniform
   const int wave = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -279,10 +219,12 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
   const unsigned row_bytes = (unsigned)p.cols * 2u;
   const __amdgpu_buffer_rsrc_t r0 = make_rsrc(p.w0, (unsigned)p.rows0 * row_bytes);
   const __amdgpu_buffer_rsrc_t r1 = make_rsrc(p.w1, (unsigned)p.rows1 * row_bytes);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)p.cols * 4u);
+  // x row b, bounded at cols (a zero-size resource past the batch)
+  auto xrow = [&](int b) { return make_rsrc(p.x + (size_t)b * p.ldx, b < p.batch ? (unsigned)p.cols * 4u : 0u); };
 
-  StagedX<NIT> xs;
-  xs.template issue<false>(rx, 0u, rx);
+  StagedX<NIT> xs[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) xs[r].template issue<false>(xrow(r), 0u, xrow(r));
   uint4 w[R][NIT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -296,18 +238,39 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
       w[r][it] = first ? buf_load16(r0, off) : buf_load16(r1, off);
     }
   }
-  xs.template store<false>(s_x);
-  __syncthreads();
+  // the R rows' dot products with staged x row m (batch row b)
+  auto emit = [&](int m, int b) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float a = 0.f;
+    for (int r = 0; r < R; ++r) {
+      float a = 0.f;
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) a = dot8_bf16(w[r][it], s_x[0][it * 64 + lane], s_x[1][it * 64 + lane], a);
-    const float s = wave_sum(a);
-    const int row = row0 + r;
-    if (lane == r && row < total) {
-      float *y = row < p.rows0 ? p.y0 + row : p.y1 + (row - p.rows0);
-      *y = p.accumulate ? *y + s : s;
+      for (int it = 0; it < NIT; ++it)
+        a = dot8_bf16(w[r][it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], a);
+      const float s = wave_sum(a);
+      const int row = row0 + r;
+      if (lane == r && row < total && b < p.batch) {
+        float *y = row < p.rows0 ? p.y0 + (size_t)b * p.ldy0 + row : p.y1 + (size_t)b * p.ldy1 + (row - p.rows0);
+        *y = p.accumulate ? *y + s : s;
+      }
+    }
+  };
+  if constexpr (ONE) {
+    xs[0].template store<false>(s_x[0]);
+    __syncthreads();
+    emit(0, 0);
+  } else {
+    for (int b0 = 0; b0 < p.batch; b0 += RB) {
+#pragma unroll
+      for (int m = 0; m < RB; ++m) {
+        xs[m].template store<false>(s_x[m]);
+        // next rows: unconditional (past the batch the resource is empty, no
+        // traffic), so the compiler's waits stay exact
+        xs[m].template issue<false>(xrow(b0 + RB + m), 0u, xrow(0));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < RB; ++m) emit(m, b0 + m);
+      if (b0 + RB < p.batch) __syncthreads();   // s_x is rewritten for the next rows
     }
   }
 }
@@ -321,10 +284,11 @@ __global__ __launch_bounds__(kThreads) void gemv1_bf16_kernel(const GemvParams p
 // the angle position * theta^(-2i/r); pairs i >= r/2, all v pairs and all
 // gate pairs are rows (2i, 2i+1), left as they are.  Sections in pair order:
 // q heads (128 pairs each), k heads, v heads, then Hq/2 gate pairs.  The dot
-// products run like the GEMV below (16-byte loads, all issued up front); then
-// lane m (batch row b0 + m) forms its sequence's angle in fp64, rotates the
-// pair in fp32 and writes: q -> q_out (fp32), k and v -> fp16, rounded once,
-// straight into the cache slot of this position; gate logits -> gate_out.
+// products run like gemv_bf16_kernel (16-byte loads, all issued up front, x
+// staged in LDS); then each batch row's angle is formed in fp64, the pair is
+// rotated in fp32 and written: q -> q_out (fp32), k and v -> fp16, rounded
+// once, straight into the cache slot of this position; gate logits ->
+// gate_out.
 // ---------------------------------------------------------------------------
 // NeoX rotation of the pair (x_i, x_{i + r/2}) by angle position * theta^(-2i/r).
 // The angle is formed and reduced mod 2*pi in fp64 (an fp32 angle at position
@@ -377,21 +341,21 @@ __device__ __forceinline__ void qkv_write(const QkvParams &p, int sec, int head,
 }
 
 // NORM: x is the raw residual stream h and each projection is
-// inv_rms(h) * W (h * w_norm), the sum of squares taken over the same loads.
-// MB == 1 (batch 1) stages x in LDS (StagedX); then waves past the last pair
-// still take part in the barrier, with out-of-range loads and no writes.
-template <int NIT, int MB, bool NORM>
+// inv_rms(h) * W (h * w_norm), the sum of squares taken over the same loads
+// and summed over the workgroup in LDS.  The batch is walked RB rows at a
+// time with x staged in LDS, as in gemv_bf16_kernel; waves past the last pair
+// take part in the barriers with out-of-range loads and no writes.
+template <int NIT, int RB, bool NORM, bool ONE>
 __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
-  constexpr bool kStaged = MB == 1;
-  __shared__ float4 s_x[kStaged ? 2 : 1][kStaged ? StagedX<NIT>::kSlots : 1];
-  __shared__ float s_ss[kThreads / 64];
+  __shared__ float4 s_x[RB][2][StagedX<NIT>::kSlots];
+  __shared__ float s_ss[RB][kThreads / 64];
   const int lane = threadIdx.x & 63;
-  const int P = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int P = blockIdx.x * (kThreads / 64) + wv;   // scalar
   const int Hq = p.num_heads, Hk = p.num_kv_heads;
   constexpr int kPairs = kHeadDim / 2;
   const int nq = Hq * kPairs, nk = Hk * kPairs, nv = Hk * kPairs;
   const bool active = P < nq + nk + nv + Hq / 2;
-  if (!kStaged && !active) return;
   int sec, head, pi;
   if (P < nq) {
     sec = 0; head = P / kPairs; pi = P % kPairs;
@@ -414,12 +378,15 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
   const int qkv_rows = (Hq + 2 * Hk) * kHeadDim;
   const __amdgpu_buffer_rsrc_t rw = sec < 3 ? make_rsrc(p.w_qkv, (unsigned)qkv_rows * row_bytes)
                                             : make_rsrc(p.w_g, (unsigned)Hq * row_bytes);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)((size_t)p.batch * p.ldx * 4u));
+  // x row b, bounded at hidden (ldx may be larger; a zero-size resource past the batch)
+  auto xrow = [&](int b) {
+    return make_rsrc(p.x + (size_t)b * p.ldx, b < p.batch ? (unsigned)p.hidden * 4u : 0u);
+  };
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u);
 
-  StagedX<NIT> xs;
-  if constexpr (kStaged)   // row 0 of x only, bounded at hidden (ldx may be larger)
-    xs.template issue<NORM>(make_rsrc(p.x, (unsigned)p.hidden * 4u), 0u,
-                            make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u));
+  StagedX<NIT> xs[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) xs[r].template issue<NORM>(xrow(r), 0u, rn);
   uint4 wa[NIT], wb[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -429,83 +396,53 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
     wb[it] = buf_load16(rw, ok ? (unsigned)(base_row + dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
   }
 
-  if constexpr (kStaged) {
-    // the rotation does not depend on the loads: formed while they are in flight
-    float sn = 0.f, cs = 1.f;
-    if (rotate) rope_sincos(p.seq[0].position, pi, p.rotary_dim, p.log2_theta, sn, cs);
-    const float ss = wave_sum(xs.template store<NORM>(s_x));
-    if (NORM && lane == 0) s_ss[threadIdx.x >> 6] = ss;
-    __syncthreads();
+  // the rotation of batch row b does not depend on the loads: formed while
+  // they are in flight
+  auto angle = [&](int b, float &sn, float &cs) {
+    sn = 0.f;
+    cs = 1.f;
+    if (rotate && b < p.batch) rope_sincos(p.seq[b].position, pi, p.rotary_dim, p.log2_theta, sn, cs);
+  };
+  auto stage = [&](int m) {
+    const float ss = wave_sum(xs[m].template store<NORM>(s_x[m]));
+    if (NORM && lane == 0) s_ss[m][wv] = ss;
+  };
+  // the pair's dot products with staged x row m, then the epilogue for batch row b
+  auto emit = [&](int m, int b, float sn, float cs) {
     float a = 0.f, c = 0.f;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      a = dot8_bf16(wa[it], s_x[0][it * 64 + lane], s_x[1][it * 64 + lane], a);
-      c = dot8_bf16(wb[it], s_x[0][it * 64 + lane], s_x[1][it * 64 + lane], c);
+      a = dot8_bf16(wa[it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], a);
+      c = dot8_bf16(wb[it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], c);
     }
     float ya = wave_sum(a), yb = wave_sum(c);
     if constexpr (NORM) {
-      const float inv = rsqrtf((s_ss[0] + s_ss[1] + s_ss[2] + s_ss[3]) / (float)p.hidden + p.rms_eps);
+      const float inv = rsqrtf((s_ss[m][0] + s_ss[m][1] + s_ss[m][2] + s_ss[m][3]) / (float)p.hidden + p.rms_eps);
       ya *= inv;
       yb *= inv;
     }
-    if (lane == 0 && active) qkv_write(p, sec, head, rotate, sn, cs, dA, dB, 0, ya, yb);
+    if (lane == 0 && active && b < p.batch) qkv_write(p, sec, head, rotate, sn, cs, dA, dB, b, ya, yb);
+  };
+  if constexpr (ONE) {
+    float sn, cs;
+    angle(0, sn, cs);
+    stage(0);
+    __syncthreads();
+    emit(0, 0, sn, cs);
   } else {
-    uint4 wn[NORM ? NIT : 1];
-    if constexpr (NORM) {
-      const __amdgpu_buffer_rsrc_t rn = make_rsrc(p.w_norm, (unsigned)p.hidden * 2u);
+    for (int b0 = 0; b0 < p.batch; b0 += RB) {
+      float sn[RB], cs[RB];
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int col = (it * 64 + lane) * 8;
-        wn[it] = buf_load16(rn, col < p.hidden ? (unsigned)col * 2u : kOutOfRange);
+      for (int m = 0; m < RB; ++m) angle(b0 + m, sn[m], cs[m]);
+#pragma unroll
+      for (int m = 0; m < RB; ++m) {
+        stage(m);
+        xs[m].template issue<NORM>(xrow(b0 + RB + m), 0u, rn);   // next rows: unconditional, as in the GEMV
       }
-    }
-
-    for (int b0 = 0; b0 < p.batch; b0 += MB) {
-      float sa[MB], sb[MB];
+      __syncthreads();
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        float a = 0.f, c = 0.f, ss = 0.f;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int col = (it * 64 + lane) * 8;
-          const unsigned xo = (col < p.hidden && b0 + m < p.batch)
-                                  ? (unsigned)(((size_t)(b0 + m) * p.ldx + col) * 4u)
-                                  : kOutOfRange;
-          float4 xa = __builtin_bit_cast(float4, buf_load16(rx, xo));
-          float4 xb = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
-          if constexpr (NORM) {
-            ss = fmaf(xa.x, xa.x, fmaf(xa.y, xa.y, fmaf(xa.z, xa.z, fmaf(xa.w, xa.w, ss))));
-            ss = fmaf(xb.x, xb.x, fmaf(xb.y, xb.y, fmaf(xb.z, xb.z, fmaf(xb.w, xb.w, ss))));
-            xa = make_float4(xa.x * bf16_lo(wn[it].x), xa.y * bf16_hi(wn[it].x), xa.z * bf16_lo(wn[it].y),
-                             xa.w * bf16_hi(wn[it].y));
-            xb = make_float4(xb.x * bf16_lo(wn[it].z), xb.y * bf16_hi(wn[it].z), xb.z * bf16_lo(wn[it].w),
-                             xb.w * bf16_hi(wn[it].w));
-          }
-          a = dot8_bf16(wa[it], xa, xb, a);
-          c = dot8_bf16(wb[it], xa, xb, c);
-        }
-        sa[m] = wave_sum(a);
-        sb[m] = wave_sum(c);
-        if constexpr (NORM) {
-          const float inv = rsqrtf(wave_sum(ss) / (float)p.hidden + p.rms_eps);
-          sa[m] *= inv;
-          sb[m] *= inv;
-        }
-      }
-      // epilogue: lane m handles batch row b0 + m
-      float ya = 0.f, yb = 0.f;
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-        if (lane == m) {
-          ya = sa[m];
-          yb = sb[m];
-        }
-      const int b = b0 + lane;
-      if (lane < MB && b < p.batch) {
-        float sn = 0.f, cs = 1.f;
-        if (rotate) rope_sincos(p.seq[b].position, pi, p.rotary_dim, p.log2_theta, sn, cs);
-        qkv_write(p, sec, head, rotate, sn, cs, dA, dB, b, ya, yb);
-      }
+      for (int m = 0; m < RB; ++m) emit(m, b0 + m, sn[m], cs[m]);
+      if (b0 + RB < p.batch) __syncthreads();   // s_x and s_ss are rewritten for the next rows
     }
   }
 }
@@ -521,9 +458,12 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
 // high and low parts, x = hi + lo up to 2^-16 |x|, as two B operands, so the
 // product keeps fp32 accuracy.
 //
-// A workgroup owns a unit of two 16-row tiles for <= 32 batch rows; its
+// A workgroup owns a unit of two 16-row tiles for up to MB 16-row batch tiles; its
 // kProjSplit waves split the columns and add their partial sums in LDS in a
-// fixed order (the result does not depend on timing).  For q_k_v_proj the two
+// fixed order (the result does not depend on timing).  Every workgroup reads
+// x for all columns of its batch rows; o_proj takes one 16-row batch tile per
+// workgroup, which spreads that traffic over twice the workgroups (2 x 80 at
+// H = 2560 and batch 32).  For q_k_v_proj the two
 // tiles of a unit are RoPE partners inside a head (rows i and i + r/2), so the
 // epilogue rotates, splits and writes q, k, v and the gate logits as the fused
 // batch-1 kernel does.
@@ -572,6 +512,15 @@ __device__ __forceinline__ void proj_to_bf16(const float4 x0, const float4 x1, b
   }
 }
 
+// 32-row units of a launch: per head 8 (q, k, v sections) plus the gate rows;
+// plain: w0's rows, then w1's
+__host__ __device__ __forceinline__ int proj_units(const QkvParams &p) {
+  return 8 * (p.num_heads + 2 * p.num_kv_heads) + 1;
+}
+__host__ __device__ __forceinline__ int proj_units(const GemvParams &p) {
+  return (p.rows0 + 31) / 32 + (p.rows1 + 31) / 32;
+}
+
 __device__ __forceinline__ const uint16_t *norm_weights(const QkvParams &p) { return p.w_norm; }
 __device__ __forceinline__ const uint16_t *norm_weights(const GemvParams &) { return nullptr; }
 
@@ -582,13 +531,20 @@ __device__ __forceinline__ const uint16_t *norm_weights(const GemvParams &) { re
 // gather over their columns and add in LDS.
 template <int MODE, int MB, bool NORM, typename Params>
 __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p) {
-  __shared__ float4 s_red[kProjSplit][2][32][4];   // [wave][tile][batch][rows 4k..4k+3] per 16-row tile
-  __shared__ float s_ss[kProjSplit][32];           // NORM: [wave][batch] partial sums of squares
+  __shared__ float4 s_red[kProjSplit][2][16 * MB][4];   // [wave][tile][batch][rows 4k..4k+3] per 16-row tile
+  __shared__ float s_ss[kProjSplit][16 * MB];           // NORM: [wave][batch] partial sums of squares
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = lane >> 4, n = lane & 15;
-  const int u = blockIdx.x;
+  // workgroup -> (unit u, batch tile bt): the batch tiles of a unit sit 8
+  // workgroups apart, i.e. on the same XCD, whose L2 then serves the second
+  // read of the unit's weights
+  const int nbt = (p.batch + 16 * MB - 1) / (16 * MB);
+  const int grp = blockIdx.x / (8 * nbt), off = blockIdx.x - grp * (8 * nbt);
+  const int u = grp * 8 + (off & 7);
+  const int b0 = (off >> 3) * 16 * MB;   // first batch row of this workgroup
+  if (u >= proj_units(p)) return;
 
   // rows of the two tiles, their matrix and its row count
   const uint16_t *wmat;
@@ -607,7 +563,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
       wmat = p.w1; wrows = p.rows1; rowA = (u - u0) * 32;
     }
     rowB = rowA + 16;
-    cols = p.cols; batch = p.batch; x = p.x; ldx = p.ldx;
+    cols = p.cols; batch = min(16 * MB, p.batch - b0); x = p.x + (size_t)b0 * p.ldx; ldx = p.ldx;
   } else {
     U = qkv_unit(p, u);
     if (U.sec == 3) {
@@ -618,7 +574,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
       wmat = p.w_qkv; wrows = (p.num_heads + 2 * p.num_kv_heads) * kHeadDim;
       rowA = hrow + U.ta * 16; rowB = hrow + U.tb * 16;
     }
-    cols = p.hidden; batch = p.batch; x = p.x; ldx = p.ldx;
+    cols = p.hidden; batch = min(16 * MB, p.batch - b0); x = p.x + (size_t)b0 * p.ldx; ldx = p.ldx;
   }
   const unsigned row_bytes = (unsigned)cols * 2u;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wmat, (unsigned)wrows * row_bytes);
@@ -724,10 +680,12 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
     }
   }
   __syncthreads();
-  // thread t: batch row b = t / 16, row xr = t % 16 of both tiles
+  // thread t: batch row b = t / 16 of this workgroup (b0 + b overall), row
+  // xr = t % 16 of both tiles
   const int t = threadIdx.x;
   const int b = t >> 4, xr = t & 15;
   if (b >= MB * 16 || b >= batch) return;
+  const int bg = b0 + b;
   float ya = 0.f, yb = 0.f;
 #pragma unroll
   for (int ww = 0; ww < kProjSplit; ++ww) {
@@ -738,11 +696,11 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
     float *y = first ? p.y0 : p.y1;
     const long ldy = first ? p.ldy0 : p.ldy1;
     if (rowA + xr < wrows) {
-      float *d = y + (size_t)b * ldy + rowA + xr;
+      float *d = y + (size_t)bg * ldy + rowA + xr;
       *d = p.accumulate ? *d + ya : ya;
     }
     if (rowB + xr < wrows) {
-      float *d = y + (size_t)b * ldy + rowB + xr;
+      float *d = y + (size_t)bg * ldy + rowB + xr;
       *d = p.accumulate ? *d + yb : yb;
     }
   } else {
@@ -755,16 +713,16 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
       yb *= inv;
     }
     if (U.sec == 3) {
-      float *gl = p.gate_out + (size_t)b * p.ld_gate;
+      float *gl = p.gate_out + (size_t)bg * p.ld_gate;
       if (xr < p.num_heads) gl[xr] = ya;
       if (16 + xr < p.num_heads) gl[16 + xr] = yb;
       return;
     }
-    const SeqDesc &sd = p.seq[b];
+    const SeqDesc &sd = p.seq[bg];
     const int dA = U.ta * 16 + xr, dB = U.tb * 16 + xr;
     if (U.rotate) rope_rotate(sd.position, dA, p.rotary_dim, p.log2_theta, ya, yb);
     if (U.sec == 0) {
-      float *q = p.q_out + (size_t)b * p.ld_q + (size_t)U.head * kHeadDim;
+      float *q = p.q_out + (size_t)bg * p.ld_q + (size_t)U.head * kHeadDim;
       q[dA] = ya;
       q[dB] = yb;
     } else {
@@ -1396,106 +1354,93 @@ __global__ __launch_bounds__(kThreads) void residual_add_kernel(float *h, const 
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) h[i] += o[i];
 }
 
-template <int R, int NIT>
-hipError_t gemv_dispatch_mb(const GemvParams &p, int waves, hipStream_t stream) {
-  const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((gemv_bf16_kernel<R, NIT, 4>), dim3(blocks), dim3(kThreads), 0, stream, p);
+template <int R, int NIT, int RB, bool ONE>
+hipError_t gemv_launch(const GemvParams &p, hipStream_t stream) {
+  const int waves = (p.rows0 + p.rows1 + R - 1) / R;
+  hipLaunchKernelGGL((gemv_bf16_kernel<R, NIT, RB, ONE>), dim3((waves + 3) / 4), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int R>
-hipError_t gemv_dispatch_nit(const GemvParams &p, int waves, hipStream_t stream) {
-  const int nit = (p.cols + 511) / 512;
-  if (nit <= 2) return gemv_dispatch_mb<R, 2>(p, waves, stream);
-  if (nit <= 4) return gemv_dispatch_mb<R, 4>(p, waves, stream);
-  if (nit <= 8) return gemv_dispatch_mb<R, 8>(p, waves, stream);
-  return gemv_dispatch_mb<R, 16>(p, waves, stream);
-}
-
-template <int R, int NIT>
-hipError_t gemv1_launch(const GemvParams &p, hipStream_t stream) {
-  const int rows = p.rows0 + p.rows1;
-  const int waves = (rows + R - 1) / R;
-  hipLaunchKernelGGL((gemv1_bf16_kernel<R, NIT>), dim3((waves + 3) / 4), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-// Two rows per wave while that still gives >= 2048 waves, else one.
+// Two weight rows per wave while that still gives >= 2048 waves, else one;
+// two batch rows per pass from batch 2 on while their x fits (NIT <= 8).
 template <int NIT>
-hipError_t gemv1_rows(const GemvParams &p, hipStream_t stream) {
-  if (p.rows0 + p.rows1 >= 4096) return gemv1_launch<2, NIT>(p, stream);
-  return gemv1_launch<1, NIT>(p, stream);
+hipError_t gemv_rows(const GemvParams &p, hipStream_t stream) {
+  const bool two = p.rows0 + p.rows1 >= 4096;
+  if (p.batch == 1) return two ? gemv_launch<2, NIT, 1, true>(p, stream) : gemv_launch<1, NIT, 1, true>(p, stream);
+  if constexpr (NIT <= 8) return two ? gemv_launch<2, NIT, 2, false>(p, stream) : gemv_launch<1, NIT, 2, false>(p, stream);
+  return two ? gemv_launch<2, NIT, 1, false>(p, stream) : gemv_launch<1, NIT, 1, false>(p, stream);
 }
 
-hipError_t gemv1_dispatch(const GemvParams &p, hipStream_t stream) {
-  switch ((p.cols + 511) / 512) {
-    case 1: return gemv1_rows<1>(p, stream);
-    case 2: return gemv1_rows<2>(p, stream);
-    case 3: return gemv1_rows<3>(p, stream);
-    case 4: return gemv1_rows<4>(p, stream);
-    case 5: return gemv1_rows<5>(p, stream);
-    case 6: return gemv1_rows<6>(p, stream);
-    case 7: return gemv1_rows<7>(p, stream);
-    case 8: return gemv1_rows<8>(p, stream);
-    case 9: case 10: return gemv1_rows<10>(p, stream);
-    case 11: case 12: return gemv1_rows<12>(p, stream);
-    default: return gemv1_rows<16>(p, stream);
-  }
-}
-
-template <int NIT>
-hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
+template <int NIT, int RB, bool ONE>
+hipError_t qkv_launch_rb(const QkvParams &p, hipStream_t stream) {
   const int pairs = (p.num_heads + 2 * p.num_kv_heads) * (kHeadDim / 2) + p.num_heads / 2;
   const dim3 grid((pairs + 3) / 4);
-  const bool norm = p.w_norm != nullptr;
-  if (p.batch == 1) {
-    if (norm)
-      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 1, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 1, false>), grid, dim3(kThreads), 0, stream, p);
-  } else {
-    if (norm)
-      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 4, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((qkv_rope_kernel<NIT, 4, false>), grid, dim3(kThreads), 0, stream, p);
-  }
+  if (p.w_norm != nullptr)
+    hipLaunchKernelGGL((qkv_rope_kernel<NIT, RB, true, ONE>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((qkv_rope_kernel<NIT, RB, false, ONE>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+// batch 1: no loop; then two batch rows per pass while their x fits (NIT <= 8)
+template <int NIT>
+hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
+  if (p.batch == 1) return qkv_launch_rb<NIT, 1, true>(p, stream);
+  if constexpr (NIT <= 8) return qkv_launch_rb<NIT, 2, false>(p, stream);
+  return qkv_launch_rb<NIT, 1, false>(p, stream);
 }
 
 }  // namespace
 
+// Grid of the batched projections: units rounded up to 8 (the unit -> XCD
+// mapping), times the batch tiles of 16 * MB rows.
+template <int MB, typename Params>
+dim3 proj_grid(const Params &p) {
+  const int nbt = (p.batch + 16 * MB - 1) / (16 * MB);
+  return dim3((unsigned)((proj_units(p) + 7) / 8 * 8 * nbt));
+}
+
+// o_proj: one 16-row batch tile per workgroup (its 80 units at H = 2560 would
+// leave most CUs idle).  q_k_v_proj: all <= 32 rows per workgroup (its 193
+// units fill the chip; measured 19.9 vs 24.7 us split at batch 32).
 hipError_t launch_proj_mfma(const GemvParams &p, hipStream_t stream) {
-  const int units = (p.rows0 + 31) / 32 + (p.rows1 + 31) / 32;
-  if (p.batch > 16)
-    hipLaunchKernelGGL((proj_mfma_kernel<0, 2, false, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((proj_mfma_kernel<0, 1, false, GemvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+  hipLaunchKernelGGL((proj_mfma_kernel<0, 1, false, GemvParams>), proj_grid<1>(p), dim3(kProjThreads), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_mfma(const QkvParams &p, hipStream_t stream) {
-  const int units = 8 * (p.num_heads + 2 * p.num_kv_heads) + 1;
   const bool norm = p.w_norm != nullptr;
   if (p.batch > 16) {
     if (norm)
-      hipLaunchKernelGGL((proj_mfma_kernel<1, 2, true, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 2, true, QkvParams>), proj_grid<2>(p), dim3(kProjThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((proj_mfma_kernel<1, 2, false, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 2, false, QkvParams>), proj_grid<2>(p), dim3(kProjThreads), 0, stream,
+                         p);
   } else {
     if (norm)
-      hipLaunchKernelGGL((proj_mfma_kernel<1, 1, true, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 1, true, QkvParams>), proj_grid<1>(p), dim3(kProjThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((proj_mfma_kernel<1, 1, false, QkvParams>), dim3(units), dim3(kProjThreads), 0, stream, p);
+      hipLaunchKernelGGL((proj_mfma_kernel<1, 1, false, QkvParams>), proj_grid<1>(p), dim3(kProjThreads), 0, stream,
+                         p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream) {
-  if (p.batch == 1) return gemv1_dispatch(p, stream);
-  const int rows = p.rows0 + p.rows1;
-  if (rows >= 4 * 1024) return gemv_dispatch_nit<4>(p, (rows + 3) / 4, stream);
-  if (rows >= 2 * 1024) return gemv_dispatch_nit<2>(p, (rows + 1) / 2, stream);
-  return gemv_dispatch_nit<1>(p, rows, stream);
+  switch ((p.cols + 511) / 512) {
+    case 1: return gemv_rows<1>(p, stream);
+    case 2: return gemv_rows<2>(p, stream);
+    case 3: return gemv_rows<3>(p, stream);
+    case 4: return gemv_rows<4>(p, stream);
+    case 5: return gemv_rows<5>(p, stream);
+    case 6: return gemv_rows<6>(p, stream);
+    case 7: return gemv_rows<7>(p, stream);
+    case 8: return gemv_rows<8>(p, stream);
+    case 9: case 10: return gemv_rows<10>(p, stream);
+    case 11: case 12: return gemv_rows<12>(p, stream);
+    default: return gemv_rows<16>(p, stream);
+  }
 }
 
 hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {

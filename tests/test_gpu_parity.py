@@ -36,6 +36,8 @@ QKV_CASES = [
     # batched (MFMA) edges: 4 rows, 17 rows (second batch tile), a tiny hidden
     (1024, True, [7, 63, 64, 3000], 0), (2560, False, list(range(100, 100 + 17 * 61, 61)), 512),
     (8, True, [1, 2, 3, 4, 5], 0),
+    # VALU batch 2-3 with x too wide to stage two rows per pass (hidden > 4096)
+    (6144, True, [10, 2000, 77], 0),
 ]
 
 
@@ -58,6 +60,26 @@ def test_qkv_rope_kv(hidden, is_full, positions, ring):
     assert_parity(q.cpu().numpy(), ref.q_roped.reshape(b, -1), "RoPE'd q")
     assert_parity(gl.cpu().numpy(), ref.gate_logits, "gate logits")
     check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, "qkv_rope_kv")
+
+
+def test_qkv_rope_kv_rotary_width_off_the_tile_grid():
+    """A full-layer rotary width that is not a multiple of 32 keeps batches on
+    the VALU kernel (the MFMA units pair whole 16-row tiles); batch 5 walks
+    the batch two rows per pass."""
+    arch = synth.Arch(hidden=1024, full_rotary_dim=48)
+    positions = [3, 700, 64, 4095, 31]
+    case = synth.block_case("qkv_r48", 1024, True, positions, seed=0, case_id=13, arch=arch)
+    say(f"qkv_rope_kv full_rotary_dim=48 batch={len(positions)}")
+    dev = DevBlock(case)
+    a = dev.arch
+    q = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda")
+    gl = torch.empty((case.batch, a.num_heads), dtype=torch.float32, device="cuda")
+    gqa.qkv_rope_kv(a, dev.w_qkv, dev.w_g, True, dev.seqs(), dev.x, q, gl)
+    torch.cuda.synchronize()
+    ref = oracle.block_decode(case.arch, True, case.w_qkv, case.w_g, case.w_o, case.x, case.seqs)
+    assert_parity(q.cpu().numpy(), ref.q_roped.reshape(case.batch, -1), "RoPE'd q (r = 48)")
+    assert_parity(gl.cpu().numpy(), ref.gate_logits, "gate logits")
+    check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, "qkv_rope_kv r=48")
 
 
 @pytest.mark.parametrize("hidden,batch", [(1024, 1), (2560, 1), (776, 3), (2560, 32), (6144, 2),
