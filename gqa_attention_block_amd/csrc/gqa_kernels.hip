@@ -470,7 +470,6 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kProjSplit = 8;                 // waves (column splits) per workgroup
 constexpr int kProjThreads = 64 * kProjSplit;
-constexpr int kProjSet = 3;                   // k-steps (32 columns each) per load set
 
 // Which two 16-row tiles a unit covers.  Plain: tiles 2u, 2u+1 of the
 // concatenated rows.  q_k_v_proj + g_proj: per head (q, k, v sections) 8
@@ -533,6 +532,7 @@ template <int MODE, int MB, bool NORM, typename Params>
 __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p) {
   __shared__ float4 s_red[kProjSplit][2][16 * MB][4];   // [wave][tile][batch][rows 4k..4k+3] per 16-row tile
   __shared__ float s_ss[kProjSplit][16 * MB];           // NORM: [wave][batch] partial sums of squares
+  __shared__ uint4 s_stage[kProjSplit * (32 * 8 + MB * 16 * 16)];   // per wave: one staged k-step pair
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -579,43 +579,86 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
   const unsigned row_bytes = (unsigned)cols * 2u;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wmat, (unsigned)wrows * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (unsigned)((size_t)batch * ldx * 4u));
-  const unsigned offA = rowA + n < wrows ? (unsigned)(rowA + n) * row_bytes : kOutOfRange;
-  const unsigned offB = rowB + n < wrows ? (unsigned)(rowB + n) * row_bytes : kOutOfRange;
-  unsigned offX[MB];
-#pragma unroll
-  for (int bt = 0; bt < MB; ++bt)
-    offX[bt] = bt * 16 + n < batch ? (unsigned)((size_t)(bt * 16 + n) * ldx * 4u) : kOutOfRange;
-
-  // this wave's k-steps: [s0, s0 + spw), spw a multiple of 2 * kProjSet
+  // this wave's k-steps: [s0, s0 + spw), in pairs (64 columns); spw a
+  // multiple of 4 so the pairs come in twos
   const int nsteps = (cols + 31) / 32;
   int spw = (nsteps + kProjSplit - 1) / kProjSplit;
-  spw = (spw + 2 * kProjSet - 1) / (2 * kProjSet) * (2 * kProjSet);
+  spw = (spw + 3) / 4 * 4;
   const int s0 = w * spw;
+  const int npairs = spw / 2;
 
-  struct Set {
-    uint4 wa[kProjSet], wb[kProjSet];
-    float4 xv[kProjSet][MB][2];
-    uint4 wn[NORM ? kProjSet : 1];
-  };
+  // Coalesced loads of one pair of k-steps.  W: 4 loads of 8 rows x 128 B
+  // (whole cache lines) of the unit's 32 rows, lane l taking row 8i + l/8,
+  // 16-byte chunk l%8.  x: per batch tile 4 loads of 4 rows x 256 B, lane l
+  // taking row 4i + l/16, chunk l%16.  The MFMA operand layout (16 rows x
+  // 64 B per fragment) read straight from memory touches twice the lines per
+  // byte; here the fragments come from LDS instead.
+  const int lwr = lane >> 3, lwc = lane & 7;
+  const int lxr = lane >> 4, lxc = lane & 15;
+  unsigned woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + lwr;                       // row of the unit: tile A, then tile B
+    const int grow = r < 16 ? rowA + r : rowB + (r - 16);
+    woff[i] = grow < wrows ? (unsigned)grow * row_bytes + (unsigned)lwc * 16u : kOutOfRange;
+  }
+  unsigned xoff[MB][4];
+#pragma unroll
+  for (int bt = 0; bt < MB; ++bt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = bt * 16 + 4 * i + lxr;
+      xoff[bt][i] = r < batch ? (unsigned)((size_t)r * ldx * 4u) + (unsigned)lxc * 16u : kOutOfRange;
+    }
   // NORM: the w_norm resource (a zero-size resource otherwise, never read)
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(NORM ? (const void *)norm_weights(p) : nullptr,
                                               NORM ? (unsigned)cols * 2u : 0u);
-  auto load = [&](Set &S, int set) {
-#pragma unroll
-    for (int j = 0; j < kProjSet; ++j) {
-      const int col = (s0 + set * kProjSet + j) * 32 + G * 8;
-      const bool ok = col < cols;
-      S.wa[j] = buf_load16(rw, ok ? offA + (unsigned)col * 2u : kOutOfRange);
-      S.wb[j] = buf_load16(rw, ok ? offB + (unsigned)col * 2u : kOutOfRange);
-#pragma unroll
-      for (int bt = 0; bt < MB; ++bt) {
-        const unsigned xo = ok ? offX[bt] + (unsigned)col * 4u : kOutOfRange;
-        S.xv[j][bt][0] = __builtin_bit_cast(float4, buf_load16(rx, xo));
-        S.xv[j][bt][1] = __builtin_bit_cast(float4, buf_load16(rx, xo + 16u));
-      }
-      if constexpr (NORM) S.wn[j] = buf_load16(rn, ok ? (unsigned)col * 2u : kOutOfRange);
-    }
+  struct Pair {
+    uint4 w[4];
+    float4 x[MB][4];
+    uint4 wn[NORM ? 2 : 1];   // w_norm at lane (G, n)'s 8 columns of each k-step
   };
+  auto load_pair = [&](Pair &P, int pr) {
+    const int c0 = (s0 + 2 * pr) * 32;             // first column of the pair
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      P.w[i] = buf_load16(rw, woff[i] != kOutOfRange && c0 + lwc * 8 < cols ? woff[i] + (unsigned)c0 * 2u
+                                                                             : kOutOfRange);
+#pragma unroll
+    for (int bt = 0; bt < MB; ++bt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        P.x[bt][i] = __builtin_bit_cast(
+            float4, buf_load16(rx, xoff[bt][i] != kOutOfRange && c0 + lxc * 4 < cols
+                                       ? xoff[bt][i] + (unsigned)c0 * 4u : kOutOfRange));
+    if constexpr (NORM)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int col = c0 + k * 32 + G * 8;
+        P.wn[k] = buf_load16(rn, col < cols ? (unsigned)col * 2u : kOutOfRange);
+      }
+  };
+  // This wave's LDS: W as 32 rows x 8 chunks, x as MB x 16 rows x 16 chunks
+  // (16 B each), chunk j of row r stored at slot j ^ (r & 7) of its row, so
+  // that the 8 lanes of a fragment read phase (8 rows, one chunk) and of a
+  // store phase (one row, 8 chunks) fall on distinct banks.
+  uint4 *const sw = s_stage + w * (32 * 8 + MB * 16 * 16);
+  float4 *const sx = reinterpret_cast<float4 *>(sw + 32 * 8);
+  auto stage_pair = [&](const Pair &P) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + lwr;
+      sw[r * 8 + (lwc ^ (r & 7))] = P.w[i];
+    }
+#pragma unroll
+    for (int bt = 0; bt < MB; ++bt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + lxr;
+        sx[(bt * 16 + r) * 16 + (lxc ^ (r & 7))] = P.x[bt][i];
+      }
+  };
+
   float ssp[MB];   // NORM: this lane's sum of squares per batch tile
 #pragma unroll
   for (int bt = 0; bt < MB; ++bt) ssp[bt] = 0.f;
@@ -625,20 +668,25 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
     accA[bt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
     accB[bt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   }
-  auto compute = [&](const Set &S) {
+  // k-step s of the staged pair: lane (G, n) takes row n (tile A) and row
+  // 16 + n (tile B), columns 8G .. 8G+7 of the step, and batch row n's x at
+  // the same columns (chunks 8s + 2G and 8s + 2G + 1 of its 64)
+  auto compute_pair = [&](const Pair &P) {
 #pragma unroll
-    for (int j = 0; j < kProjSet; ++j) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, S.wa[j]);
-      const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, S.wb[j]);
+    for (int s = 0; s < 2; ++s) {
+      const int jw = (4 * s + G) ^ (n & 7);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, sw[n * 8 + jw]);
+      const bf16x8_t b2 = __builtin_bit_cast(bf16x8_t, sw[(16 + n) * 8 + jw]);
 #pragma unroll
       for (int bt = 0; bt < MB; ++bt) {
-        float4 x0 = S.xv[j][bt][0], x1 = S.xv[j][bt][1];
+        float4 x0 = sx[(bt * 16 + n) * 16 + ((8 * s + 2 * G) ^ (n & 7))];
+        float4 x1 = sx[(bt * 16 + n) * 16 + ((8 * s + 2 * G + 1) ^ (n & 7))];
         if constexpr (NORM) {
           float q = ssp[bt];
           q = fmaf(x0.x, x0.x, fmaf(x0.y, x0.y, fmaf(x0.z, x0.z, fmaf(x0.w, x0.w, q))));
           q = fmaf(x1.x, x1.x, fmaf(x1.y, x1.y, fmaf(x1.z, x1.z, fmaf(x1.w, x1.w, q))));
           ssp[bt] = q;
-          const uint4 wv = S.wn[j];
+          const uint4 wv = P.wn[s];
           x0 = make_float4(x0.x * bf16_lo(wv.x), x0.y * bf16_hi(wv.x), x0.z * bf16_lo(wv.y), x0.w * bf16_hi(wv.y));
           x1 = make_float4(x1.x * bf16_lo(wv.z), x1.y * bf16_hi(wv.z), x1.z * bf16_lo(wv.w), x1.w * bf16_hi(wv.w));
         }
@@ -651,20 +699,25 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
       }
     }
   };
-  // two load sets in flight; no load is conditional (steps past the end
-  // are out of range: zeros without HBM traffic), so the waits stay exact
-  const int nsets = spw / kProjSet;
-  Set SA, SB;
-  load(SA, 0);
-  load(SB, 1);
-  for (int set = 0; set + 2 < nsets; set += 2) {
-    compute(SA);
-    load(SA, set + 2);
-    compute(SB);
-    load(SB, set + 3);
+  // two pairs in flight; no load is conditional (columns past the end are
+  // out of range: zeros without HBM traffic), so the waits stay exact.  A
+  // wave's LDS stores and reads are issued in order, so staging a pair over
+  // the previous one needs no barrier.
+  Pair PA, PB;
+  load_pair(PA, 0);
+  load_pair(PB, 1);
+  for (int pr = 0; pr + 2 < npairs; pr += 2) {
+    stage_pair(PA);
+    compute_pair(PA);
+    load_pair(PA, pr + 2);
+    stage_pair(PB);
+    compute_pair(PB);
+    load_pair(PB, pr + 3);
   }
-  compute(SA);
-  compute(SB);
+  stage_pair(PA);
+  compute_pair(PA);
+  stage_pair(PB);
+  compute_pair(PB);
 
   // partial sums: lane (G, n) holds rows 4G..4G+3 of batch column n
 #pragma unroll
