@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     Arch,
     GqaError,
     KvSeq,
+    attention_block_chunk,
     attention_block_decode,
     attention_gated,
     attention_layer_decode,

@@ -65,6 +65,7 @@ def _load():
         "gqa_workspace_size": (ctypes.c_int, [A, I32, I32, ctypes.POINTER(S)]),
         "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_attention_layer_decode": (ctypes.c_int, [A, W, P, ctypes.c_int, K, I32, P, P, S, P]),
+        "gqa_attention_block_chunk": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_qkv_rope_kv": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, P]),
         "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, S, P]),
         "gqa_attention_partials": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, I32,
@@ -87,7 +88,8 @@ _lib = _load()
 #: symbols the header declares; tests check the library exports all of them
 EXPORTED_SYMBOLS = (
     "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size",
-    "gqa_attention_block_decode", "gqa_attention_layer_decode", "gqa_qkv_rope_kv", "gqa_attention_gated",
+    "gqa_attention_block_decode", "gqa_attention_block_chunk", "gqa_attention_layer_decode", "gqa_qkv_rope_kv",
+    "gqa_attention_gated",
     "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
     "gqa_last_error",
 )
@@ -246,6 +248,21 @@ def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Seq
         _ptr(out, torch.float32, "out", b * arch.hidden),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
         "gqa_attention_block_decode")
+
+
+def attention_block_chunk(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seq: KvSeq, x: torch.Tensor,
+                          out: torch.Tensor, workspace: torch.Tensor, stream=None):
+    """M consecutive tokens of one sequence (x, out: [M][hidden]); seq.position is the first token's."""
+    m = x.shape[0] if x.dim() == 2 else 1
+    a = arch._c()
+    w = _weights(arch, w_qkv, w_g, w_o)
+    ks = _seqs(arch, [seq])
+    _check(_lib.gqa_attention_block_chunk(
+        ctypes.byref(a), ctypes.byref(w), int(is_full), ks, m,
+        _ptr(x, torch.float32, "x", m * arch.hidden),
+        _ptr(out, torch.float32, "out", m * arch.hidden),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+        "gqa_attention_block_chunk")
 
 
 def attention_layer_decode(arch: Arch, w_norm, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],

@@ -426,6 +426,35 @@ gqa_status run_attention_oproj(const gqa_arch *a, const gqa_layer_weights *w, co
   return e == hipSuccess ? GQA_OK : gpu_error(e, "combine + o_proj launch");
 }
 
+// The block for resolved sequence descriptors (one per token or sequence):
+// pointers and the workspace size are checked here, then qkv -> attention ->
+// o_proj are enqueued.
+gqa_status run_block(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,
+                     const std::vector<SeqDesc> &descs, const float *x_normed, float *out, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  gqa_status st;
+  const int32_t batch = (int32_t)descs.size();
+  if ((st = check_ptr(x_normed, "x_normed")) != GQA_OK) return st;
+  if ((st = check_ptr(out, "out")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  const Plan plan = make_plan(descs, arch->num_kv_heads, true);
+  const Layout L = block_layout(arch, batch, plan.max_group_chunks);
+  if (workspace_bytes < L.total)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the block needs %zu", workspace_bytes,
+                L.total);
+  char *ws = static_cast<char *>(workspace);
+  float *q = reinterpret_cast<float *>(ws + L.q);
+  float *gate = reinterpret_cast<float *>(ws + L.gate);
+  float *attn = reinterpret_cast<float *>(ws + L.attn);
+  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
+  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
+  if (fused_tail(plan, batch))
+    return run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, out, false, s);
+  if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
+  return run_o_proj(arch, weights, batch, attn, out, s);
+}
 }  // namespace
 }  // namespace gqa
 
@@ -595,29 +624,34 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
   std::vector<SeqDesc> descs;
   if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
   if (batch == 0) return ok();
-  if ((st = check_ptr(x_normed, "x_normed")) != GQA_OK) return st;
-  if ((st = check_ptr(out, "out")) != GQA_OK) return st;
-  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
-  const Plan plan = make_plan(descs, arch->num_kv_heads, true);
-  const Layout L = block_layout(arch, batch, plan.max_group_chunks);
-  if (workspace_bytes < L.total)
-    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the block needs %zu", workspace_bytes,
-                L.total);
-  char *ws = static_cast<char *>(workspace);
-  float *q = reinterpret_cast<float *>(ws + L.q);
-  float *gate = reinterpret_cast<float *>(ws + L.gate);
-  float *attn = reinterpret_cast<float *>(ws + L.attn);
-  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
-  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
-  if (fused_tail(plan, batch)) {
-    st = run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, out, false, s);
-    return st == GQA_OK ? ok() : st;
-  }
-  if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
-  if ((st = run_o_proj(arch, weights, batch, attn, out, s)) != GQA_OK) return st;
-  return ok();
+  st = run_block(arch, weights, is_full, descs, x_normed, out, workspace, workspace_bytes, stream);
+  return st == GQA_OK ? ok() : st;
+}
+
+gqa_status gqa_attention_block_chunk(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,
+                                     const gqa_kv_seq *seq, int32_t m_tokens, const float *x_normed, float *out,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_weights(weights, true, true)) != GQA_OK) return st;
+  if (!seq) return fail(GQA_ERR_INVALID_ARGUMENT, "seq is null");
+  if (m_tokens < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "m_tokens=%d must be >= 1", m_tokens);
+  if ((st = check_batch(arch, m_tokens)) != GQA_OK) return st;
+  if (seq->position < 0 || seq->position > INT32_MAX - m_tokens)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "position=%d with m_tokens=%d: positions out of range", seq->position,
+                m_tokens);
+  if (seq->ring_capacity > 0 &&
+      (int64_t)seq->ring_capacity < (int64_t)arch->sliding_window + m_tokens - 1)
+    return fail(GQA_ERR_INVALID_ARGUMENT,
+                "ring_capacity=%d < sliding_window + m_tokens - 1 = %lld: a later token's slot would overwrite a "
+                "row an earlier token of the chunk reads",
+                seq->ring_capacity, (long long)arch->sliding_window + m_tokens - 1);
+  std::vector<gqa_kv_seq> toks((size_t)m_tokens, *seq);
+  for (int32_t t = 0; t < m_tokens; ++t) toks[t].position = seq->position + t;
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, toks.data(), m_tokens, &descs)) != GQA_OK) return st;
+  st = run_block(arch, weights, is_full, descs, x_normed, out, workspace, workspace_bytes, stream);
+  return st == GQA_OK ? ok() : st;
 }
 
 gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weights *weights, const void *w_norm,

@@ -162,6 +162,31 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
                                       const float *x_normed, float *out, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* M consecutive tokens of ONE sequence in one call: chunked prefill or the
+ * verify step of a draft ([mod] the family's `prefill` module; [kvw] module
+ * doc: chunked prefill reuses the per-token block, while the M-row path
+ * projects K/V for all M rows with one GEMM).  Token t is at position
+ * seq->position + t; its result is exactly the single-token block's at that
+ * position after tokens 0 .. t-1 have been decoded: the projections run as
+ * an M-row product that writes all M cache slots first, then token t attends
+ * over its own window, which ends at its position (causal inside the chunk).
+ *   seq        host pointer to ONE cache descriptor; position = the first
+ *              token's position
+ *   m_tokens   M >= 1
+ *   x_normed   device fp32 [M][H]: the normed inputs of the M tokens
+ *   out        device fp32 [M][H]
+ *   workspace  device, at least gqa_workspace_size(arch, M, position + M)
+ * Side effect: the cache slots of all M positions are written.
+ * Errors: those of gqa_attention_block_decode for each token's position, and
+ * INVALID_ARGUMENT when m_tokens < 1, when a linear cache has fewer than
+ * position + M rows, or when a ring holds fewer than sliding_window + M - 1
+ * slots (a later token's slot would overwrite a row an earlier token reads).
+ * Determinism: M == 1 is gqa_attention_block_decode; M > 1 is bit-reproducible. */
+gqa_status gqa_attention_block_chunk(const gqa_arch *arch, const gqa_layer_weights *weights,
+                                     int is_full, const gqa_kv_seq *seq, int32_t m_tokens,
+                                     const float *x_normed, float *out, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* The attention half of one decoder layer, in place on the residual stream
  * ([mod] `produce_real_spark_inner`: input RMSNorm with a plain bf16 weight,
  * the block, the raw residual add):

@@ -9,11 +9,13 @@ are silent.
 from .block import (  # noqa: F401
     AttentionStepResult,
     BlockResult,
+    ChunkResult,
     OracleSeq,
     StackResult,
     attention_decode,
     attention_step,
     bf16_bits_to_f64,
+    block_chunk,
     block_decode,
     gemv,
     head_gate,

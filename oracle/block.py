@@ -287,6 +287,42 @@ def block_decode(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
 
 
 # ----------------------------------------------------------------------------
+# several tokens of one sequence  [mod: the family's `prefill` module; kvw:
+#   module doc -- chunked prefill runs the per-token block token after token]
+# ----------------------------------------------------------------------------
+
+@dataclass
+class ChunkResult:
+    out: np.ndarray          # [M][hidden]
+    k_cache: np.ndarray      # float16 cache after all M tokens
+    v_cache: np.ndarray
+    slots: List[int]
+
+
+def block_chunk(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
+                x: np.ndarray, seq, m_tokens: int) -> ChunkResult:
+    """M consecutive tokens of one sequence at positions seq.position + t.
+
+    Token t is the single-token block at its position, run once tokens
+    0 .. t-1 have written their cache slots, so it sees them and nothing
+    later.  ``seq`` exposes k, v (fp16 caches), ring_capacity and position;
+    the caches are copied.
+    """
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    k = np.array(seq.k, dtype=np.float16, copy=True)
+    v = np.array(seq.v, dtype=np.float16, copy=True)
+    outs, slots = [], []
+    for t in range(m_tokens):
+        cur = OracleSeq(k=k, v=v, ring_capacity=int(seq.ring_capacity),
+                        position=int(seq.position) + t)
+        r = block_decode(arch, is_full, w_qkv_bits, w_g_bits, w_o_bits, x[t:t + 1], [cur])
+        k, v = r.k_caches[0], r.v_caches[0]
+        outs.append(r.out[0])
+        slots.append(r.slots[0])
+    return ChunkResult(out=np.stack(outs), k_cache=k, v_cache=v, slots=slots)
+
+
+# ----------------------------------------------------------------------------
 # stack harness  [mod: `produce_real_spark_inner` layer loop: input RMSNorm with
 #                 bf16 weight and eps 1e-6, the block, raw residual add]
 # ----------------------------------------------------------------------------

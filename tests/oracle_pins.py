@@ -454,6 +454,63 @@ def pin_block_zero_input(O):
 
 
 # ----------------------------------------------------------------------------
+# several tokens of one sequence
+# ----------------------------------------------------------------------------
+
+def pin_chunk_of_one_is_the_block(O):
+    """A one-token chunk is the single-token block (output and cache)."""
+    arch = tiny_arch(window=6)
+    rng = _rng(20)
+    w_qkv, w_g, w_o = _tiny_weights(arch, rng)
+    x = rng.standard_normal((1, arch.hidden))
+    k, v = _cache(arch, rng, 12)
+    c = O.block_chunk(arch, True, w_qkv, w_g, w_o, x, _seq(k, v, 0, 9), 1)
+    b = O.block_decode(arch, True, w_qkv, w_g, w_o, x, [_seq(k, v, 0, 9)])
+    assert np.array_equal(c.out, b.out)
+    assert np.array_equal(c.k_cache, b.k_caches[0]) and np.array_equal(c.v_cache, b.v_caches[0])
+
+
+def pin_chunk_is_causal(O):
+    """Token t's output does not depend on the inputs of later tokens, and it
+    does depend on every earlier token's input (through the k, v rows that
+    token wrote)."""
+    arch = tiny_arch(window=6)
+    rng = _rng(21)
+    w_qkv, w_g, w_o = _tiny_weights(arch, rng)
+    m, pos = 4, 7
+    x = rng.standard_normal((m, arch.hidden))
+    k, v = _cache(arch, rng, pos + m)
+    for is_full in (True, False):
+        base = O.block_chunk(arch, is_full, w_qkv, w_g, w_o, x, _seq(k, v, 0, pos), m)
+        for t in range(m):
+            x2 = x.copy()
+            x2[t] += 1.0
+            r = O.block_chunk(arch, is_full, w_qkv, w_g, w_o, x2, _seq(k, v, 0, pos), m)
+            assert np.array_equal(r.out[:t], base.out[:t]), (is_full, t)
+            assert np.all(np.abs(r.out[t:] - base.out[t:]).max(axis=1) > 1e-9), (is_full, t)
+
+
+def pin_chunk_ring_equals_linear(O):
+    """A chunk through a ring of sliding_window + M - 1 slots equals, bitwise,
+    the chunk over a linear cache holding the same history."""
+    arch = tiny_arch(window=6)
+    rng = _rng(22)
+    w_qkv, w_g, w_o = _tiny_weights(arch, rng)
+    m, ring = 3, 8
+    for pos in (2, 9, 30):
+        x = rng.standard_normal((m, arch.hidden))
+        lin_k, lin_v = _cache(arch, rng, pos + m)
+        ring_k = np.full((ring, arch.num_kv_heads, arch.head_dim), np.nan, np.float16)
+        ring_v = ring_k.copy()
+        for t in range(max(0, pos - ring), pos):
+            ring_k[t % ring], ring_v[t % ring] = lin_k[t], lin_v[t]
+        a = O.block_chunk(arch, False, w_qkv, w_g, w_o, x, _seq(ring_k, ring_v, ring, pos), m)
+        b = O.block_chunk(arch, False, w_qkv, w_g, w_o, x, _seq(lin_k, lin_v, 0, pos), m)
+        assert np.array_equal(a.out, b.out), pos
+        assert a.slots == [(pos + t) % ring for t in range(m)] and b.slots == list(range(pos, pos + m))
+
+
+# ----------------------------------------------------------------------------
 # stack harness
 # ----------------------------------------------------------------------------
 

@@ -14,8 +14,8 @@ import torch
 import gqa_attention_block_amd as gqa
 import oracle
 import synth
-from tests.gpu_util import (DevBlock, arch_of, assert_parity, bits_to_dev, check_caches,
-                            f16_to_dev, f32_to_dev, say)
+from tests.gpu_util import (DevBlock, arch_of, assert_fp16_within_one_ulp, assert_parity, bits_to_dev,
+                            check_caches, f16_to_dev, f32_to_dev, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -442,6 +442,48 @@ def test_block_fused_tail_other_head_counts(num_kv_heads, position):
     ref = oracle.block_decode(case.arch, case.is_full, case.w_qkv, case.w_g, case.w_o, case.x, case.seqs)
     assert_parity(out, ref.out, f"Hk={num_kv_heads} block output")
     check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, case.name)
+
+
+CHUNK_CASES = [
+    # (name, hidden, is_full, first position, tokens, ring)
+    ("full_h1024_p100_m5", 1024, True, 100, 5, 0),
+    ("full_h264_p300_m40", 264, True, 300, 40, 0),           # two launch groups of 32 tokens
+    ("sliding_ring_h1024_p1035_m9", 1024, False, 1035, 9, 520),   # slots 515..519 then 0..3
+    ("sliding_linear_h1024_p600_m8", 1024, False, 600, 8, 0),
+    ("full_h2560_p4090_m1", 2560, True, 4090, 1, 0),          # one token: the single-token block
+]
+
+
+@pytest.mark.parametrize("name,hidden,is_full,p0,m,ring", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_block_chunk_matches_oracle(name, hidden, is_full, p0, m, ring):
+    """M consecutive tokens of one sequence in one call against the oracle's
+    token-after-token chunk: outputs, the M written slots, and every other
+    cache row untouched."""
+    cap = ring if ring else p0 + m
+    case = synth.block_case(name, hidden, is_full, [p0], capacities=[cap], ring_capacity=ring, seed=0,
+                            case_id=32)
+    x = synth.random_hidden(hidden, m, 0, 32, tensor_id=90)
+    say(f"block_chunk {name}")
+    a = arch_of(case.arch)
+    k = f16_to_dev(case.seqs[0].k)
+    v = f16_to_dev(case.seqs[0].v)
+    ws = torch.empty(gqa.workspace_size(a, m, p0 + m), dtype=torch.uint8, device="cuda")
+    out = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
+    gqa.attention_block_chunk(a, bits_to_dev(case.w_qkv), bits_to_dev(case.w_g), bits_to_dev(case.w_o), is_full,
+                              gqa.KvSeq(k=k, v=v, position=p0, ring_capacity=ring), f32_to_dev(x), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.block_chunk(case.arch, is_full, case.w_qkv, case.w_g, case.w_o, x, case.seqs[0], m)
+    assert_parity(out.cpu().numpy(), ref.out, f"{name} chunk output")
+    kg, vg = k.cpu().numpy(), v.cpu().numpy()
+    rest = np.ones(cap, bool)
+    rest[ref.slots] = False
+    assert np.array_equal(kg[rest].view(np.int16), case.seqs[0].k[rest].view(np.int16)), "K rows outside the chunk"
+    assert np.array_equal(vg[rest].view(np.int16), case.seqs[0].v[rest].view(np.int16)), "V rows outside the chunk"
+    for s in ref.slots:   # fp32 sums near zero: one ulp plus 2^-18 of the row's scale, as for one token
+        kscale = float(np.max(np.abs(ref.k_cache[s].astype(np.float64))))
+        vscale = float(np.max(np.abs(ref.v_cache[s].astype(np.float64))))
+        assert_fp16_within_one_ulp(kg[s], ref.k_cache[s], f"{name} K slot {s}", kscale)
+        assert_fp16_within_one_ulp(vg[s], ref.v_cache[s], f"{name} V slot {s}", vscale)
 
 
 def test_batch_zero_is_a_no_op():

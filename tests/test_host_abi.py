@@ -236,6 +236,32 @@ def test_layer_entry_validates():
                       0, 0, 0, None) == OK                  # batch 0: nothing to do
 
 
+def test_chunk_entry_validates():
+    """gqa_attention_block_chunk: every check before any launch (FAKE device
+    pointers are never touched, so a GQA_OK here would mean a launch)."""
+    a = B.c_arch(gqa.Arch(hidden=1024))
+    w = B.c_weights(FAKE, FAKE, FAKE)
+    seq = B.c_seq_array(1)
+
+    def call(m, ws_bytes=1 << 30, seq_p=seq, x=FAKE):
+        return B.raw_call("gqa_attention_block_chunk", ctypes.byref(a), ctypes.byref(w), 0, seq_p, m, x,
+                          FAKE, FAKE, ws_bytes, None)
+
+    seq[0] = _seq(pos=100, cap=200)
+    assert call(0) == INVALID                          # m_tokens < 1
+    assert call(-3) == INVALID
+    assert call(4, seq_p=None) == INVALID              # no descriptor
+    assert call(4, x=MISALIGNED) == INVALID
+    assert call(4, ws_bytes=1024) == WS_SMALL
+    seq[0] = _seq(pos=197, cap=200)
+    assert call(4) == INVALID                          # last token at 200 needs a 201-row cache
+    seq[0] = _seq(pos=1000, cap=520, ring=519)         # window 512 + 8 - 1 = 519 slots: enough
+    assert call(8, ws_bytes=1024) == WS_SMALL          # got as far as the workspace check
+    assert call(9) == INVALID                          # 512 + 9 - 1 = 520 > 519
+    seq[0] = _seq(pos=2 ** 31 - 4, cap=200, ring=519)
+    assert call(8) == INVALID                          # positions overflow int32
+
+
 def test_status_strings():
     assert B.status_string(0) == "GQA_OK"
     assert B.status_string(3) == "GQA_ERR_WORKSPACE_TOO_SMALL"

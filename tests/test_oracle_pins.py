@@ -61,6 +61,10 @@ MUTANTS = [
      "return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float16)"),
     ("bf16_shift", "<< np.uint32(16)", "<< np.uint32(15)"),
     ("gemv_transposed", "return x @ w.T", "return x @ w"),
+    ("chunk_reuses_first_input", "x[t:t + 1], [cur])", "x[0:1], [cur])"),
+    ("chunk_cache_not_threaded", "        k, v = r.k_caches[0], r.v_caches[0]\n        outs.append",
+     "        outs.append"),
+    ("chunk_positions_frozen", "position=int(seq.position) + t)", "position=int(seq.position))"),
 ]
 
 
