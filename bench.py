@@ -244,13 +244,70 @@ def bench_stack(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_chunk(args):
+    """Several tokens of one sequence per call (gqa_attention_block_chunk): a
+    full layer, hidden 2560, 32 tokens at positions 4096 .. 4127 (a chunk of
+    prefill at 4K context).  One step = one call = 32 tokens."""
+    import numpy as np
+    import torch
+    import gqa_attention_block_amd as gqa
+    import synth
+    m, p0, hid = 32, 4096, 2560
+    case = synth.block_case("chunk_full_h2560_p4096_m32", hid, True, [p0], capacities=[p0 + m], seed=0,
+                            case_id=40)
+    x = synth.random_hidden(hid, m, 0, 40, tensor_id=90)
+    a = gqa.Arch(hidden=hid)
+    up = lambda arr: torch.from_numpy(arr.view(np.int16) if arr.dtype == np.uint16 else arr).to("cuda:0")  # noqa: E731
+    w = [up(case.w_qkv), up(case.w_g), up(case.w_o)]
+    seq = gqa.KvSeq(k=up(case.seqs[0].k), v=up(case.seqs[0].v), position=p0, ring_capacity=0)
+    xd = up(x)
+    out = torch.empty((m, hid), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(gqa.workspace_size(a, m, p0 + m), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        gqa.attention_block_chunk(a, w[0], w[1], w[2], True, seq, xd, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert torch.isfinite(out).all(), "non-finite chunk output"
+    ms = 1e3 * elapsed / args.steps
+    wbytes = case.w_qkv.nbytes + case.w_g.nbytes + case.w_o.nbytes
+    kv_union = 4096 * (p0 + m)                              # K + V rows of every window, once
+    kv_per_token = sum(4096 * (p0 + t + 1) for t in range(m))  # what per-token attention reads
+    io = 8 * m * hid
+    alg = wbytes + kv_union + io
+    log(f"chunk ({m} tokens at {p0}): {ms * 1e3:.2f} us/call, {m / (ms * 1e-3):.1f} tokens/s; "
+        f"algorithmic {alg / 1e6:.1f} MB -> {alg / (ms * 1e-3) / 1e9:.1f} GB/s; the per-token attention "
+        f"reads {(wbytes + kv_per_token + io) / 1e6:.1f} MB")
+    line = {
+        "metric": METRIC, "value": round(m / (ms * 1e-3), 3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": case.name, "hidden": hid, "tokens_per_call": m, "positions": [p0, p0 + m - 1],
+                   "weights": "bf16", "kv_cache": "fp16", "algorithmic_bytes_per_call": alg},
+        "block_hbm_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+        "block_frac_of_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="full32k", choices=sorted(list(workloads()) + ["cfg4"]),
-                    help="cfg4 is the 36-layer stack at position 8191 (no dominant-kernel roofline)")
+    ap.add_argument("--workload", default="full32k", choices=sorted(list(workloads()) + ["cfg4", "chunk"]),
+                    help="cfg4 is the 36-layer stack at position 8191, chunk 32 tokens of one sequence "
+                         "per call (neither has a dominant-kernel roofline)")
     ap.add_argument("--copies", type=int, default=0, help="weight/cache copies rotated (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample length (0 skips the baseline)")
@@ -279,6 +336,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "cfg4":
         bench_stack(args)
+        return
+    if args.workload == "chunk":
+        bench_chunk(args)
         return
     case = workloads()[args.workload]()
     a = gqa.Arch(hidden=case.arch.hidden)
