@@ -229,6 +229,36 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads, bool allow_di
   return plan;
 }
 
+// Several tokens of one sequence (attn_chunk_kernel): the rows every token
+// attends, [r0, position + M), are cut into chunks of a multiple of 32 rows,
+// the largest that still gives kAttnTargetWgs workgroups of (chunk, KV head,
+// 16 tokens).
+struct ChunkPlan {
+  int r0 = 0, rows = 0, chunk = 32, nchunks = 1, window = 0;
+};
+
+ChunkPlan make_chunk_plan(const gqa_arch *a, int is_full, int32_t first_pos, int32_t m) {
+  ChunkPlan cp;
+  cp.window = is_full ? first_pos + m : a->sliding_window;
+  cp.r0 = std::max(0, first_pos + 1 - cp.window);
+  cp.rows = first_pos + m - cp.r0;
+  const long groups = (long)a->num_kv_heads * ceil_div(m, 16);
+  const int cap = ceil_div(cp.rows, 32) * 32;
+  while (cp.chunk + 32 <= cap && (long)ceil_div(cp.rows, cp.chunk + 32) * groups >= kAttnTargetWgs) cp.chunk += 32;
+  cp.nchunks = ceil_div(cp.rows, cp.chunk);
+  return cp;
+}
+
+// Partial rows (token x chunk) of a chunk plan for m tokens: by the argument
+// of max_chunks below, nchunks <= 2 * ceil(target / groups) + 1.
+size_t chunk_partial_rows(int num_kv_heads, int32_t m, int32_t max_seq_len) {
+  if (m < 2) return 0;
+  const size_t groups = (size_t)num_kv_heads * ceil_div(m, 16);
+  const size_t per = std::min((size_t)ceil_div(max_seq_len, 32),
+                              2 * ((kAttnTargetWgs + groups - 1) / groups) + 1);
+  return (size_t)m * per;
+}
+
 // Upper bound of Plan::max_group_chunks for `batch` sequences of at most
 // max_seq_len attended rows.  If the plan stops at chunk c > q (q =
 // kChunkQuantum) because C(c + q) * Hk < target, then C(c) <= N / c + B <=
@@ -237,7 +267,7 @@ size_t max_chunks(int num_kv_heads, int32_t batch, int32_t max_seq_len) {
   const size_t seqs = (size_t)std::min<int32_t>(batch, kMaxSeqPerLaunch);
   const size_t finest = (size_t)ceil_div(max_seq_len, kChunkQuantum) * seqs;
   const size_t bound = 2 * (size_t)ceil_div(kAttnTargetWgs, num_kv_heads) + seqs;
-  return std::min(finest, bound);
+  return std::max(std::min(finest, bound), chunk_partial_rows(num_kv_heads, batch, max_seq_len));
 }
 
 // ---- workspace layout -----------------------------------------------------
@@ -650,7 +680,69 @@ gqa_status gqa_attention_block_chunk(const gqa_arch *arch, const gqa_layer_weigh
   for (int32_t t = 0; t < m_tokens; ++t) toks[t].position = seq->position + t;
   std::vector<SeqDesc> descs;
   if ((st = resolve_seqs(arch, is_full, toks.data(), m_tokens, &descs)) != GQA_OK) return st;
-  st = run_block(arch, weights, is_full, descs, x_normed, out, workspace, workspace_bytes, stream);
+  if (m_tokens == 1) {
+    st = run_block(arch, weights, is_full, descs, x_normed, out, workspace, workspace_bytes, stream);
+    return st == GQA_OK ? ok() : st;
+  }
+  if ((st = check_ptr(x_normed, "x_normed")) != GQA_OK) return st;
+  if ((st = check_ptr(out, "out")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  const ChunkPlan cp = make_chunk_plan(arch, is_full, seq->position, m_tokens);
+  const Layout L = block_layout(arch, m_tokens, (size_t)m_tokens * cp.nchunks);
+  if (workspace_bytes < L.total)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the chunk needs %zu", workspace_bytes,
+                L.total);
+  char *ws = static_cast<char *>(workspace);
+  float *q = reinterpret_cast<float *>(ws + L.q);
+  float *gate = reinterpret_cast<float *>(ws + L.gate);
+  float *attn = reinterpret_cast<float *>(ws + L.attn);
+  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
+  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // M-row projections: q, gate logits, and every token's k, v into its slot
+  if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
+  const long q_dim = (long)arch->num_heads * arch->head_dim;
+  ChunkAttnParams ca{};
+  ca.q = q;
+  ca.ld_q = q_dim;
+  ca.part_o = part_o;
+  ca.part_ml = part_ml;
+  ca.num_kv_heads = arch->num_kv_heads;
+  ca.qscale = (float)((double)arch->attention_scale * kLog2e);
+  ca.m_tokens = m_tokens;
+  ca.first_pos = seq->position;
+  ca.window = cp.window;
+  ca.r0 = cp.r0;
+  ca.chunk = cp.chunk;
+  ca.nchunks = cp.nchunks;
+  ca.seq = descs[0];
+  ca.seq.ring = seq->ring_capacity;   // physical row = position mod ring for every row, wrapped or not
+  hipError_t e = launch_attention_chunk(ca, s);
+  if (e != hipSuccess) return gpu_error(e, "chunk attention launch");
+  // merge + gate per token, up to kMaxSeqPerLaunch tokens per launch
+  for (int first = 0; first < m_tokens; first += kMaxSeqPerLaunch) {
+    AttnParams ap{};
+    const int cnt = std::min(kMaxSeqPerLaunch, m_tokens - first);
+    const size_t rows0 = (size_t)first * cp.nchunks * arch->num_heads;
+    ap.part_o = part_o + rows0 * kHeadDim;
+    ap.part_ml = part_ml + rows0 * 2;
+    ap.gate = gate + (size_t)first * arch->num_heads;
+    ap.ld_gate = arch->num_heads;
+    ap.out = attn + (size_t)first * q_dim;
+    ap.ld_out = q_dim;
+    ap.num_kv_heads = arch->num_kv_heads;
+    ap.chunk = cp.chunk;
+    ap.nseq = cnt;
+    ap.total_chunks = cnt * cp.nchunks;
+    for (int i = 0; i < cnt; ++i) {
+      ap.seq[i] = descs[first + i];
+      ap.seq[i].n = cp.rows;                  // every token: nchunks partials
+      ap.seq[i].chunk_begin = i * cp.nchunks;
+    }
+    e = launch_combine(ap, arch->num_heads, s);
+    if (e != hipSuccess) return gpu_error(e, "chunk merge launch");
+  }
+  st = run_o_proj(arch, weights, m_tokens, attn, out, s);
   return st == GQA_OK ? ok() : st;
 }
 

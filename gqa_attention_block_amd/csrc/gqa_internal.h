@@ -70,6 +70,28 @@ struct AttnParams {
   SeqDesc seq[kMaxSeqPerLaunch];
 };
 
+// Several tokens of one sequence (attn_chunk_kernel): token t at position
+// first_pos + t attends rows [ks_t, first_pos + t], ks_t = 0 (full) or
+// max(0, first_pos + t + 1 - window) (sliding).  The rows [r0, first_pos + M)
+// are cut into nchunks chunks of `chunk` rows; the partial of token t, chunk
+// c, query head h is row (t * nchunks + c) * Hq + h of part_o / part_ml (the
+// layout attn_combine_kernel reads with one "sequence" per token).
+struct ChunkAttnParams {
+  const float *q;       // [M][ld_q] RoPE'd queries of the M tokens
+  long ld_q;
+  float *part_o;
+  float *part_ml;
+  int num_kv_heads;
+  float qscale;         // attention_scale * log2(e)
+  int m_tokens;
+  int first_pos;
+  int window;           // sliding window; full layers: first_pos + M (every row from 0)
+  int r0;               // first attended row of token 0
+  int chunk;            // rows per chunk, a multiple of 32
+  int nchunks;
+  SeqDesc seq;          // the cache (k, v, cache_bytes; ring = ring_capacity or 0)
+};
+
 // Merge of one sequence's split-K partials, the gate and o_proj in one launch
 // (combine_oproj_kernel): y[r] += sum_h W_o[r][h*D .. h*D + D) a_h.
 struct OprojParams {
@@ -129,6 +151,10 @@ hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stre
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
 // One sequence, any number of chunks.
 hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream);
+// The merge + gate launch of launch_attention alone (partials already written).
+hipError_t launch_combine(const AttnParams &p, int num_heads, hipStream_t stream);
+// Token groups of 16 (4 waves x 4 tokens) per chunk and KV head.
+hipError_t launch_attention_chunk(const ChunkAttnParams &p, hipStream_t stream);
 // Batched projections on MFMA (batch <= 32 per launch; see kMfmaMinBatch).
 hipError_t launch_proj_mfma(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_mfma(const QkvParams &p, hipStream_t stream);

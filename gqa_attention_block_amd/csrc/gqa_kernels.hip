@@ -1122,6 +1122,223 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
     for (int k = threadIdx.x; k < p.zero_n; k += kThreads) p.zero_out[k] = 0.f;
 }
 
+// ---------------------------------------------------------------------------
+// Attention for several tokens of one sequence (a chunk of prefill, a
+// verify step): every K/V tile is read once for 16 query vectors at a time.
+//
+// Wave w of workgroup (row chunk c, KV head g, token group tg) serves tokens
+// 4 (4 tg + w) .. +3, i.e. 16 query vectors n = 4 * token + head (the KV
+// head's 4 query heads), over all rows of chunk c; the 4 waves of a
+// workgroup read the same rows (from L1/L2 after the first), the token
+// groups of a (c, g) sit 8 workgroups apart, i.e. on one XCD.  Per 16-row
+// tile, as in attn_partial_wave but with 16 query columns:
+//   S^T = K Qf on v_mfma_f32_16x16x32_f16, q split into fp16 high and low
+//         parts as two B operands (two chains of 8);
+//   causal mask per column: row r counts for token t iff ks_t <= r <= pos_t;
+//   online softmax per column with the lazy reference max;
+//   O += P V on v_mfma_f32_16x16x16_f16 with P's high and low parts as two
+//         A operands (S^T's output layout is already P's A layout: lane
+//         (G, n) holds column n, rows 4G .. 4G+3).
+// O's rows are the 16 queries; each wave writes its own partials (no merge
+// inside the workgroup).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void attn_chunk_wave(const ChunkAttnParams &p, int c, int g, int tb,
+                                                _Float16 *__restrict__ sv0, _Float16 *__restrict__ sv1) {
+  const int lane = threadIdx.x & 63;
+  const int Hk = p.num_kv_heads;
+  const int Hq = Hk * kGroup;
+  const int G = lane >> 4, n = lane & 15;
+  const SeqDesc &sd = p.seq;
+  const int rbase = p.r0 + c * p.chunk;               // first row (logical position) of the chunk
+  const int rend = p.first_pos + p.m_tokens;           // rows end (exclusive)
+  const int nrows = min(p.chunk, rend - rbase);
+  const int ne = p.chunk / kTileRows;                  // even: chunk is a multiple of 32
+  const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
+  const int ring = sd.ring;
+  const int pb = ring ? rbase % ring : rbase;          // physical row of rbase; a chunk wraps at most once
+  const int ring_end = ring ? ring : 0x7FFFFFFF;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(sd.k, sd.cache_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(sd.v, sd.cache_bytes);
+  const unsigned head_off = (unsigned)g * kHeadDim * 2u;
+
+  auto row_off = [&](int rel) -> unsigned {
+    int ph = pb + rel;
+    ph -= ph >= ring_end ? ring : 0;
+    const unsigned off = __umul24((unsigned)ph, row_bytes) + head_off;
+    return rel < nrows ? off : kOutOfRange;
+  };
+  auto load_k = [&](half8_t (&kf)[8], int t) {
+    const unsigned off = row_off(t * kTileRows + n) + (unsigned)G * 16u;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(half8_t, buf_load16(krs, off + (unsigned)s * 64u));
+  };
+  auto load_v = [&](_Float16 *sv, int t) {
+    const int r = lane >> 2;
+    const int q = lane & 3;
+    const unsigned off = row_off(t * kTileRows + r) + 32u * (unsigned)(((q >> 1) ^ (r >> 2)) & 1) +
+                         16u * (unsigned)(q & 1);
+    vload_block<0>(vrs, sv, off);
+    vload_block<1>(vrs, sv, off);
+    vload_block<2>(vrs, sv, off);
+    vload_block<3>(vrs, sv, off);
+    vload_block<4>(vrs, sv, off);
+    vload_block<5>(vrs, sv, off);
+    vload_block<6>(vrs, sv, off);
+    vload_block<7>(vrs, sv, off);
+  };
+
+  // this lane's column: query n = token tq, query head g*4 + (n & 3)
+  const int tq = 4 * tb + (n >> 2);
+  const int qpos = p.first_pos + tq;
+  const int qlo = max(0, qpos + 1 - p.window);         // first row token tq reads
+  const bool qvalid = tq < p.m_tokens;
+  // its q, dims 32s + 8G .. +8 (out of range past the last token: zeros)
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q, (unsigned)((size_t)p.m_tokens * p.ld_q * 4u));
+  const unsigned qoff = (unsigned)(((size_t)tq * p.ld_q + (size_t)(g * kGroup + (n & 3)) * kHeadDim) * 4u) +
+                        (unsigned)G * 32u;
+  float4 qa[8], qb[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const unsigned o = qvalid ? qoff + (unsigned)s * 128u : kOutOfRange;
+    qa[s] = __builtin_bit_cast(float4, buf_load16(rq, o));
+    qb[s] = __builtin_bit_cast(float4, buf_load16(rq, o == kOutOfRange ? o : o + 16u));
+  }
+  half8_t kA[8], kB[8];
+  load_k(kA, 0);
+  load_v(sv0, 0);
+  load_k(kB, 1);
+  load_v(sv1, 1);
+  // Qf B-fragments: q * scale * log2(e) as fp16 high + low parts
+  half8_t qh[8], ql[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const float x[8] = {qa[s].x, qa[s].y, qa[s].z, qa[s].w, qb[s].x, qb[s].y, qb[s].z, qb[s].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = x[j] * p.qscale;
+      const _Float16 h = (_Float16)v;
+      qh[s][j] = h;
+      ql[s][j] = (_Float16)(v - (float)h);
+    }
+  }
+
+  // acc[c][i] at lane (G, n): query 4G + i, dim 16c + n
+  floatx4_t acc[16];
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) acc[cc] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // column n's reference max (log2 units), in every lane group
+  float l_run = 0.f;         // this lane group's share of column n's sum
+  const int vrow = 4 * G + (n >> 2);
+  const int rd_even = vrow * 64 + (G & 1) * 32 + (n & 3) * 8;
+  const int rd_odd = vrow * 64 + ((G & 1) ^ 1) * 32 + (n & 3) * 8;
+
+  auto process = [&](const half8_t (&kf)[8], const _Float16 *sv, int t) {
+    floatx4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qh[s], d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], ql[s], d1, 0, 0, 0);
+    }
+    float sc[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rbase + t * kTileRows + 4 * G + i;   // row of d[i]
+      sc[i] = d0[i] + d1[i];
+      if (!qvalid || r < qlo || r > qpos) sc[i] = -INFINITY;
+      tmax = fmaxf(tmax, sc[i]);
+    }
+    tmax = max_across_rows(tmax);
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      // acc row 4G + i is query 4G + i: its factor sits in lane 4G + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float al = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * G + i) * 4, __float_as_int(alpha)));
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) acc[cc][i] *= al;
+      }
+    }
+    half4_t ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = sc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - m_run);
+      l_run += pv;
+      const _Float16 h = (_Float16)pv;
+      ph[i] = h;
+      pl[i] = (_Float16)(pv - (float)h);
+    }
+    const char *base = reinterpret_cast<const char *>(sv);
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) {
+      const half4_t vt = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4_t *)(base + (cc & 1 ? rd_odd : rd_even) + (cc >> 1) * 1024)));
+      acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vt, acc[cc], 0, 0, 0);
+      acc[cc] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vt, acc[cc], 0, 0, 0);
+    }
+  };
+  for (int t = 0; t + 2 < ne; t += 2) {
+    process(kA, sv0, t);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kA, t + 2);
+    load_v(sv0, t + 2);
+    process(kB, sv1, t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kB, t + 3);
+    load_v(sv1, t + 3);
+  }
+  process(kA, sv0, ne - 2);
+  process(kB, sv1, ne - 1);
+
+  // ---- partials of the 16 queries: O staged through this wave's V buffers
+  // (query q' < 8 in sv0, else sv1; element n * 16 + c holds dim 16c + n) ----
+  l_run = sum_across_rows(l_run);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qq = 4 * G + i;
+    float *st = reinterpret_cast<float *>(qq < 8 ? sv0 : sv1) + (qq & 7) * kHeadDim + n * 16;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+      *reinterpret_cast<float4 *>(st + c4 * 4) =
+          make_float4(acc[c4 * 4][i], acc[c4 * 4 + 1][i], acc[c4 * 4 + 2][i], acc[c4 * 4 + 3][i]);
+  }
+  // (LDS writes and reads of one wave are in order: no barrier)
+#pragma unroll
+  for (int qq = 0; qq < 16; ++qq) {
+    const int t2 = 4 * tb + (qq >> 2);
+    if (t2 >= p.m_tokens) break;
+    const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(qq < 8 ? sv0 : sv1) +
+                                                       (qq & 7) * kHeadDim + lane * 4);
+    const size_t row = ((size_t)t2 * p.nchunks + c) * Hq + g * kGroup + (qq & 3);
+    *reinterpret_cast<float4 *>(p.part_o + row * kHeadDim + lane * 4) = v;
+  }
+  if (G == 0 && qvalid) {
+    const size_t row = ((size_t)tq * p.nchunks + c) * Hq + g * kGroup + (n & 3);
+    *reinterpret_cast<float2 *>(p.part_ml + row * 2) = make_float2(m_run, l_run);
+  }
+}
+
+// Grid: units (chunk, KV head) rounded up to 8, times token groups; the token
+// groups of a unit are 8 workgroups apart (one XCD).
+__global__ __launch_bounds__(kThreads, 2) void attn_chunk_kernel(const ChunkAttnParams p) {
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v0[4][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v1[4][kTileHalves];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntg = (p.m_tokens + 15) / 16;
+  const int grp = blockIdx.x / (8 * ntg), off = blockIdx.x - grp * (8 * ntg);
+  const int u = grp * 8 + (off & 7);
+  const int tg = off >> 3;
+  if (u >= p.nchunks * p.num_kv_heads) return;
+  const int c = u / p.num_kv_heads;
+  const int g = u - c * p.num_kv_heads;
+  const int tb = 4 * tg + w;                            // token block: tokens 4 tb .. 4 tb + 3
+  if (4 * tb >= p.m_tokens) return;                     // no token of this wave (no barrier follows)
+  attn_chunk_wave(p, c, g, tb, s_v0[w], s_v1[w]);
+}
+
 // Merge of the split-K partials and the headwise gate.
 // Grid (Hq * kCombineSplit, nseq).  Workgroup (h, part) owns query head h and
 // the 16 stored elements [part*16, part*16 + 16) of its partials (stored
@@ -1523,10 +1740,21 @@ hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_attention_chunk(const ChunkAttnParams &p, hipStream_t stream) {
+  const int ntg = (p.m_tokens + 15) / 16;
+  const int units = p.nchunks * p.num_kv_heads;
+  hipLaunchKernelGGL(attn_chunk_kernel, dim3((unsigned)((units + 7) / 8 * 8 * ntg)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
   hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.direct) return e;
+  return launch_combine(p, num_heads, stream);
+}
+
+hipError_t launch_combine(const AttnParams &p, int num_heads, hipStream_t stream) {
   int most = 0;
   for (int i = 0; i < p.nseq; ++i) most = std::max(most, (p.seq[i].n + p.chunk - 1) / p.chunk);
   if (most <= kCombineSmallChunks)
