@@ -125,6 +125,19 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned o
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Cache policy of the loads that stream bytes read once per call: the KV
+// tiles of the attention and the projection weights.  2 = nt (non-temporal):
+// the lines are not kept in the caches for reuse, which lets the memory
+// system sustain a higher read rate on long streams.
+constexpr int kKPolicy = 2;
+constexpr int kVPolicy = 2;
+constexpr int kWeightPolicy = 2;
+
+template <int POLICY>
+__device__ __forceinline__ uint4 buf_load16_p(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
+
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p)
     for (int it = 0; it < NIT; ++it) {
       const int col = (it * 64 + lane) * 8;
       const unsigned off = (row < total && col < p.cols) ? base + (unsigned)col * 2u : kOutOfRange;
-      w[r][it] = first ? buf_load16(r0, off) : buf_load16(r1, off);
+      w[r][it] = first ? buf_load16_p<kWeightPolicy>(r0, off) : buf_load16_p<kWeightPolicy>(r1, off);
     }
   }
   // the R rows' dot products with staged x row m (batch row b)
@@ -392,8 +405,8 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
   for (int it = 0; it < NIT; ++it) {
     const int col = (it * 64 + lane) * 8;
     const bool ok = active && col < p.hidden;
-    wa[it] = buf_load16(rw, ok ? (unsigned)(base_row + dA) * row_bytes + (unsigned)col * 2u : kOutOfRange);
-    wb[it] = buf_load16(rw, ok ? (unsigned)(base_row + dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+    wa[it] = buf_load16_p<kWeightPolicy>(rw, ok ? (unsigned)(base_row + dA) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+    wb[it] = buf_load16_p<kWeightPolicy>(rw, ok ? (unsigned)(base_row + dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
   }
 
   // the rotation of batch row b does not depend on the loads: formed while
@@ -622,7 +635,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
     const int c0 = (s0 + 2 * pr) * 32;             // first column of the pair
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      P.w[i] = buf_load16(rw, woff[i] != kOutOfRange && c0 + lwc * 8 < cols ? woff[i] + (unsigned)c0 * 2u
+      P.w[i] = buf_load16_p<kWeightPolicy>(rw, woff[i] != kOutOfRange && c0 + lwc * 8 < cols ? woff[i] + (unsigned)c0 * 2u
                                                                              : kOutOfRange);
 #pragma unroll
     for (int bt = 0; bt < MB; ++bt)
@@ -821,6 +834,27 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
 // partial per query head; attn_combine_kernel merges the chunks.
 // ---------------------------------------------------------------------------
 
+// Workgroup -> (chunk cid, KV head g).  The hardware deals workgroups to the
+// 8 XCDs round-robin (workgroup b runs on XCD b % 8).  When the chunk count
+// is a multiple of 8, XCD x takes chunks x, x + 8, x + 16, ... with all of
+// their KV heads, so each XCD's L2 sees whole cache rows; otherwise
+// consecutive workgroups are the KV heads of one chunk.  Either way the map
+// is a bijection onto [0, total_chunks) x [0, Hk).
+constexpr bool kXcdChunkMap = true;
+__device__ __forceinline__ void partial_unit(const AttnParams &p, int &cid, int &g) {
+  const int b = blockIdx.x;
+  const int Hk = p.num_kv_heads;
+  if (kXcdChunkMap && (p.total_chunks & 7) == 0) {
+    const int k = b >> 3;
+    const int j = k / Hk;
+    g = k - j * Hk;
+    cid = (b & 7) + 8 * j;
+  } else {
+    cid = b / Hk;
+    g = b - cid * Hk;
+  }
+}
+
 __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
   int s = 0;
   for (int i = 1; i < p.nseq; ++i)
@@ -834,9 +868,9 @@ constexpr int kTileHalves = kTileRows * kHeadDim;   // one staged V tile: 8 KB
 // at sv + J KB + 16 B * lane.  The block's 64 B of each row is selected with
 // the scalar offset J * 64, which moves only the global address (the
 // instruction's immediate offset would move the LDS address as well).
-template <int J>
+template <int J, int POLICY = 0>
 __device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 *sv, unsigned off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sv + J * 512), 16, off, J * 64, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sv + J * 512), 16, off, J * 64, 0, POLICY);
 }
 
 // Staged V tile in LDS: eight 1 KB column blocks j (dims 32j .. 32j+31), each
@@ -850,13 +884,14 @@ __device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 
 // compiler waits for a buffer's LDS-bound loads only before reading that
 // buffer (not for the other buffer's loads, which are still in flight).
 // sq is this wave's 4 KB staging area for its query fragments.
-__device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _Float16 *__restrict__ sv0,
+__device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _Float16 *__restrict__ sk0,
+                                                  _Float16 *__restrict__ sk1, _Float16 *__restrict__ sv0,
                                                   _Float16 *__restrict__ sv1, _Float16 *__restrict__ sq,
                                                   float &m_out, float &l_out) {
   const int lane = threadIdx.x & 63;
   const int Hk = p.num_kv_heads;
-  const int cid = blockIdx.x / Hk;
-  const int g = blockIdx.x - cid * Hk;
+  int cid, g;
+  partial_unit(p, cid, g);
   const int b = find_seq(p, cid);
   const SeqDesc sd = p.seq[b];
   const int t0 = sd.kv_start + (cid - sd.chunk_begin) * p.chunk;
@@ -882,27 +917,28 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     const unsigned off = __umul24((unsigned)ph, row_bytes) + head_off;   // ph, row_bytes < 2^24
     return rel < wend ? off : kOutOfRange;
   };
-  // K A-fragments of tile t: lane (G, n) holds row 16t + n, dims 32s + 8G .. +8
-  auto load_k = [&](half8_t (&kf)[8], int t) {
-    const unsigned off = row_off(wr0 + t * kTileRows + n) + (unsigned)G * 16u;
+  // Tile t of this wave into a staged buffer: instruction j brings rows 2j
+  // and 2j + 1 of the tile (lane l: row 2j + l/32, LDS position l % 32 of
+  // that row's 32 pieces of 16 B), so every instruction reads whole 128 B
+  // lines, which the non-temporal policy needs.  Row r's piece p sits at
+  // position p ^ swz(r) (K: swz = r % 16; V: swz = 2 (r % 8)), chosen so
+  // that the fragment reads below hit distinct LDS banks.
+  auto load_tile = [&](_Float16 *sbuf, int t, auto k_tag) {
+    constexpr bool is_k = decltype(k_tag)::value;
+    const __amdgpu_buffer_rsrc_t rs = is_k ? krs : vrs;
+    const int pos = lane & 31;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kf[s] = __builtin_bit_cast(half8_t, buf_load16(krs, off + (unsigned)s * 64u));
+    for (int jj = 0; jj < 8; ++jj) {
+      const int r = 2 * jj + (lane >> 5);
+      const int pc = is_k ? (pos & 16) | ((pos ^ r) & 15) : pos ^ (2 * (r & 7));
+      const unsigned off = row_off(wr0 + t * kTileRows + r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sbuf + jj * 512), 16,
+                                               off == kOutOfRange ? off : off + 16u * (unsigned)pc, 0, 0,
+                                               is_k ? kKPolicy : kVPolicy);
+    }
   };
-  // V tile t into a staged buffer (layout above)
-  auto load_v = [&](_Float16 *sv, int t) {
-    const int r = lane >> 2;
-    const int q = lane & 3;
-    const unsigned off = row_off(wr0 + t * kTileRows + r) + 32u * (unsigned)(((q >> 1) ^ (r >> 2)) & 1) +
-                         16u * (unsigned)(q & 1);
-    vload_block<0>(vrs, sv, off);
-    vload_block<1>(vrs, sv, off);
-    vload_block<2>(vrs, sv, off);
-    vload_block<3>(vrs, sv, off);
-    vload_block<4>(vrs, sv, off);
-    vload_block<5>(vrs, sv, off);
-    vload_block<6>(vrs, sv, off);
-    vload_block<7>(vrs, sv, off);
-  };
+  auto load_k = [&](_Float16 *sk, int t) { load_tile(sk, t, std::true_type{}); };
+  auto load_v = [&](_Float16 *sv, int t) { load_tile(sv, t, std::false_type{}); };
 
   // q first (its wait then does not include the tile loads): lane l takes
   // dims 4l .. 4l+3 of the KV head's 4 query heads
@@ -918,10 +954,9 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   // A wave without rows (a short chunk) runs two fully masked tiles: its
   // loads are out of range and it contributes m = -inf, l = 0, O = 0.
   const int ne = ntiles > 2 ? (ntiles + 1) & ~1 : 2;
-  half8_t kA[8], kB[8];
-  load_k(kA, 0);
+  load_k(sk0, 0);
   load_v(sv0, 0);
-  load_k(kB, 1);
+  load_k(sk1, 1);
   load_v(sv1, 1);
 
   // Query fragments, built while the first tiles are in flight: each lane
@@ -958,17 +993,36 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   for (int c = 0; c < 16; ++c) acc[c] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;   // lanes (G, n < 4): reference max of head n (log2 units)
   float l_run = 0.f;         // lanes (G, n < 4): this lane group's share of head n's sum
-  // transposed-read source of this lane: row 4G + n/4, 8 B at 8 (n % 4) within
-  // the 32 B of a slice; even slices sit in half (G & 1), odd ones in the other
+  // K A-fragment of k-step s: lane (G, n) reads row n, piece 4s + G, i.e.
+  // byte 512 n + 256 (s / 4) + 16 ((4 (s % 4) + G) ^ n); a quarter wave
+  // (fixed G) covers 16 distinct bank groups.
+  int kaddr[4];
+#pragma unroll
+  for (int s3 = 0; s3 < 4; ++s3) kaddr[s3] = n * 512 + 16 * ((4 * s3 + G) ^ n);
+  // V transposed read of dim slice c (dims 16c .. 16c+15): lane (G, n) points
+  // at row 4G + n/4, dims 16c + 4 (n % 4) .. +3 = piece 2c + (n % 4) / 2, half
+  // n % 2; with the swizzle that is byte 512 row + 256 (c / 8)
+  // + 32 ((c % 8) ^ (row % 8)) + 16 ((n / 2) % 2) + 8 (n % 2).  A half wave
+  // reads 8 rows x 32 B on distinct banks.
   const int vrow = 4 * G + (n >> 2);
-  const int rd_even = vrow * 64 + (G & 1) * 32 + (n & 3) * 8;   // bytes
-  const int rd_odd = vrow * 64 + ((G & 1) ^ 1) * 32 + (n & 3) * 8;
+  int vaddr[8];
+#pragma unroll
+  for (int c7 = 0; c7 < 8; ++c7) vaddr[c7] = vrow * 512 + 32 * (c7 ^ (vrow & 7)) + 16 * ((n >> 1) & 1) + 8 * (n & 1);
 
-  auto process = [&](const half8_t (&kf)[8], const _Float16 *sv, int t) {
-    // S^T = K Qf: d[i] = S[row 4G+i][column n]; column n+4 holds the low part
+  // S^T = K Qf for the staged K tile: d[i] = S[row 4G+i][column n]; column
+  // n+4 holds the low part
+  auto scores = [&](const _Float16 *sk) {
+    const char *kbase = reinterpret_cast<const char *>(sk);
+    half8_t kf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const half8_t *>(kbase + kaddr[s & 3] + (s >> 2) * 256);
     floatx4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], d, 0, 0, 0);
+    return d;
+  };
+  // online softmax of tile t's scores and O += P V from the staged V tile
+  auto process = [&](floatx4_t d, const _Float16 *sv, int t) {
     float sc[4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -1017,23 +1071,29 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const short4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4_t *)(base + (c & 1 ? rd_odd : rd_even) + (c >> 1) * 1024));
+          (lds_short4_t *)(base + vaddr[c & 7] + (c >> 3) * 256));
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pf, __builtin_bit_cast(half4_t, vt), acc[c], 0, 0, 0);
     }
   };
-  // sched_barrier: the refill of a buffer stays behind the reads of it
+  // A K buffer is refilled as soon as its scores are formed (the MFMAs have
+  // consumed every read of it), a V buffer after O += P V; sched_barrier keeps
+  // each refill behind the reads of its buffer.
   for (int t = 0; t + 2 < ne; t += 2) {
-    process(kA, sv0, t);
+    floatx4_t d = scores(sk0);
     __builtin_amdgcn_sched_barrier(0);
-    load_k(kA, t + 2);
+    load_k(sk0, t + 2);
+    process(d, sv0, t);
+    __builtin_amdgcn_sched_barrier(0);
     load_v(sv0, t + 2);
-    process(kB, sv1, t + 1);
+    d = scores(sk1);
     __builtin_amdgcn_sched_barrier(0);
-    load_k(kB, t + 3);
+    load_k(sk1, t + 3);
+    process(d, sv1, t + 1);
+    __builtin_amdgcn_sched_barrier(0);
     load_v(sv1, t + 3);
   }
-  process(kA, sv0, ne - 2);
-  process(kB, sv1, ne - 1);
+  process(scores(sk0), sv0, ne - 2);
+  process(scores(sk1), sv1, ne - 1);
 
   // ---- this wave's partial: add the high and low rows, stage (m, l, O) ----
   l_run = sum_across_rows(l_run);
@@ -1062,6 +1122,8 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 // Workgroup = (chunk cid, KV head g); its 4 waves split the chunk's rows and
 // then merge in LDS, so one partial per (chunk, query head) is written.
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) _Float16 s_k0[4][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_k1[4][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_v0[4][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_v1[4][kTileHalves];
   // per wave: its query fragments during the loop, then its (m, l) per query head
@@ -1069,7 +1131,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
   float m_run, l_run;
-  attn_partial_wave(p, w, s_v0[w], s_v1[w], s_q[w], m_run, l_run);
+  attn_partial_wave(p, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w], s_q[w], m_run, l_run);
   if (lane < kGroup) {
     float *ml = reinterpret_cast<float *>(s_q[w]);
     ml[lane] = m_run;
@@ -1079,8 +1141,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnPar
   // wave w merges query head i = w of this KV head: lane l owns elements 4l .. 4l+3
   const int Hk = p.num_kv_heads;
   const int Hq = Hk * kGroup;
-  const int cid = blockIdx.x / Hk;
-  const int g = blockIdx.x - cid * Hk;
+  int cid, g;
+  partial_unit(p, cid, g);
   const int i = w;
   auto m_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[i]; };
   auto l_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[kGroup + i]; };
@@ -1532,7 +1594,7 @@ __global__ __launch_bounds__(kThreads) void combine_oproj_kernel(const OprojPara
 #pragma unroll
   for (int i = 0; i < kOprojPairs; ++i) {
     const int r = rbase + 2 * i;
-    wv[i] = buf_load16(rw, r < p.hidden ? (unsigned)r * row_bytes + (unsigned)(h * kHeadDim + cg * 8) * 2u
+    wv[i] = buf_load16_p<kWeightPolicy>(rw, r < p.hidden ? (unsigned)r * row_bytes + (unsigned)(h * kHeadDim + cg * 8) * 2u
                                         : kOutOfRange);
   }
 
