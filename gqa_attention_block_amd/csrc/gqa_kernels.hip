@@ -95,19 +95,6 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 
-// fp16 -> fp32 of the low / high half of a dword, one full-rate VALU op each.
-// Written out so the compiler keeps one conversion feeding several plain
-// FMAs instead of fusing it into a (half-rate) mixed-precision FMA per use.
-__device__ __forceinline__ float h2f_lo(uint32_t w) {
-  float f;
-  asm("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(w));
-  return f;
-}
-__device__ __forceinline__ float h2f_hi(uint32_t w) {
-  float f;
-  asm("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(f) : "v"(w));
-  return f;
-}
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------
@@ -896,10 +883,8 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   const SeqDesc sd = p.seq[b];
   const int t0 = sd.kv_start + (cid - sd.chunk_begin) * p.chunk;
   const int nrows = min(p.chunk, sd.kv_start + sd.n - t0);
-  const int cw = p.chunk / 4;                    // rows per wave
-  const int wr0 = w * cw;                        // this wave's rows: [wr0, wend) relative to t0
-  const int wend = min(nrows, wr0 + cw);
-  const int ntiles = wend > wr0 ? (wend - wr0 + kTileRows - 1) / kTileRows : 0;
+  // wave w takes tiles w, w + 4, w + 8, ... of the chunk
+  const int ntiles = nrows > kTileRows * w ? (nrows - kTileRows * w + 4 * kTileRows - 1) / (4 * kTileRows) : 0;
   const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
   const int ring = sd.ring;
   const int p0 = ring ? (t0 % ring) : t0;        // physical row of t0; a chunk wraps at most once
@@ -915,7 +900,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     int ph = p0 + rel;
     ph -= ph >= ring_end ? ring : 0;
     const unsigned off = __umul24((unsigned)ph, row_bytes) + head_off;   // ph, row_bytes < 2^24
-    return rel < wend ? off : kOutOfRange;
+    return rel < nrows ? off : kOutOfRange;
   };
   // Tile t of this wave into a staged buffer: instruction j brings rows 2j
   // and 2j + 1 of the tile (lane l: row 2j + l/32, LDS position l % 32 of
@@ -931,7 +916,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     for (int jj = 0; jj < 8; ++jj) {
       const int r = 2 * jj + (lane >> 5);
       const int pc = is_k ? (pos & 16) | ((pos ^ r) & 15) : pos ^ (2 * (r & 7));
-      const unsigned off = row_off(wr0 + t * kTileRows + r);
+      const unsigned off = row_off((4 * t + w) * kTileRows + r);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sbuf + jj * 512), 16,
                                                off == kOutOfRange ? off : off + 16u * (unsigned)pc, 0, 0,
                                                is_k ? kKPolicy : kVPolicy);
@@ -1028,7 +1013,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[i] = d[i] + dpp<0x104>(d[i]);             // row_shl:4 -> value of lane n+4
-      if (n >= kGroup || wr0 + t * kTileRows + 4 * G + i >= wend) sc[i] = -INFINITY;
+      if (n >= kGroup || (4 * t + w) * kTileRows + 4 * G + i >= nrows) sc[i] = -INFINITY;
       tmax = fmaxf(tmax, sc[i]);
     }
     tmax = max_across_rows(tmax);
@@ -1121,7 +1106,8 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 
 // Workgroup = (chunk cid, KV head g); its 4 waves split the chunk's rows and
 // then merge in LDS, so one partial per (chunk, query head) is written.
-__global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnParams p) {
+// 144 KB of LDS: one workgroup per CU, one wave per SIMD.
+__global__ __launch_bounds__(kThreads, 1) void attn_partial_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) _Float16 s_k0[4][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_k1[4][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_v0[4][kTileHalves];

@@ -127,6 +127,7 @@ ATTN_CASES = [
     ("full_batch_mixed", True, [0, 5, 63, 64, 65, 1000, 4095], 0, None),
     ("ring_batch_mixed", False, [3, 511, 512, 777, 32767], 512, None),
     ("full_batch33_two_launches", True, list(range(7, 7 + 33 * 37, 37)), 0, None),
+    ("full_batch_long", True, [20000, 3000, 40000, 100], 0, None),
 ]
 
 
@@ -189,7 +190,7 @@ def test_attention_gated(name, is_full, positions, ring, caps):
 # ----------------------------------------------------------------------------
 
 PARTIAL_CASES = ["full_pos0_single_key", "full_pos1000_ragged", "full_pos32767", "ring_pos513",
-                 "ring_pos32905", "full_batch_mixed", "ring_batch_mixed"]
+                 "ring_pos32905", "full_batch_mixed", "ring_batch_mixed", "full_batch_long"]
 # stored element e of a partial holds dim 16 * (e % 16) + e // 16
 _PERM = np.array([16 * (e % 16) + e // 16 for e in range(256)])
 
@@ -286,6 +287,7 @@ ROWSET_CASES = [
     ("ring_pos32905", False, 32768 + 137, 512, 512),
     ("ring640_pos1500", False, 1500, 640, 640),
     ("full_pos0", True, 0, 0, 4),
+    ("full_pos32767", True, 32767, 0, 32768),
 ]
 
 
