@@ -10,6 +10,7 @@ from .block import (  # noqa: F401
     AttentionStepResult,
     BlockResult,
     ChunkResult,
+    MlpResult,
     OracleSeq,
     StackResult,
     attention_decode,
@@ -17,10 +18,13 @@ from .block import (  # noqa: F401
     bf16_bits_to_f64,
     block_chunk,
     block_decode,
+    decoder_stack_decode,
+    gelu_erf,
     gemv,
     head_gate,
     kv_slot,
     kv_window,
+    mlp_decode,
     physical_rows,
     rms_norm,
     rope_neox,

@@ -15,6 +15,11 @@ pages of the crate turbospark-runtime 0.3.0, cited below as:
   [kvw]   src/kv_write.rs             (`kv_write_target`, `encode_kv_commit`,
           `encode_attention_any`)
 
+The rest of the decoder layer (post-attention RMSNorm, erf-GELU gated MLP,
+residual add) follows [mod]'s transcribed layer; its intermediate size is not
+on the pages, so inputs are synthetic (reading O21: W_gate, W_up [inter][hidden],
+W_down [hidden][inter], row-major like O1).
+
 Readings where the pages leave a step open (numbered O1..O20 throughout):
   O1 weights are row-major [out][in] and y = W x; O2 head h of a section is the
   contiguous block [256h, 256h+256); O3 query head h reads KV head
@@ -34,6 +39,7 @@ from dataclasses import dataclass
 from typing import List, Sequence, Tuple
 
 import numpy as np
+from scipy.special import erf as _erf
 
 
 # ----------------------------------------------------------------------------
@@ -356,4 +362,60 @@ def stack_decode(arch, h0: np.ndarray, layers: Sequence) -> StackResult:
         h = h + r.out
         outs.append(r.out)
         normed.append(xn)
+    return StackResult(h=h, block_outs=outs, normed=normed)
+
+
+# ----------------------------------------------------------------------------
+# the rest of the decoder layer  [mod: module doc, transcribed layer -- after
+#   the attention's raw residual add: x = rms(h, post_attention_layernorm,
+#   1e-6); h = h + down(gelu_erf(x @ gate_proj) * (x @ up_proj)); the family's
+#   GELU is the erf form (the module doc's closing remark on mlp.rs)]
+# ----------------------------------------------------------------------------
+
+def gelu_erf(x: np.ndarray) -> np.ndarray:
+    """x * Phi(x) = x / 2 * (1 + erf(x / sqrt(2))): the exact (erf) GELU, not
+    the tanh approximation."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + _erf(x / np.sqrt(2.0)))
+
+
+@dataclass
+class MlpResult:
+    h: np.ndarray        # [B][hidden] residual stream after the MLP's add
+    x: np.ndarray        # post-attention-normed input [B][hidden]
+    gate: np.ndarray     # x @ gate_proj  [B][inter]
+    up: np.ndarray       # x @ up_proj    [B][inter]
+    act: np.ndarray      # gelu_erf(gate) * up
+    out: np.ndarray      # down(act): the MLP's contribution [B][hidden]
+
+
+def mlp_decode(h: np.ndarray, w_post_bits, w_gate_bits, w_up_bits, w_down_bits,
+               eps: float) -> MlpResult:
+    """[mod: transcribed layer, last two lines] for B rows of the residual stream."""
+    h = np.atleast_2d(np.asarray(h, dtype=np.float64))
+    x = rms_norm(h, w_post_bits, eps)
+    gate = gemv(bf16_bits_to_f64(w_gate_bits), x)
+    up = gemv(bf16_bits_to_f64(w_up_bits), x)
+    act = gelu_erf(gate) * up
+    out = gemv(bf16_bits_to_f64(w_down_bits), act)
+    return MlpResult(h=h + out, x=x, gate=gate, up=up, act=act, out=out)
+
+
+def decoder_stack_decode(arch, h0: np.ndarray, layers: Sequence) -> StackResult:
+    """Whole decoder layers, batch 1 [mod: transcribed layer]: per layer
+    h += block(rms(h) * w_norm), then h += mlp(h).  Each layer exposes the
+    attention fields of ``stack_decode`` plus w_post, w_gate, w_up, w_down.
+    ``block_outs`` holds each layer's total contribution (attention + MLP)."""
+    h = np.atleast_2d(np.asarray(h0, dtype=np.float64)).copy()
+    outs, normed = [], []
+    for layer in layers:
+        xn = rms_norm(h, layer.w_norm, arch.rms_eps)
+        r = block_decode(arch, layer.is_full, layer.w_qkv, layer.w_g, layer.w_o,
+                         xn, [layer.cache])
+        h_mid = h + r.out
+        m = mlp_decode(h_mid, layer.w_post, layer.w_gate, layer.w_up, layer.w_down,
+                       arch.rms_eps)
+        outs.append(m.h - h)
+        normed.append(xn)
+        h = m.h
     return StackResult(h=h, block_outs=outs, normed=normed)

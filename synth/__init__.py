@@ -11,6 +11,8 @@ Layouts (all row-major, C order):
   * ``w_g``    uint16 bf16 bits ``[num_heads][hidden]``
   * ``w_o``    uint16 bf16 bits ``[hidden][q_dim]``
   * ``w_norm`` uint16 bf16 bits ``[hidden]`` (stack cases only)
+  * MLP (decoder stack cases): ``w_post`` bf16 ``[hidden]``, ``w_gate`` and
+    ``w_up`` bf16 ``[inter][hidden]``, ``w_down`` bf16 ``[hidden][inter]``
   * ``x``      float32 ``[batch][hidden]`` (already-normed block input)
   * per sequence ``k``/``v`` float16 ``[capacity][num_kv_heads][head_dim]``
 
@@ -299,3 +301,67 @@ def random_hidden(hidden: int, batch: int, seed: int, case_id: int,
 def random_bf16(shape, seed: int, case_id: int, tensor_id: int,
                 std: float = WEIGHT_STD, mean: float = 0.0) -> np.ndarray:
     return round_to_bf16_bits(_normal(seed, case_id, tensor_id, shape, std, mean))
+
+
+# ----------------------------------------------------------------------------
+# the rest of the decoder layer (post-attention norm + gated MLP); the pages
+# print no intermediate size, so it is taken as 3 * hidden here
+# ----------------------------------------------------------------------------
+
+_T_WPOST, _T_WGATE, _T_WUP, _T_WDOWN = 16, 17, 18, 19   # inside a layer's block of 32 ids
+
+
+def mlp_inter(hidden: int) -> int:
+    return 3 * hidden
+
+
+@dataclass
+class MlpWeights:
+    w_post: np.ndarray   # uint16 bf16 bits [hidden] (post_attention_layernorm)
+    w_gate: np.ndarray   # uint16 bf16 bits [inter][hidden]
+    w_up: np.ndarray     # uint16 bf16 bits [inter][hidden]
+    w_down: np.ndarray   # uint16 bf16 bits [hidden][inter]
+
+    @property
+    def inter(self) -> int:
+        return int(self.w_gate.shape[0])
+
+
+def make_mlp(hidden: int, inter: int, seed: int, case_id: int, base: int) -> MlpWeights:
+    """Norm weight ~ N(1, 0.1), projections ~ N(0, 0.02), rounded to bf16."""
+    return MlpWeights(
+        w_post=round_to_bf16_bits(_normal(seed, case_id, base + _T_WPOST, (hidden,), 0.1, 1.0)),
+        w_gate=round_to_bf16_bits(_normal(seed, case_id, base + _T_WGATE, (inter, hidden), WEIGHT_STD)),
+        w_up=round_to_bf16_bits(_normal(seed, case_id, base + _T_WUP, (inter, hidden), WEIGHT_STD)),
+        w_down=round_to_bf16_bits(_normal(seed, case_id, base + _T_WDOWN, (hidden, inter), WEIGHT_STD)))
+
+
+@dataclass
+class DecoderLayer:
+    """A whole decoder layer: the attention fields of StackLayer plus the MLP."""
+    is_full: bool
+    w_norm: np.ndarray
+    w_qkv: np.ndarray
+    w_g: np.ndarray
+    w_o: np.ndarray
+    cache: SeqCache
+    w_post: np.ndarray
+    w_gate: np.ndarray
+    w_up: np.ndarray
+    w_down: np.ndarray
+
+
+def decoder_stack(seed: int = 0, num_layers: int = 36, position: int = 8191, hidden: int = 2560,
+                  inter: Optional[int] = None, phase_full_first: bool = False,
+                  case_id: int = 4) -> StackCase:
+    """The attention stack of ``cfg4_stack`` (same draws) with each layer's MLP."""
+    base_case = cfg4_stack(seed, num_layers, position, hidden, phase_full_first, case_id)
+    inter = inter or mlp_inter(hidden)
+    layers = []
+    for li, L in enumerate(base_case.layers):
+        m = make_mlp(hidden, inter, seed, case_id, 1000 + 32 * li)
+        layers.append(DecoderLayer(is_full=L.is_full, w_norm=L.w_norm, w_qkv=L.w_qkv, w_g=L.w_g,
+                                   w_o=L.w_o, cache=L.cache, w_post=m.w_post, w_gate=m.w_gate,
+                                   w_up=m.w_up, w_down=m.w_down))
+    return StackCase(name=f"decoder_stack{num_layers}_pos{position}_inter{inter}",
+                     arch=base_case.arch, h=base_case.h, layers=layers)

@@ -547,4 +547,85 @@ def pin_stack_is_residual_sum(O):
     assert np.allclose(r.normed[0], h0 / np.sqrt(np.mean(h0 ** 2) + 1e-6), rtol=1e-13)
 
 
+
+
+# ----------------------------------------------------------------------------
+# the rest of the decoder layer: erf GELU, gated MLP, whole-layer stack
+# ----------------------------------------------------------------------------
+
+def pin_gelu_erf_closed_forms(O):
+    """GELU(x) = x * Phi(x) with the standard normal CDF Phi (textbook values to
+    10 digits), GELU(0) = 0, and GELU(x) - GELU(-x) = x (erf is odd).  The tanh
+    form differs from these by ~1e-4."""
+    phi = {1.0: 0.8413447461, 2.0: 0.9772498681, 0.5: 0.6914624613, 3.0: 0.9986501020}
+    for x, p in phi.items():
+        assert abs(float(O.gelu_erf(np.array([x]))[0]) - x * p) < 1e-9 * max(1.0, x)
+        assert abs(float(O.gelu_erf(np.array([-x]))[0]) + x * (1.0 - p)) < 1e-9 * max(1.0, x)
+    assert float(O.gelu_erf(np.array([0.0]))[0]) == 0.0
+    x = np.linspace(-6.0, 6.0, 49)
+    assert np.max(np.abs(O.gelu_erf(x) - O.gelu_erf(-x) - x)) < 1e-14
+
+
+def _tiny_mlp(rng, hidden=8, inter=12):
+    return (_bf16(1.0 + 0.1 * rng.standard_normal(hidden).astype(np.float32)),
+            _bf16(0.5 * rng.standard_normal((inter, hidden)).astype(np.float32)),
+            _bf16(0.5 * rng.standard_normal((inter, hidden)).astype(np.float32)),
+            _bf16(0.5 * rng.standard_normal((hidden, inter)).astype(np.float32)))
+
+
+def pin_mlp_brute_force(O):
+    """The layer's last two lines written out element by element (math.erf)."""
+    rng = _rng(41)
+    w_post, w_gate, w_up, w_down = _tiny_mlp(rng)
+    dec = lambda b: float(np.array([int(b) << 16], np.uint32).view(np.float32)[0])  # noqa: E731
+    hid, inter = w_gate.shape[1], w_gate.shape[0]
+    for b in range(2):
+        h = rng.standard_normal(hid)
+        ms = sum(v * v for v in h) / hid
+        x = [h[c] / math.sqrt(ms + 1e-6) * dec(w_post[c]) for c in range(hid)]
+        act = []
+        for i in range(inter):
+            g = sum(dec(w_gate[i, c]) * x[c] for c in range(hid))
+            u = sum(dec(w_up[i, c]) * x[c] for c in range(hid))
+            act.append(0.5 * g * (1.0 + math.erf(g / math.sqrt(2.0))) * u)
+        want = [h[r] + sum(dec(w_down[r, i]) * act[i] for i in range(inter)) for r in range(hid)]
+        got = O.mlp_decode(h, w_post, w_gate, w_up, w_down, 1e-6).h[0]
+        assert np.max(np.abs(got - np.array(want))) < 1e-11 * (1 + np.max(np.abs(want)))
+
+
+def pin_mlp_zero_gate_adds_nothing(O):
+    """gate_proj = 0 makes GELU(0) = 0, so the MLP leaves h exactly as it was."""
+    rng = _rng(42)
+    w_post, w_gate, w_up, w_down = _tiny_mlp(rng)
+    h = rng.standard_normal((3, w_gate.shape[1]))
+    r = O.mlp_decode(h, w_post, np.zeros_like(w_gate), w_up, w_down, 1e-6)
+    assert np.array_equal(r.h, h) and not r.out.any()
+
+
+def pin_decoder_stack_order(O):
+    """Whole layers: the MLP reads the stream after the attention's add, and the
+    stack is h0 plus every layer's contribution."""
+    arch = tiny_arch()
+    rng = _rng(43)
+    layers = []
+    for li in range(3):
+        w_qkv, w_g, w_o = _tiny_weights(arch, rng)
+        k, v = _cache(arch, rng, 8)
+        w_post, w_gate, w_up, w_down = _tiny_mlp(rng, hidden=arch.hidden, inter=24)
+        layers.append(SimpleNamespace(is_full=li == 2, w_norm=_bf16(1.0 + 0.1 * rng.standard_normal(
+            arch.hidden).astype(np.float32)), w_qkv=w_qkv, w_g=w_g, w_o=w_o,
+            cache=_seq(k, v, 0, 5), w_post=w_post, w_gate=w_gate, w_up=w_up, w_down=w_down))
+    h0 = rng.standard_normal((1, arch.hidden))
+    res = O.decoder_stack_decode(arch, h0, layers)
+    h = h0.copy()
+    for L in layers:
+        # attention block on the normed stream, raw add, then the MLP on the new stream
+        xn = h / np.sqrt(np.mean(h * h) + 1e-6) * O.bf16_bits_to_f64(L.w_norm)
+        a = O.block_decode(arch, L.is_full, L.w_qkv, L.w_g, L.w_o, xn, [L.cache]).out
+        h = h + a
+        h = O.mlp_decode(h, L.w_post, L.w_gate, L.w_up, L.w_down, 1e-6).h
+    assert np.max(np.abs(res.h - h)) < 1e-12 * (1 + np.max(np.abs(h)))
+    assert np.max(np.abs(h0 + sum(res.block_outs) - res.h)) < 1e-12 * (1 + np.max(np.abs(h)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

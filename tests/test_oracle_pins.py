@@ -65,6 +65,12 @@ MUTANTS = [
     ("chunk_cache_not_threaded", "        k, v = r.k_caches[0], r.v_caches[0]\n        outs.append",
      "        outs.append"),
     ("chunk_positions_frozen", "position=int(seq.position) + t)", "position=int(seq.position))"),
+    ("gelu_tanh_form", "0.5 * x * (1.0 + _erf(x / np.sqrt(2.0)))",
+     "0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))"),
+    ("gelu_on_up", "act = gelu_erf(gate) * up", "act = gelu_erf(up) * gate"),
+    ("mlp_no_residual", "return MlpResult(h=h + out,", "return MlpResult(h=out,"),
+    ("mlp_norm_skipped", "x = rms_norm(h, w_post_bits, eps)", "x = h"),
+    ("mlp_reads_stream_before_attention_add", "m = mlp_decode(h_mid,", "m = mlp_decode(h,"),
 ]
 
 
