@@ -157,33 +157,50 @@ def stack_bytes(st) -> int:
         c = synth.BlockCase(name="layer", arch=st.arch, is_full=L.is_full, w_qkv=L.w_qkv, w_g=L.w_g,
                             w_o=L.w_o, x=np.zeros((1, h), np.float32), seqs=[L.cache])
         total += block_bytes(c) + (4 * h * 2 + 2 * h) + 4 * h * 3
+        if hasattr(L, "w_gate"):
+            # the MLP: post-attention norm (h in, x out, bf16 w), gate/up (bf16
+            # weights, x in, two [inter] fp32 out), activation (2 in, 1 out),
+            # down (bf16 weights, act in) with the residual add (h in and out)
+            inter = int(L.w_gate.shape[0])
+            total += (4 * h * 2 + 2 * h) + (2 * 2 * inter * h + 4 * h + 2 * 4 * inter) \
+                + 3 * 4 * inter + (2 * h * inter + 4 * inter + 2 * 4 * h)
     return total
 
 
 def bench_stack(args):
-    """The 36-layer stack (RMSNorm -> block -> residual add per layer, no MLP,
-    each layer one gqa_attention_layer_decode call)
-    at position 8191: 9 full layers over 8192 rows, 27 sliding layers over a
-    wrapped 512-slot ring.  One step = one token through all 36 layers."""
+    """The 36-layer stack (RMSNorm -> block -> residual add per layer, each
+    layer one gqa_attention_layer_decode call) at position 8191: 9 full layers
+    over 8192 rows, 27 sliding layers over a wrapped 512-slot ring.  With
+    --workload decoder every layer also runs its MLP (gqa_mlp_decode:
+    post-attention norm, erf-GELU gated MLP with intermediate 3 x hidden,
+    residual add), i.e. a whole decode step.  One step = one token through
+    all 36 layers."""
     import numpy as np
     import torch
     import gqa_attention_block_amd as gqa
     import synth
-    st = synth.cfg4_stack()
+    mlp = args.workload == "decoder"
+    st = synth.decoder_stack() if mlp else synth.cfg4_stack()
     a = gqa.Arch(hidden=st.arch.hidden)
     up = lambda arr: torch.from_numpy(arr.view(np.int16) if arr.dtype == np.uint16 else arr).to("cuda:0")  # noqa: E731
     layers = [dict(w_norm=up(L.w_norm), w_qkv=up(L.w_qkv), w_g=up(L.w_g), w_o=up(L.w_o),
                    seq=gqa.KvSeq(k=up(L.cache.k), v=up(L.cache.v), position=L.cache.position,
-                                 ring_capacity=L.cache.ring_capacity), full=L.is_full)
+                                 ring_capacity=L.cache.ring_capacity), full=L.is_full,
+                   mlp=(up(L.w_post), up(L.w_gate), up(L.w_up), up(L.w_down)) if mlp else None)
               for L in st.layers]
     h0 = up(st.h)
     h = h0.clone()
     ws = torch.empty(gqa.workspace_size(a, 1, st.layers[0].cache.position + 1), dtype=torch.uint8,
                      device="cuda:0")
 
-    def step():   # one gqa_attention_layer_decode per layer: h += block(RMSNorm(h) * w)
+    ws_mlp = (torch.empty(gqa.mlp_workspace_size(a, int(st.layers[0].w_gate.shape[0]), 1), dtype=torch.uint8,
+                          device="cuda:0") if mlp else None)
+
+    def step():   # per layer: h += block(RMSNorm(h) * w) [, then h += mlp(h)]
         for L in layers:
             gqa.attention_layer_decode(a, L["w_norm"], L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], h, ws)
+            if mlp:
+                gqa.mlp_decode(a, *L["mlp"], h, ws_mlp)
 
     run = step
     if args.graph:
@@ -217,7 +234,7 @@ def bench_stack(args):
         # bounded sample: the fp64 oracle over the first layers, scaled to 36
         done, t0 = 0, time.perf_counter()
         while done < len(st.layers) and time.perf_counter() - t0 < args.cpu_seconds:
-            oracle.stack_decode(st.arch, st.h, st.layers[done:done + 1])
+            (oracle.decoder_stack_decode if mlp else oracle.stack_decode)(st.arch, st.h, st.layers[done:done + 1])
             done += 1
         el = time.perf_counter() - t0
         try:
@@ -305,7 +322,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="full32k", choices=sorted(list(workloads()) + ["cfg4", "chunk"]),
+    ap.add_argument("--workload", default="full32k", choices=sorted(list(workloads()) + ["cfg4", "chunk", "decoder"]),
                     help="cfg4 is the 36-layer stack at position 8191, chunk 32 tokens of one sequence "
                          "per call (neither has a dominant-kernel roofline)")
     ap.add_argument("--copies", type=int, default=0, help="weight/cache copies rotated (0: auto)")
@@ -334,7 +351,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    if args.workload == "cfg4":
+    if args.workload in ("cfg4", "decoder"):
         bench_stack(args)
         return
     if args.workload == "chunk":

@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     kv_slot,
     kv_window,
     library_path,
+    mlp_decode,
+    mlp_workspace_size,
     o_proj_gemv,
     qkv_rope_kv,
     residual_add,

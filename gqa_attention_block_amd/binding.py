@@ -42,6 +42,12 @@ class _Weights(ctypes.Structure):
                 ("o_proj", ctypes.c_void_p)]
 
 
+class _MlpWeights(ctypes.Structure):
+    _fields_ = [("post_attention_layernorm", ctypes.c_void_p), ("gate_proj", ctypes.c_void_p),
+                ("up_proj", ctypes.c_void_p), ("down_proj", ctypes.c_void_p),
+                ("intermediate", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class _KvSeq(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32),
                 ("ring_capacity", ctypes.c_int32), ("position", ctypes.c_int32),
@@ -72,6 +78,8 @@ def _load():
                                                   ctypes.POINTER(I32), ctypes.POINTER(I32), P]),
         "gqa_o_proj_gemv": (ctypes.c_int, [A, W, I32, P, P, P]),
         "gqa_rms_norm_bf16w": (ctypes.c_int, [P, P, P, I32, I32, F, P]),
+        "gqa_mlp_workspace_size": (ctypes.c_int, [A, I32, I32, ctypes.POINTER(S)]),
+        "gqa_mlp_decode": (ctypes.c_int, [A, ctypes.POINTER(_MlpWeights), I32, P, P, S, P]),
         "gqa_residual_add": (ctypes.c_int, [P, P, I64, P]),
         "gqa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "gqa_last_error": (ctypes.c_char_p, []),
@@ -91,7 +99,7 @@ EXPORTED_SYMBOLS = (
     "gqa_attention_block_decode", "gqa_attention_block_chunk", "gqa_attention_layer_decode", "gqa_qkv_rope_kv",
     "gqa_attention_gated",
     "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
-    "gqa_last_error",
+    "gqa_last_error", "gqa_mlp_workspace_size", "gqa_mlp_decode",
 )
 
 
@@ -277,6 +285,30 @@ def attention_layer_decode(arch: Arch, w_norm, w_qkv, w_g, w_o, is_full: bool, s
         _ptr(h, torch.float32, "h", b * arch.hidden),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
         "gqa_attention_layer_decode")
+
+
+def mlp_workspace_size(arch: Arch, intermediate: int, batch: int) -> int:
+    n = ctypes.c_size_t()
+    a = arch._c()
+    _check(_lib.gqa_mlp_workspace_size(ctypes.byref(a), intermediate, batch, ctypes.byref(n)),
+           "gqa_mlp_workspace_size")
+    return n.value
+
+
+def mlp_decode(arch: Arch, w_post, w_gate, w_up, w_down, h: torch.Tensor, workspace: torch.Tensor,
+               stream=None):
+    """h += down(gelu_erf(gate(x)) * up(x)), x = RMSNorm(h) * w_post, in place (the
+    rest of the decoder layer); w_gate and w_up are [inter, hidden], w_down
+    [hidden, inter], bf16 (or raw 16-bit bits)."""
+    b = h.shape[0] if h.dim() == 2 else 1
+    inter = int(w_gate.shape[0])
+    hd = arch.hidden
+    w = _MlpWeights(_wptr(w_post, "w_post", hd), _wptr(w_gate, "w_gate", inter * hd),
+                    _wptr(w_up, "w_up", inter * hd), _wptr(w_down, "w_down", hd * inter), inter, 0)
+    a = arch._c()
+    _check(_lib.gqa_mlp_decode(ctypes.byref(a), ctypes.byref(w), b, _ptr(h, torch.float32, "h", b * hd),
+                               _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                               _stream(stream)), "gqa_mlp_decode")
 
 
 def qkv_rope_kv(arch: Arch, w_qkv, w_g, is_full: bool, seqs: Sequence[KvSeq], x: torch.Tensor,

@@ -456,6 +456,59 @@ gqa_status run_attention_oproj(const gqa_arch *a, const gqa_layer_weights *w, co
   return e == hipSuccess ? GQA_OK : gpu_error(e, "combine + o_proj launch");
 }
 
+// y0 (= or +=) W0 x and y1 (= or +=) W1 x for `batch` rows of x [batch][cols]
+// (y0 [batch][rows0], y1 [batch][rows1]; w1 may be null): the MFMA kernel in
+// groups of up to 32 rows from kMfmaMinBatch rows on (a short last group on
+// the VALU GEMV), the VALU GEMV for smaller batches.
+gqa_status run_proj(const uint16_t *w0, int rows0, const uint16_t *w1, int rows1, int cols, int batch,
+                    const float *x, float *y0, float *y1, bool accumulate, hipStream_t stream, const char *what) {
+  const int group = batch >= kMfmaMinBatch ? 32 : batch;
+  for (int first = 0; first < batch; first += group) {
+    GemvParams p{};
+    p.w0 = w0;
+    p.rows0 = rows0;
+    p.w1 = w1;
+    p.rows1 = w1 ? rows1 : 0;
+    p.cols = cols;
+    p.batch = std::min(group, batch - first);
+    p.x = x + (size_t)first * cols;
+    p.ldx = cols;
+    p.y0 = y0 + (size_t)first * rows0;
+    p.ldy0 = rows0;
+    p.y1 = w1 ? y1 + (size_t)first * rows1 : nullptr;
+    p.ldy1 = rows1;
+    p.accumulate = accumulate ? 1 : 0;
+    hipError_t e = p.batch >= kMfmaMinBatch ? launch_proj_mfma(p, stream) : launch_gemv(p, stream);
+    if (e != hipSuccess) return gpu_error(e, what);
+  }
+  return GQA_OK;
+}
+
+// ---- the rest of the decoder layer: post-attention norm + gated MLP --------
+
+gqa_status check_mlp(const gqa_arch *a, const gqa_mlp_weights *w, int32_t batch) {
+  gqa_status st;
+  if ((st = check_arch(a)) != GQA_OK) return st;
+  if (!w) return fail(GQA_ERR_INVALID_ARGUMENT, "mlp weights is null");
+  if (w->reserved != 0) return fail(GQA_ERR_INVALID_ARGUMENT, "mlp weights reserved must be 0");
+  if (w->intermediate < 8 || w->intermediate % 8 != 0)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "intermediate=%d must be a positive multiple of 8", w->intermediate);
+  if (w->intermediate > kMaxHidden)
+    return fail(GQA_ERR_UNSUPPORTED, "intermediate=%d exceeds the supported %d", w->intermediate, kMaxHidden);
+  if (!(a->rms_eps >= 0.f) || !isfinite(a->rms_eps))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  if ((size_t)batch * std::max(a->hidden, w->intermediate) * sizeof(float) > kMaxBufferBytes)
+    return fail(GQA_ERR_UNSUPPORTED, "batch=%d makes an activation larger than %u bytes", batch, kMaxBufferBytes);
+  return GQA_OK;
+}
+
+// MLP workspace: [x fp32 [B][H] | gate [B][I] | up [B][I]]
+size_t mlp_bytes(const gqa_arch *a, int32_t inter, int32_t batch) {
+  return round_up((size_t)batch * a->hidden * sizeof(float), 256) +
+         2 * round_up((size_t)batch * inter * sizeof(float), 256);
+}
+
 // The block for resolved sequence descriptors (one per token or sequence):
 // pointers and the workspace size are checked here, then qkv -> attention ->
 // o_proj are enqueued.
@@ -808,6 +861,55 @@ gqa_status gqa_residual_add(float *h, const float *o, int64_t n, void *stream) {
   if ((st = check_ptr(o, "o")) != GQA_OK) return st;
   hipError_t e = launch_residual_add(h, o, n, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : gpu_error(e, "residual_add launch");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+gqa_status gqa_mlp_workspace_size(const gqa_arch *arch, int32_t intermediate, int32_t batch, size_t *bytes) {
+  if (!bytes) return fail(GQA_ERR_INVALID_ARGUMENT, "bytes is null");
+  gqa_mlp_weights w{};
+  w.intermediate = intermediate;
+  gqa_status st = check_mlp(arch, &w, batch);
+  if (st != GQA_OK) return st;
+  *bytes = mlp_bytes(arch, intermediate, batch);
+  return ok();
+}
+
+gqa_status gqa_mlp_decode(const gqa_arch *arch, const gqa_mlp_weights *weights, int32_t batch, float *h,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  gqa_status st;
+  if ((st = check_mlp(arch, weights, batch)) != GQA_OK) return st;
+  if (batch == 0) return ok();
+  if ((st = check_ptr(weights->post_attention_layernorm, "post_attention_layernorm")) != GQA_OK) return st;
+  if ((st = check_ptr(weights->gate_proj, "gate_proj")) != GQA_OK) return st;
+  if ((st = check_ptr(weights->up_proj, "up_proj")) != GQA_OK) return st;
+  if ((st = check_ptr(weights->down_proj, "down_proj")) != GQA_OK) return st;
+  if ((st = check_ptr(h, "h")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  const int H = arch->hidden, I = weights->intermediate;
+  const size_t need = mlp_bytes(arch, I, batch);
+  if (workspace_bytes < need)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the MLP needs %zu", workspace_bytes, need);
+  char *ws = static_cast<char *>(workspace);
+  float *x = reinterpret_cast<float *>(ws);
+  float *gate = reinterpret_cast<float *>(ws + round_up((size_t)batch * H * sizeof(float), 256));
+  float *up = reinterpret_cast<float *>(reinterpret_cast<char *>(gate) +
+                                        round_up((size_t)batch * I * sizeof(float), 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_rms_norm(h, static_cast<const uint16_t *>(weights->post_attention_layernorm), x, batch, H,
+                                 arch->rms_eps, s);
+  if (e != hipSuccess) return gpu_error(e, "post-attention RMSNorm launch");
+  if ((st = run_proj(static_cast<const uint16_t *>(weights->gate_proj), I,
+                     static_cast<const uint16_t *>(weights->up_proj), I, H, batch, x, gate, up, false, s,
+                     "gate/up projection launch")) != GQA_OK)
+    return st;
+  if ((e = launch_gelu_mul(gate, up, (int64_t)batch * I, s)) != hipSuccess) return gpu_error(e, "activation launch");
+  if ((st = run_proj(static_cast<const uint16_t *>(weights->down_proj), H, nullptr, 0, I, batch, gate, h, nullptr,
+                     true, s, "down projection launch")) != GQA_OK)
+    return st;
+  return ok();
 }
 
 }  // extern "C"

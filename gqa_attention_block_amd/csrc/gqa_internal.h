@@ -149,6 +149,7 @@ hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
+hipError_t launch_gelu_mul(float *gate, const float *up, int64_t n, hipStream_t stream);
 // One sequence, any number of chunks.
 hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream);
 // The merge + gate launch of launch_attention alone (partials already written).

@@ -1783,6 +1783,21 @@ hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// gate[i] <- gelu_erf(gate[i]) * up[i] for i < n ([mod] transcribed layer:
+// the erf GELU of the gate projection times the up projection).
+__global__ __launch_bounds__(kThreads) void gelu_mul_kernel(float *gate, const float *up, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+    const float g = gate[i];
+    gate[i] = 0.5f * g * (1.0f + erff(g * 0.70710678118654752f)) * up[i];
+  }
+}
+
+hipError_t launch_gelu_mul(float *gate, const float *up, int64_t n, hipStream_t stream) {
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + kThreads - 1) / kThreads, 2048));
+  hipLaunchKernelGGL(gelu_mul_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, gate, up, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream) {
   hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

@@ -288,6 +288,44 @@ gqa_status gqa_rms_norm_bf16w(const float *h, const void *w, float *out, int32_t
 gqa_status gqa_residual_add(float *h, const float *o, int64_t n, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * The rest of the decoder layer ([mod] module doc, the transcribed layer's
+ * last two lines): after the attention's residual add,
+ *   x = rms(h, post_attention_layernorm, rms_eps)   (plain w)
+ *   h = h + down_proj(gelu_erf(gate_proj x) * up_proj x)
+ * with the exact (erf) GELU, x * Phi(x).  The pages print no intermediate
+ * size; any multiple of 8 up to 8192 is taken.
+ * ------------------------------------------------------------------------- */
+
+typedef struct {
+  const void *post_attention_layernorm; /* bf16 [hidden] */
+  const void *gate_proj;                /* bf16 [intermediate][hidden], row-major */
+  const void *up_proj;                  /* bf16 [intermediate][hidden] */
+  const void *down_proj;                /* bf16 [hidden][intermediate] */
+  int32_t intermediate;
+  int32_t reserved;                     /* must be 0 */
+} gqa_mlp_weights;
+
+/* Workspace bytes gqa_mlp_decode needs for `batch` rows (x, gate and up
+ * projections, fp32).  Errors: as for gqa_mlp_decode's shape checks. */
+gqa_status gqa_mlp_workspace_size(const gqa_arch *arch, int32_t intermediate, int32_t batch,
+                                  size_t *bytes);
+
+/* h[b] += down_proj(gelu_erf(gate_proj x_b) * up_proj x_b), x_b the RMSNorm of
+ * h[b] with post_attention_layernorm and arch->rms_eps, for b < batch, in
+ * place.  h is device fp32 [batch][hidden]; the weights are device bf16 as
+ * above; workspace is device memory of at least gqa_mlp_workspace_size
+ * bytes, owned by the caller.  Four launches on `stream`: the norm, the gate
+ * and up projections (one launch), the activation, the down projection with
+ * the residual add in its epilogue.
+ * Errors: null or misaligned pointers, intermediate not a multiple of 8 or
+ * below 8, reserved != 0, rms_eps negative or not finite
+ * (INVALID_ARGUMENT); intermediate above 8192 (UNSUPPORTED); a workspace
+ * smaller than needed (WORKSPACE_TOO_SMALL); a launch failure (GPU).
+ * batch 0 is a no-op. */
+gqa_status gqa_mlp_decode(const gqa_arch *arch, const gqa_mlp_weights *weights, int32_t batch,
+                          float *h, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------- */
 const char *gqa_status_string(gqa_status status);

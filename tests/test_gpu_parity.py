@@ -591,6 +591,71 @@ def test_stack_of_fused_layers_matches_oracle(phase_full_first):
     assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "fused-layer stack residual delta")
 
 
+# ----------------------------------------------------------------------------
+# the rest of the decoder layer: post-attention norm + erf-GELU gated MLP
+# ----------------------------------------------------------------------------
+
+MLP_CASES = [(1024, 3072, 1), (1024, 3072, 3), (776, 1160, 2), (2560, 7680, 1), (2560, 7680, 5),
+             (2560, 7680, 32), (1024, 8192, 37)]
+
+
+@pytest.mark.parametrize("hidden,inter,batch", MLP_CASES, ids=[f"h{c[0]}_i{c[1]}_b{c[2]}" for c in MLP_CASES])
+def test_mlp_decode_matches_oracle(hidden, inter, batch):
+    """gqa_mlp_decode: h += down(gelu_erf(gate x) * up x), x = rms(h) w_post, on the
+    VALU GEMV (batch 1-3), the MFMA projections (4 and more, in groups of 32),
+    and a ragged shape; compared on the MLP's contribution h_out - h_in."""
+    say(f"mlp hidden={hidden} inter={inter} batch={batch}")
+    arch = synth.Arch(hidden=hidden)
+    m = synth.make_mlp(hidden, inter, 0, 60 + batch, 2000)
+    h0 = synth.random_hidden(hidden, batch, 0, 60 + batch, tensor_id=950)
+    a = arch_of(arch)
+    h = f32_to_dev(h0)
+    ws = torch.empty(gqa.mlp_workspace_size(a, inter, batch), dtype=torch.uint8, device="cuda")
+    gqa.mlp_decode(a, bits_to_dev(m.w_post), bits_to_dev(m.w_gate), bits_to_dev(m.w_up),
+                   bits_to_dev(m.w_down), h, ws)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_decode(h0, m.w_post, m.w_gate, m.w_up, m.w_down, arch.rms_eps)
+    got = h.cpu().numpy().astype(np.float64) - np.asarray(h0, np.float64)
+    for b in range(batch):
+        assert_parity(got[b], ref.out[b], f"mlp row {b} contribution")
+
+
+def test_mlp_batch_zero_is_a_no_op():
+    arch = synth.Arch(hidden=1024)
+    a = arch_of(arch)
+    h = torch.ones((0, 1024), dtype=torch.float32, device="cuda")
+    w = torch.zeros((8, 1024), dtype=torch.int16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    gqa.mlp_decode(a, torch.zeros(1024, dtype=torch.int16, device="cuda"), w, w,
+                   torch.zeros((1024, 8), dtype=torch.int16, device="cuda"), h, ws)
+
+
+@pytest.mark.parametrize("phase_full_first", [False, True])
+def test_decoder_stack_matches_oracle(phase_full_first):
+    """Whole decoder layers, batch 1: gqa_attention_layer_decode then
+    gqa_mlp_decode per layer, against the oracle's layer order."""
+    case = synth.decoder_stack(num_layers=4, position=1000, phase_full_first=phase_full_first)
+    say(f"decoder stack {case.name} phase_full_first={phase_full_first}")
+    a = arch_of(case.arch)
+    h = f32_to_dev(case.h)
+    inter = case.layers[0].w_gate.shape[0]
+    ws = torch.empty(gqa.workspace_size(a, 1, case.layers[0].cache.position + 1), dtype=torch.uint8,
+                     device="cuda")
+    ws_mlp = torch.empty(gqa.mlp_workspace_size(a, inter, 1), dtype=torch.uint8, device="cuda")
+    for L in case.layers:
+        k, v = f16_to_dev(L.cache.k), f16_to_dev(L.cache.v)
+        gqa.attention_layer_decode(a, bits_to_dev(L.w_norm), bits_to_dev(L.w_qkv), bits_to_dev(L.w_g),
+                                   bits_to_dev(L.w_o), L.is_full,
+                                   [gqa.KvSeq(k=k, v=v, position=L.cache.position,
+                                              ring_capacity=L.cache.ring_capacity)], h, ws)
+        gqa.mlp_decode(a, bits_to_dev(L.w_post), bits_to_dev(L.w_gate), bits_to_dev(L.w_up),
+                       bits_to_dev(L.w_down), h, ws_mlp)
+    torch.cuda.synchronize()
+    ref = oracle.decoder_stack_decode(case.arch, case.h, case.layers)
+    delta = h.cpu().numpy().astype(np.float64) - np.asarray(case.h, np.float64)
+    assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "decoder stack residual delta")
+
+
 def test_rms_norm_and_residual_add():
     say("rms_norm + residual_add")
     hidden, rows = 2560, 3

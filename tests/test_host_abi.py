@@ -266,3 +266,34 @@ def test_status_strings():
     assert B.status_string(0) == "GQA_OK"
     assert B.status_string(3) == "GQA_ERR_WORKSPACE_TOO_SMALL"
     assert B.status_string(99) == "GQA_ERR_UNKNOWN"
+
+
+def test_mlp_entry_validates():
+    """gqa_mlp_decode / gqa_mlp_workspace_size: every check before any launch."""
+    a = B.c_arch(gqa.Arch(hidden=1024))
+
+    def w(inter=3072, reserved=0, post=FAKE, gate=FAKE, up=FAKE, down=FAKE):
+        return B._MlpWeights(post, gate, up, down, inter, reserved)
+
+    def call(weights, batch=1, h=FAKE, ws=FAKE, nbytes=1 << 30, arch=a):
+        return B.raw_call("gqa_mlp_decode", ctypes.byref(arch), ctypes.byref(weights) if weights else None,
+                          batch, h, ws, nbytes, None)
+    assert call(None) == INVALID
+    assert call(w(inter=0)) == INVALID
+    assert call(w(inter=3070)) == INVALID
+    assert call(w(inter=8200)) == UNSUPPORTED
+    assert call(w(reserved=1)) == INVALID
+    assert call(w(post=0)) == INVALID
+    assert call(w(gate=MISALIGNED)) == INVALID
+    assert call(w(up=0)) == INVALID
+    assert call(w(down=MISALIGNED)) == INVALID
+    assert call(w(), h=MISALIGNED) == INVALID
+    assert call(w(), ws=0) == INVALID
+    assert call(w(), batch=-1) == INVALID
+    assert call(w(), nbytes=16) == WS_SMALL
+    assert call(w(), arch=B.c_arch(gqa.Arch(hidden=1024, rms_eps=-1.0))) == INVALID
+    assert call(w(), batch=0, h=0, ws=0) == OK                  # nothing to do
+    n = ctypes.c_size_t()
+    assert B.raw_call("gqa_mlp_workspace_size", ctypes.byref(a), 3072, 2, ctypes.byref(n)) == OK
+    assert n.value >= (2 * 1024 + 2 * 2 * 3072) * 4
+    assert B.raw_call("gqa_mlp_workspace_size", ctypes.byref(a), 3072, 2, None) == INVALID
