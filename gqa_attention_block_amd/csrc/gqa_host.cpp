@@ -898,8 +898,27 @@ gqa_status gqa_mlp_decode(const gqa_arch *arch, const gqa_mlp_weights *weights, 
   float *up = reinterpret_cast<float *>(reinterpret_cast<char *>(gate) +
                                         round_up((size_t)batch * I * sizeof(float), 256));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_rms_norm(h, static_cast<const uint16_t *>(weights->post_attention_layernorm), x, batch, H,
-                                 arch->rms_eps, s);
+  hipError_t e;
+  if (batch < kMfmaMinBatch) {
+    // norm, gate and up projections and the activation in one launch, then the
+    // down projection with the residual add
+    MlpParams mp{};
+    mp.w_post = static_cast<const uint16_t *>(weights->post_attention_layernorm);
+    mp.w_gate = static_cast<const uint16_t *>(weights->gate_proj);
+    mp.w_up = static_cast<const uint16_t *>(weights->up_proj);
+    mp.h = h;
+    mp.act = gate;
+    mp.hidden = H;
+    mp.inter = I;
+    mp.batch = batch;
+    mp.eps = arch->rms_eps;
+    if ((e = launch_mlp_gate_up(mp, s)) != hipSuccess) return gpu_error(e, "norm + gate/up + activation launch");
+    st = run_proj(static_cast<const uint16_t *>(weights->down_proj), H, nullptr, 0, I, batch, gate, h, nullptr, true,
+                  s, "down projection launch");
+    return st == GQA_OK ? ok() : st;
+  }
+  e = launch_rms_norm(h, static_cast<const uint16_t *>(weights->post_attention_layernorm), x, batch, H,
+                      arch->rms_eps, s);
   if (e != hipSuccess) return gpu_error(e, "post-attention RMSNorm launch");
   if ((st = run_proj(static_cast<const uint16_t *>(weights->gate_proj), I,
                      static_cast<const uint16_t *>(weights->up_proj), I, H, batch, x, gate, up, false, s,

@@ -128,6 +128,20 @@ struct QkvParams {
   SeqDesc seq[kMaxSeqPerLaunch];
 };
 
+// The MLP's first half for small batches: act[b][i] = gelu_erf(g) * u with
+// g = gate_i . x_b, u = up_i . x_b, x_b = rms(h_b) * w_post.
+struct MlpParams {
+  const uint16_t *w_post;  // bf16 [hidden]
+  const uint16_t *w_gate;  // bf16 [inter][hidden]
+  const uint16_t *w_up;    // bf16 [inter][hidden]
+  const float *h;          // [batch][hidden] residual stream
+  float *act;              // [batch][inter]
+  int hidden;
+  int inter;
+  int batch;
+  float eps;
+};
+
 struct GemvParams {
   const uint16_t *w0; // bf16 [rows0][cols]
   const uint16_t *w1; // bf16 [rows1][cols], rows appended after w0's
@@ -150,6 +164,7 @@ hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
 hipError_t launch_gelu_mul(float *gate, const float *up, int64_t n, hipStream_t stream);
+hipError_t launch_mlp_gate_up(const MlpParams &p, hipStream_t stream);
 // One sequence, any number of chunks.
 hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream);
 // The merge + gate launch of launch_attention alone (partials already written).

@@ -1792,6 +1792,99 @@ __global__ __launch_bounds__(kThreads) void gelu_mul_kernel(float *gate, const f
   }
 }
 
+// The MLP's first half for batch 1-3 ([mod] transcribed layer): x = rms(h) *
+// w_post is staged in LDS (the sum of squares comes from the staging loads,
+// summed over the workgroup), and wave i computes gate_i . x and up_i . x for
+// every batch row, so it can write act[b][i] = gelu_erf(g) * u itself: the
+// norm, both projections and the activation in one launch.  Weight loads are
+// issued before the first FMA, as in gemv_bf16_kernel.
+template <int NIT, int RB, bool ONE>
+__global__ __launch_bounds__(kThreads) void mlp_gate_up_kernel(const MlpParams p) {
+  __shared__ float4 s_x[RB][2][StagedX<NIT>::kSlots];
+  __shared__ float s_ss[RB][kThreads / 64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * (kThreads / 64) + wv;   // intermediate index of this wave
+  const unsigned row_bytes = (unsigned)p.hidden * 2u;
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.w_gate, (unsigned)p.inter * row_bytes);
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.w_up, (unsigned)p.inter * row_bytes);
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(p.w_post, row_bytes);
+  auto hrow = [&](int b) {
+    return make_rsrc(p.h + (size_t)b * p.hidden, b < p.batch ? (unsigned)p.hidden * 4u : 0u);
+  };
+  StagedX<NIT> xs[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) xs[r].template issue<true>(hrow(r), 0u, rn);
+  uint4 wg[NIT], wu[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int col = (it * 64 + lane) * 8;
+    const unsigned off = (i < p.inter && col < p.hidden) ? (unsigned)i * row_bytes + (unsigned)col * 2u : kOutOfRange;
+    wg[it] = buf_load16_p<kWeightPolicy>(rg, off);
+    wu[it] = buf_load16_p<kWeightPolicy>(ru, off);
+  }
+  auto emit = [&](int m, int b) {
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      g = dot8_bf16(wg[it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], g);
+      u = dot8_bf16(wu[it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], u);
+    }
+    const float inv = rsqrtf((s_ss[m][0] + s_ss[m][1] + s_ss[m][2] + s_ss[m][3]) / (float)p.hidden + p.eps);
+    g = wave_sum(g) * inv;
+    u = wave_sum(u) * inv;
+    if (lane == 0 && i < p.inter && b < p.batch)
+      p.act[(size_t)b * p.inter + i] = 0.5f * g * (1.0f + erff(g * 0.70710678118654752f)) * u;
+  };
+  if constexpr (ONE) {
+    const float ss = wave_sum(xs[0].template store<true>(s_x[0]));
+    if (lane == 0) s_ss[0][wv] = ss;
+    __syncthreads();
+    emit(0, 0);
+  } else {
+    for (int b0 = 0; b0 < p.batch; b0 += RB) {
+#pragma unroll
+      for (int m = 0; m < RB; ++m) {
+        const float ss = wave_sum(xs[m].template store<true>(s_x[m]));
+        if (lane == 0) s_ss[m][wv] = ss;
+        xs[m].template issue<true>(hrow(b0 + RB + m), 0u, rn);   // next rows, unconditional
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < RB; ++m) emit(m, b0 + m);
+      if (b0 + RB < p.batch) __syncthreads();   // s_x and s_ss are rewritten for the next rows
+    }
+  }
+}
+
+template <int NIT>
+hipError_t mlp_gate_up_nit(const MlpParams &p, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.inter + 3) / 4));
+  if (p.batch == 1)
+    hipLaunchKernelGGL((mlp_gate_up_kernel<NIT, 1, true>), grid, dim3(kThreads), 0, stream, p);
+  else if constexpr (NIT <= 8)
+    hipLaunchKernelGGL((mlp_gate_up_kernel<NIT, 2, false>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((mlp_gate_up_kernel<NIT, 1, false>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mlp_gate_up(const MlpParams &p, hipStream_t stream) {
+  switch ((p.hidden + 511) / 512) {
+    case 1: return mlp_gate_up_nit<1>(p, stream);
+    case 2: return mlp_gate_up_nit<2>(p, stream);
+    case 3: return mlp_gate_up_nit<3>(p, stream);
+    case 4: return mlp_gate_up_nit<4>(p, stream);
+    case 5: return mlp_gate_up_nit<5>(p, stream);
+    case 6: return mlp_gate_up_nit<6>(p, stream);
+    case 7: return mlp_gate_up_nit<7>(p, stream);
+    case 8: return mlp_gate_up_nit<8>(p, stream);
+    case 9: case 10: return mlp_gate_up_nit<10>(p, stream);
+    case 11: case 12: return mlp_gate_up_nit<12>(p, stream);
+    default: return mlp_gate_up_nit<16>(p, stream);
+  }
+}
+
 hipError_t launch_gelu_mul(float *gate, const float *up, int64_t n, hipStream_t stream) {
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + kThreads - 1) / kThreads, 2048));
   hipLaunchKernelGGL(gelu_mul_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, gate, up, n);

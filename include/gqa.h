@@ -314,9 +314,10 @@ gqa_status gqa_mlp_workspace_size(const gqa_arch *arch, int32_t intermediate, in
  * h[b] with post_attention_layernorm and arch->rms_eps, for b < batch, in
  * place.  h is device fp32 [batch][hidden]; the weights are device bf16 as
  * above; workspace is device memory of at least gqa_mlp_workspace_size
- * bytes, owned by the caller.  Four launches on `stream`: the norm, the gate
- * and up projections (one launch), the activation, the down projection with
- * the residual add in its epilogue.
+ * bytes, owned by the caller.  Below batch 4 two launches on `stream`: the
+ * norm, both projections and the activation in one, then the down projection
+ * with the residual add in its epilogue; from batch 4 (matrix cores) four:
+ * the norm, the gate and up projections, the activation, the down projection.
  * Errors: null or misaligned pointers, intermediate not a multiple of 8 or
  * below 8, reserved != 0, rms_eps negative or not finite
  * (INVALID_ARGUMENT); intermediate above 8192 (UNSUPPORTED); a workspace
