@@ -19,11 +19,13 @@ from .block import (  # noqa: F401
     block_chunk,
     block_decode,
     decoder_stack_decode,
+    embed_gather,
     gelu_erf,
     gemv,
     head_gate,
     kv_slot,
     kv_window,
+    lm_head,
     mlp_decode,
     physical_rows,
     rms_norm,

@@ -419,3 +419,22 @@ def decoder_stack_decode(arch, h0: np.ndarray, layers: Sequence) -> StackResult:
         normed.append(xn)
         h = m.h
     return StackResult(h=h, block_outs=outs, normed=normed)
+
+
+# ----------------------------------------------------------------------------
+# the ends of the decode step  [mod: `produce_real_spark_inner` -- the token's
+#   embedding row is used raw (no sqrt(hidden) scale, no embedding norm); after
+#   the last layer the final RMSNorm (model.norm, plain w) and the TIED head,
+#   logits = x @ embed_tokens^T, raw logits; vocab is not on the pages
+#   (reading O22: synthetic)]
+# ----------------------------------------------------------------------------
+
+def embed_gather(e_bits: np.ndarray, ids) -> np.ndarray:
+    """h[b] = embed_tokens[ids[b]], the bf16 row as it is."""
+    return bf16_bits_to_f64(np.asarray(e_bits)[np.asarray(ids, dtype=np.int64)])
+
+
+def lm_head(h: np.ndarray, w_final_bits: np.ndarray, e_bits: np.ndarray, eps: float) -> np.ndarray:
+    """logits[b] = rms(h[b], model.norm) @ embed_tokens^T  [vocab per row]."""
+    x = rms_norm(h, w_final_bits, eps)
+    return gemv(bf16_bits_to_f64(e_bits), x)

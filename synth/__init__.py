@@ -365,3 +365,33 @@ def decoder_stack(seed: int = 0, num_layers: int = 36, position: int = 8191, hid
                                    w_up=m.w_up, w_down=m.w_down))
     return StackCase(name=f"decoder_stack{num_layers}_pos{position}_inter{inter}",
                      arch=base_case.arch, h=base_case.h, layers=layers)
+
+
+# ----------------------------------------------------------------------------
+# the ends of the decode step (embedding / tied head); the pages print no
+# vocabulary size, so it is a parameter here (65536 in the benchmark)
+# ----------------------------------------------------------------------------
+
+_T_EMBED, _T_WFINAL, _T_IDS = 7001, 7002, 7003
+
+
+@dataclass
+class HeadCase:
+    embed: np.ndarray      # uint16 bf16 bits [vocab][hidden] (embed_tokens, tied head)
+    w_final: np.ndarray    # uint16 bf16 bits [hidden] (model.norm)
+    ids: np.ndarray        # int32 [batch] token ids
+    h: np.ndarray          # float32 [batch][hidden] residual stream after the last layer
+
+    @property
+    def vocab(self) -> int:
+        return int(self.embed.shape[0])
+
+
+def head_case(hidden: int, vocab: int, batch: int, seed: int = 0, case_id: int = 70) -> HeadCase:
+    """Embedding ~ N(0, 0.02), final norm weight ~ N(1, 0.1), ids uniform in
+    [0, vocab), h ~ N(0, 1)."""
+    ids = _rng(seed, case_id, _T_IDS).integers(0, vocab, size=batch).astype(np.int32)
+    return HeadCase(
+        embed=round_to_bf16_bits(_normal(seed, case_id, _T_EMBED, (vocab, hidden), WEIGHT_STD)),
+        w_final=round_to_bf16_bits(_normal(seed, case_id, _T_WFINAL, (hidden,), 0.1, 1.0)),
+        ids=ids, h=_normal(seed, case_id, _T_H, (batch, hidden)))

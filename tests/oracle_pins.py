@@ -628,4 +628,50 @@ def pin_decoder_stack_order(O):
     assert np.max(np.abs(h0 + sum(res.block_outs) - res.h)) < 1e-12 * (1 + np.max(np.abs(h)))
 
 
+# ----------------------------------------------------------------------------
+# the ends of the decode step: raw embedding row, final norm, tied head
+# ----------------------------------------------------------------------------
+
+def pin_embed_is_the_raw_row(O):
+    """The embedding row is used as stored: no sqrt(hidden) scale, no norm
+    (the bf16 value decoded through struct, independently of the oracle)."""
+    import struct
+    rng = _rng(51)
+    e = _bf16(rng.standard_normal((10, 16)).astype(np.float32))
+    ids = [3, 0, 9, 3]
+    got = O.embed_gather(e, ids)
+    for b, t in enumerate(ids):
+        want = [struct.unpack("<f", struct.pack("<I", int(v) << 16))[0] for v in e[t]]
+        assert np.array_equal(got[b], np.array(want))
+
+
+def pin_lm_head_one_hot_closed_form(O):
+    """h = e_k: mean(h^2) = 1/H, so logits_j = E[j][k] * w_k / sqrt(1/H + eps)."""
+    rng = _rng(52)
+    hid, vocab, eps = 16, 24, 1e-6
+    e = _bf16(rng.standard_normal((vocab, hid)).astype(np.float32))
+    w = _bf16(1.0 + 0.1 * rng.standard_normal(hid).astype(np.float32))
+    ev, wv = O.bf16_bits_to_f64(e), O.bf16_bits_to_f64(w)
+    for k in (0, 5, 15):
+        h = np.zeros((1, hid))
+        h[0, k] = 1.0
+        want = ev[:, k] * wv[k] / math.sqrt(1.0 / hid + eps)
+        assert np.max(np.abs(O.lm_head(h, w, e, eps)[0] - want)) < 1e-12
+
+
+def pin_lm_head_brute_force(O):
+    rng = _rng(53)
+    hid, vocab = 8, 11
+    e = _bf16(rng.standard_normal((vocab, hid)).astype(np.float32))
+    w = _bf16(1.0 + 0.1 * rng.standard_normal(hid).astype(np.float32))
+    dec = lambda b: float(np.array([int(b) << 16], np.uint32).view(np.float32)[0])  # noqa: E731
+    h = rng.standard_normal((2, hid))
+    got = O.lm_head(h, w, e, 1e-6)
+    for b in range(2):
+        r = math.sqrt(sum(v * v for v in h[b]) / hid + 1e-6)
+        for j in range(vocab):
+            want = sum(dec(e[j, c]) * h[b, c] / r * dec(w[c]) for c in range(hid))
+            assert abs(got[b, j] - want) < 1e-12 * (1 + abs(want))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

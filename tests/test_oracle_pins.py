@@ -71,6 +71,10 @@ MUTANTS = [
     ("mlp_no_residual", "return MlpResult(h=h + out,", "return MlpResult(h=out,"),
     ("mlp_norm_skipped", "x = rms_norm(h, w_post_bits, eps)", "x = h"),
     ("mlp_reads_stream_before_attention_add", "m = mlp_decode(h_mid,", "m = mlp_decode(h,"),
+    ("embedding_scaled", "return bf16_bits_to_f64(np.asarray(e_bits)[np.asarray(ids, dtype=np.int64)])",
+     "return bf16_bits_to_f64(np.asarray(e_bits)[np.asarray(ids, dtype=np.int64)]) * np.sqrt(np.asarray(e_bits).shape[1])"),
+    ("head_without_final_norm", "x = rms_norm(h, w_final_bits, eps)\n    return gemv",
+     "x = np.atleast_2d(np.asarray(h, dtype=np.float64))\n    return gemv"),
 ]
 
 
