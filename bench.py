@@ -261,6 +261,51 @@ def bench_stack(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_head(args):
+    """The ends of the decode step, batch 1: the embedding gather of the next
+    token and the final RMSNorm + tied head over a 65536-token table at hidden
+    2560 (the pages print no vocabulary size).  One step = gather + head."""
+    import torch
+    import gqa_attention_block_amd as gqa
+    import synth
+    hid, vocab = 2560, 65536
+    hc = synth.head_case(hid, vocab, 1)
+    a = gqa.Arch(hidden=hid)
+    up = lambda arr: torch.from_numpy(arr.view("int16") if arr.dtype.name == "uint16" else arr).to("cuda:0")  # noqa: E731
+    table, w_final, h = up(hc.embed), up(hc.w_final), up(hc.h)
+    he = torch.empty_like(h)
+    logits = torch.empty((1, vocab), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(gqa.lm_head_workspace_size(a, 1), dtype=torch.uint8, device="cuda:0")
+    ids = [int(hc.ids[0])]
+
+    def step():
+        gqa.embed_tokens(a, table, ids, he)
+        gqa.lm_head(a, w_final, table, h, logits, ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    alg = 2 * vocab * hid + 2 * hid + 4 * hid + (4 * hid * 2 + 2 * hid) + 4 * hid + 4 * vocab
+    log(f"head (gather + final norm + tied head, vocab {vocab}): {ms * 1e3:.2f} us/token, "
+        f"{alg / 1e6:.1f} MB -> {alg / (ms * 1e-3) / 1e9:.1f} GB/s")
+    line = {
+        "metric": METRIC, "value": round(1e3 / ms, 3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"head_h{hid}_vocab{vocab}", "hidden": hid, "vocab": vocab, "batch": 1,
+                   "weights": "bf16", "algorithmic_bytes_per_step": alg},
+        "block_hbm_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+        "block_frac_of_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_chunk(args):
     """Several tokens of one sequence per call (gqa_attention_block_chunk): a
     full layer, hidden 2560, 32 tokens at positions 4096 .. 4127 (a chunk of
@@ -322,7 +367,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="full32k", choices=sorted(list(workloads()) + ["cfg4", "chunk", "decoder"]),
+    ap.add_argument("--workload", default="full32k", choices=sorted(list(workloads()) + ["cfg4", "chunk", "decoder", "head"]),
                     help="cfg4 is the 36-layer stack at position 8191, chunk 32 tokens of one sequence "
                          "per call (neither has a dominant-kernel roofline)")
     ap.add_argument("--copies", type=int, default=0, help="weight/cache copies rotated (0: auto)")
@@ -353,6 +398,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload in ("cfg4", "decoder"):
         bench_stack(args)
+        return
+    if args.workload == "head":
+        bench_head(args)
         return
     if args.workload == "chunk":
         bench_chunk(args)

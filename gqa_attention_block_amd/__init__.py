@@ -14,9 +14,12 @@ from .binding import (  # noqa: F401
     attention_gated,
     attention_layer_decode,
     attention_partials,
+    embed_tokens,
     kv_slot,
     kv_window,
     library_path,
+    lm_head,
+    lm_head_workspace_size,
     mlp_decode,
     mlp_workspace_size,
     o_proj_gemv,

@@ -80,6 +80,9 @@ def _load():
         "gqa_rms_norm_bf16w": (ctypes.c_int, [P, P, P, I32, I32, F, P]),
         "gqa_mlp_workspace_size": (ctypes.c_int, [A, I32, I32, ctypes.POINTER(S)]),
         "gqa_mlp_decode": (ctypes.c_int, [A, ctypes.POINTER(_MlpWeights), I32, P, P, S, P]),
+        "gqa_embed_tokens": (ctypes.c_int, [A, P, I32, ctypes.POINTER(I32), I32, P, P]),
+        "gqa_lm_head_workspace_size": (ctypes.c_int, [A, I32, ctypes.POINTER(S)]),
+        "gqa_lm_head": (ctypes.c_int, [A, P, P, I32, P, I32, P, P, S, P]),
         "gqa_residual_add": (ctypes.c_int, [P, P, I64, P]),
         "gqa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "gqa_last_error": (ctypes.c_char_p, []),
@@ -99,7 +102,8 @@ EXPORTED_SYMBOLS = (
     "gqa_attention_block_decode", "gqa_attention_block_chunk", "gqa_attention_layer_decode", "gqa_qkv_rope_kv",
     "gqa_attention_gated",
     "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
-    "gqa_last_error", "gqa_mlp_workspace_size", "gqa_mlp_decode",
+    "gqa_last_error", "gqa_mlp_workspace_size", "gqa_mlp_decode", "gqa_embed_tokens", "gqa_lm_head_workspace_size",
+    "gqa_lm_head",
 )
 
 
@@ -309,6 +313,39 @@ def mlp_decode(arch: Arch, w_post, w_gate, w_up, w_down, h: torch.Tensor, worksp
     _check(_lib.gqa_mlp_decode(ctypes.byref(a), ctypes.byref(w), b, _ptr(h, torch.float32, "h", b * hd),
                                _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                _stream(stream)), "gqa_mlp_decode")
+
+
+def embed_tokens(arch: Arch, table, ids: Sequence[int], h: torch.Tensor, stream=None):
+    """h[b] = table[ids[b]] as fp32 (the raw bf16 row); table [vocab, hidden]."""
+    b = len(ids)
+    vocab = int(table.shape[0])
+    a = arch._c()
+    arr = (ctypes.c_int32 * max(1, b))(*[int(i) for i in ids])
+    _check(_lib.gqa_embed_tokens(ctypes.byref(a), _wptr(table, "embed_tokens", vocab * arch.hidden), vocab, arr, b,
+                                 _ptr(h, torch.float32, "h", b * arch.hidden), _stream(stream)),
+           "gqa_embed_tokens")
+
+
+def lm_head_workspace_size(arch: Arch, batch: int) -> int:
+    n = ctypes.c_size_t()
+    a = arch._c()
+    _check(_lib.gqa_lm_head_workspace_size(ctypes.byref(a), batch, ctypes.byref(n)), "gqa_lm_head_workspace_size")
+    return n.value
+
+
+def lm_head(arch: Arch, final_norm, table, h: torch.Tensor, logits: torch.Tensor, workspace: torch.Tensor,
+            stream=None):
+    """logits = RMSNorm(h) * final_norm @ table^T (the tied head); h [batch,
+    hidden], logits [batch, vocab], fp32."""
+    b = h.shape[0]
+    vocab = int(table.shape[0])
+    a = arch._c()
+    _check(_lib.gqa_lm_head(ctypes.byref(a), _wptr(final_norm, "final_norm", arch.hidden),
+                            _wptr(table, "embed_tokens", vocab * arch.hidden), vocab,
+                            _ptr(h, torch.float32, "h", b * arch.hidden), b,
+                            _ptr(logits, torch.float32, "logits", b * vocab),
+                            _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+           "gqa_lm_head")
 
 
 def qkv_rope_kv(arch: Arch, w_qkv, w_g, is_full: bool, seqs: Sequence[KvSeq], x: torch.Tensor,

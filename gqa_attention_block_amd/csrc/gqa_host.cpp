@@ -932,3 +932,86 @@ gqa_status gqa_mlp_decode(const gqa_arch *arch, const gqa_mlp_weights *weights, 
 }
 
 }  // extern "C"
+
+// ---- the ends of the decode step: embedding gather, final norm + tied head --
+
+namespace gqa {
+namespace {
+gqa_status check_table(const gqa_arch *a, const void *table, int32_t vocab) {
+  gqa_status st;
+  if ((st = check_arch(a)) != GQA_OK) return st;
+  if ((st = check_ptr(table, "embed_tokens")) != GQA_OK) return st;
+  if (vocab < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "vocab=%d must be >= 1", vocab);
+  if ((size_t)vocab * a->hidden * 2u > kMaxBufferBytes)
+    return fail(GQA_ERR_UNSUPPORTED, "a %d x %d bf16 table exceeds %u bytes", vocab, a->hidden, kMaxBufferBytes);
+  return GQA_OK;
+}
+}  // namespace
+}  // namespace gqa
+
+extern "C" {
+
+gqa_status gqa_embed_tokens(const gqa_arch *arch, const void *embed_tokens, int32_t vocab, const int32_t *ids,
+                            int32_t batch, float *h, void *stream) {
+  gqa_status st;
+  if ((st = check_table(arch, embed_tokens, vocab)) != GQA_OK) return st;
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  if (batch == 0) return ok();
+  if (!ids) return fail(GQA_ERR_INVALID_ARGUMENT, "ids is null");
+  for (int32_t b = 0; b < batch; ++b)
+    if (ids[b] < 0 || ids[b] >= vocab)
+      return fail(GQA_ERR_INVALID_ARGUMENT, "ids[%d]=%d is outside [0, %d)", b, ids[b], vocab);
+  if ((st = check_ptr(h, "h")) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  for (int32_t first = 0; first < batch; first += kMaxEmbedIds) {
+    EmbedParams p{};
+    p.table = static_cast<const uint16_t *>(embed_tokens);
+    p.h = h + (size_t)first * arch->hidden;
+    p.hidden = arch->hidden;
+    p.count = std::min<int32_t>(kMaxEmbedIds, batch - first);
+    for (int i = 0; i < p.count; ++i) p.ids[i] = ids[first + i];
+    hipError_t e = launch_embed_gather(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return gpu_error(e, "embedding gather launch");
+  }
+  return ok();
+}
+
+gqa_status gqa_lm_head_workspace_size(const gqa_arch *arch, int32_t batch, size_t *bytes) {
+  if (!bytes) return fail(GQA_ERR_INVALID_ARGUMENT, "bytes is null");
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  *bytes = round_up((size_t)batch * arch->hidden * sizeof(float), 256);
+  return ok();
+}
+
+gqa_status gqa_lm_head(const gqa_arch *arch, const void *final_norm, const void *embed_tokens, int32_t vocab,
+                       const float *h, int32_t batch, float *logits, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  gqa_status st;
+  if ((st = check_table(arch, embed_tokens, vocab)) != GQA_OK) return st;
+  if (!(arch->rms_eps >= 0.f) || !isfinite(arch->rms_eps))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  if (batch == 0) return ok();
+  if ((st = check_ptr(final_norm, "final_norm")) != GQA_OK) return st;
+  if ((st = check_ptr(h, "h")) != GQA_OK) return st;
+  if ((st = check_ptr(logits, "logits")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  if ((size_t)batch * vocab * sizeof(float) > kMaxBufferBytes)
+    return fail(GQA_ERR_UNSUPPORTED, "batch=%d x vocab=%d logits exceed %u bytes", batch, vocab, kMaxBufferBytes);
+  const size_t need = round_up((size_t)batch * arch->hidden * sizeof(float), 256);
+  if (workspace_bytes < need)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the head needs %zu", workspace_bytes, need);
+  float *x = static_cast<float *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_rms_norm(h, static_cast<const uint16_t *>(final_norm), x, batch, arch->hidden, arch->rms_eps, s);
+  if (e != hipSuccess) return gpu_error(e, "final RMSNorm launch");
+  st = run_proj(static_cast<const uint16_t *>(embed_tokens), vocab, nullptr, 0, arch->hidden, batch, x, logits,
+                nullptr, false, s, "tied head launch");
+  return st == GQA_OK ? ok() : st;
+}
+
+}  // extern "C"
+

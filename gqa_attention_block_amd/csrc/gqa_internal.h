@@ -128,6 +128,17 @@ struct QkvParams {
   SeqDesc seq[kMaxSeqPerLaunch];
 };
 
+// The embedding gather: h[b] = table[ids[b]] (bf16 row -> fp32), up to
+// kMaxEmbedIds tokens per launch; ids are checked on the host.
+constexpr int kMaxEmbedIds = 64;
+struct EmbedParams {
+  const uint16_t *table;  // bf16 [vocab][hidden]
+  float *h;               // [count][hidden]
+  int hidden;             // a multiple of 8
+  int count;
+  int ids[kMaxEmbedIds];
+};
+
 // The MLP's first half for small batches: act[b][i] = gelu_erf(g) * u with
 // g = gate_i . x_b, u = up_i . x_b, x_b = rms(h_b) * w_post.
 struct MlpParams {
@@ -165,6 +176,7 @@ hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stre
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
 hipError_t launch_gelu_mul(float *gate, const float *up, int64_t n, hipStream_t stream);
 hipError_t launch_mlp_gate_up(const MlpParams &p, hipStream_t stream);
+hipError_t launch_embed_gather(const EmbedParams &p, hipStream_t stream);
 // One sequence, any number of chunks.
 hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream);
 // The merge + gate launch of launch_attention alone (partials already written).

@@ -327,6 +327,38 @@ gqa_status gqa_mlp_decode(const gqa_arch *arch, const gqa_mlp_weights *weights, 
                           float *h, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * The ends of the decode step ([mod] `produce_real_spark_inner`): the token's
+ * embedding row enters the stack raw (no sqrt(hidden) scale, no norm); after
+ * the last layer the final RMSNorm (model.norm, plain w) and the TIED head,
+ * logits = x @ embed_tokens^T (raw logits, fp32 here).  The pages print no
+ * vocabulary size.
+ * ------------------------------------------------------------------------- */
+
+/* h[b] = embed_tokens[ids[b]] as fp32, b < batch.
+ *   embed_tokens device bf16 [vocab][hidden]; ids HOST int32 [batch], each in
+ *   [0, vocab); h device fp32 [batch][hidden].
+ * Errors: null or misaligned pointers, vocab < 1, an id out of range
+ * (INVALID_ARGUMENT); vocab * hidden * 2 >= 2^31 (UNSUPPORTED).  batch 0 is a
+ * no-op. */
+gqa_status gqa_embed_tokens(const gqa_arch *arch, const void *embed_tokens, int32_t vocab,
+                            const int32_t *ids, int32_t batch, float *h, void *stream);
+
+/* Workspace bytes of gqa_lm_head for `batch` rows (the normed x, fp32). */
+gqa_status gqa_lm_head_workspace_size(const gqa_arch *arch, int32_t batch, size_t *bytes);
+
+/* logits[b] = rms(h[b], final_norm, arch->rms_eps) @ embed_tokens^T.
+ *   final_norm device bf16 [hidden]; embed_tokens device bf16 [vocab][hidden];
+ *   h device fp32 [batch][hidden] (read only); logits device fp32
+ *   [batch][vocab]; workspace device, caller-owned.  Two launches: the norm,
+ *   the head GEMV (VALU below batch 4, matrix cores from 4).
+ * Errors: as gqa_embed_tokens for the table, null or misaligned pointers,
+ * rms_eps negative or not finite (INVALID_ARGUMENT), a small workspace
+ * (WORKSPACE_TOO_SMALL), launch failures (GPU). */
+gqa_status gqa_lm_head(const gqa_arch *arch, const void *final_norm, const void *embed_tokens,
+                       int32_t vocab, const float *h, int32_t batch, float *logits, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------- */
 const char *gqa_status_string(gqa_status status);

@@ -656,6 +656,38 @@ def test_decoder_stack_matches_oracle(phase_full_first):
     assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "decoder stack residual delta")
 
 
+# ----------------------------------------------------------------------------
+# the ends of the decode step: embedding gather (bit-exact), final norm + tied head
+# ----------------------------------------------------------------------------
+
+HEAD_CASES = [(1024, 1000, 1), (1024, 1000, 3), (2560, 32768, 1), (2560, 65536, 5), (776, 4099, 70)]
+
+
+@pytest.mark.parametrize("hidden,vocab,batch", HEAD_CASES, ids=[f"h{c[0]}_v{c[1]}_b{c[2]}" for c in HEAD_CASES])
+def test_embed_and_head_match_oracle(hidden, vocab, batch):
+    say(f"embed + head hidden={hidden} vocab={vocab} batch={batch}")
+    arch = synth.Arch(hidden=hidden)
+    hc = synth.head_case(hidden, vocab, batch)
+    a = arch_of(arch)
+    table = bits_to_dev(hc.embed)
+    h = torch.full((batch, hidden), float("nan"), dtype=torch.float32, device="cuda")
+    gqa.embed_tokens(a, table, hc.ids.tolist(), h)
+    torch.cuda.synchronize()
+    # the gather is a copy of bf16 values into fp32: bit-exact
+    want = oracle.embed_gather(hc.embed, hc.ids)
+    assert np.array_equal(h.cpu().numpy().astype(np.float64), want), "embedding rows differ"
+    hs = f32_to_dev(hc.h)
+    logits = torch.empty((batch, vocab), dtype=torch.float32, device="cuda")
+    ws = torch.empty(gqa.lm_head_workspace_size(a, batch), dtype=torch.uint8, device="cuda")
+    gqa.lm_head(a, bits_to_dev(hc.w_final), table, hs, logits, ws)
+    torch.cuda.synchronize()
+    ref = oracle.lm_head(hc.h, hc.w_final, hc.embed, arch.rms_eps)
+    got = logits.cpu().numpy().astype(np.float64)
+    for b in range(batch):
+        assert_parity(got[b], ref[b], f"logits row {b}")
+    assert np.array_equal(hs.cpu().numpy(), hc.h), "the head must not write h"
+
+
 def test_rms_norm_and_residual_add():
     say("rms_norm + residual_add")
     hidden, rows = 2560, 3

@@ -297,3 +297,38 @@ def test_mlp_entry_validates():
     assert B.raw_call("gqa_mlp_workspace_size", ctypes.byref(a), 3072, 2, ctypes.byref(n)) == OK
     assert n.value >= (2 * 1024 + 2 * 2 * 3072) * 4
     assert B.raw_call("gqa_mlp_workspace_size", ctypes.byref(a), 3072, 2, None) == INVALID
+
+
+def test_head_entries_validate():
+    """gqa_embed_tokens / gqa_lm_head: every check before any launch."""
+    a = B.c_arch(gqa.Arch(hidden=1024))
+    ids = (ctypes.c_int32 * 3)(0, 5, 9)
+
+    def emb(table=FAKE, vocab=10, idp=ids, batch=3, h=FAKE):
+        return B.raw_call("gqa_embed_tokens", ctypes.byref(a), table, vocab, idp, batch, h, None)
+    assert emb(table=0) == INVALID
+    assert emb(table=MISALIGNED) == INVALID
+    assert emb(vocab=0) == INVALID
+    assert emb(vocab=9) == INVALID                 # id 9 out of range
+    assert emb(idp=None) == INVALID
+    assert emb(h=MISALIGNED) == INVALID
+    assert emb(batch=-1) == INVALID
+    assert emb(vocab=1 << 20) == UNSUPPORTED       # table beyond 2 GiB at hidden 1024
+    assert emb(batch=0, idp=None, h=0) == OK
+    neg = (ctypes.c_int32 * 1)(-1)
+    assert emb(idp=neg, batch=1) == INVALID
+
+    def head(norm=FAKE, table=FAKE, vocab=10, h=FAKE, batch=2, logits=FAKE, ws=FAKE, n=1 << 20, arch=a):
+        return B.raw_call("gqa_lm_head", ctypes.byref(arch), norm, table, vocab, h, batch, logits, ws, n, None)
+    assert head(norm=0) == INVALID
+    assert head(table=MISALIGNED) == INVALID
+    assert head(vocab=0) == INVALID
+    assert head(h=0) == INVALID
+    assert head(logits=MISALIGNED) == INVALID
+    assert head(ws=0) == INVALID
+    assert head(n=16) == WS_SMALL
+    assert head(arch=B.c_arch(gqa.Arch(hidden=1024, rms_eps=float("inf")))) == INVALID
+    assert head(batch=0, norm=0, h=0, logits=0, ws=0) == OK
+    n = ctypes.c_size_t()
+    assert B.raw_call("gqa_lm_head_workspace_size", ctypes.byref(a), 3, ctypes.byref(n)) == OK
+    assert n.value >= 3 * 1024 * 4
