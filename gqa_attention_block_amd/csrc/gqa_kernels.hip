@@ -1527,6 +1527,70 @@ __global__ __launch_bounds__(64) void attn_combine_small_kernel(const AttnParams
   }
 }
 
+// The merge for plans with at most kCombineMidChunks chunks per sequence and
+// enough (sequence, query head) pairs to fill the chip (several tokens of one
+// sequence, batches of long windows): one workgroup per pair.  Lane c holds
+// chunk c's (m, l), so every wave has the common reference max and the
+// weights; wave w sums chunks w, w + 4, ... (all its loads issued at once),
+// lane l owning elements 4l .. 4l+3, and the four sums are added in LDS.
+constexpr int kCombineMidChunks = 64;
+
+__global__ __launch_bounds__(kThreads) void attn_combine_mid_kernel(const AttnParams p) {
+  __shared__ float4 s_acc[kThreads / 64][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const SeqDesc sd = p.seq[b];
+  const int Hq = p.num_kv_heads * kGroup;
+  const int nchunks = (sd.n + p.chunk - 1) / p.chunk;
+  constexpr int kPer = kCombineMidChunks / (kThreads / 64);
+  float4 o[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = w + (kThreads / 64) * u;
+    o[u] = c < nchunks ? *reinterpret_cast<const float4 *>(
+                             p.part_o + ((size_t)(sd.chunk_begin + c) * Hq + h) * kHeadDim + lane * 4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float2 mlc = lane < nchunks
+                         ? *reinterpret_cast<const float2 *>(p.part_ml + ((size_t)(sd.chunk_begin + lane) * Hq + h) * 2)
+                         : make_float2(-INFINITY, 0.f);
+  const float M = wave_max(mlc.x);
+  const float wtc = mlc.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mlc.x - M);
+  const float L = wave_sum(wtc * mlc.y);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = w + (kThreads / 64) * u;     // uniform: the weight comes from lane c
+    const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wtc), c));
+    acc.x = fmaf(wt, o[u].x, acc.x);
+    acc.y = fmaf(wt, o[u].y, acc.y);
+    acc.z = fmaf(wt, o[u].z, acc.z);
+    acc.w = fmaf(wt, o[u].w, acc.w);
+  }
+  s_acc[w][lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int k = 1; k < kThreads / 64; ++k) {
+    const float4 t = s_acc[k][lane];
+    acc.x += t.x;
+    acc.y += t.y;
+    acc.z += t.z;
+    acc.w += t.w;
+  }
+  const float gl = p.gate[(size_t)b * p.ld_gate + h];
+  const float sc = (1.0f / (1.0f + expf(-gl))) / L;
+  float *dst = p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim;
+  const float v[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane * 4 + j;                    // element e holds dim 16 (e % 16) + e / 16
+    dst[16 * (e & 15) + (e >> 4)] = v[j] * sc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Merge of one sequence's split-K partials, the headwise gate and o_proj in
 // one launch.
@@ -1915,6 +1979,8 @@ hipError_t launch_combine(const AttnParams &p, int num_heads, hipStream_t stream
   for (int i = 0; i < p.nseq; ++i) most = std::max(most, (p.seq[i].n + p.chunk - 1) / p.chunk);
   if (most <= kCombineSmallChunks)
     hipLaunchKernelGGL(attn_combine_small_kernel, dim3(num_heads, p.nseq), dim3(64), 0, stream, p);
+  else if (most <= kCombineMidChunks && p.nseq * num_heads >= kAttnTargetWgs)
+    hipLaunchKernelGGL(attn_combine_mid_kernel, dim3(num_heads, p.nseq), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(attn_combine_kernel, dim3(num_heads * kCombineSplit, p.nseq), dim3(kThreads), 0,
                        stream, p);
