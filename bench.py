@@ -196,11 +196,17 @@ def bench_stack(args):
     ws_mlp = (torch.empty(gqa.mlp_workspace_size(a, int(st.layers[0].w_gate.shape[0]), 1), dtype=torch.uint8,
                           device="cuda:0") if mlp else None)
 
-    def step():   # per layer: h += block(RMSNorm(h) * w) [, then h += mlp(h)]
-        for L in layers:
-            gqa.attention_layer_decode(a, L["w_norm"], L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], h, ws)
-            if mlp:
-                gqa.mlp_decode(a, *L["mlp"], h, ws_mlp)
+    # per layer: h += block(RMSNorm(h) * w) [, then h += mlp(h)], each call
+    # marshalled once (the binding's prepared calls)
+    calls = []
+    for L in layers:
+        calls.append(gqa.PreparedLayer(a, L["w_norm"], L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], h, ws))
+        if mlp:
+            calls.append(gqa.PreparedMlp(a, *L["mlp"], h, ws_mlp))
+
+    def step():
+        for c in calls:
+            c.step()
 
     run = step
     if args.graph:
@@ -432,10 +438,13 @@ def main():
                      dtype=torch.uint8, device="cuda:0")
     torch.cuda.synchronize()
 
+    # each copy's block call marshalled once (the binding's prepared call):
+    # a step enqueues the same gqa_attention_block_decode
+    prepared = [gqa.PreparedBlock(a, s["w_qkv"], s["w_g"], s["w_o"], case.is_full, s["seqs"], x, out, ws)
+                for s in sets]
+
     def block_step(c):
-        s = sets[c]
-        gqa.attention_block_decode(a, s["w_qkv"], s["w_g"], s["w_o"], case.is_full, s["seqs"],
-                                   x, out, ws)
+        prepared[c].step()
 
     # dominant kernel: the attention step (split-K attention over the window,
     # combine + gate), on a q produced once by the projection step

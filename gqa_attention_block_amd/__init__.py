@@ -9,6 +9,9 @@ from .binding import (  # noqa: F401
     Arch,
     GqaError,
     KvSeq,
+    PreparedBlock,
+    PreparedLayer,
+    PreparedMlp,
     attention_block_chunk,
     attention_block_decode,
     attention_gated,

@@ -262,6 +262,76 @@ def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Seq
         "gqa_attention_block_decode")
 
 
+class _Prepared:
+    """A library call with its arguments marshalled once.  The tensors it was
+    built from must stay alive and in place while it is used; step() updates
+    only the sequences' positions and enqueues the call on the current stream
+    (or the stream given at construction)."""
+
+    def __init__(self, fn, name: str, ks, args_before_stream, stream):
+        self._fn, self._name, self._ks = fn, name, ks
+        self._args = args_before_stream
+        self._stream = None if stream is None else _stream(stream)
+
+    def step(self, positions: Optional[Sequence[int]] = None):
+        if positions is not None:
+            for i, p in enumerate(positions):
+                self._ks[i].position = int(p)
+        st = self._fn(*self._args, self._stream if self._stream is not None
+                      else torch.cuda.current_stream().cuda_stream)
+        if st != GQA_OK:
+            raise GqaError(st, _lib.gqa_last_error().decode(), self._name)
+
+
+class PreparedBlock(_Prepared):
+    """attention_block_decode with fixed weights, caches, x, out and workspace."""
+
+    def __init__(self, arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq], x: torch.Tensor,
+                 out: torch.Tensor, workspace: torch.Tensor, stream=None):
+        b = len(seqs)
+        self._a = arch._c()
+        self._w = _weights(arch, w_qkv, w_g, w_o)
+        ks = _seqs(arch, seqs)
+        super().__init__(_lib.gqa_attention_block_decode, "gqa_attention_block_decode", ks,
+                         (ctypes.byref(self._a), ctypes.byref(self._w), int(is_full), ks, b,
+                          _ptr(x, torch.float32, "x", b * arch.hidden),
+                          _ptr(out, torch.float32, "out", b * arch.hidden),
+                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream)
+
+
+class PreparedLayer(_Prepared):
+    """attention_layer_decode (h += block(RMSNorm(h) * w_norm), in place) with
+    fixed weights, caches, h and workspace."""
+
+    def __init__(self, arch: Arch, w_norm, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],
+                 h: torch.Tensor, workspace: torch.Tensor, stream=None):
+        b = len(seqs)
+        self._a = arch._c()
+        self._w = _weights(arch, w_qkv, w_g, w_o)
+        ks = _seqs(arch, seqs)
+        super().__init__(_lib.gqa_attention_layer_decode, "gqa_attention_layer_decode", ks,
+                         (ctypes.byref(self._a), ctypes.byref(self._w), _wptr(w_norm, "w_norm", arch.hidden),
+                          int(is_full), ks, b, _ptr(h, torch.float32, "h", b * arch.hidden),
+                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream)
+
+
+class PreparedMlp(_Prepared):
+    """mlp_decode (h += down(gelu_erf(gate x) * up x), in place) with fixed
+    weights, h and workspace."""
+
+    def __init__(self, arch: Arch, w_post, w_gate, w_up, w_down, h: torch.Tensor, workspace: torch.Tensor,
+                 stream=None):
+        b = h.shape[0] if h.dim() == 2 else 1
+        inter = int(w_gate.shape[0])
+        hd = arch.hidden
+        self._a = arch._c()
+        self._w = _MlpWeights(_wptr(w_post, "w_post", hd), _wptr(w_gate, "w_gate", inter * hd),
+                              _wptr(w_up, "w_up", inter * hd), _wptr(w_down, "w_down", hd * inter), inter, 0)
+        super().__init__(_lib.gqa_mlp_decode, "gqa_mlp_decode", None,
+                         (ctypes.byref(self._a), ctypes.byref(self._w), b, _ptr(h, torch.float32, "h", b * hd),
+                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream)
+
+
 def attention_block_chunk(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seq: KvSeq, x: torch.Tensor,
                           out: torch.Tensor, workspace: torch.Tensor, stream=None):
     """M consecutive tokens of one sequence (x, out: [M][hidden]); seq.position is the first token's."""

@@ -688,6 +688,60 @@ def test_embed_and_head_match_oracle(hidden, vocab, batch):
     assert np.array_equal(hs.cpu().numpy(), hc.h), "the head must not write h"
 
 
+def test_prepared_calls_equal_the_plain_calls():
+    """PreparedBlock / PreparedLayer / PreparedMlp enqueue the same entry points
+    with arguments marshalled once; step(positions) moves the token."""
+    case = synth.block_case("prepared_ring", 1024, False, [700], ring_capacity=512, seed=0, case_id=80)
+    a = arch_of(case.arch)
+    s = case.seqs[0]
+    x, w_qkv, w_g, w_o = f32_to_dev(case.x), bits_to_dev(case.w_qkv), bits_to_dev(case.w_g), bits_to_dev(case.w_o)
+    ws = torch.empty(gqa.workspace_size(a, 1, 2048), dtype=torch.uint8, device="cuda")
+    outs = []
+    for prepared in (False, True):
+        k, v = f16_to_dev(s.k), f16_to_dev(s.v)
+        out = torch.empty((1, 1024), dtype=torch.float32, device="cuda")
+        seqs = [gqa.KvSeq(k=k, v=v, position=700, ring_capacity=512)]
+        if prepared:
+            pb = gqa.PreparedBlock(a, w_qkv, w_g, w_o, False, seqs, x, out, ws)
+            pb.step()
+            first = out.clone()
+            pb.step([701])
+        else:
+            gqa.attention_block_decode(a, w_qkv, w_g, w_o, False, seqs, x, out, ws)
+            first = out.clone()
+            gqa.attention_block_decode(a, w_qkv, w_g, w_o, False,
+                                       [gqa.KvSeq(k=k, v=v, position=701, ring_capacity=512)], x, out, ws)
+        torch.cuda.synchronize()
+        outs.append((first.cpu().numpy(), out.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()))
+    # the cache rows bitwise; the outputs to fp32 rounding (the fused merge +
+    # o_proj tail adds the heads' parts with atomics in no fixed order)
+    for i in (2, 3):
+        assert np.array_equal(outs[0][i], outs[1][i]), f"prepared block differs in cache item {i}"
+    for i in (0, 1):
+        ref = outs[0][i]
+        assert np.max(np.abs(outs[1][i] - ref)) <= 1e-5 * np.max(np.abs(ref)), f"prepared block output {i}"
+    # layer + MLP on a residual stream
+    m = synth.make_mlp(1024, 3072, 0, 81, 2000)
+    wn = bits_to_dev(synth.round_to_bf16_bits(np.ones(1024, np.float32)))
+    wsm = torch.empty(gqa.mlp_workspace_size(a, 3072, 1), dtype=torch.uint8, device="cuda")
+    res = []
+    for prepared in (False, True):
+        k, v = f16_to_dev(s.k), f16_to_dev(s.v)
+        h = f32_to_dev(case.x)
+        seqs = [gqa.KvSeq(k=k, v=v, position=700, ring_capacity=512)]
+        mw = (bits_to_dev(m.w_post), bits_to_dev(m.w_gate), bits_to_dev(m.w_up), bits_to_dev(m.w_down))
+        if prepared:
+            gqa.PreparedLayer(a, wn, w_qkv, w_g, w_o, False, seqs, h, ws).step()
+            gqa.PreparedMlp(a, *mw, h, wsm).step()
+        else:
+            gqa.attention_layer_decode(a, wn, w_qkv, w_g, w_o, False, seqs, h, ws)
+            gqa.mlp_decode(a, *mw, h, wsm)
+        torch.cuda.synchronize()
+        res.append(h.cpu().numpy())
+    d = res[1] - res[0]
+    assert np.max(np.abs(d)) <= 1e-5 * np.max(np.abs(res[0] - case.x)), "prepared layer + MLP differ"
+
+
 def test_rms_norm_and_residual_add():
     say("rms_norm + residual_add")
     hidden, rows = 2560, 3
