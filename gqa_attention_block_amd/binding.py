@@ -263,13 +263,15 @@ def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Seq
 
 
 class _Prepared:
-    """A library call with its arguments marshalled once.  The tensors it was
-    built from must stay alive and in place while it is used; step() updates
-    only the sequences' positions and enqueues the call on the current stream
-    (or the stream given at construction)."""
+    """A library call with its arguments marshalled once.  The object holds
+    references to the tensors it was built from (their storage must not be
+    resized or moved while it is used); step() updates only the sequences'
+    positions and enqueues the call on the current stream (or the stream given
+    at construction)."""
 
-    def __init__(self, fn, name: str, ks, args_before_stream, stream):
+    def __init__(self, fn, name: str, ks, args_before_stream, stream, keep=()):
         self._fn, self._name, self._ks = fn, name, ks
+        self._keep = tuple(keep)
         self._args = args_before_stream
         self._stream = None if stream is None else _stream(stream)
 
@@ -296,7 +298,8 @@ class PreparedBlock(_Prepared):
                          (ctypes.byref(self._a), ctypes.byref(self._w), int(is_full), ks, b,
                           _ptr(x, torch.float32, "x", b * arch.hidden),
                           _ptr(out, torch.float32, "out", b * arch.hidden),
-                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream)
+                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream,
+                         keep=(w_qkv, w_g, w_o, x, out, workspace, *[t for q in seqs for t in (q.k, q.v)]))
 
 
 class PreparedLayer(_Prepared):
@@ -312,7 +315,8 @@ class PreparedLayer(_Prepared):
         super().__init__(_lib.gqa_attention_layer_decode, "gqa_attention_layer_decode", ks,
                          (ctypes.byref(self._a), ctypes.byref(self._w), _wptr(w_norm, "w_norm", arch.hidden),
                           int(is_full), ks, b, _ptr(h, torch.float32, "h", b * arch.hidden),
-                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream)
+                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream,
+                         keep=(w_norm, w_qkv, w_g, w_o, h, workspace, *[t for q in seqs for t in (q.k, q.v)]))
 
 
 class PreparedMlp(_Prepared):
@@ -329,7 +333,8 @@ class PreparedMlp(_Prepared):
                               _wptr(w_up, "w_up", inter * hd), _wptr(w_down, "w_down", hd * inter), inter, 0)
         super().__init__(_lib.gqa_mlp_decode, "gqa_mlp_decode", None,
                          (ctypes.byref(self._a), ctypes.byref(self._w), b, _ptr(h, torch.float32, "h", b * hd),
-                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream)
+                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream,
+                         keep=(w_post, w_gate, w_up, w_down, h, workspace))
 
 
 def attention_block_chunk(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seq: KvSeq, x: torch.Tensor,
