@@ -742,6 +742,66 @@ def test_prepared_calls_equal_the_plain_calls():
     assert np.max(np.abs(d)) <= 1e-5 * np.max(np.abs(res[0] - case.x)), "prepared layer + MLP differ"
 
 
+def test_graph_replays_match_eager():
+    """A block (one sequence, fused merge + o_proj tail, whose output is zeroed
+    inside the partial kernel) and a whole decoder layer captured in HIP
+    graphs: every replay, with eager work and synchronisations in between,
+    matches the eager result (outputs to fp32 rounding, cache rows bitwise)."""
+    case = synth.block_case("graph_full", 1024, True, [6000], seed=0, case_id=82)
+    a = arch_of(case.arch)
+    s = case.seqs[0]
+    x, w_qkv, w_g, w_o = f32_to_dev(case.x), bits_to_dev(case.w_qkv), bits_to_dev(case.w_g), bits_to_dev(case.w_o)
+    ws = torch.empty(gqa.workspace_size(a, 1, 8192), dtype=torch.uint8, device="cuda")
+    k, v = f16_to_dev(s.k), f16_to_dev(s.v)
+    out = torch.empty((1, 1024), dtype=torch.float32, device="cuda")
+    pb = gqa.PreparedBlock(a, w_qkv, w_g, w_o, True, [gqa.KvSeq(k=k, v=v, position=6000)], x, out, ws)
+    pb.step()
+    torch.cuda.synchronize()
+    eager, k_eager = out.clone(), k.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            pb.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    scale = float(eager.abs().max())
+    for rep in range(4):
+        out.fill_(float("nan"))              # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert float((out - eager).abs().max()) <= 1e-5 * scale, f"block replay {rep}"
+        assert torch.equal(k, k_eager), f"cache rows after replay {rep}"
+    # a whole decoder layer (attention layer + MLP) on the residual stream
+    m = synth.make_mlp(1024, 3072, 0, 83, 2000)
+    wn = bits_to_dev(synth.round_to_bf16_bits(np.ones(1024, np.float32)))
+    wsm = torch.empty(gqa.mlp_workspace_size(a, 3072, 1), dtype=torch.uint8, device="cuda")
+    h0 = f32_to_dev(case.x)
+    h = h0.clone()
+    calls = [gqa.PreparedLayer(a, wn, w_qkv, w_g, w_o, True, [gqa.KvSeq(k=k, v=v, position=6000)], h, ws),
+             gqa.PreparedMlp(a, bits_to_dev(m.w_post), bits_to_dev(m.w_gate), bits_to_dev(m.w_up),
+                             bits_to_dev(m.w_down), h, wsm)]
+    for c in calls:
+        c.step()
+    torch.cuda.synchronize()
+    eager_h = h.clone()
+    with torch.cuda.stream(side):
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=side):
+            for c in calls:
+                c.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    d0 = float((eager_h - h0).abs().max())
+    for rep in range(4):
+        h.copy_(h0)                          # eager work between replays
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert float((h - eager_h).abs().max()) <= 1e-5 * d0, f"decoder layer replay {rep}"
+
+
 def test_rms_norm_and_residual_add():
     say("rms_norm + residual_add")
     hidden, rows = 2560, 3
