@@ -244,7 +244,7 @@ ChunkPlan make_chunk_plan(const gqa_arch *a, int is_full, int32_t first_pos, int
   cp.rows = first_pos + m - cp.r0;
   const long groups = (long)a->num_kv_heads * ceil_div(m, 16);
   const int cap = ceil_div(cp.rows, 32) * 32;
-  while (cp.chunk + 32 <= cap && (long)ceil_div(cp.rows, cp.chunk + 32) * groups >= kAttnTargetWgs) cp.chunk += 32;
+  while (cp.chunk + 32 <= cap && (long)ceil_div(cp.rows, cp.chunk + 32) * groups >= kChunkTargetWgs) cp.chunk += 32;
   cp.nchunks = ceil_div(cp.rows, cp.chunk);
   return cp;
 }
@@ -255,7 +255,7 @@ size_t chunk_partial_rows(int num_kv_heads, int32_t m, int32_t max_seq_len) {
   if (m < 2) return 0;
   const size_t groups = (size_t)num_kv_heads * ceil_div(m, 16);
   const size_t per = std::min((size_t)ceil_div(max_seq_len, 32),
-                              2 * ((kAttnTargetWgs + groups - 1) / groups) + 1);
+                              2 * ((kChunkTargetWgs + groups - 1) / groups) + 1);
   return (size_t)m * per;
 }
 

@@ -22,6 +22,12 @@ constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles f
 // the split plan, and the workspace bound derived from it, are the same
 // everywhere.
 constexpr int kAttnTargetWgs = 256;
+// Workgroups the several-token path aims for: (chunk, KV head, 16 tokens)
+// each, every wave walking all tiles of its chunk in sequence.  Measured on
+// 32 tokens at 4K rows (whole chunk step): 128 -> 57.6 us, 256 -> 60.2 us,
+// 64 -> 76.5 us, 512 -> 69.8 us: fewer, longer chains write fewer partials
+// until too few workgroups are left to stream the cache.
+constexpr int kChunkTargetWgs = 128;
 // Windows of at most this many rows run as one chunk per sequence and KV
 // head, finished inside the partial kernel (no combine launch).  Measured:
 // at 64 rows this saves the combine (~3.4 us); at 512 rows the 16 waves of
