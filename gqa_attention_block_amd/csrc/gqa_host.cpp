@@ -206,14 +206,22 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads, bool allow_di
     return n;
   };
   int longest = 1;
-  for (const SeqDesc &s : seqs) longest = std::max(longest, s.n);
+  long total = 0;
+  for (const SeqDesc &s : seqs) {
+    longest = std::max(longest, s.n);
+    total += s.n;
+  }
+  // short launches: half the workgroups, two tiles per wave instead of one
+  // (measured at 4096 rows: 22.9 against 24.6 us per block; at 8192 rows and
+  // beyond the full target is faster)
+  const int target = total <= kShortPlanRows ? kAttnTargetWgs / 2 : kAttnTargetWgs;
   const int cap = ceil_div(longest, kChunkQuantum) * kChunkQuantum;
   int chunk = kChunkQuantum;
   if (allow_direct && longest <= kDirectMaxRows) {
     chunk = cap;
     plan.direct = true;
   } else {
-    while (chunk + kChunkQuantum <= cap && wgs(chunk + kChunkQuantum) >= kAttnTargetWgs) chunk += kChunkQuantum;
+    while (chunk + kChunkQuantum <= cap && wgs(chunk + kChunkQuantum) >= target) chunk += kChunkQuantum;
   }
   plan.chunk = chunk;
   for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {

@@ -22,6 +22,7 @@ constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles f
 // the split plan, and the workspace bound derived from it, are the same
 // everywhere.
 constexpr int kAttnTargetWgs = 256;
+constexpr long kShortPlanRows = 4096;  // launches of at most this many window rows aim for half
 // Workgroups the several-token path aims for: (chunk, KV head, 16 tokens)
 // each, every wave walking all tiles of its chunk in sequence.  Measured on
 // 32 tokens at 4K rows (whole chunk step): 128 -> 57.6 us, 256 -> 60.2 us,
