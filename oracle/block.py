@@ -20,7 +20,7 @@ residual add) follows [mod]'s transcribed layer; its intermediate size is not
 on the pages, so inputs are synthetic (reading O21: W_gate, W_up [inter][hidden],
 W_down [hidden][inter], row-major like O1).
 
-Readings where the pages leave a step open (numbered O1..O20 throughout):
+Readings where the pages leave a step open (numbered O1..O23 throughout):
   O1 weights are row-major [out][in] and y = W x; O2 head h of a section is the
   contiguous block [256h, 256h+256); O3 query head h reads KV head
   h // (num_heads / num_kv_heads); O4 NeoX pairs (i, i + r/2) over the leading r
@@ -157,11 +157,17 @@ def physical_rows(seq_len: int, kv_start: int, active_ring: int) -> np.ndarray:
 
 def attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                      seq_len: int, kv_start: int, active_ring: int,
-                     scale: float) -> np.ndarray:
+                     scale: float, sinks=None) -> np.ndarray:
     """Softmax attention of one query per head over the cache window.
 
     q [Hq][D]; caches [capacity][Hk][D].  Query head h reads KV head
-    h // (Hq / Hk) (reading O3).  No softcap, no sinks, no bias.
+    h // (Hq / Hk) (reading O3).  No softcap, no bias.
+
+    ``sinks`` (optional, [Hq]): the attention-sink operand that the attention
+    call takes and the pages leave unset [attn: the attention step passes no
+    sinks; kvw: `encode_attention_any` signature].  Reading O23: sink
+    sigma_h is one more logit in head h's softmax, in the units of the scaled
+    scores, with no value row: p_t = e^{s_t} / (sum_u e^{s_u} + e^{sigma_h}).
     """
     num_heads, head_dim = q.shape
     num_kv = k_cache.shape[1]
@@ -173,8 +179,14 @@ def attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         kk = np.asarray(k_cache[rows, g, :], dtype=np.float64)
         vv = np.asarray(v_cache[rows, g, :], dtype=np.float64)
         s = scale * (kk @ np.asarray(q[h], dtype=np.float64))
-        p = np.exp(s - s.max())
-        p /= p.sum()
+        if sinks is None:
+            p = np.exp(s - s.max())
+            p /= p.sum()
+        else:
+            sig = float(sinks[h])
+            ref = max(float(s.max()), sig)
+            p = np.exp(s - ref)
+            p = p / (p.sum() + np.exp(sig - ref))
         out[h] = p @ vv
     return out
 
@@ -221,7 +233,7 @@ class BlockResult(AttentionStepResult):
 
 
 def attention_step(arch, is_full: bool, qkv: np.ndarray, gate_logits: np.ndarray,
-                   seqs: Sequence) -> AttentionStepResult:
+                   seqs: Sequence, sinks=None) -> AttentionStepResult:
     """Everything between the projections and o_proj, per sequence b:
 
     split qkv[b] [attn: THE SPLIT]; RoPE q and k with the layer class's
@@ -231,6 +243,7 @@ def attention_step(arch, is_full: bool, qkv: np.ndarray, gate_logits: np.ndarray
     [attn: window step, `encode_attention_any`]; apply the headwise gate
     [attn: gate step].  Each element of ``seqs`` exposes k, v (fp16 caches),
     ring_capacity and position; caches are copied and the copies updated.
+    ``sinks``: optional per-head sink logits (``attention_decode``).
     """
     hq, hk, d = arch.num_heads, arch.num_kv_heads, arch.head_dim
     qkv = np.atleast_2d(np.asarray(qkv, dtype=np.float64))
@@ -251,7 +264,7 @@ def attention_step(arch, is_full: bool, qkv: np.ndarray, gate_logits: np.ndarray
         kc[slot] = k16
         vc[slot] = v16
         win = kv_window(is_full, pos, arch.sliding_window, int(seq.ring_capacity))
-        a = attention_decode(q_r, kc, vc, win[0], win[1], win[2], arch.attention_scale)
+        a = attention_decode(q_r, kc, vc, win[0], win[1], win[2], arch.attention_scale, sinks)
         res["q_roped"].append(q_r)
         res["k16"].append(k16)
         res["v16"].append(v16)
@@ -269,14 +282,14 @@ def attention_step(arch, is_full: bool, qkv: np.ndarray, gate_logits: np.ndarray
 
 
 def block_decode(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
-                 x: np.ndarray, seqs: Sequence) -> BlockResult:
+                 x: np.ndarray, seqs: Sequence, sinks=None) -> BlockResult:
     """One decode step of the attention block for B independent sequences
     [attn: `encode_attention_block`, steps in its order].
 
     ``arch`` exposes num_heads, num_kv_heads, head_dim, full_rotary_dim,
     sliding_window, full_rope_theta, rope_theta and attention_scale.  The fused
     QKV GEMV and the g_proj GEMV read the same normed x; o_proj reads the
-    gated attention.
+    gated attention.  ``sinks``: optional per-head sink logits.
     """
     w_qkv = bf16_bits_to_f64(w_qkv_bits)
     w_g = bf16_bits_to_f64(w_g_bits)
@@ -284,7 +297,7 @@ def block_decode(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
     x = np.atleast_2d(np.asarray(x, dtype=np.float64))
     qkv = gemv(w_qkv, x)
     gl = gemv(w_g, x)
-    st = attention_step(arch, is_full, qkv, gl, seqs)
+    st = attention_step(arch, is_full, qkv, gl, seqs, sinks)
     out = gemv(w_o, st.gated)
     return BlockResult(q_roped=st.q_roped, k16=st.k16, v16=st.v16, slots=st.slots,
                        windows=st.windows, attn=st.attn, gated=st.gated,
@@ -306,7 +319,7 @@ class ChunkResult:
 
 
 def block_chunk(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
-                x: np.ndarray, seq, m_tokens: int) -> ChunkResult:
+                x: np.ndarray, seq, m_tokens: int, sinks=None) -> ChunkResult:
     """M consecutive tokens of one sequence at positions seq.position + t.
 
     Token t is the single-token block at its position, run once tokens
@@ -321,7 +334,7 @@ def block_chunk(arch, is_full: bool, w_qkv_bits, w_g_bits, w_o_bits,
     for t in range(m_tokens):
         cur = OracleSeq(k=k, v=v, ring_capacity=int(seq.ring_capacity),
                         position=int(seq.position) + t)
-        r = block_decode(arch, is_full, w_qkv_bits, w_g_bits, w_o_bits, x[t:t + 1], [cur])
+        r = block_decode(arch, is_full, w_qkv_bits, w_g_bits, w_o_bits, x[t:t + 1], [cur], sinks)
         k, v = r.k_caches[0], r.v_caches[0]
         outs.append(r.out[0])
         slots.append(r.slots[0])

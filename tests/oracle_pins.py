@@ -674,4 +674,85 @@ def pin_lm_head_brute_force(O):
             assert abs(got[b, j] - want) < 1e-12 * (1 + abs(want))
 
 
+# ----------------------------------------------------------------------------
+# attention sinks (reading O23: one more logit per head, no value row)
+# ----------------------------------------------------------------------------
+
+def pin_sink_closed_form(O):
+    """Zero keys make every score 0, so with n rows and sink sigma each row
+    weighs 1 / (n + e^sigma): sigma = ln 3 over 5 rows gives 1/8, ln 11 gives
+    1/16, -inf gives the plain mean 1/5, whatever the scale and the query."""
+    rng = _rng(40)
+    hq, hk, d, n = 4, 2, 8, 5
+    k = np.zeros((n, hk, d), np.float16)
+    v = rng.standard_normal((n, hk, d)).astype(np.float16)
+    q = rng.standard_normal((hq, d))
+    sinks = np.array([math.log(3.0), math.log(11.0), -np.inf, 0.0])
+    got = O.attention_decode(q, k, v, n, 0, 0, 0.37, sinks)
+    for h, den in zip(range(hq), (8.0, 16.0, 5.0, 6.0)):
+        want = v[:, h // 2].astype(np.float64).sum(axis=0) / den
+        assert np.allclose(got[h], want, rtol=1e-13, atol=1e-15), h
+
+
+def pin_sink_is_a_valueless_extra_key(O):
+    """Against scipy's softmax over the window's scores with sigma_h appended
+    as one more entry, whose value row is zero; through a ring window."""
+    from scipy.special import softmax
+    rng = _rng(41)
+    hq, hk, d, ring, pos, window = 8, 2, 16, 12, 30, 9
+    k = rng.standard_normal((ring, hk, d)).astype(np.float16)
+    v = rng.standard_normal((ring, hk, d)).astype(np.float16)
+    q = 2.0 * rng.standard_normal((hq, d))
+    sinks = rng.standard_normal(hq) * 3.0
+    sl, ks, ar = O.kv_window(False, pos, window, ring)
+    got = O.attention_decode(q, k, v, sl, ks, ar, 0.3, sinks)
+    rows = [t % ring for t in range(pos - window + 1, pos + 1)]
+    for h in range(hq):
+        kk = k[rows, h // 4].astype(np.float64)
+        vv = v[rows, h // 4].astype(np.float64)
+        p = softmax(np.append(0.3 * (kk @ q[h]), sinks[h]))
+        want = p[:-1] @ vv
+        assert np.allclose(got[h], want, rtol=1e-12, atol=1e-14), h
+
+
+def pin_sink_scales_the_plain_attention(O):
+    """With S = sum_t e^{s_t}, the sink multiplies the plain attention by
+    S / (S + e^sigma): checked per head with S summed by brute force."""
+    rng = _rng(42)
+    hq, hk, d, n = 4, 1, 8, 7
+    k = rng.standard_normal((n, hk, d)).astype(np.float16)
+    v = rng.standard_normal((n, hk, d)).astype(np.float16)
+    q = rng.standard_normal((hq, d))
+    sinks = np.array([-2.0, 0.5, 3.0, 40.0])
+    plain = O.attention_decode(q, k, v, n, 0, 0, 0.5)
+    got = O.attention_decode(q, k, v, n, 0, 0, 0.5, sinks)
+    for h in range(hq):
+        S = sum(math.exp(0.5 * float(np.dot(k[t, 0].astype(np.float64), q[h]))) for t in range(n))
+        f = S / (S + math.exp(sinks[h]))
+        assert np.allclose(got[h], f * plain[h], rtol=1e-12, atol=1e-300), h
+
+
+def pin_block_and_chunk_pass_sinks_on(O):
+    """The block and the several-token path hand the sinks to the attention:
+    sinks of -inf change nothing (bit for bit), sinks of +1e4 make every
+    attention weight underflow to 0, so gated attention and output are 0."""
+    arch = tiny_arch()
+    rng = _rng(43)
+    w_qkv, w_g, w_o = _tiny_weights(arch, rng)
+    x = rng.standard_normal((3, arch.hidden))
+    k, v = _cache(arch, rng, 16)
+    seq = _seq(k, v, 0, 6)
+    plain = O.block_decode(arch, True, w_qkv, w_g, w_o, x[:1], [seq])
+    minus = O.block_decode(arch, True, w_qkv, w_g, w_o, x[:1], [seq],
+                           np.full(arch.num_heads, -np.inf))
+    assert np.array_equal(plain.out, minus.out) and np.array_equal(plain.gated, minus.gated)
+    big = O.block_decode(arch, True, w_qkv, w_g, w_o, x[:1], [seq], np.full(arch.num_heads, 1e4))
+    assert not np.any(big.gated) and not np.any(big.out)
+    assert np.array_equal(big.k_caches[0], plain.k_caches[0])
+    c_plain = O.block_chunk(arch, False, w_qkv, w_g, w_o, x, seq, 3)
+    c_big = O.block_chunk(arch, False, w_qkv, w_g, w_o, x, seq, 3, np.full(arch.num_heads, 1e4))
+    assert not np.any(c_big.out)
+    assert np.array_equal(c_big.k_cache, c_plain.k_cache)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

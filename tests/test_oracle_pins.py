@@ -61,7 +61,7 @@ MUTANTS = [
      "return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float16)"),
     ("bf16_shift", "<< np.uint32(16)", "<< np.uint32(15)"),
     ("gemv_transposed", "return x @ w.T", "return x @ w"),
-    ("chunk_reuses_first_input", "x[t:t + 1], [cur])", "x[0:1], [cur])"),
+    ("chunk_reuses_first_input", "x[t:t + 1], [cur], sinks)", "x[0:1], [cur], sinks)"),
     ("chunk_cache_not_threaded", "        k, v = r.k_caches[0], r.v_caches[0]\n        outs.append",
      "        outs.append"),
     ("chunk_positions_frozen", "position=int(seq.position) + t)", "position=int(seq.position))"),
@@ -73,6 +73,12 @@ MUTANTS = [
     ("mlp_reads_stream_before_attention_add", "m = mlp_decode(h_mid,", "m = mlp_decode(h,"),
     ("embedding_scaled", "return bf16_bits_to_f64(np.asarray(e_bits)[np.asarray(ids, dtype=np.int64)])",
      "return bf16_bits_to_f64(np.asarray(e_bits)[np.asarray(ids, dtype=np.int64)]) * np.sqrt(np.asarray(e_bits).shape[1])"),
+    ("sink_ignored", "sig = float(sinks[h])", "sig = -np.inf"),
+    ("sink_scaled_like_a_score", "sig = float(sinks[h])", "sig = scale * float(sinks[h])"),
+    ("sink_base_2", "p = p / (p.sum() + np.exp(sig - ref))", "p = p / (p.sum() + np.exp2(sig - ref))"),
+    ("sink_renormalised_away", "p = p / (p.sum() + np.exp(sig - ref))", "p = p / p.sum()"),
+    ("block_drops_sinks", "st = attention_step(arch, is_full, qkv, gl, seqs, sinks)",
+     "st = attention_step(arch, is_full, qkv, gl, seqs)"),
     ("head_without_final_norm", "x = rms_norm(h, w_final_bits, eps)\n    return gemv",
      "x = np.atleast_2d(np.asarray(h, dtype=np.float64))\n    return gemv"),
 ]
