@@ -39,7 +39,7 @@ class _Arch(ctypes.Structure):
 
 class _Weights(ctypes.Structure):
     _fields_ = [("q_k_v_proj", ctypes.c_void_p), ("g_proj", ctypes.c_void_p),
-                ("o_proj", ctypes.c_void_p)]
+                ("o_proj", ctypes.c_void_p), ("sinks", ctypes.c_void_p)]
 
 
 class _MlpWeights(ctypes.Structure):
@@ -73,7 +73,7 @@ def _load():
         "gqa_attention_layer_decode": (ctypes.c_int, [A, W, P, ctypes.c_int, K, I32, P, P, S, P]),
         "gqa_attention_block_chunk": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_qkv_rope_kv": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, P]),
-        "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, S, P]),
+        "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, P, S, P]),
         "gqa_attention_partials": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, I32,
                                                   ctypes.POINTER(I32), ctypes.POINTER(I32), P]),
         "gqa_o_proj_gemv": (ctypes.c_int, [A, W, I32, P, P, P]),
@@ -225,11 +225,16 @@ def _wptr(t: Optional[torch.Tensor], name: str, numel: int) -> int:
     return _ptr(t, t.dtype, name, numel)
 
 
-def _weights(arch: Arch, w_qkv, w_g, w_o) -> _Weights:
+def _sinks_ptr(arch: Arch, sinks) -> int:
+    """Optional per-head attention-sink logits: fp32 [num_heads] on the device."""
+    return 0 if sinks is None else _ptr(sinks, torch.float32, "sinks", arch.num_heads)
+
+
+def _weights(arch: Arch, w_qkv, w_g, w_o, sinks=None) -> _Weights:
     h = arch.hidden
     return _Weights(_wptr(w_qkv, "w_qkv", arch.qkv_rows * h),
                     _wptr(w_g, "w_g", arch.num_heads * h),
-                    _wptr(w_o, "w_o", h * arch.q_dim))
+                    _wptr(w_o, "w_o", h * arch.q_dim), _sinks_ptr(arch, sinks))
 
 
 def _seqs(arch: Arch, seqs: Sequence[KvSeq]):
@@ -249,10 +254,12 @@ def _seqs(arch: Arch, seqs: Sequence[KvSeq]):
 
 def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],
                            x: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
-                           stream=None):
+                           stream=None, sinks=None):
+    """One decode step of the block; ``sinks``: optional fp32 [num_heads]
+    attention-sink logits (None: the family's own block, without sinks)."""
     b = len(seqs)
     a = arch._c()
-    w = _weights(arch, w_qkv, w_g, w_o)
+    w = _weights(arch, w_qkv, w_g, w_o, sinks)
     ks = _seqs(arch, seqs)
     _check(_lib.gqa_attention_block_decode(
         ctypes.byref(a), ctypes.byref(w), int(is_full), ks, b,
@@ -289,17 +296,17 @@ class PreparedBlock(_Prepared):
     """attention_block_decode with fixed weights, caches, x, out and workspace."""
 
     def __init__(self, arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq], x: torch.Tensor,
-                 out: torch.Tensor, workspace: torch.Tensor, stream=None):
+                 out: torch.Tensor, workspace: torch.Tensor, stream=None, sinks=None):
         b = len(seqs)
         self._a = arch._c()
-        self._w = _weights(arch, w_qkv, w_g, w_o)
+        self._w = _weights(arch, w_qkv, w_g, w_o, sinks)
         ks = _seqs(arch, seqs)
         super().__init__(_lib.gqa_attention_block_decode, "gqa_attention_block_decode", ks,
                          (ctypes.byref(self._a), ctypes.byref(self._w), int(is_full), ks, b,
                           _ptr(x, torch.float32, "x", b * arch.hidden),
                           _ptr(out, torch.float32, "out", b * arch.hidden),
                           _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream,
-                         keep=(w_qkv, w_g, w_o, x, out, workspace, *[t for q in seqs for t in (q.k, q.v)]))
+                         keep=(w_qkv, w_g, w_o, sinks, x, out, workspace, *[t for q in seqs for t in (q.k, q.v)]))
 
 
 class PreparedLayer(_Prepared):
@@ -307,16 +314,17 @@ class PreparedLayer(_Prepared):
     fixed weights, caches, h and workspace."""
 
     def __init__(self, arch: Arch, w_norm, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],
-                 h: torch.Tensor, workspace: torch.Tensor, stream=None):
+                 h: torch.Tensor, workspace: torch.Tensor, stream=None, sinks=None):
         b = len(seqs)
         self._a = arch._c()
-        self._w = _weights(arch, w_qkv, w_g, w_o)
+        self._w = _weights(arch, w_qkv, w_g, w_o, sinks)
         ks = _seqs(arch, seqs)
         super().__init__(_lib.gqa_attention_layer_decode, "gqa_attention_layer_decode", ks,
                          (ctypes.byref(self._a), ctypes.byref(self._w), _wptr(w_norm, "w_norm", arch.hidden),
                           int(is_full), ks, b, _ptr(h, torch.float32, "h", b * arch.hidden),
                           _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream,
-                         keep=(w_norm, w_qkv, w_g, w_o, h, workspace, *[t for q in seqs for t in (q.k, q.v)]))
+                         keep=(w_norm, w_qkv, w_g, w_o, sinks, h, workspace,
+                               *[t for q in seqs for t in (q.k, q.v)]))
 
 
 class PreparedMlp(_Prepared):
@@ -338,11 +346,11 @@ class PreparedMlp(_Prepared):
 
 
 def attention_block_chunk(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seq: KvSeq, x: torch.Tensor,
-                          out: torch.Tensor, workspace: torch.Tensor, stream=None):
+                          out: torch.Tensor, workspace: torch.Tensor, stream=None, sinks=None):
     """M consecutive tokens of one sequence (x, out: [M][hidden]); seq.position is the first token's."""
     m = x.shape[0] if x.dim() == 2 else 1
     a = arch._c()
-    w = _weights(arch, w_qkv, w_g, w_o)
+    w = _weights(arch, w_qkv, w_g, w_o, sinks)
     ks = _seqs(arch, [seq])
     _check(_lib.gqa_attention_block_chunk(
         ctypes.byref(a), ctypes.byref(w), int(is_full), ks, m,
@@ -353,11 +361,11 @@ def attention_block_chunk(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seq: KvSeq
 
 
 def attention_layer_decode(arch: Arch, w_norm, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],
-                           h: torch.Tensor, workspace: torch.Tensor, stream=None):
+                           h: torch.Tensor, workspace: torch.Tensor, stream=None, sinks=None):
     """h += block(RMSNorm(h) * w_norm), in place (the attention half of a decoder layer)."""
     b = len(seqs)
     a = arch._c()
-    w = _weights(arch, w_qkv, w_g, w_o)
+    w = _weights(arch, w_qkv, w_g, w_o, sinks)
     ks = _seqs(arch, seqs)
     _check(_lib.gqa_attention_layer_decode(
         ctypes.byref(a), ctypes.byref(w), _wptr(w_norm, "w_norm", arch.hidden), int(is_full), ks, b,
@@ -440,8 +448,9 @@ def qkv_rope_kv(arch: Arch, w_qkv, w_g, is_full: bool, seqs: Sequence[KvSeq], x:
 
 def attention_gated(arch: Arch, is_full: bool, seqs: Sequence[KvSeq], q_roped: torch.Tensor,
                     gate_logits: torch.Tensor, attn_gated: torch.Tensor,
-                    workspace: torch.Tensor, stream=None):
-    """Attention over each cache window and the headwise gate (reads the caches only)."""
+                    workspace: torch.Tensor, stream=None, sinks=None):
+    """Attention over each cache window and the headwise gate (reads the caches
+    only); ``sinks``: optional fp32 [num_heads] attention-sink logits."""
     b = len(seqs)
     a = arch._c()
     ks = _seqs(arch, seqs)
@@ -449,6 +458,7 @@ def attention_gated(arch: Arch, is_full: bool, seqs: Sequence[KvSeq], q_roped: t
         ctypes.byref(a), int(is_full), ks, b,
         _ptr(q_roped, torch.float32, "q_roped", b * arch.q_dim),
         _ptr(gate_logits, torch.float32, "gate_logits", b * arch.num_heads),
+        _sinks_ptr(arch, sinks),
         _ptr(attn_gated, torch.float32, "attn_gated", b * arch.q_dim),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
         "gqa_attention_gated")

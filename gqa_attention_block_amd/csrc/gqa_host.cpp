@@ -422,10 +422,11 @@ AttnParams attn_params(const gqa_arch *a, const std::vector<SeqDesc> &seqs, cons
 }
 
 gqa_status run_attention(const gqa_arch *a, const std::vector<SeqDesc> &seqs, const Plan &plan,
-                         const float *q, const float *gate, float *attn, float *part_o, float *part_ml,
-                         hipStream_t stream) {
+                         const float *q, const float *gate, const float *sinks, float *attn, float *part_o,
+                         float *part_ml, hipStream_t stream) {
   for (const Plan::Group &g : plan.groups) {
-    const AttnParams p = attn_params(a, seqs, plan, g, q, gate, attn, part_o, part_ml);
+    AttnParams p = attn_params(a, seqs, plan, g, q, gate, attn, part_o, part_ml);
+    p.sinks = sinks;
     hipError_t e = launch_attention(p, a->num_heads, stream);
     if (e != hipSuccess) return gpu_error(e, "attention launch");
   }
@@ -455,6 +456,7 @@ gqa_status run_attention_oproj(const gqa_arch *a, const gqa_layer_weights *w, co
   op.part_o = part_o;
   op.part_ml = part_ml;
   op.gate = gate;
+  op.sinks = w->sinks;
   op.nchunks = g.total_chunks;
   op.num_heads = a->num_heads;
   op.w_o = static_cast<const uint16_t *>(w->o_proj);
@@ -543,7 +545,8 @@ gqa_status run_block(const gqa_arch *arch, const gqa_layer_weights *weights, int
   if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
   if (fused_tail(plan, batch))
     return run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, out, false, s);
-  if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
+  if ((st = run_attention(arch, descs, plan, q, gate, weights->sinks, attn, part_o, part_ml, s)) != GQA_OK)
+    return st;
   return run_o_proj(arch, weights, batch, attn, out, s);
 }
 }  // namespace
@@ -649,8 +652,8 @@ gqa_status gqa_o_proj_gemv(const gqa_arch *arch, const gqa_layer_weights *weight
 }
 
 gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs, int32_t batch,
-                               const float *q_roped, const float *gate_logits, float *attn_gated,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+                               const float *q_roped, const float *gate_logits, const float *sinks,
+                               float *attn_gated, void *workspace, size_t workspace_bytes, void *stream) {
   gqa_status st;
   if ((st = check_arch(arch)) != GQA_OK) return st;
   if ((st = check_batch(arch, batch)) != GQA_OK) return st;
@@ -669,7 +672,7 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
   char *ws = static_cast<char *>(workspace);
   float *part_o = reinterpret_cast<float *>(ws);
   float *part_ml = reinterpret_cast<float *>(ws + partial_bytes_o(arch, plan.max_group_chunks));
-  st = run_attention(arch, descs, plan, q_roped, gate_logits, attn_gated, part_o, part_ml,
+  st = run_attention(arch, descs, plan, q_roped, gate_logits, sinks, attn_gated, part_o, part_ml,
                      static_cast<hipStream_t>(stream));
   return st == GQA_OK ? ok() : st;
 }
@@ -789,6 +792,7 @@ gqa_status gqa_attention_block_chunk(const gqa_arch *arch, const gqa_layer_weigh
     ap.part_ml = part_ml + rows0 * 2;
     ap.gate = gate + (size_t)first * arch->num_heads;
     ap.ld_gate = arch->num_heads;
+    ap.sinks = weights->sinks;
     ap.out = attn + (size_t)first * q_dim;
     ap.ld_out = q_dim;
     ap.num_kv_heads = arch->num_kv_heads;
@@ -841,7 +845,8 @@ gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weig
     st = run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, h, true, s);
     return st == GQA_OK ? ok() : st;
   }
-  if ((st = run_attention(arch, descs, plan, q, gate, attn, part_o, part_ml, s)) != GQA_OK) return st;
+  if ((st = run_attention(arch, descs, plan, q, gate, weights->sinks, attn, part_o, part_ml, s)) != GQA_OK)
+    return st;
   if ((st = run_o_proj(arch, weights, batch, attn, h, s, true)) != GQA_OK) return st;
   return ok();
 }

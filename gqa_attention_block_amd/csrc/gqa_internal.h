@@ -64,6 +64,8 @@ struct AttnParams {
   float *part_o;      // [total_chunks][Hq][D]   unnormalised partial outputs, element
                       // n * 16 + c of a head holding dim 16c + n
   float *part_ml;     // [total_chunks][Hq][2]   (reference max in log2 units, sum)
+  const float *sinks; // [Hq] attention-sink logits (one more softmax term per query
+                      // head, no value row), or null: none
   int num_kv_heads;
   float qscale;       // attention_scale * log2(e): scores come out in log2 units
   int chunk;          // rows per chunk (one workgroup per chunk and KV head, a quarter
@@ -105,6 +107,7 @@ struct OprojParams {
   const float *part_o;   // as AttnParams, chunks [0, nchunks) of the sequence
   const float *part_ml;
   const float *gate;     // [Hq] gate logits
+  const float *sinks;    // [Hq] attention-sink logits, or null
   int nchunks;
   int num_heads;         // Hq
   const uint16_t *w_o;   // bf16 [hidden][Hq * D]

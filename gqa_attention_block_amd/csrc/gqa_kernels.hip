@@ -1107,6 +1107,15 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 // Workgroup = (chunk cid, KV head g); its 4 waves split the chunk's rows and
 // then merge in LDS, so one partial per (chunk, query head) is written.
 // 144 KB of LDS: one workgroup per CU, one wave per SIMD.
+// The attention-sink term of query head h's softmax denominator, relative to
+// the reference point M of the merged sum (log2 units): 2^(sigma_h log2(e) - M),
+// 0 without sinks.  Sink logits are in the units of the scaled scores and
+// carry no value row, so only the denominator grows.  A term past the fp32
+// range gives 0 output, which is the limit.
+__device__ __forceinline__ float sink_term(const float *sinks, int h, float M) {
+  return sinks ? __builtin_amdgcn_exp2f(fmaf(sinks[h], 1.4426950408889634f, -M)) : 0.f;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void attn_partial_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) _Float16 s_k0[4][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_k1[4][kTileHalves];
@@ -1153,7 +1162,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_partial_kernel(const AttnPar
     // the chunk is the whole window of sequence cid: normalise, gate, write
     const int qh = g * kGroup + i;
     const float gl = p.gate[(size_t)cid * p.ld_gate + qh];
-    const float sc = (1.0f / (1.0f + expf(-gl))) / L;
+    const float sc = (1.0f / (1.0f + expf(-gl))) / (L + sink_term(p.sinks, qh, M));
     float *dst = p.out + (size_t)cid * p.ld_out + (size_t)qh * kHeadDim;
     const float v[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
@@ -1465,7 +1474,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const AttnParams
   if (lane == 0) {
     const float gl = p.gate[(size_t)b * p.ld_gate + h];
     const float gate = 1.0f / (1.0f + expf(-gl));
-    const float sc = gate / L;
+    const float sc = gate / (L + sink_term(p.sinks, h, M));
     // element e = n * 16 + c holds dim 16c + n
     const int e = part * kCombineElems + q * 4;
     float *dst = p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim + (e >> 4);
@@ -1517,7 +1526,7 @@ __global__ __launch_bounds__(64) void attn_combine_small_kernel(const AttnParams
     acc.w = fmaf(wt, o[u].w, acc.w);
   }
   const float gl = p.gate[(size_t)b * p.ld_gate + h];
-  const float sc = (1.0f / (1.0f + expf(-gl))) / L;
+  const float sc = (1.0f / (1.0f + expf(-gl))) / (L + sink_term(p.sinks, h, M));
   float *dst = p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim;
   const float v[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
@@ -1581,7 +1590,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_mid_kernel(const AttnPa
     acc.w += t.w;
   }
   const float gl = p.gate[(size_t)b * p.ld_gate + h];
-  const float sc = (1.0f / (1.0f + expf(-gl))) / L;
+  const float sc = (1.0f / (1.0f + expf(-gl))) / (L + sink_term(p.sinks, h, M));
   float *dst = p.out + (size_t)b * p.ld_out + (size_t)h * kHeadDim;
   const float v[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
@@ -1686,7 +1695,7 @@ __global__ __launch_bounds__(kThreads) void combine_oproj_kernel(const OprojPara
 
   // ---- a_h at this lane's 8 dims 8cg .. 8cg+7: element e = n * 16 + c holds
   // dim 16c + n, so dim 8cg + k is element (8 (cg & 1) + k) * 16 + cg / 2 ----
-  const float sc = (1.0f / (1.0f + expf(-p.gate[h]))) / L;
+  const float sc = (1.0f / (1.0f + expf(-p.gate[h]))) / (L + sink_term(p.sinks, h, M));
   const float *sa = reinterpret_cast<const float *>(s_acc);
   float xv[8];
 #pragma unroll

@@ -76,11 +76,20 @@ typedef struct {
 } gqa_arch;
 
 /* One layer's projection weights, bf16, row-major [out][in] so that y = W x
- * ([attn] the GEMV calls pass rows = outputs, cols = inputs). Device, read-only. */
+ * ([attn] the GEMV calls pass rows = outputs, cols = inputs). Device, read-only.
+ * `sinks` is the attention call's optional sink operand ([attn] the attention
+ * step passes none; [kvw] `encode_attention_any` takes one): NULL for this
+ * family, else device fp32 [Hq], one logit per query head that joins that
+ * head's softmax with no value row, in the units of the scaled scores:
+ *   p_t = e^{s_t} / (sum_u e^{s_u} + e^{sinks[h]}),  s_t = attention_scale q.k_t
+ * (the pages leave the operand's meaning open; this is the reading taken).
+ * A sink logit of -inf is the same as none; non-finite values other than -inf
+ * are not checked (the memory is on the device) and give NaN or 0 outputs. */
 typedef struct {
   const void *q_k_v_proj;    /* [Hq*D + 2*Hk*D][H], rows q | k | v, head-major */
   const void *g_proj;        /* [Hq][H]                                        */
   const void *o_proj;        /* [H][Hq*D]                                      */
+  const float *sinks;        /* [Hq] fp32 sink logits, or NULL (none)          */
 } gqa_layer_weights;
 
 /* One sequence's K/V cache for this layer ([kvw] a slot is one position's row
@@ -233,13 +242,15 @@ gqa_status gqa_qkv_rope_kv(const gqa_arch *arch, const gqa_layer_weights *weight
  * cache must already hold this token's row (gqa_qkv_rope_kv writes it).
  *   q_roped      device fp32 [batch][Hq*D]
  *   gate_logits  device fp32 [batch][Hq]
+ *   sinks        device fp32 [Hq] or NULL, as gqa_layer_weights.sinks (the
+ *                same logits for every sequence)
  *   attn_gated   device fp32 [batch][Hq*D]: head h at [h*D, (h+1)*D)
  *   seqs, is_full, workspace as for gqa_attention_block_decode.
  * Reads the caches only. */
 gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs,
                                int32_t batch, const float *q_roped, const float *gate_logits,
-                               float *attn_gated, void *workspace, size_t workspace_bytes,
-                               void *stream);
+                               const float *sinks, float *attn_gated, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /* The split-K pass of gqa_attention_gated alone (the dominant kernel of the
  * block), for one launch group of at most 32 sequences; exposed so the pass
@@ -252,7 +263,8 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
  *   part_ml[c][h] = (m, l)  with  l * 2^m = sum_r 2^s_r  (m is a reference
  *                   point within 8 of the chunk's largest s_r)
  *   part_o[c][h][e] = (sum_r 2^(s_r - m) v_r)[16 * (e % 16) + e / 16]
- * so that part_o / l is the attention of q_h over the chunk's rows.
+ * so that part_o / l is the attention of q_h over the chunk's rows.  Sink logits do
+ * not enter the partials: they join the softmax where the chunks are merged.
  *   q_roped      device fp32 [batch][Hq*D]
  *   part_o       device fp32 [max_chunks][Hq][D]
  *   part_ml      device fp32 [max_chunks][Hq][2]

@@ -293,6 +293,14 @@ def random_gate_logits(arch: Arch, batch: int, seed: int, case_id: int) -> np.nd
     return _normal(seed, case_id, 901, (batch, arch.num_heads))
 
 
+def random_sinks(arch: Arch, seed: int, case_id: int, lo: float = -2.0, hi: float = 14.0) -> np.ndarray:
+    """Per-head attention-sink logits, fp32 [num_heads], uniform on [lo, hi).
+    The log of a window's partition function runs from about 1 (a few rows)
+    to about 11 (32K rows) on these inputs, so across the heads the sink takes
+    anything from a negligible share to most of the softmax."""
+    return _rng(seed, case_id, 904).uniform(lo, hi, arch.num_heads).astype(np.float32)
+
+
 def random_hidden(hidden: int, batch: int, seed: int, case_id: int,
                   tensor_id: int = 902, std: float = 1.0) -> np.ndarray:
     return _normal(seed, case_id, tensor_id, (batch, hidden), std)

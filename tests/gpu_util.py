@@ -111,10 +111,11 @@ class DevBlock:
                           ring_capacity=s.ring_capacity)
                 for i, s in enumerate(self.case.seqs)]
 
-    def run_block(self) -> np.ndarray:
+    def run_block(self, sinks=None) -> np.ndarray:
         out = torch.empty((self.case.batch, self.arch.hidden), dtype=torch.float32, device="cuda")
         gqa.attention_block_decode(self.arch, self.w_qkv, self.w_g, self.w_o, self.case.is_full,
-                                   self.seqs(), self.x, out, self.ws)
+                                   self.seqs(), self.x, out, self.ws,
+                                   sinks=None if sinks is None else f32_to_dev(sinks))
         torch.cuda.synchronize()
         return out.cpu().numpy()
 

@@ -144,19 +144,19 @@ def _attn_inputs(name, is_full, positions, ring, caps, case_id):
     return arch, case, q, gl
 
 
-def _oracle_attention(arch, case, q, gl):
+def _oracle_attention(arch, case, q, gl, sinks=None):
     """Attention over each cache as it is (the slot row already written) + gate."""
     out = []
     for i, s in enumerate(case.seqs):
         sl, ks, ar = oracle.kv_window(case.is_full, s.position, arch.sliding_window,
                                       s.ring_capacity)
         att = oracle.attention_decode(np.asarray(q[i], np.float64).reshape(arch.num_heads, -1),
-                                      s.k, s.v, sl, ks, ar, arch.attention_scale)
+                                      s.k, s.v, sl, ks, ar, arch.attention_scale, sinks)
         out.append(oracle.head_gate(att, gl[i]).reshape(-1))
     return np.stack(out)
 
 
-def _run_attention(arch, case, q, gl):
+def _run_attention(arch, case, q, gl, sinks=None):
     ga = arch_of(arch)
     k = [f16_to_dev(s.k) for s in case.seqs]
     v = [f16_to_dev(s.v) for s in case.seqs]
@@ -165,7 +165,8 @@ def _run_attention(arch, case, q, gl):
     ws = torch.empty(gqa.workspace_size(ga, len(seqs), max(s.position + 1 for s in case.seqs)),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((len(seqs), ga.q_dim), dtype=torch.float32, device="cuda")
-    gqa.attention_gated(ga, case.is_full, seqs, f32_to_dev(q), f32_to_dev(gl), out, ws)
+    gqa.attention_gated(ga, case.is_full, seqs, f32_to_dev(q), f32_to_dev(gl), out, ws,
+                        sinks=None if sinks is None else f32_to_dev(sinks))
     torch.cuda.synchronize()
     return out.cpu().numpy(), k, v
 
@@ -569,6 +570,95 @@ def test_layer_decode_matches_oracle(name, hidden, is_full, positions, ring):
     ref = oracle.block_decode(case.arch, is_full, case.w_qkv, case.w_g, case.w_o, xn, case.seqs)
     assert_parity(delta, ref.out, f"{name} residual delta")
     check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, name)
+
+
+# ----------------------------------------------------------------------------
+# attention sinks: one more logit per query head in each softmax, no value row
+# ----------------------------------------------------------------------------
+
+def _sinks(arch, case_id):
+    s = synth.random_sinks(arch, 0, case_id)
+    s[0] = -np.inf          # the same as no sink
+    s[1] = 200.0            # past fp32's exp range: the head's attention is 0
+    return s
+
+
+# every merge: in the partial kernel (<= 128 rows), small, mid and wide
+# combines, two launch groups
+SINK_ATTN_CASES = ["full_pos0_single_key", "full_pos63", "ring_pos513", "full_pos4095", "full_pos32767",
+                   "full_batch_mixed", "ring_batch_mixed", "full_batch33_two_launches", "full_batch_long"]
+
+
+@pytest.mark.parametrize("name", SINK_ATTN_CASES)
+def test_attention_gated_with_sinks(name):
+    _, is_full, positions, ring, caps = next(c for c in ATTN_CASES if c[0] == name)
+    say(f"attention_gated with sinks {name} positions={positions[:8]} ring={ring}")
+    arch, case, q, gl = _attn_inputs(name, is_full, positions, ring, caps, 20)
+    sinks = _sinks(arch, 21)
+    got, _, _ = _run_attention(arch, case, q, gl, sinks)
+    ref = _oracle_attention(arch, case, q, gl, sinks)
+    for b in range(len(positions)):
+        assert_parity(got[b], ref[b], f"{name}[{b}] gated attention with sinks")
+    assert not np.any(got[:, arch.head_dim:2 * arch.head_dim]), "head 1's sink must take all the weight"
+    plain, _, _ = _run_attention(arch, case, q, gl)
+    assert np.array_equal(got[:, :arch.head_dim].view(np.int32), plain[:, :arch.head_dim].view(np.int32)), \
+        "a sink of -inf must change nothing"
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3", "cfg5", "full32k"])
+def test_block_with_sinks_matches_oracle(name):
+    """The block's own merges (in the partial kernel, the fused merge +
+    o_proj launch, the batched combine) with sink logits."""
+    case = synth.NAMED_BLOCK_CASES[name]()
+    say(f"block with sinks {case.name} batch={case.batch}")
+    sinks = _sinks(case.arch, 22)
+    dev = DevBlock(case)
+    out = dev.run_block(sinks)
+    ref = oracle.block_decode(case.arch, case.is_full, case.w_qkv, case.w_g, case.w_o, case.x,
+                              case.seqs, sinks)
+    assert_parity(out, ref.out, f"{name} block output with sinks")
+    check_caches(case, dev.k, dev.v, ref.k16, ref.v16, ref.slots, name)
+
+
+@pytest.mark.parametrize("name", ["full_h264_p300_m40", "sliding_ring_h1024_p1035_m9"])
+def test_block_chunk_with_sinks_matches_oracle(name):
+    _, hidden, is_full, p0, m, ring = next(c for c in CHUNK_CASES if c[0] == name)
+    cap = ring if ring else p0 + m
+    case = synth.block_case(name, hidden, is_full, [p0], capacities=[cap], ring_capacity=ring, seed=0,
+                            case_id=32)
+    x = synth.random_hidden(hidden, m, 0, 32, tensor_id=90)
+    sinks = _sinks(case.arch, 23)
+    say(f"block_chunk with sinks {name}")
+    a = arch_of(case.arch)
+    k = f16_to_dev(case.seqs[0].k)
+    v = f16_to_dev(case.seqs[0].v)
+    ws = torch.empty(gqa.workspace_size(a, m, p0 + m), dtype=torch.uint8, device="cuda")
+    out = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
+    gqa.attention_block_chunk(a, bits_to_dev(case.w_qkv), bits_to_dev(case.w_g), bits_to_dev(case.w_o), is_full,
+                              gqa.KvSeq(k=k, v=v, position=p0, ring_capacity=ring), f32_to_dev(x), out, ws,
+                              sinks=f32_to_dev(sinks))
+    torch.cuda.synchronize()
+    ref = oracle.block_chunk(case.arch, is_full, case.w_qkv, case.w_g, case.w_o, x, case.seqs[0], m, sinks)
+    assert_parity(out.cpu().numpy(), ref.out, f"{name} chunk output with sinks")
+
+
+@pytest.mark.parametrize("name", ["full_h2560_pos4100_b1", "full_h1024_b5"])
+def test_layer_decode_with_sinks_matches_oracle(name):
+    _, hidden, is_full, positions, ring = next(c for c in LAYER_CASES if c[0] == name)
+    say(f"attention_layer_decode with sinks {name}")
+    case = synth.block_case(name, hidden, is_full, positions, ring_capacity=ring, seed=0, case_id=30)
+    w_norm = synth.random_bf16((hidden,), 0, 30, 77, std=0.1, mean=1.0)
+    h0 = synth.random_hidden(hidden, case.batch, 0, 30, tensor_id=78)
+    sinks = _sinks(case.arch, 24)
+    dev = DevBlock(case)
+    h = f32_to_dev(h0)
+    gqa.attention_layer_decode(dev.arch, bits_to_dev(w_norm), dev.w_qkv, dev.w_g, dev.w_o, is_full,
+                               dev.seqs(), h, dev.ws, sinks=f32_to_dev(sinks))
+    torch.cuda.synchronize()
+    delta = h.cpu().numpy().astype(np.float64) - h0.astype(np.float64)
+    xn = oracle.rms_norm(h0, w_norm, case.arch.rms_eps)
+    ref = oracle.block_decode(case.arch, is_full, case.w_qkv, case.w_g, case.w_o, xn, case.seqs, sinks)
+    assert_parity(delta, ref.out, f"{name} residual delta with sinks")
 
 
 @pytest.mark.parametrize("phase_full_first", [False, True])

@@ -183,10 +183,10 @@ def test_step_entry_points_validate():
                       1, FAKE, FAKE, None) == INVALID
     arr = B.c_seq_array(1)
     arr[0] = _seq(pos=100, cap=100)
-    assert B.raw_call("gqa_attention_gated", ctypes.byref(a), 1, arr, 1, FAKE, FAKE, FAKE, FAKE,
+    assert B.raw_call("gqa_attention_gated", ctypes.byref(a), 1, arr, 1, FAKE, FAKE, None, FAKE, FAKE,
                       1 << 30, None) == INVALID
     arr[0] = _seq()
-    assert B.raw_call("gqa_attention_gated", ctypes.byref(a), 1, arr, 1, FAKE, FAKE, FAKE, FAKE,
+    assert B.raw_call("gqa_attention_gated", ctypes.byref(a), 1, arr, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
                       16, None) == WS_SMALL
     assert B.raw_call("gqa_rms_norm_bf16w", FAKE, FAKE, FAKE, 1, 0, ctypes.c_float(1e-6),
                       None) == INVALID
