@@ -110,7 +110,12 @@ def counted_traffic(workload: str):
     return float(t.group(1))
 
 
-def cpu_baseline(case, seconds: float):
+def synth_sinks(case):
+    import synth
+    return synth.random_sinks(case.arch, 0, 1)
+
+
+def cpu_baseline(case, seconds: float, sinks=None):
     import numpy as np
     import oracle
     try:
@@ -121,7 +126,7 @@ def cpu_baseline(case, seconds: float):
     runs, t0 = 0, time.perf_counter()
     while True:
         oracle.block_decode(case.arch, case.is_full, case.w_qkv, case.w_g, case.w_o, case.x,
-                            case.seqs)
+                            case.seqs, sinks)
         runs += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -381,6 +386,8 @@ def main():
                     help="CPU oracle sample length (0 skips the baseline)")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per step instead of launching from the host")
+    ap.add_argument("--sinks", action="store_true",
+                    help="block workloads: pass per-head attention-sink logits (seeded, fp32 [Hq])")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -433,6 +440,8 @@ def main():
                                          position=s.position, ring_capacity=s.ring_capacity)
                                for i, s in enumerate(case.seqs)]))
     x = up(case.x)
+    sinks_np = synth_sinks(case) if args.sinks else None
+    sinks = up(sinks_np) if args.sinks else None
     out = torch.empty((case.batch, a.hidden), dtype=torch.float32, device="cuda:0")
     ws = torch.empty(gqa.workspace_size(a, case.batch, max(s.position + 1 for s in case.seqs)),
                      dtype=torch.uint8, device="cuda:0")
@@ -440,7 +449,8 @@ def main():
 
     # each copy's block call marshalled once (the binding's prepared call):
     # a step enqueues the same gqa_attention_block_decode
-    prepared = [gqa.PreparedBlock(a, s["w_qkv"], s["w_g"], s["w_o"], case.is_full, s["seqs"], x, out, ws)
+    prepared = [gqa.PreparedBlock(a, s["w_qkv"], s["w_g"], s["w_o"], case.is_full, s["seqs"], x, out, ws,
+                                  sinks=sinks)
                 for s in sets]
 
     def block_step(c):
@@ -454,7 +464,7 @@ def main():
     gqa.qkv_rope_kv(a, sets[0]["w_qkv"], sets[0]["w_g"], case.is_full, sets[0]["seqs"], x, q, gl)
 
     def attn_step(c):
-        gqa.attention_gated(a, case.is_full, sets[c]["seqs"], q, gl, attn, ws)
+        gqa.attention_gated(a, case.is_full, sets[c]["seqs"], q, gl, attn, ws, sinks=sinks)
 
     for c in range(copies):          # eager warm-up of every copy (also caches the CU count)
         block_step(c)
@@ -544,7 +554,7 @@ def main():
                 "algorithmic_bytes_per_launch": pb}
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(case, args.cpu_seconds)
+        cpu = cpu_baseline(case, args.cpu_seconds, sinks_np)
         log(f"cpu oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads ({cpu['sample']})")
 
     line = {
@@ -557,7 +567,7 @@ def main():
                    "kv_rows_attended": attended_rows(case), "weights": "bf16",
                    "kv_cache": "fp16", "block_bytes_per_step": bb, "copies_rotated": copies,
                    "launch": "hip_graph" if args.graph else "eager",
-                   "attention_chunk_rows": chunk_rows},
+                   "attention_chunk_rows": chunk_rows, "sinks": bool(args.sinks)},
         "attention_step_us": round(att_s * 1e6, 3),
         "host_submit_us_per_step": round(submitted / args.steps * 1e6, 3),
         "block_hbm_gbs": round(bb / (ms_per_step * 1e-3) / 1e9, 1),
