@@ -1607,7 +1607,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_mid_kernel(const AttnPa
 // o_proj is linear in the gated attention output, y = sum_h W_o[:, h] a_h
 // (W_o's column block h: head h's 256 dims), so the product splits over
 // query heads.  Workgroup (h, s) merges head h's chunk partials into a_h,
-// multiplies it into rows [s * kOprojRows, +kOprojRows) of column block h and
+// multiplies it into rows [s * ROWS, +ROWS) of column block h and
 // adds the result into y with fp32 atomics.  Every wave forms the chunk
 // weights itself (lane c holds chunk c's), wave w sums chunk group w of the
 // partials (chunks w, w + 4, ...), and one barrier joins the four groups in
@@ -1621,11 +1621,18 @@ __global__ __launch_bounds__(kThreads) void attn_combine_mid_kernel(const AttnPa
 // sum.  y must hold zeros (plain product: the partial kernel writes them) or
 // the residual stream (layer) before the launch.
 // ---------------------------------------------------------------------------
-constexpr int kOprojPairs = 10;                                // row pairs per wave
-constexpr int kOprojRows = 2 * kOprojPairs * (kThreads / 64);  // 80 rows per workgroup
+// PAIRS = row pairs per wave (at most 32, the lanes of a half wave); a
+// workgroup covers ROWS = 2 * PAIRS * 4 rows.  Each row slice re-reads the
+// head's 64 KB of partials from L2, so fewer, taller slices read less, as
+// long as the grid still fills the chip: 20 pairs (160 rows, 256 workgroups
+// at hidden 2560) measured 40.1 us per 32K block against 40.4-40.8 with 10
+// pairs and 41.5-41.9 with 14 or 16; at hidden 1024 (112 workgroups) 20
+// pairs were slower than 10 (cfg3 block 18.0 against 17.0-17.3 us).
 constexpr int kOprojBatch = 16;                                // chunks per thread loaded up front
-
+template <int PAIRS>
 __global__ __launch_bounds__(kThreads) void combine_oproj_kernel(const OprojParams p) {
+  static_assert(PAIRS >= 1 && PAIRS <= 32, "one row pair per lane of a half wave");
+  constexpr int ROWS = 2 * PAIRS * (kThreads / 64);
   __shared__ float4 s_acc[kThreads / 64][64];  // per chunk group: elements 4q .. 4q+3
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1648,10 +1655,10 @@ __global__ __launch_bounds__(kThreads) void combine_oproj_kernel(const OprojPara
   const int half = lane >> 5, cg = lane & 31;
   const unsigned row_bytes = (unsigned)Hq * kHeadDim * 2u;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_o, (unsigned)p.hidden * row_bytes);
-  const int rbase = blockIdx.y * kOprojRows + w * 2 * kOprojPairs + half;
-  uint4 wv[kOprojPairs];
+  const int rbase = blockIdx.y * ROWS + w * 2 * PAIRS + half;
+  uint4 wv[PAIRS];
 #pragma unroll
-  for (int i = 0; i < kOprojPairs; ++i) {
+  for (int i = 0; i < PAIRS; ++i) {
     const int r = rbase + 2 * i;
     wv[i] = buf_load16_p<kWeightPolicy>(rw, r < p.hidden ? (unsigned)r * row_bytes + (unsigned)(h * kHeadDim + cg * 8) * 2u
                                         : kOutOfRange);
@@ -1712,12 +1719,12 @@ __global__ __launch_bounds__(kThreads) void combine_oproj_kernel(const OprojPara
   // ---- rows: dot with a_h, sum over the 32 lanes of each half, add into y ----
   float mine = 0.f;
 #pragma unroll
-  for (int i = 0; i < kOprojPairs; ++i) {
+  for (int i = 0; i < PAIRS; ++i) {
     const float2 t = pair16(row_sum16(dot8_bf16(wv[i], xa, xb, 0.f)));
     if (cg == i) mine = t.x + t.y;
   }
   const int r = rbase + 2 * cg;
-  if (cg < kOprojPairs && r < p.hidden) unsafeAtomicAdd(p.y + r, mine);
+  if (cg < PAIRS && r < p.hidden) unsafeAtomicAdd(p.y + r, mine);
 }
 
 // ---------------------------------------------------------------------------
@@ -1851,8 +1858,15 @@ hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream) {
-  const dim3 grid(p.num_heads, (p.hidden + kOprojRows - 1) / kOprojRows);
-  hipLaunchKernelGGL(combine_oproj_kernel, grid, dim3(kThreads), 0, stream, p);
+  // the taller slices when they still give every CU a workgroup
+  constexpr int kTall = 20, kShort = 10;
+  const int tall_slices = (p.hidden + 8 * kTall - 1) / (8 * kTall);
+  if ((long)tall_slices * p.num_heads >= kAttnTargetWgs) {
+    hipLaunchKernelGGL(combine_oproj_kernel<kTall>, dim3(p.num_heads, tall_slices), dim3(kThreads), 0, stream, p);
+  } else {
+    const int slices = (p.hidden + 8 * kShort - 1) / (8 * kShort);
+    hipLaunchKernelGGL(combine_oproj_kernel<kShort>, dim3(p.num_heads, slices), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
