@@ -39,6 +39,36 @@ def test_library_exports_every_declared_symbol():
     assert sorted(B.EXPORTED_SYMBOLS) == names
 
 
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes mirrors have the size and field offsets that a C
+    compiler gives the header's structs (gcc on the host: plain C, no GPU)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    mirrors = {"gqa_arch": B._Arch, "gqa_layer_weights": B._Weights, "gqa_kv_seq": B._KvSeq,
+               "gqa_mlp_weights": B._MlpWeights}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
+    for cname, py in mirrors.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    # the header names hipStream_t nowhere (streams are void *), so plain C compiles it
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, field, val = ln.split()
+        got[(cname, field)] = int(val)
+    for cname, py in mirrors.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
 def test_rope_params_golden():
     for c in json.load(open(os.path.join(GOLDEN, "rope_params_for.json")))["cases"]:
         assert gqa.rope_params_for(c["is_full"], c["full_rotary_dim"], c["head_dim"],
