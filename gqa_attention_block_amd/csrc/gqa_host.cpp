@@ -132,6 +132,7 @@ gqa_status window_of(int is_full, int32_t position, int32_t window, int32_t ring
 struct Plan {
   int chunk = kChunkQuantum;
   bool direct = false;   // one chunk per sequence, finished by the partial kernel
+  int waves = 4;         // waves per workgroup of the partial kernel (4 or 2)
   struct Group {
     int first = 0, count = 0, total_chunks = 0;
   };
@@ -193,10 +194,11 @@ gqa_status resolve_seqs(const gqa_arch *a, int is_full, const gqa_kv_seq *seqs, 
 
 // Split-K plan.  One attention workgroup covers a chunk of rows for one KV
 // head (a quarter of the rows per wave).  The chunk is the largest multiple
-// of kChunkQuantum that still gives every launch about kAttnTargetWgs
+// of kChunkQuantum that still gives every launch about kAttnTargetWgs (twice
+// that for 2-wave workgroups)
 // workgroups (longer chunks spend less on each wave's set-up and on the
 // partials; fewer workgroups than the chip holds leave HBM bandwidth unused).
-// With C(c) chunks at chunk size c this keeps C <= 2 * kAttnTargetWgs / Hk +
+// With C(c) chunks at chunk size c this keeps C <= 2 * target / Hk +
 // sequences (see max_chunks).
 Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads, bool allow_direct) {
   Plan plan;
@@ -214,10 +216,14 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads, bool allow_di
   // short launches: half the workgroups, two tiles per wave instead of one
   // (measured at 4096 rows: 22.9 against 24.6 us per block; at 8192 rows and
   // beyond the full target is faster)
-  const int target = total <= kShortPlanRows ? kAttnTargetWgs / 2 : kAttnTargetWgs;
+  const bool direct = allow_direct && longest <= kDirectMaxRows;
+  // many long sequences: 2-wave workgroups, twice as many (two resident per CU)
+  plan.waves = !direct && (int)seqs.size() >= kNarrowMinSeqs && total > kShortPlanRows ? 2 : 4;
+  const int full = plan.waves == 2 ? 2 * kAttnTargetWgs : kAttnTargetWgs;
+  const int target = total <= kShortPlanRows ? full / 2 : full;
   const int cap = ceil_div(longest, kChunkQuantum) * kChunkQuantum;
   int chunk = kChunkQuantum;
-  if (allow_direct && longest <= kDirectMaxRows) {
+  if (direct) {
     chunk = cap;
     plan.direct = true;
   } else {
@@ -274,7 +280,7 @@ size_t chunk_partial_rows(int num_kv_heads, int32_t m, int32_t max_seq_len) {
 size_t max_chunks(int num_kv_heads, int32_t batch, int32_t max_seq_len) {
   const size_t seqs = (size_t)std::min<int32_t>(batch, kMaxSeqPerLaunch);
   const size_t finest = (size_t)ceil_div(max_seq_len, kChunkQuantum) * seqs;
-  const size_t bound = 2 * (size_t)ceil_div(kAttnTargetWgs, num_kv_heads) + seqs;
+  const size_t bound = 2 * (size_t)ceil_div(2 * kAttnTargetWgs, num_kv_heads) + seqs;   // the 2-wave target
   return std::max(std::min(finest, bound), chunk_partial_rows(num_kv_heads, batch, max_seq_len));
 }
 
@@ -410,6 +416,7 @@ AttnParams attn_params(const gqa_arch *a, const std::vector<SeqDesc> &seqs, cons
   p.qscale = (float)((double)a->attention_scale * kLog2e);
   p.chunk = plan.chunk;
   p.direct = plan.direct ? 1 : 0;
+  p.waves = plan.waves;
   p.nseq = g.count;
   p.total_chunks = g.total_chunks;
   int cb = 0;

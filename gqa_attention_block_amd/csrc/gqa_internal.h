@@ -22,6 +22,10 @@ constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles f
 // the split plan, and the workspace bound derived from it, are the same
 // everywhere.
 constexpr int kAttnTargetWgs = 256;
+// attn_partial_kernel runs workgroups of 4 waves (144 KB of LDS: one per CU)
+// or, for launches of at least kNarrowMinSeqs sequences longer than a short
+// plan, of 2 waves (72 KB: two per CU) aiming for twice the workgroups
+constexpr int kNarrowMinSeqs = 16;
 constexpr long kShortPlanRows = 4096;  // launches of at most this many window rows aim for half
 // Workgroups the several-token path aims for: (chunk, KV head, 16 tokens)
 // each, every wave walking all tiles of its chunk in sequence.  Measured on
@@ -72,6 +76,7 @@ struct AttnParams {
                       // per wave): a multiple of kChunkQuantum
   int direct;         // 1: every sequence is one chunk and the partial kernel writes
                       // the gated output itself (no partials, no combine)
+  int waves;          // waves per workgroup of attn_partial_kernel: 4 or 2
   int nseq;
   int total_chunks;
   float *zero_out;    // or null: workgroup 0 also writes zero_n zeros here (the output that

@@ -871,6 +871,7 @@ __device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 
 // compiler waits for a buffer's LDS-bound loads only before reading that
 // buffer (not for the other buffer's loads, which are still in flight).
 // sq is this wave's 4 KB staging area for its query fragments.
+template <int W>
 __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _Float16 *__restrict__ sk0,
                                                   _Float16 *__restrict__ sk1, _Float16 *__restrict__ sv0,
                                                   _Float16 *__restrict__ sv1, _Float16 *__restrict__ sq,
@@ -883,8 +884,8 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   const SeqDesc sd = p.seq[b];
   const int t0 = sd.kv_start + (cid - sd.chunk_begin) * p.chunk;
   const int nrows = min(p.chunk, sd.kv_start + sd.n - t0);
-  // wave w takes tiles w, w + 4, w + 8, ... of the chunk
-  const int ntiles = nrows > kTileRows * w ? (nrows - kTileRows * w + 4 * kTileRows - 1) / (4 * kTileRows) : 0;
+  // wave w of the W takes tiles w, w + W, w + 2W, ... of the chunk
+  const int ntiles = nrows > kTileRows * w ? (nrows - kTileRows * w + W * kTileRows - 1) / (W * kTileRows) : 0;
   const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
   const int ring = sd.ring;
   const int p0 = ring ? (t0 % ring) : t0;        // physical row of t0; a chunk wraps at most once
@@ -916,7 +917,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     for (int jj = 0; jj < 8; ++jj) {
       const int r = 2 * jj + (lane >> 5);
       const int pc = is_k ? (pos & 16) | ((pos ^ r) & 15) : pos ^ (2 * (r & 7));
-      const unsigned off = row_off((4 * t + w) * kTileRows + r);
+      const unsigned off = row_off((W * t + w) * kTileRows + r);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sbuf + jj * 512), 16,
                                                off == kOutOfRange ? off : off + 16u * (unsigned)pc, 0, 0,
                                                is_k ? kKPolicy : kVPolicy);
@@ -1013,7 +1014,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[i] = d[i] + dpp<0x104>(d[i]);             // row_shl:4 -> value of lane n+4
-      if (n >= kGroup || (4 * t + w) * kTileRows + 4 * G + i >= nrows) sc[i] = -INFINITY;
+      if (n >= kGroup || (W * t + w) * kTileRows + 4 * G + i >= nrows) sc[i] = -INFINITY;
       tmax = fmaxf(tmax, sc[i]);
     }
     tmax = max_across_rows(tmax);
@@ -1104,9 +1105,6 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   l_out = l_run;
 }
 
-// Workgroup = (chunk cid, KV head g); its 4 waves split the chunk's rows and
-// then merge in LDS, so one partial per (chunk, query head) is written.
-// 144 KB of LDS: one workgroup per CU, one wave per SIMD.
 // The attention-sink term of query head h's softmax denominator, relative to
 // the reference point M of the merged sum (log2 units): 2^(sigma_h log2(e) - M),
 // 0 without sinks.  Sink logits are in the units of the scaled scores and
@@ -1116,67 +1114,77 @@ __device__ __forceinline__ float sink_term(const float *sinks, int h, float M) {
   return sinks ? __builtin_amdgcn_exp2f(fmaf(sinks[h], 1.4426950408889634f, -M)) : 0.f;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void attn_partial_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) _Float16 s_k0[4][kTileHalves];
-  __shared__ __attribute__((aligned(1024))) _Float16 s_k1[4][kTileHalves];
-  __shared__ __attribute__((aligned(1024))) _Float16 s_v0[4][kTileHalves];
-  __shared__ __attribute__((aligned(1024))) _Float16 s_v1[4][kTileHalves];
+// Workgroup = (chunk cid, KV head g); its W waves split the chunk's rows and
+// then merge in LDS, so one partial per (chunk, query head) is written.
+// 36 KB of LDS per wave: W = 4 (144 KB) runs one workgroup per CU, W = 2
+// (72 KB) two; either way one wave per SIMD.  Measured on 32 sequences of up
+// to 16K rows: W = 2 with 512 workgroups 202.4 us against 209.6 us for W = 4
+// with 256; on one 32K sequence W = 2 was slower (26.5 against 26.1 us, and
+// 128 chunks slow the fused merge + o_proj).
+template <int W>
+__global__ __launch_bounds__(64 * W, 4 / W) void attn_partial_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) _Float16 s_k0[W][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_k1[W][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v0[W][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v1[W][kTileHalves];
   // per wave: its query fragments during the loop, then its (m, l) per query head
-  __shared__ __attribute__((aligned(16))) _Float16 s_q[4][2 * kGroup * kHeadDim];
+  __shared__ __attribute__((aligned(16))) _Float16 s_q[W][2 * kGroup * kHeadDim];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
   float m_run, l_run;
-  attn_partial_wave(p, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w], s_q[w], m_run, l_run);
+  attn_partial_wave<W>(p, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w], s_q[w], m_run, l_run);
   if (lane < kGroup) {
     float *ml = reinterpret_cast<float *>(s_q[w]);
     ml[lane] = m_run;
     ml[kGroup + lane] = l_run;
   }
   __syncthreads();
-  // wave w merges query head i = w of this KV head: lane l owns elements 4l .. 4l+3
+  // wave w merges query heads i = w, w + W, ... of this KV head: lane l owns
+  // elements 4l .. 4l+3
   const int Hk = p.num_kv_heads;
   const int Hq = Hk * kGroup;
   int cid, g;
   partial_unit(p, cid, g);
-  const int i = w;
-  auto m_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[i]; };
-  auto l_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[kGroup + i]; };
-  float M = -INFINITY;
+  for (int i = w; i < kGroup; i += W) {
+    auto m_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[i]; };
+    auto l_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[kGroup + i]; };
+    float M = -INFINITY;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, m_of(ww));
-  float L = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int ww = 0; ww < W; ++ww) M = fmaxf(M, m_of(ww));
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) {
-    const float mw = m_of(ww);
-    const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);   // a wave without rows
-    L = fmaf(wt, l_of(ww), L);
-    const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(s_v0[ww]) +
-                                                       i * kHeadDim + lane * 4);
-    o.x = fmaf(wt, v.x, o.x);
-    o.y = fmaf(wt, v.y, o.y);
-    o.z = fmaf(wt, v.z, o.z);
-    o.w = fmaf(wt, v.w, o.w);
-  }
-  if (p.direct) {
-    // the chunk is the whole window of sequence cid: normalise, gate, write
-    const int qh = g * kGroup + i;
-    const float gl = p.gate[(size_t)cid * p.ld_gate + qh];
-    const float sc = (1.0f / (1.0f + expf(-gl))) / (L + sink_term(p.sinks, qh, M));
-    float *dst = p.out + (size_t)cid * p.ld_out + (size_t)qh * kHeadDim;
-    const float v[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane * 4 + j;                  // element e holds dim 16 (e % 16) + e / 16
-      dst[16 * (e & 15) + (e >> 4)] = v[j] * sc;
+    for (int ww = 0; ww < W; ++ww) {
+      const float mw = m_of(ww);
+      const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);   // a wave without rows
+      L = fmaf(wt, l_of(ww), L);
+      const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(s_v0[ww]) +
+                                                         i * kHeadDim + lane * 4);
+      o.x = fmaf(wt, v.x, o.x);
+      o.y = fmaf(wt, v.y, o.y);
+      o.z = fmaf(wt, v.z, o.z);
+      o.w = fmaf(wt, v.w, o.w);
     }
-    return;
+    if (p.direct) {
+      // the chunk is the whole window of sequence cid: normalise, gate, write
+      const int qh = g * kGroup + i;
+      const float gl = p.gate[(size_t)cid * p.ld_gate + qh];
+      const float sc = (1.0f / (1.0f + expf(-gl))) / (L + sink_term(p.sinks, qh, M));
+      float *dst = p.out + (size_t)cid * p.ld_out + (size_t)qh * kHeadDim;
+      const float v[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane * 4 + j;                  // element e holds dim 16 (e % 16) + e / 16
+        dst[16 * (e & 15) + (e >> 4)] = v[j] * sc;
+      }
+      continue;
+    }
+    const size_t row = (size_t)cid * Hq + g * kGroup + i;
+    *reinterpret_cast<float4 *>(p.part_o + row * kHeadDim + lane * 4) = o;
+    if (lane == 0) *reinterpret_cast<float2 *>(p.part_ml + row * 2) = make_float2(M, L);
   }
-  const size_t row = (size_t)cid * Hq + g * kGroup + i;
-  *reinterpret_cast<float4 *>(p.part_o + row * kHeadDim + lane * 4) = o;
-  if (lane == 0) *reinterpret_cast<float2 *>(p.part_ml + row * 2) = make_float2(M, L);
-  if (blockIdx.x == 0 && p.zero_out)
-    for (int k = threadIdx.x; k < p.zero_n; k += kThreads) p.zero_out[k] = 0.f;
+  if (!p.direct && blockIdx.x == 0 && p.zero_out)
+    for (int k = threadIdx.x; k < p.zero_n; k += 64 * W) p.zero_out[k] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1979,7 +1987,11 @@ hipError_t launch_gelu_mul(float *gate, const float *up, int64_t n, hipStream_t 
 }
 
 hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
+  const dim3 grid(p.total_chunks * p.num_kv_heads);
+  if (p.waves == 2)
+    hipLaunchKernelGGL(attn_partial_kernel<2>, grid, dim3(128), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_partial_kernel<4>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1991,8 +2003,7 @@ hipError_t launch_attention_chunk(const ChunkAttnParams &p, hipStream_t stream) 
 }
 
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_partial_kernel, dim3(p.total_chunks * p.num_kv_heads), dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_attention_partials(p, stream);
   if (e != hipSuccess || p.direct) return e;
   return launch_combine(p, num_heads, stream);
 }
