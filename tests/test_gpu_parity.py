@@ -128,6 +128,10 @@ ATTN_CASES = [
     ("ring_batch_mixed", False, [3, 511, 512, 777, 32767], 512, None),
     ("full_batch33_two_launches", True, list(range(7, 7 + 33 * 37, 37)), 0, None),
     ("full_batch_long", True, [20000, 3000, 40000, 100], 0, None),
+    # 16 long sequences: the split-K pass runs 2-wave workgroups; 15: 4-wave
+    ("full_batch16_two_wave", True, list(range(700, 700 + 16 * 553, 553)), 0, None),
+    ("full_batch15_four_wave", True, list(range(700, 700 + 15 * 553, 553)), 0, None),
+    ("ring_batch16_two_wave", False, list(range(400, 400 + 16 * 2001, 2001)), 512, None),
 ]
 
 
@@ -191,7 +195,8 @@ def test_attention_gated(name, is_full, positions, ring, caps):
 # ----------------------------------------------------------------------------
 
 PARTIAL_CASES = ["full_pos0_single_key", "full_pos1000_ragged", "full_pos32767", "ring_pos513",
-                 "ring_pos32905", "full_batch_mixed", "ring_batch_mixed", "full_batch_long"]
+                 "ring_pos32905", "full_batch_mixed", "ring_batch_mixed", "full_batch_long",
+                 "full_batch16_two_wave", "ring_batch16_two_wave"]
 # stored element e of a partial holds dim 16 * (e % 16) + e // 16
 _PERM = np.array([16 * (e % 16) + e // 16 for e in range(256)])
 
@@ -586,7 +591,8 @@ def _sinks(arch, case_id):
 # every merge: in the partial kernel (<= 128 rows), small, mid and wide
 # combines, two launch groups
 SINK_ATTN_CASES = ["full_pos0_single_key", "full_pos63", "ring_pos513", "full_pos4095", "full_pos32767",
-                   "full_batch_mixed", "ring_batch_mixed", "full_batch33_two_launches", "full_batch_long"]
+                   "full_batch_mixed", "ring_batch_mixed", "full_batch33_two_launches", "full_batch_long",
+                   "full_batch16_two_wave"]
 
 
 @pytest.mark.parametrize("name", SINK_ATTN_CASES)
