@@ -23,9 +23,13 @@ constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles f
 // everywhere.
 constexpr int kAttnTargetWgs = 256;
 // attn_partial_kernel runs workgroups of 4 waves (144 KB of LDS: one per CU)
-// or, for launches of at least kNarrowMinSeqs sequences longer than a short
-// plan, of 2 waves (72 KB: two per CU) aiming for twice the workgroups
-constexpr int kNarrowMinSeqs = 16;
+// or, for launches of at least kNarrowMinSeqs sequences with more rows than
+// a short plan, of 2 waves (72 KB: two per CU) aiming for twice the
+// workgroups.  Measured (attention step, full layers, 16K rows per
+// sequence): 2, 4 and 8 sequences the same either way; 12 sequences 185 us
+// with 4 waves (288 workgroups on 256 CUs: a second round) against 137 us;
+// 32 ragged sequences (up to 16K) 209.6 against 201.7 us for the pass.
+constexpr int kNarrowMinSeqs = 2;
 constexpr long kShortPlanRows = 4096;  // launches of at most this many window rows aim for half
 // Workgroups the several-token path aims for: (chunk, KV head, 16 tokens)
 // each, every wave walking all tiles of its chunk in sequence.  Measured on

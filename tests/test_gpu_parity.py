@@ -128,9 +128,9 @@ ATTN_CASES = [
     ("ring_batch_mixed", False, [3, 511, 512, 777, 32767], 512, None),
     ("full_batch33_two_launches", True, list(range(7, 7 + 33 * 37, 37)), 0, None),
     ("full_batch_long", True, [20000, 3000, 40000, 100], 0, None),
-    # 16 long sequences: the split-K pass runs 2-wave workgroups; 15: 4-wave
+    # several long sequences: the split-K pass runs 2-wave workgroups
     ("full_batch16_two_wave", True, list(range(700, 700 + 16 * 553, 553)), 0, None),
-    ("full_batch15_four_wave", True, list(range(700, 700 + 15 * 553, 553)), 0, None),
+    ("full_batch15_two_wave", True, list(range(700, 700 + 15 * 553, 553)), 0, None),
     ("ring_batch16_two_wave", False, list(range(400, 400 + 16 * 2001, 2001)), 512, None),
 ]
 
