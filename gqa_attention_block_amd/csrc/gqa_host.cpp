@@ -228,6 +228,24 @@ Plan make_plan(const std::vector<SeqDesc> &seqs, int num_kv_heads, bool allow_di
     plan.direct = true;
   } else {
     while (chunk + kChunkQuantum <= cap && wgs(chunk + kChunkQuantum) >= target) chunk += kChunkQuantum;
+    // Workgroups past a multiple of the resident slots (one per CU, two with
+    // 2-wave workgroups) run as another round of full-length workgroups: from
+    // this chunk size up, take the least rounds x rows per chunk (ties: the
+    // larger chunk, fewer partials).  A round costs at least its chunk, so
+    // the search ends once the chunk alone exceeds the best cost.  Fewer
+    // chunks than the loop above chose, so the workspace bound still holds.
+    if (total > kShortPlanRows) {
+      const long slots = (long)kAttnTargetWgs * (plan.waves == 2 ? 2 : 1);
+      auto rounds = [&](int c) { return (wgs(c) + slots - 1) / slots; };
+      long best = rounds(chunk) * chunk;
+      for (int c = chunk + kChunkQuantum; c <= cap && c <= best; c += kChunkQuantum) {
+        const long cost = rounds(c) * c;
+        if (cost <= best) {
+          best = cost;
+          chunk = c;
+        }
+      }
+    }
   }
   plan.chunk = chunk;
   for (int first = 0; first < (int)seqs.size(); first += kMaxSeqPerLaunch) {
