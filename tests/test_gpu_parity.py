@@ -838,6 +838,32 @@ def test_prepared_calls_equal_the_plain_calls():
     assert np.max(np.abs(d)) <= 1e-5 * np.max(np.abs(res[0] - case.x)), "prepared layer + MLP differ"
 
 
+def test_prepared_calls_with_sinks_match_the_oracle():
+    """PreparedBlock and PreparedLayer pass the sink logits on (a full layer,
+    one sequence: the fused merge + o_proj tail), against the oracle."""
+    case = synth.block_case("prepared_sinks", 2560, True, [5000], seed=0, case_id=82)
+    sinks = _sinks(case.arch, 25)
+    dev = DevBlock(case)
+    out = torch.empty((1, 2560), dtype=torch.float32, device="cuda")
+    pb = gqa.PreparedBlock(dev.arch, dev.w_qkv, dev.w_g, dev.w_o, True, dev.seqs(), dev.x, out, dev.ws,
+                           sinks=f32_to_dev(sinks))
+    pb.step()
+    torch.cuda.synchronize()
+    ref = oracle.block_decode(case.arch, True, case.w_qkv, case.w_g, case.w_o, case.x, case.seqs, sinks)
+    assert_parity(out.cpu().numpy(), ref.out, "prepared block with sinks")
+    w_norm = synth.random_bf16((2560,), 0, 82, 77, std=0.1, mean=1.0)
+    h0 = synth.random_hidden(2560, 1, 0, 82, tensor_id=78)
+    dev2 = DevBlock(case)
+    h = f32_to_dev(h0)
+    gqa.PreparedLayer(dev2.arch, bits_to_dev(w_norm), dev2.w_qkv, dev2.w_g, dev2.w_o, True, dev2.seqs(), h,
+                      dev2.ws, sinks=f32_to_dev(sinks)).step()
+    torch.cuda.synchronize()
+    xn = oracle.rms_norm(h0, w_norm, case.arch.rms_eps)
+    ref2 = oracle.block_decode(case.arch, True, case.w_qkv, case.w_g, case.w_o, xn, case.seqs, sinks)
+    assert_parity(h.cpu().numpy().astype(np.float64) - h0.astype(np.float64), ref2.out,
+                  "prepared layer with sinks")
+
+
 def test_graph_replays_match_eager():
     """A block (one sequence, fused merge + o_proj tail, whose output is zeroed
     inside the partial kernel) and a whole decoder layer captured in HIP
