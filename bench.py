@@ -32,6 +32,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attn-block tokens/s + achieved HBM GB/s (% peak) at 32K ctx"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD published
+# what the path computes in: bf16 weights and fp16 K/V as stored, every
+# product accumulated in fp32
+DTYPE = "bf16w+fp16kv->fp32acc"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "gqa_attention_block_amd", "csrc", "gqa_kernels.hip")
 
@@ -52,11 +55,12 @@ def workloads():
 
 
 def attended_rows(case):
-    import oracle
+    """K/V rows the block reads, from the library's own window function."""
+    import gqa_attention_block_amd as gqa
     n = 0
     for s in case.seqs:
-        sl, ks, _ = oracle.kv_window(case.is_full, s.position, case.arch.sliding_window,
-                                     s.ring_capacity)
+        sl, ks, _ = gqa.kv_window(case.is_full, s.position, case.arch.sliding_window,
+                                  s.ring_capacity)
         n += sl - ks
     return n
 
@@ -81,14 +85,12 @@ def attention_bytes(case) -> int:
     return kv_row * attended_rows(case) + 4 * b * (a.q_dim + a.num_heads + a.q_dim)
 
 
-def partial_bytes(case, chunks: int) -> int:
-    """HBM bytes the split-K pass (the dominant kernel) must move: attended K/V
-    rows (fp16, all KV heads) and fp32 q in, one fp32 (O, m, l) partial per
-    chunk and query head out."""
+def kv_bytes(case) -> int:
+    """Algorithmic HBM bytes of the split-K pass (the dominant kernel): the
+    attended K/V rows, fp16, all KV heads, each read once.  The q it reads
+    (16 KB) and the partials it writes are workspace traffic, not counted."""
     a = case.arch
-    kv_row = 2 * 2 * a.num_kv_heads * a.head_dim
-    return (kv_row * attended_rows(case) + 4 * case.batch * a.q_dim
-            + 4 * chunks * a.num_heads * (a.head_dim + 2))
+    return 2 * 2 * a.num_kv_heads * a.head_dim * attended_rows(case)
 
 
 def source_digest() -> str:
@@ -258,7 +260,7 @@ def bench_stack(args):
     line = {
         "metric": METRIC, "value": round(1e3 / ms, 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": st.name, "hidden": a.hidden, "batch": 1, "layers": len(st.layers),
                    "positions": [st.layers[0].cache.position], "weights": "bf16", "kv_cache": "fp16",
@@ -306,7 +308,7 @@ def bench_head(args):
     line = {
         "metric": METRIC, "value": round(1e3 / ms, 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": f"head_h{hid}_vocab{vocab}", "hidden": hid, "vocab": vocab, "batch": 1,
                    "weights": "bf16", "algorithmic_bytes_per_step": alg},
@@ -361,7 +363,7 @@ def bench_chunk(args):
     line = {
         "metric": METRIC, "value": round(m / (ms * 1e-3), 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": case.name, "hidden": hid, "tokens_per_call": m, "positions": [p0, p0 + m - 1],
                    "weights": "bf16", "kv_cache": "fp16", "algorithmic_bytes_per_call": alg},
@@ -537,10 +539,10 @@ def main():
         return e0.elapsed_time(e1) * 1e-3 / n_runs
 
     part_s = timed(part_step)
-    pb = partial_bytes(case, begin[-1])
+    pb = kv_bytes(case)
     achieved = pb / part_s / 1e9
     log(f"attn_partial_kernel: {part_s * 1e6:.2f} us avg over {n_runs} back-to-back launches, "
-        f"{begin[-1]} chunks of {chunk_rows} rows, {pb / 1e6:.2f} MB -> {achieved:.1f} GB/s = "
+        f"{begin[-1]} chunks of {chunk_rows} rows, {pb / 1e6:.2f} MB of K/V -> {achieved:.1f} GB/s = "
         f"{achieved / HBM_PEAK_GBS:.3f} of peak")
     att_s = timed(attn_step)
     ab = attention_bytes(case)
@@ -552,6 +554,12 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "us_per_launch": round(part_s * 1e6, 3),
                 "algorithmic_bytes_per_launch": pb}
+    # the block as a whole (what the metric names): its algorithmic bytes over
+    # the wall time of a step
+    block_gbs = bb / (ms_per_step * 1e-3) / 1e9
+    block_roofline = {"bound": "hbm", "achieved": round(block_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(block_gbs / HBM_PEAK_GBS, 4), "us_per_step": round(ms_per_step * 1e3, 3),
+                      "algorithmic_bytes_per_step": bb}
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(case, args.cpu_seconds, sinks_np)
@@ -560,7 +568,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": case.name, "hidden": a.hidden, "batch": case.batch,
                    "positions": [s.position for s in case.seqs][:4],
@@ -573,6 +581,7 @@ def main():
         "block_hbm_gbs": round(bb / (ms_per_step * 1e-3) / 1e9, 1),
         "block_frac_of_peak": round(bb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "block_roofline": block_roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -30,5 +30,6 @@ from .binding import (  # noqa: F401
     residual_add,
     rms_norm_bf16w,
     rope_params_for,
+    split_plan,
     workspace_size,
 )

@@ -69,6 +69,9 @@ def _load():
                                          ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "gqa_kv_slot": (I32, [I32, I32]),
         "gqa_workspace_size": (ctypes.c_int, [A, I32, I32, ctypes.POINTER(S)]),
+        "gqa_split_plan": (ctypes.c_int, [A, ctypes.c_int, K, I32, ctypes.c_int, ctypes.POINTER(I32),
+                                          ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                          ctypes.POINTER(I32), ctypes.POINTER(I64)]),
         "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_attention_layer_decode": (ctypes.c_int, [A, W, P, ctypes.c_int, K, I32, P, P, S, P]),
         "gqa_attention_block_chunk": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
@@ -98,7 +101,7 @@ _lib = _load()
 
 #: symbols the header declares; tests check the library exports all of them
 EXPORTED_SYMBOLS = (
-    "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size",
+    "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size", "gqa_split_plan",
     "gqa_attention_block_decode", "gqa_attention_block_chunk", "gqa_attention_layer_decode", "gqa_qkv_rope_kv",
     "gqa_attention_gated",
     "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
@@ -183,6 +186,35 @@ def workspace_size(arch: Arch, batch: int, max_seq_len: int) -> int:
     _check(_lib.gqa_workspace_size(ctypes.byref(a), batch, max_seq_len, ctypes.byref(n)),
            "gqa_workspace_size")
     return n.value
+
+
+@dataclass
+class SplitPlan:
+    """The split-K schedule of one attention launch set (gqa_split_plan)."""
+    chunk_rows: int
+    waves: int
+    direct: bool
+    groups: int
+    max_group_chunks: int
+    chunk_bound: int
+
+
+def split_plan(arch: Arch, is_full: bool, positions: Sequence[int], ring_capacity: int = 0,
+               capacities: Optional[Sequence[int]] = None, allow_direct: bool = True) -> SplitPlan:
+    """Host-only: the plan for sequences at ``positions`` (cache capacities
+    default to position + 1, or ring_capacity on a ring).  The cache pointers
+    handed to the library are placeholders it checks but never dereferences."""
+    n = len(positions)
+    arr = (_KvSeq * max(1, n))()
+    for i, p in enumerate(positions):
+        cap = capacities[i] if capacities is not None else (ring_capacity or int(p) + 1)
+        arr[i] = _KvSeq(0x1000, 0x2000, int(cap), int(ring_capacity), int(p), 0)
+    out = [ctypes.c_int32() for _ in range(5)]
+    bound = ctypes.c_int64()
+    a = arch._c()
+    _check(_lib.gqa_split_plan(ctypes.byref(a), int(is_full), arr, n, int(allow_direct),
+                               *[ctypes.byref(o) for o in out], ctypes.byref(bound)), "gqa_split_plan")
+    return SplitPlan(out[0].value, out[1].value, bool(out[2].value), out[3].value, out[4].value, bound.value)
 
 
 # ----------------------------------------------------------------------------

@@ -106,6 +106,15 @@ gqa_status check_ptr(const void *p, const char *name) {
   return GQA_OK;
 }
 
+gqa_status check_batch(const gqa_arch *a, int32_t batch) {
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
+  const size_t widest = (size_t)std::max(a->hidden, a->num_heads * a->head_dim);
+  if ((size_t)batch * widest * sizeof(float) > kMaxBufferBytes)
+    return fail(GQA_ERR_UNSUPPORTED, "batch=%d makes an activation larger than %u bytes", batch,
+                kMaxBufferBytes);
+  return GQA_OK;
+}
+
 // ---- window, slot, RoPE parameters (pure) ---------------------------------
 
 gqa_status window_of(int is_full, int32_t position, int32_t window, int32_t ring, int32_t *seq_len,
@@ -575,6 +584,28 @@ gqa_status run_block(const gqa_arch *arch, const gqa_layer_weights *weights, int
   return run_o_proj(arch, weights, batch, attn, out, s);
 }
 }  // namespace
+
+gqa_status report(gqa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gqa_status block_workspace_need(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,
+                                const gqa_kv_seq *seqs, int32_t batch, size_t *need) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if ((st = check_weights(weights, true, true)) != GQA_OK) return st;
+  if ((st = check_batch(arch, batch)) != GQA_OK) return st;
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
+  *need = batch == 0 ? 0 : block_layout(arch, batch, make_plan(descs, arch->num_kv_heads, true).max_group_chunks).total;
+  return GQA_OK;
+}
 }  // namespace gqa
 
 using namespace gqa;
@@ -637,13 +668,26 @@ gqa_status gqa_workspace_size(const gqa_arch *arch, int32_t batch, int32_t max_s
   return ok();
 }
 
-gqa_status check_batch(const gqa_arch *a, int32_t batch) {
-  if (batch < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 0", batch);
-  const size_t widest = (size_t)std::max(a->hidden, a->num_heads * a->head_dim);
-  if ((size_t)batch * widest * sizeof(float) > kMaxBufferBytes)
-    return fail(GQA_ERR_UNSUPPORTED, "batch=%d makes an activation larger than %u bytes", batch,
-                kMaxBufferBytes);
-  return GQA_OK;
+gqa_status gqa_split_plan(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs, int32_t batch,
+                          int allow_direct, int32_t *chunk_rows, int32_t *waves, int32_t *direct,
+                          int32_t *groups, int32_t *max_group_chunks, int64_t *chunk_bound) {
+  if (!chunk_rows || !waves || !direct || !groups || !max_group_chunks || !chunk_bound)
+    return fail(GQA_ERR_INVALID_ARGUMENT, "null output pointer");
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if (batch < 1) return fail(GQA_ERR_INVALID_ARGUMENT, "batch=%d must be >= 1", batch);
+  std::vector<SeqDesc> descs;
+  if ((st = resolve_seqs(arch, is_full, seqs, batch, &descs)) != GQA_OK) return st;
+  const Plan plan = make_plan(descs, arch->num_kv_heads, allow_direct != 0);
+  int32_t longest = 1;
+  for (int32_t b = 0; b < batch; ++b) longest = std::max(longest, seqs[b].position + 1);
+  *chunk_rows = plan.chunk;
+  *waves = plan.waves;
+  *direct = plan.direct ? 1 : 0;
+  *groups = (int32_t)plan.groups.size();
+  *max_group_chunks = (int32_t)plan.max_group_chunks;
+  *chunk_bound = (int64_t)max_chunks(arch->num_kv_heads, batch, longest);
+  return ok();
 }
 
 gqa_status gqa_qkv_rope_kv(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,

@@ -13,7 +13,7 @@ constexpr int kGroup = 4;            // query heads per KV head
 constexpr int kThreads = 256;        // 4 wave64 per workgroup
 constexpr int kMaxSeqPerLaunch = 32; // sequence descriptors carried in kernel arguments
 constexpr int kTileRows = 16;        // attention rows per MFMA tile
-constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: whole tiles for each of 4 waves
+constexpr int kChunkQuantum = 4 * kTileRows;  // attention chunks: a multiple of 4 tiles (whole tiles per wave)
 // Attention workgroups a launch aims for: one wave per SIMD of MI355X
 // (256 CUs x 4 SIMDs, 4 waves per workgroup).  Measured on a 32K-row window:
 // 1024 waves of 8 tiles finish together, while 2048 waves of 4 tiles (the two
@@ -76,8 +76,8 @@ struct AttnParams {
                       // head, no value row), or null: none
   int num_kv_heads;
   float qscale;       // attention_scale * log2(e): scores come out in log2 units
-  int chunk;          // rows per chunk (one workgroup per chunk and KV head, a quarter
-                      // per wave): a multiple of kChunkQuantum
+  int chunk;          // rows per chunk (one workgroup per chunk and KV head, interleaved
+                      // 16-row tiles per wave): a multiple of kChunkQuantum
   int direct;         // 1: every sequence is one chunk and the partial kernel writes
                       // the gated output itself (no partials, no combine)
   int waves;          // waves per workgroup of attn_partial_kernel: 4 or 2
@@ -208,5 +208,13 @@ hipError_t launch_qkv_mfma(const QkvParams &p, hipStream_t stream);
 hipError_t launch_rms_norm(const float *h, const uint16_t *w, float *out, int rows,
                            int hidden, float eps, hipStream_t stream);
 hipError_t launch_residual_add(float *h, const float *o, int64_t n, hipStream_t stream);
+
+// Host side (gqa_host.cpp): checks every argument of gqa_attention_block_decode
+// except x_normed, out and the workspace, and gives the workspace bytes the
+// block needs for these sequences (0 for batch 0).  Sets the error string.
+gqa_status block_workspace_need(const gqa_arch *arch, const gqa_layer_weights *weights, int is_full,
+                                const gqa_kv_seq *seqs, int32_t batch, size_t *need);
+// Records a failure in the thread-local error string and returns st.
+gqa_status report(gqa_status st, const char *fmt, ...);
 
 }  // namespace gqa

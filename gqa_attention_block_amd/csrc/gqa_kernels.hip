@@ -790,21 +790,20 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
 // ---------------------------------------------------------------------------
 // Attention, split-K over the window, on the matrix cores.
 //
-// Workgroup blockIdx.x = cid * Hk + g owns chunk cid (logical positions
-// [t0, t0 + chunk) of one sequence) for KV head g and serves that head's 4
-// query heads, so each KV byte is read from HBM once; consecutive workgroups
-// are the KV heads of one chunk (neighbouring bytes of the same rows).  Wave w
-// takes the w-th quarter of the chunk's rows.  This token's k and v are
-// already in the cache (the qkv kernel wrote them), so every row of the window
-// is read the same way.
+// A workgroup owns chunk cid (logical positions [t0, t0 + chunk) of one
+// sequence) for KV head g (partial_unit gives the map) and serves that head's
+// 4 query heads, so each KV byte is read from HBM once.  Its W waves (4, or 2
+// for batches) take interleaved 16-row tiles of the chunk: wave w tiles w,
+// w + W, w + 2W, ...  This token's k and v are already in the cache (the qkv
+// kernel wrote them), so every row of the window is read the same way.
 //
 // Both products are small dense contractions per 16-row tile -- S = K q for
 // 4 query heads and O += P V -- and on VALU they cost ~65 instructions per
 // row, more than the HBM stream leaves room for; on MFMA they cost ~2.
 // Per 16-row tile:
 //   S^T[16 rows x 16] = K[16 x 256] * Qf[256 x 16] with
-//           v_mfma_f32_16x16x32_f16: the K fragments come straight from HBM
-//           into registers (lane l: row l%16, 8 dims), Qf's columns 0-3 hold
+//           v_mfma_f32_16x16x32_f16: the K tile is staged in LDS and read
+//           as A fragments (lane l: row l%16, 8 dims), Qf's columns 0-3 hold
 //           the fp16 high part of the 4 query heads (pre-scaled by
 //           scale*log2(e)) and 4-7 the fp16 low part (q - hi), so
 //           S = hi + lo keeps fp32 accuracy.
@@ -814,11 +813,11 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
 //           exp2(s - m) for the 4 heads, rows 4-7 the low part; V goes from
 //           HBM straight into LDS (buffer_load ... lds) and is read back
 //           transposed (ds_read_b64_tr_b16) into the B-operand layout.
-// K and V of the next tile are in flight while a tile is computed (K in
-// ping-pong registers, V in two LDS buffers).  Buffer loads whose offsets are
-// out of range return zeros without an HBM access, which pads the last tile.
-// The 4 waves then merge their (m, l, O) in LDS and the workgroup writes one
-// partial per query head; attn_combine_kernel merges the chunks.
+// K and V of the next tile are in flight while a tile is computed (two LDS
+// buffers each per wave).  Buffer loads whose offsets are out of range return
+// zeros without an HBM access, which pads the last tile.  The W waves then
+// merge their (m, l, O) in LDS and the workgroup writes one partial per query
+// head; a combine kernel (or the fused merge + o_proj) merges the chunks.
 // ---------------------------------------------------------------------------
 
 // Workgroup -> (chunk cid, KV head g).  The hardware deals workgroups to the

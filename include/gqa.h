@@ -37,6 +37,23 @@
  *     activations and every intermediate fp32, accumulation fp32.
  *   - Kernels specialise head_dim == 256 and num_heads == 4 * num_kv_heads;
  *     other shapes return GQA_ERR_UNSUPPORTED.
+ *
+ * Precision and range (all within the parity bar of relative L2 error <= 1e-3
+ * and max abs error <= 5e-3 max|ref| against an fp64 evaluation; not checked
+ * at run time, since the values live on the device):
+ *   - Attention runs on fp16 matrix cores with fp32 accumulation.  Each query
+ *     element is scaled by attention_scale * log2(e) and carried as an fp16
+ *     high part plus an fp16 low part (about 22 significant bits), so every
+ *     |q_i| * attention_scale * log2(e) must stay below 65504, the fp16
+ *     maximum: |q_i| < 7.2e5 at the published scale 1/16.  Larger values
+ *     overflow to inf.  Softmax weights are split the same way and are at
+ *     most 2^8.
+ *   - Projections below batch 4 run on fp32 VALU.  From batch 4 they run on
+ *     bf16 matrix cores: each activation element is carried as a bf16 high
+ *     part plus a bf16 low part, i.e. to within 2^-16 of its magnitude
+ *     (about 16 significant bits), while the bf16 weights are exact.
+ *   - RoPE angles are formed and reduced mod 2 pi in fp64; sin and cos are
+ *     then taken in fp32.  k and v are rounded to fp16 once, after RoPE.
  */
 #ifndef GQA_H_
 #define GQA_H_
@@ -145,6 +162,28 @@ int32_t gqa_kv_slot(int32_t position, int32_t ring_capacity);
  * max_seq_len (an upper bound valid for every layer class). */
 gqa_status gqa_workspace_size(const gqa_arch *arch, int32_t batch, int32_t max_seq_len,
                               size_t *bytes);
+
+/* The split-K plan the attention launches use for these sequences (the
+ * library's own schedule, not a step of the pages; exposed so that its
+ * invariants can be checked on the host).  The attended rows of sequence i
+ * (gqa_kv_window) are cut into ceil(n_i / *chunk_rows) chunks, one workgroup
+ * per chunk and KV head; sequences go to launch groups of at most 32.
+ *   allow_direct  1: windows of at most 128 rows may run as one chunk that
+ *                 the partial pass finishes itself (the block's plan); 0: the
+ *                 plan of gqa_attention_partials
+ *   chunk_rows    rows per chunk (a multiple of 64)
+ *   waves         waves per attention workgroup (4, or 2 for batches)
+ *   direct        1 if the plan is the one-chunk direct form
+ *   groups        launch groups
+ *   max_group_chunks  chunks of the largest launch group
+ *   chunk_bound   the chunk count gqa_workspace_size provisions for this
+ *                 batch and the longest seq_len; max_group_chunks never
+ *                 exceeds it
+ * Host only; seqs[].k and .v must be non-null and 16-byte aligned but are not
+ * dereferenced.  Errors: as gqa_attention_block_decode's argument checks. */
+gqa_status gqa_split_plan(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs, int32_t batch,
+                          int allow_direct, int32_t *chunk_rows, int32_t *waves, int32_t *direct,
+                          int32_t *groups, int32_t *max_group_chunks, int64_t *chunk_bound);
 
 /* ---------------------------------------------------------------------------
  * The block.

@@ -189,6 +189,25 @@ def test_attention_gated(name, is_full, positions, ring, caps):
         assert np.array_equal(v[i].cpu().numpy().view(np.int16), s.v.view(np.int16))
 
 
+@pytest.mark.parametrize("qmax", [1e3, 6e5])
+@pytest.mark.parametrize("name,is_full,positions,ring", [("full_pos4095", True, [4095], 0),
+                                                          ("ring_pos32767", False, [32767], 512),
+                                                          ("full_batch_long", True, [20000, 3000, 40000, 100], 0)])
+def test_attention_large_q_in_range(name, is_full, positions, ring, qmax):
+    """Query elements far from the N(0,1) of the other cases but inside the
+    documented range (|q_i| * scale * log2(e) below the fp16 maximum; 6e5 is
+    0.83 of that bound): the scores span thousands of log2 units and the
+    softmax is nearly one-hot, yet the output meets the same bar."""
+    say(f"attention_gated large q {name} qmax={qmax:g}")
+    arch, case, q, gl = _attn_inputs(name, is_full, positions, ring, None, 21)
+    q = (q / np.max(np.abs(q), axis=1, keepdims=True) * qmax).astype(np.float32)
+    assert float(np.max(np.abs(q))) * arch.attention_scale * 1.4426950408889634 < 65504.0
+    got, _, _ = _run_attention(arch, case, q, gl)
+    ref = _oracle_attention(arch, case, q, gl)
+    for b in range(len(positions)):
+        assert_parity(got[b], ref[b], f"{name}[{b}] gated attention, |q| up to {qmax:g}")
+
+
 # ----------------------------------------------------------------------------
 # the split-K pass alone: every chunk's partial against the oracle's attention
 # over that chunk's rows, and its partition function
@@ -534,12 +553,32 @@ def _run_stack(case: synth.StackCase):
     return (h - h0).cpu().numpy(), outs
 
 
+_STACKS = {}
+
+
+def _stack_and_ref(kind: str, phase_full_first: bool):
+    """The 36-layer stacks at position 8191 (the configuration the stack
+    benchmarks time) and their oracle results, generated once per session:
+    each takes about a minute to draw on the host."""
+    key = (kind, phase_full_first)
+    if key not in _STACKS:
+        if kind == "attention":
+            case = synth.cfg4_stack(phase_full_first=phase_full_first)
+            ref = oracle.stack_decode(case.arch, case.h, case.layers)
+        else:
+            case = synth.decoder_stack(phase_full_first=phase_full_first)
+            ref = oracle.decoder_stack_decode(case.arch, case.h, case.layers)
+        for other in [k for k in _STACKS if k[0] != kind]:
+            del _STACKS[other]   # one kind of stack (both phases) in host memory at a time
+        _STACKS[key] = (case, ref)
+    return _STACKS[key]
+
+
 @pytest.mark.parametrize("phase_full_first", [False, True])
 def test_stack_delta_matches_oracle(phase_full_first):
-    case = synth.cfg4_stack(phase_full_first=phase_full_first)
+    case, ref = _stack_and_ref("attention", phase_full_first)
     say(f"stack {case.name} phase_full_first={phase_full_first}")
     delta, outs = _run_stack(case)
-    ref = oracle.stack_decode(case.arch, case.h, case.layers)
     assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "stack residual delta")
     for li in range(len(case.layers)):
         assert_parity(outs[li], ref.block_outs[li], f"stack layer {li} block output")
@@ -667,6 +706,42 @@ def test_layer_decode_with_sinks_matches_oracle(name):
     assert_parity(delta, ref.out, f"{name} residual delta with sinks")
 
 
+def _run_fused_layer_stack(case):
+    """gqa_attention_layer_decode once per layer on one residual stream;
+    returns the total delta and each layer's contribution."""
+    a = arch_of(case.arch)
+    h = f32_to_dev(case.h)
+    ws = torch.empty(gqa.workspace_size(a, 1, case.layers[0].cache.position + 1), dtype=torch.uint8,
+                     device="cuda")
+    contrib = []
+    for L in case.layers:
+        k, v = f16_to_dev(L.cache.k), f16_to_dev(L.cache.v)
+        before = h.clone()
+        gqa.attention_layer_decode(a, bits_to_dev(L.w_norm), bits_to_dev(L.w_qkv), bits_to_dev(L.w_g),
+                                   bits_to_dev(L.w_o), L.is_full,
+                                   [gqa.KvSeq(k=k, v=v, position=L.cache.position,
+                                              ring_capacity=L.cache.ring_capacity)], h, ws)
+        contrib.append((h.double() - before.double()).cpu().numpy())
+    torch.cuda.synchronize()
+    delta = h.cpu().numpy().astype(np.float64) - np.asarray(case.h, np.float64)
+    return delta, contrib
+
+
+@pytest.mark.parametrize("phase_full_first", [False, True])
+def test_stack36_of_fused_layers_matches_oracle(phase_full_first):
+    """The benchmarked stack path at its own configuration: 36 layers of
+    gqa_attention_layer_decode at position 8191 (9 full layers over 8192
+    rows, 27 sliding layers over wrapped 512-slot rings), both phases of the
+    3:1 pattern; the total delta and every layer's contribution against the
+    oracle's block outputs."""
+    case, ref = _stack_and_ref("attention", phase_full_first)
+    say(f"fused-layer stack {case.name} phase_full_first={phase_full_first}")
+    delta, contrib = _run_fused_layer_stack(case)
+    assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "36-layer fused stack residual delta")
+    for li in range(len(case.layers)):
+        assert_parity(contrib[li], ref.block_outs[li], f"36-layer fused stack layer {li} contribution")
+
+
 @pytest.mark.parametrize("phase_full_first", [False, True])
 def test_stack_of_fused_layers_matches_oracle(phase_full_first):
     case = synth.cfg4_stack(num_layers=8, position=1000, phase_full_first=phase_full_first)
@@ -750,6 +825,38 @@ def test_decoder_stack_matches_oracle(phase_full_first):
     ref = oracle.decoder_stack_decode(case.arch, case.h, case.layers)
     delta = h.cpu().numpy().astype(np.float64) - np.asarray(case.h, np.float64)
     assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "decoder stack residual delta")
+
+
+def test_decoder_stack36_matches_oracle():
+    """The benchmarked whole-decoder path at its own configuration: 36 layers
+    of gqa_attention_layer_decode then gqa_mlp_decode (intermediate 7680) at
+    position 8191; the total delta and every layer's contribution (attention
+    plus MLP) against the oracle."""
+    case, ref = _stack_and_ref("decoder", False)
+    say(f"decoder stack {case.name}")
+    a = arch_of(case.arch)
+    h = f32_to_dev(case.h)
+    inter = case.layers[0].w_gate.shape[0]
+    ws = torch.empty(gqa.workspace_size(a, 1, case.layers[0].cache.position + 1), dtype=torch.uint8,
+                     device="cuda")
+    ws_mlp = torch.empty(gqa.mlp_workspace_size(a, inter, 1), dtype=torch.uint8, device="cuda")
+    contrib = []
+    for L in case.layers:
+        k, v = f16_to_dev(L.cache.k), f16_to_dev(L.cache.v)
+        before = h.clone()
+        gqa.attention_layer_decode(a, bits_to_dev(L.w_norm), bits_to_dev(L.w_qkv), bits_to_dev(L.w_g),
+                                   bits_to_dev(L.w_o), L.is_full,
+                                   [gqa.KvSeq(k=k, v=v, position=L.cache.position,
+                                              ring_capacity=L.cache.ring_capacity)], h, ws)
+        gqa.mlp_decode(a, bits_to_dev(L.w_post), bits_to_dev(L.w_gate), bits_to_dev(L.w_up),
+                       bits_to_dev(L.w_down), h, ws_mlp)
+        contrib.append((h.double() - before.double()).cpu().numpy())
+    torch.cuda.synchronize()
+    delta = h.cpu().numpy().astype(np.float64) - np.asarray(case.h, np.float64)
+    assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "36-layer decoder residual delta")
+    for li in range(len(case.layers)):
+        assert_parity(contrib[li], ref.block_outs[li], f"36-layer decoder layer {li} contribution")
+    _STACKS.clear()
 
 
 # ----------------------------------------------------------------------------
