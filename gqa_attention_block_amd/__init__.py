@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     PreparedMlp,
     attention_block_chunk,
     attention_block_decode,
+    attention_block_decode_noalloc,
     attention_gated,
     attention_layer_decode,
     attention_partials,

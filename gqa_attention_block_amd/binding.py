@@ -73,6 +73,7 @@ def _load():
                                           ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
                                           ctypes.POINTER(I32), ctypes.POINTER(I64)]),
         "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
+        "gqa_attention_block_decode_noalloc": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P]),
         "gqa_attention_layer_decode": (ctypes.c_int, [A, W, P, ctypes.c_int, K, I32, P, P, S, P]),
         "gqa_attention_block_chunk": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_qkv_rope_kv": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, P]),
@@ -102,7 +103,7 @@ _lib = _load()
 #: symbols the header declares; tests check the library exports all of them
 EXPORTED_SYMBOLS = (
     "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size", "gqa_split_plan",
-    "gqa_attention_block_decode", "gqa_attention_block_chunk", "gqa_attention_layer_decode", "gqa_qkv_rope_kv",
+    "gqa_attention_block_decode", "gqa_attention_block_decode_noalloc", "gqa_attention_block_chunk", "gqa_attention_layer_decode", "gqa_qkv_rope_kv",
     "gqa_attention_gated",
     "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
     "gqa_last_error", "gqa_mlp_workspace_size", "gqa_mlp_decode", "gqa_embed_tokens", "gqa_lm_head_workspace_size",
@@ -299,6 +300,21 @@ def attention_block_decode(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Seq
         _ptr(out, torch.float32, "out", b * arch.hidden),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
         "gqa_attention_block_decode")
+
+
+def attention_block_decode_noalloc(arch: Arch, w_qkv, w_g, w_o, is_full: bool, seqs: Sequence[KvSeq],
+                                   x: torch.Tensor, out: torch.Tensor, stream=None, sinks=None):
+    """The same block with its workspace in the library's static per-GPU
+    scratch (gqa_attention_block_decode_noalloc): no device allocation."""
+    b = len(seqs)
+    a = arch._c()
+    w = _weights(arch, w_qkv, w_g, w_o, sinks)
+    ks = _seqs(arch, seqs)
+    _check(_lib.gqa_attention_block_decode_noalloc(
+        ctypes.byref(a), ctypes.byref(w), int(is_full), ks, b,
+        _ptr(x, torch.float32, "x", b * arch.hidden),
+        _ptr(out, torch.float32, "out", b * arch.hidden), _stream(stream)),
+        "gqa_attention_block_decode_noalloc")
 
 
 class _Prepared:

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["gqa_kernels.hip", "gqa_head.hip", "gqa_host.cpp"]
+SOURCES = ["gqa_kernels.hip", "gqa_head.hip", "gqa_noalloc.hip", "gqa_host.cpp"]
 
 # Packed fp32 (v_pk_*_f32) is switched off for all device code; the host
 # pass warns that it does not know the feature, which is harmless.

@@ -210,6 +210,30 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
                                       const float *x_normed, float *out, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * block as gqa_attention_block_decode -- the same kernels, the same results --
+ * with its workspace in the library's own static device scratch of 8 MiB per
+ * GPU instead of a caller buffer.  The scratch is placed on each GPU when the
+ * library's code object is loaded there and is held until the process ends;
+ * its device address is looked up on the first call on a device (the
+ * calling thread's current device, which must own `stream` and the buffers;
+ * make that first call outside graph capture).  The call allocates no device
+ * memory.
+ *   arguments as for gqa_attention_block_decode, without the workspace.
+ * Every call on one GPU uses that GPU's one scratch, which keeps the last
+ * call's contents (nothing in it needs clearing between calls): calls that
+ * overlap on one GPU (other streams, other threads) race on it and must be
+ * serialised by the caller.
+ * Errors: those of gqa_attention_block_decode; GQA_ERR_WORKSPACE_TOO_SMALL
+ * when these sequences need more than the 8 MiB (the need grows with the
+ * batch: at the published head counts one sequence of any length takes about
+ * 1 MiB and 96 sequences about 4 MiB; gqa_workspace_size is an upper bound);
+ * GQA_ERR_GPU when the scratch's address cannot be obtained. */
+gqa_status gqa_attention_block_decode_noalloc(const gqa_arch *arch, const gqa_layer_weights *weights,
+                                              int is_full, const gqa_kv_seq *seqs, int32_t batch,
+                                              const float *x_normed, float *out, void *stream);
+
 /* M consecutive tokens of ONE sequence in one call: chunked prefill or the
  * verify step of a draft ([mod] the family's `prefill` module; [kvw] module
  * doc: chunked prefill reuses the per-token block, while the M-row path
