@@ -324,12 +324,14 @@ size_t partial_bytes_ml(const gqa_arch *a, size_t chunks) {
   return round_up(chunks * (size_t)a->num_heads * 2 * sizeof(float), 256);
 }
 
-// Block layout: [q | gate | attn | part_o | part_ml]; the attention step
-// alone uses [part_o | part_ml] from offset 0.
+// Block layout: [sync | q | gate | attn | part_o | part_ml]; the attention
+// step alone uses [sync | part_o | part_ml].  The synchronisation words of
+// the one-launch block (kSyncBytes) come first in both, so other paths never
+// overwrite them.
 Layout block_layout(const gqa_arch *a, int32_t batch, size_t chunks) {
   Layout L;
   const size_t q_dim = (size_t)a->num_heads * a->head_dim;
-  L.q = 0;
+  L.q = kSyncBytes;
   L.gate = L.q + round_up((size_t)batch * q_dim * sizeof(float), 256);
   L.attn = L.gate + round_up((size_t)batch * a->num_heads * sizeof(float), 256);
   L.part_o = L.attn + round_up((size_t)batch * a->num_heads * a->head_dim * sizeof(float), 256);
@@ -467,37 +469,80 @@ gqa_status run_attention(const gqa_arch *a, const std::vector<SeqDesc> &seqs, co
   return GQA_OK;
 }
 
-// One sequence whose window needs more than one chunk: the partial pass, then
-// the merge, gate and o_proj in one launch (combine_oproj_kernel), which adds
-// into y.  accumulate: y += W_o attn (the residual add) instead of y = W_o attn
-// (the partial kernel then zeroes y first).
-bool fused_tail(const Plan &plan, int32_t batch) {
-  return batch == 1 && !plan.direct && plan.groups.size() == 1;
+// One sequence whose window needs more than one chunk (longer than the
+// direct form's 128 rows) runs its attention through block_fused_kernel: the
+// whole block in one launch when x fits the kernel's LDS staging and o_proj
+// its registers, else its attention + merge phase between the projection and
+// o_proj launches.  Either way the merge of the chunks has one fixed order.
+bool fused_attention(const gqa_arch *a, const Plan &plan, int32_t batch) {
+  return batch == 1 && !plan.direct && plan.groups.size() == 1 &&
+         plan.groups[0].total_chunks <= kFusedMaxChunks && a->num_kv_heads <= 8;
+}
+bool fused_whole(const gqa_arch *a) {
+  return a->hidden <= kFusedMaxHidden && a->num_heads * a->head_dim <= kFusedMaxQDim;
 }
 
-gqa_status run_attention_oproj(const gqa_arch *a, const gqa_layer_weights *w, const std::vector<SeqDesc> &seqs,
-                               const Plan &plan, const float *q, const float *gate, float *part_o,
-                               float *part_ml, float *y, bool accumulate, hipStream_t stream) {
-  const Plan::Group &g = plan.groups[0];
-  AttnParams p = attn_params(a, seqs, plan, g, q, gate, nullptr, part_o, part_ml);
-  if (!accumulate) {
-    p.zero_out = y;
-    p.zero_n = a->hidden;
+FusedParams fused_params(const gqa_arch *a, int is_full, const SeqDesc &sd, const Plan &plan, int phases,
+                         const float *q, const float *gate, const float *sinks, float *part_o, float *part_ml,
+                         float *attn, void *sync) {
+  FusedParams p{};
+  p.phases = phases;
+  p.hidden = a->hidden;
+  p.rms_eps = a->rms_eps;
+  int32_t rdim;
+  double theta;
+  gqa_rope_params_for(is_full, a->full_rotary_dim, a->head_dim, a->full_rope_theta, a->rope_theta, &rdim, &theta);
+  p.rotary_dim = rdim;
+  p.log2_theta = log2(theta);
+  p.q = const_cast<float *>(q);
+  p.gate = const_cast<float *>(gate);
+  p.seq = sd;
+  p.seq.chunk_begin = 0;
+  p.chunk = plan.chunk;
+  p.nchunks = plan.groups[0].total_chunks;
+  p.qscale = (float)((double)a->attention_scale * kLog2e);
+  p.sinks = sinks;
+  p.part_o = part_o;
+  p.part_ml = part_ml;
+  p.a = attn;
+  p.sync = static_cast<unsigned long long *>(sync);
+  p.num_heads = a->num_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  return p;
+}
+
+// The block (or, with w_norm, the layer: y is then the residual stream and
+// takes y += W_o a) for one sequence through block_fused_kernel.
+gqa_status run_fused_block(const gqa_arch *a, const gqa_layer_weights *w, int is_full, const SeqDesc &sd,
+                           const Plan &plan, const float *x, const uint16_t *w_norm, float *y, bool accumulate,
+                           char *ws, const Layout &L, hipStream_t stream) {
+  float *q = reinterpret_cast<float *>(ws + L.q);
+  float *gate = reinterpret_cast<float *>(ws + L.gate);
+  float *attn = reinterpret_cast<float *>(ws + L.attn);
+  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
+  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+  const bool whole = fused_whole(a);
+  FusedParams p = fused_params(a, is_full, sd, plan, whole ? kPhaseQkv | kPhaseAttn | kPhaseOproj : kPhaseAttn, q,
+                               gate, w->sinks, part_o, part_ml, attn, ws);
+  hipError_t e;
+  if (whole) {
+    p.w_qkv = static_cast<const uint16_t *>(w->q_k_v_proj);
+    p.w_g = static_cast<const uint16_t *>(w->g_proj);
+    p.x = x;
+    p.w_norm = w_norm;
+    p.w_o = static_cast<const uint16_t *>(w->o_proj);
+    p.y = y;
+    p.accumulate = accumulate ? 1 : 0;
+    fused_tasks(p);
+    e = launch_block_fused(p, stream);
+    return e == hipSuccess ? GQA_OK : gpu_error(e, "one-launch block");
   }
-  hipError_t e = launch_attention_partials(p, stream);
-  if (e != hipSuccess) return gpu_error(e, "attention partial launch");
-  OprojParams op{};
-  op.part_o = part_o;
-  op.part_ml = part_ml;
-  op.gate = gate;
-  op.sinks = w->sinks;
-  op.nchunks = g.total_chunks;
-  op.num_heads = a->num_heads;
-  op.w_o = static_cast<const uint16_t *>(w->o_proj);
-  op.hidden = a->hidden;
-  op.y = y;
-  e = launch_combine_oproj(op, stream);
-  return e == hipSuccess ? GQA_OK : gpu_error(e, "combine + o_proj launch");
+  gqa_status st;
+  const std::vector<SeqDesc> one(1, sd);
+  if ((st = run_qkv_rope(a, w, is_full, one, x, q, gate, stream, w_norm)) != GQA_OK) return st;
+  fused_tasks(p);
+  if ((e = launch_block_fused(p, stream)) != hipSuccess) return gpu_error(e, "attention + merge launch");
+  return run_o_proj(a, w, 1, attn, y, stream, accumulate);
 }
 
 // y0 (= or +=) W0 x and y1 (= or +=) W1 x for `batch` rows of x [batch][cols]
@@ -576,9 +621,9 @@ gqa_status run_block(const gqa_arch *arch, const gqa_layer_weights *weights, int
   float *part_o = reinterpret_cast<float *>(ws + L.part_o);
   float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused_attention(arch, plan, batch))
+    return run_fused_block(arch, weights, is_full, descs[0], plan, x_normed, nullptr, out, false, ws, L, s);
   if ((st = run_qkv_rope(arch, weights, is_full, descs, x_normed, q, gate, s)) != GQA_OK) return st;
-  if (fused_tail(plan, batch))
-    return run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, out, false, s);
   if ((st = run_attention(arch, descs, plan, q, gate, weights->sinks, attn, part_o, part_ml, s)) != GQA_OK)
     return st;
   return run_o_proj(arch, weights, batch, attn, out, s);
@@ -734,13 +779,22 @@ gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_s
   if ((st = check_ptr(attn_gated, "attn_gated")) != GQA_OK) return st;
   if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
   const Plan plan = make_plan(descs, arch->num_kv_heads, true);
-  const size_t need = partial_bytes_o(arch, plan.max_group_chunks) + partial_bytes_ml(arch, plan.max_group_chunks);
+  const size_t need =
+      kSyncBytes + partial_bytes_o(arch, plan.max_group_chunks) + partial_bytes_ml(arch, plan.max_group_chunks);
   if (workspace_bytes < need)
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the attention needs %zu",
                 workspace_bytes, need);
   char *ws = static_cast<char *>(workspace);
-  float *part_o = reinterpret_cast<float *>(ws);
-  float *part_ml = reinterpret_cast<float *>(ws + partial_bytes_o(arch, plan.max_group_chunks));
+  float *part_o = reinterpret_cast<float *>(ws + kSyncBytes);
+  float *part_ml = reinterpret_cast<float *>(ws + kSyncBytes + partial_bytes_o(arch, plan.max_group_chunks));
+  if (fused_attention(arch, plan, batch)) {
+    // the block's attention + merge phase: the same kernel and order as the block
+    FusedParams p = fused_params(arch, is_full, descs[0], plan, kPhaseAttn, q_roped, gate_logits, sinks, part_o,
+                                 part_ml, attn_gated, ws);
+    fused_tasks(p);
+    hipError_t e = launch_block_fused(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : gpu_error(e, "attention + merge launch");
+  }
   st = run_attention(arch, descs, plan, q_roped, gate_logits, sinks, attn_gated, part_o, part_ml,
                      static_cast<hipStream_t>(stream));
   return st == GQA_OK ? ok() : st;
@@ -907,13 +961,14 @@ gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weig
   float *part_o = reinterpret_cast<float *>(ws + L.part_o);
   float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused_attention(arch, plan, batch)) {
+    st = run_fused_block(arch, weights, is_full, descs[0], plan, h, static_cast<const uint16_t *>(w_norm), h, true, ws,
+                         L, s);
+    return st == GQA_OK ? ok() : st;
+  }
   if ((st = run_qkv_rope(arch, weights, is_full, descs, h, q, gate, s, static_cast<const uint16_t *>(w_norm))) !=
       GQA_OK)
     return st;
-  if (fused_tail(plan, batch)) {
-    st = run_attention_oproj(arch, weights, descs, plan, q, gate, part_o, part_ml, h, true, s);
-    return st == GQA_OK ? ok() : st;
-  }
   if ((st = run_attention(arch, descs, plan, q, gate, weights->sinks, attn, part_o, part_ml, s)) != GQA_OK)
     return st;
   if ((st = run_o_proj(arch, weights, batch, attn, h, s, true)) != GQA_OK) return st;

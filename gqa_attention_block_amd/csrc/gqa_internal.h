@@ -83,8 +83,6 @@ struct AttnParams {
   int waves;          // waves per workgroup of attn_partial_kernel: 4 or 2
   int nseq;
   int total_chunks;
-  float *zero_out;    // or null: workgroup 0 also writes zero_n zeros here (the output that
-  int zero_n;         // combine_oproj_kernel then adds into with atomics)
   SeqDesc seq[kMaxSeqPerLaunch];
 };
 
@@ -110,20 +108,6 @@ struct ChunkAttnParams {
   SeqDesc seq;          // the cache (k, v, cache_bytes; ring = ring_capacity or 0)
 };
 
-// Merge of one sequence's split-K partials, the gate and o_proj in one launch
-// (combine_oproj_kernel): y[r] += sum_h W_o[r][h*D .. h*D + D) a_h.
-struct OprojParams {
-  const float *part_o;   // as AttnParams, chunks [0, nchunks) of the sequence
-  const float *part_ml;
-  const float *gate;     // [Hq] gate logits
-  const float *sinks;    // [Hq] attention-sink logits, or null
-  int nchunks;
-  int num_heads;         // Hq
-  const uint16_t *w_o;   // bf16 [hidden][Hq * D]
-  int hidden;
-  float *y;              // [hidden]: zeros (plain product) or the residual stream (layer)
-};
-
 // The fused projection step: q_k_v_proj and g_proj over the same x, then the
 // split, RoPE and the fp16 KV-slot write (uses seq[].k, .v, .slot, .position).
 struct QkvParams {
@@ -145,6 +129,52 @@ struct QkvParams {
                           // the projections see RMSNorm(h) * w_norm (eps rms_eps)
   float rms_eps;
   SeqDesc seq[kMaxSeqPerLaunch];
+};
+
+// The block for ONE sequence as one persistent launch (block_fused_kernel):
+// tasks of up to four phases run in dependency order, each marking itself
+// done in a flag word of the workspace's synchronisation area.
+constexpr int kPhaseQkv = 1;      // projections, split, RoPE, KV-slot write
+constexpr int kPhaseAttn = 2;     // split-K attention and the merge with the gate
+constexpr int kPhaseOproj = 4;    // o_proj
+constexpr int kSyncBytes = 32768; // synchronisation words at the start of the workspace
+constexpr int kFusedMaxChunks = 256;   // chunks per sequence the merge tasks take
+constexpr int kFusedMaxHidden = 4096;  // x staged in LDS beside the attention buffers
+constexpr int kFusedMaxQDim = 4096;    // o_proj rows held in registers
+// RoPE pairs per wave of a projection task: 3, so that the 4 x 768 pairs of
+// the family's 4 KV head groups make 256 tasks, one per CU
+__host__ __device__ constexpr int fused_pairs_per_wave(int) { return 3; }
+struct FusedParams {
+  int phases;             // kPhaseQkv | kPhaseAttn | kPhaseOproj, or kPhaseAttn alone
+  // projections
+  const uint16_t *w_qkv;  // bf16 [(Hq + 2 Hk) * D][hidden]
+  const uint16_t *w_g;    // bf16 [Hq][hidden]
+  int hidden;
+  const float *x;         // [hidden]: the normed input, or (w_norm set) the residual stream h
+  const uint16_t *w_norm; // bf16 [hidden] or null
+  float rms_eps;
+  int rotary_dim;
+  double log2_theta;
+  float *q;               // [Hq * D] RoPE'd q (written by the projections, read by the attention)
+  float *gate;            // [Hq] gate logits
+  // attention
+  SeqDesc seq;            // chunk_begin 0
+  int chunk;              // rows per chunk (the split-K plan's)
+  int nchunks;
+  float qscale;           // attention_scale * log2(e)
+  const float *sinks;     // [Hq] or null
+  float *part_o;          // [nchunks][Hq][D]
+  float *part_ml;         // [nchunks][Hq][2]
+  float *a;               // [Hq * D] gated attention (written by the merge, read by o_proj)
+  // o_proj
+  const uint16_t *w_o;    // bf16 [hidden][Hq * D]
+  float *y;               // [hidden]
+  int accumulate;         // 1: y += W_o a (the layer's residual add)
+  // scheduling
+  unsigned long long *sync;  // kSyncBytes of workspace
+  int num_heads, num_kv_heads;
+  int t_qkv, t_attn, t_merge, t_oproj;  // tasks of each phase (0 if it does not run)
+  int qkv_per_group;      // projection tasks per KV head group
 };
 
 // The embedding gather: h[b] = table[ids[b]] (bf16 row -> fp32), up to
@@ -189,6 +219,9 @@ struct GemvParams {
 };
 
 // Launchers (gqa_kernels.hip).  They return the hipError_t of the launch.
+// fused_tasks fills the task counts of p for its phases (hidden, heads, nchunks set).
+void fused_tasks(FusedParams &p);
+hipError_t launch_block_fused(const FusedParams &p, hipStream_t stream);
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);
@@ -196,8 +229,6 @@ hipError_t launch_attention_partials(const AttnParams &p, hipStream_t stream);
 hipError_t launch_gelu_mul(float *gate, const float *up, int64_t n, hipStream_t stream);
 hipError_t launch_mlp_gate_up(const MlpParams &p, hipStream_t stream);
 hipError_t launch_embed_gather(const EmbedParams &p, hipStream_t stream);
-// One sequence, any number of chunks.
-hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream);
 // The merge + gate launch of launch_attention alone (partials already written).
 hipError_t launch_combine(const AttnParams &p, int num_heads, hipStream_t stream);
 // Token groups of 16 (4 waves x 4 tokens) per chunk and KV head.

@@ -13,9 +13,11 @@
 //                           [kv_write.rs] `encode_attention_any`)
 //   attn_combine_kernel  -- merge of the split-K partials and the headwise
 //                           sigmoid gate ([attn.rs] gate step, before o_proj)
-//   combine_oproj_kernel -- for one sequence: that merge, the gate and the
-//                           o_proj GEMV in one launch ([attn.rs] gate step
-//                           and last GEMV)
+//   block_fused_kernel   -- the whole block for one sequence in one
+//                           persistent launch (every step above, then the
+//                           merge with the gate and the o_proj GEMV: [attn.rs]
+//                           gate step and last GEMV), or its attention and
+//                           merge alone
 //   gemv_bf16_kernel     -- the o_proj GEMV below the MFMA batch
 //                           ([attn.rs] last GEMV)
 //   proj_mfma_kernel     -- both projections on the matrix cores for batches
@@ -45,6 +47,8 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -318,25 +322,91 @@ __device__ __forceinline__ void rope_rotate(int position, int i, int rotary_dim,
   rope_apply(sn, cs, ya, yb);
 }
 
-// Epilogue of one output pair (rows dA, dB of section sec, head `head`) for
-// batch row b: RoPE, then q -> q_out (fp32), k and v -> fp16 into the cache
-// slot of this position, gate logits -> gate_out.
-__device__ __forceinline__ void qkv_write(const QkvParams &p, int sec, int head, bool rotate, float sn, float cs,
-                                          int dA, int dB, int b, float ya, float yb) {
-  const SeqDesc &sd = p.seq[b];
-  if (rotate) rope_apply(sn, cs, ya, yb);
-  if (sec == 0) {
-    float *q = p.q_out + (size_t)b * p.ld_q + (size_t)head * kHeadDim;
-    q[dA] = ya;
-    q[dB] = yb;
-  } else if (sec == 3) {
-    float *gl = p.gate_out + (size_t)b * p.ld_gate;
-    gl[dA] = ya;
-    gl[dB] = yb;
+// One RoPE pair of output rows: section sec (0 q, 1 k, 2 v, 3 gate logits),
+// head, pair index pi; rows dA, dB inside the head (rotated pairs (i, i+r/2),
+// the others (2i, 2i+1)) and the first weight row of the head.
+struct PairRows {
+  int sec, head, pi, dA, dB, base_row;
+  bool rotate;
+};
+
+__device__ __forceinline__ PairRows pair_rows(int sec, int head, int pi, int Hq, int Hk, int rotary_dim) {
+  PairRows r;
+  r.sec = sec;
+  r.head = head;
+  r.pi = pi;
+  const int rhalf = rotary_dim >> 1;
+  r.rotate = sec <= 1 && pi < rhalf;
+  r.dA = r.rotate ? pi : 2 * pi;
+  r.dB = r.rotate ? pi + rhalf : 2 * pi + 1;
+  r.base_row = sec == 0 ? head * kHeadDim
+             : sec == 1 ? (Hq + head) * kHeadDim
+             : sec == 2 ? (Hq + Hk + head) * kHeadDim : 0;
+  return r;
+}
+
+// Stores whose values other workgroups of the same launch read: written
+// through to the device's point of coherence (the sc1 scope bit), so a
+// reader on another XCD that loads them coherently sees them once the store
+// has completed.  COHERENT = false: plain stores (a later launch reads them).
+template <bool COHERENT>
+__device__ __forceinline__ void store_f32(float *p, float v) {
+  if constexpr (COHERENT)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+template <bool COHERENT>
+__device__ __forceinline__ void store_f16(_Float16 *p, float v) {
+  const _Float16 h = (_Float16)v;
+  if constexpr (COHERENT)
+    __hip_atomic_store(reinterpret_cast<uint16_t *>(p), __builtin_bit_cast(uint16_t, h), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = h;
+}
+constexpr int kCoherent = 16;   // buffer-instruction cache policy: sc1, device-coherent
+
+// Epilogue of one output pair for one sequence: RoPE, then q -> q_out
+// (fp32, [Hq][D]), k and v -> fp16 into the cache slot of this position,
+// gate logits -> gate_out ([Hq]).
+template <bool COHERENT = false>
+__device__ __forceinline__ void pair_store(float *q_out, float *gate_out, const SeqDesc &sd, int Hk, const PairRows &r,
+                                           float sn, float cs, float ya, float yb) {
+  if (r.rotate) rope_apply(sn, cs, ya, yb);
+  if (r.sec == 0) {
+    float *q = q_out + (size_t)r.head * kHeadDim;
+    store_f32<COHERENT>(q + r.dA, ya);
+    store_f32<COHERENT>(q + r.dB, yb);
+  } else if (r.sec == 3) {
+    store_f32<COHERENT>(gate_out + r.dA, ya);
+    store_f32<COHERENT>(gate_out + r.dB, yb);
   } else {
-    _Float16 *dst = (sec == 1 ? sd.k : sd.v) + (size_t)sd.slot * p.num_kv_heads * kHeadDim + (size_t)head * kHeadDim;
-    dst[dA] = (_Float16)ya;
-    dst[dB] = (_Float16)yb;
+    _Float16 *dst = (r.sec == 1 ? sd.k : sd.v) + (size_t)sd.slot * Hk * kHeadDim + (size_t)r.head * kHeadDim;
+    store_f16<COHERENT>(dst + r.dA, ya);
+    store_f16<COHERENT>(dst + r.dB, yb);
+  }
+}
+
+// The pair's two dot products with the staged x (s0: columns 8j .. 8j+3, s1:
+// 8j+4 .. 8j+7), summed over the wave; NORM scales them by inv_rms(h), the
+// workgroup's four wave sums of squares added in a fixed order.
+template <int NIT, bool NORM>
+__device__ __forceinline__ void pair_dots(const uint4 (&wa)[NIT], const uint4 (&wb)[NIT], const float4 *s0,
+                                          const float4 *s1, const float *ss, int hidden, float eps, int lane,
+                                          float &ya, float &yb) {
+  float a = 0.f, c = 0.f;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    a = dot8_bf16(wa[it], s0[it * 64 + lane], s1[it * 64 + lane], a);
+    c = dot8_bf16(wb[it], s0[it * 64 + lane], s1[it * 64 + lane], c);
+  }
+  ya = wave_sum(a);
+  yb = wave_sum(c);
+  if constexpr (NORM) {
+    const float inv = rsqrtf((ss[0] + ss[1] + ss[2] + ss[3]) / (float)hidden + eps);
+    ya *= inv;
+    yb *= inv;
   }
 }
 
@@ -366,14 +436,9 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
   } else {
     sec = 3; head = 0; pi = P - nq - nk - nv;
   }
-  const int rhalf = p.rotary_dim >> 1;
-  const bool rotate = sec <= 1 && pi < rhalf;
-  const int dA = rotate ? pi : 2 * pi;
-  const int dB = rotate ? pi + rhalf : 2 * pi + 1;
-  // rows in the weight matrices
-  const int base_row = sec == 0 ? head * kHeadDim
-                     : sec == 1 ? (Hq + head) * kHeadDim
-                     : sec == 2 ? (Hq + Hk + head) * kHeadDim : 0;
+  const PairRows pr = pair_rows(sec, head, pi, Hq, Hk, p.rotary_dim);
+  const bool rotate = pr.rotate;
+  const int dA = pr.dA, dB = pr.dB, base_row = pr.base_row;
   const unsigned row_bytes = (unsigned)p.hidden * 2u;
   const int qkv_rows = (Hq + 2 * Hk) * kHeadDim;
   const __amdgpu_buffer_rsrc_t rw = sec < 3 ? make_rsrc(p.w_qkv, (unsigned)qkv_rows * row_bytes)
@@ -409,19 +474,10 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
   };
   // the pair's dot products with staged x row m, then the epilogue for batch row b
   auto emit = [&](int m, int b, float sn, float cs) {
-    float a = 0.f, c = 0.f;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      a = dot8_bf16(wa[it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], a);
-      c = dot8_bf16(wb[it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], c);
-    }
-    float ya = wave_sum(a), yb = wave_sum(c);
-    if constexpr (NORM) {
-      const float inv = rsqrtf((s_ss[m][0] + s_ss[m][1] + s_ss[m][2] + s_ss[m][3]) / (float)p.hidden + p.rms_eps);
-      ya *= inv;
-      yb *= inv;
-    }
-    if (lane == 0 && active && b < p.batch) qkv_write(p, sec, head, rotate, sn, cs, dA, dB, b, ya, yb);
+    float ya, yb;
+    pair_dots<NIT, NORM>(wa, wb, s_x[m][0], s_x[m][1], s_ss[m], p.hidden, p.rms_eps, lane, ya, yb);
+    if (lane == 0 && active && b < p.batch)
+      pair_store(p.q_out + (size_t)b * p.ld_q, p.gate_out + (size_t)b * p.ld_gate, p.seq[b], Hk, pr, sn, cs, ya, yb);
   };
   if constexpr (ONE) {
     float sn, cs;
@@ -850,6 +906,20 @@ __device__ __forceinline__ int find_seq(const AttnParams &p, int chunk_id) {
 
 constexpr int kTileHalves = kTileRows * kHeadDim;   // one staged V tile: 8 KB
 
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (s_waitcnt vmcnt(N) in the gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their no-wait maxima).  The attention's tile
+// pipeline states its own waits: the compiler's tracking of loads into LDS
+// cannot always tell which staged buffer a read depends on, and where it
+// cannot it has been seen to leave the wait out.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // One column block J of a staged V tile: 64 lanes x 16 B from HBM into LDS
 // at sv + J KB + 16 B * lane.  The block's 64 B of each row is selected with
 // the scalar offset J * 64, which moves only the global address (the
@@ -870,19 +940,29 @@ __device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 
 // compiler waits for a buffer's LDS-bound loads only before reading that
 // buffer (not for the other buffer's loads, which are still in flight).
 // sq is this wave's 4 KB staging area for its query fragments.
-template <int W>
-__device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _Float16 *__restrict__ sk0,
+// The chunk: rows [t0, t0 + chunk) of sequence sd (chunk index ci inside
+// the sequence), KV head g, whose 4 query heads start at q_seq + g * 4 * D.
+// before_q() runs after the first tiles' loads are issued and before q is
+// read (the fused block kernel waits there for q); with tiles_after_wait the
+// first tiles are issued after it instead (the chunk holding this token's
+// row, which the wait makes visible).
+struct NoWait {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// QC: q is read coherently (other workgroups of the same launch wrote it);
+// its first tiles are then issued before before_q() waits for it.  TC: the
+// tiles are read coherently too and issued after the wait (the chunk holding
+// this token's cache row, written in the same launch).
+template <int W, bool QC = false, bool TC = false, typename BeforeQ = NoWait>
+__device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqDesc &sd, int ci, int chunk, int Hk,
+                                                  float qscale, int g, int w, _Float16 *__restrict__ sk0,
                                                   _Float16 *__restrict__ sk1, _Float16 *__restrict__ sv0,
                                                   _Float16 *__restrict__ sv1, _Float16 *__restrict__ sq,
-                                                  float &m_out, float &l_out) {
+                                                  float &m_out, float &l_out, BeforeQ before_q = BeforeQ()) {
   const int lane = threadIdx.x & 63;
-  const int Hk = p.num_kv_heads;
-  int cid, g;
-  partial_unit(p, cid, g);
-  const int b = find_seq(p, cid);
-  const SeqDesc sd = p.seq[b];
-  const int t0 = sd.kv_start + (cid - sd.chunk_begin) * p.chunk;
-  const int nrows = min(p.chunk, sd.kv_start + sd.n - t0);
+  const int t0 = sd.kv_start + ci * chunk;
+  const int nrows = min(chunk, sd.kv_start + sd.n - t0);
   // wave w of the W takes tiles w, w + W, w + 2W, ... of the chunk
   const int ntiles = nrows > kTileRows * w ? (nrows - kTileRows * w + W * kTileRows - 1) / (W * kTileRows) : 0;
   const unsigned row_bytes = (unsigned)Hk * kHeadDim * 2u;
@@ -919,30 +999,52 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
       const unsigned off = row_off((W * t + w) * kTileRows + r);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sbuf + jj * 512), 16,
                                                off == kOutOfRange ? off : off + 16u * (unsigned)pc, 0, 0,
-                                               is_k ? kKPolicy : kVPolicy);
+                                               (is_k ? kKPolicy : kVPolicy) | (TC ? kCoherent : 0));
     }
   };
   auto load_k = [&](_Float16 *sk, int t) { load_tile(sk, t, std::true_type{}); };
   auto load_v = [&](_Float16 *sv, int t) { load_tile(sv, t, std::false_type{}); };
 
-  // q first (its wait then does not include the tile loads): lane l takes
-  // dims 4l .. 4l+3 of the KV head's 4 query heads
-  float4 qv[kGroup];
-  {
-    const float *qh = p.q + (size_t)b * p.ld_q + (size_t)g * kGroup * kHeadDim + lane * 4;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) qv[i] = *reinterpret_cast<const float4 *>(qh + i * kHeadDim);
-  }
   // An even number of tiles (a padding tile is fully masked and its loads
   // are out of range: no HBM traffic), so that no load below is conditional
   // and the compiler's waits stay exact.
   // A wave without rows (a short chunk) runs two fully masked tiles: its
   // loads are out of range and it contributes m = -inf, l = 0, O = 0.
   const int ne = ntiles > 2 ? (ntiles + 1) & ~1 : 2;
-  load_k(sk0, 0);
-  load_v(sv0, 0);
-  load_k(sk1, 1);
-  load_v(sv1, 1);
+  auto first_tiles = [&]() {
+    load_k(sk0, 0);
+    load_v(sv0, 0);
+    load_k(sk1, 1);
+    load_v(sv1, 1);
+  };
+  // Without a wait, q is loaded first (its wait then does not include the
+  // tile loads); lane l takes dims 4l .. 4l+3 of the KV head's 4 query heads.
+  float4 qv[kGroup];
+  auto load_q = [&]() {
+    const float *qh = q_seq + (size_t)g * kGroup * kHeadDim + lane * 4;
+    if constexpr (QC) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(q_seq + (size_t)g * kGroup * kHeadDim, (unsigned)(kGroup * kHeadDim * 4));
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i)
+        qv[i] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(rq, (unsigned)((i * kHeadDim + lane * 4) * 4)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) qv[i] = *reinterpret_cast<const float4 *>(qh + i * kHeadDim);
+    }
+  };
+  if constexpr (TC) {
+    before_q();
+    first_tiles();
+    load_q();
+  } else if constexpr (QC) {
+    first_tiles();
+    before_q();
+    load_q();
+  } else {
+    before_q();
+    load_q();
+    first_tiles();
+  }
 
   // Query fragments, built while the first tiles are in flight: each lane
   // splits its dims (pre-scaled by scale * log2(e)) into fp16 high and low
@@ -951,7 +1053,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   // n < 4: hi(q_n); 4 <= n < 8: lo(q_{n-4}); else 0.
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) {
-    const float x[4] = {qv[i].x * p.qscale, qv[i].y * p.qscale, qv[i].z * p.qscale, qv[i].w * p.qscale};
+    const float x[4] = {qv[i].x * qscale, qv[i].y * qscale, qv[i].z * qscale, qv[i].w * qscale};
     half4_t hi, lo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -994,9 +1096,15 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
 #pragma unroll
   for (int c7 = 0; c7 < 8; ++c7) vaddr[c7] = vrow * 512 + 32 * (c7 ^ (vrow & 7)) + 16 * ((n >> 1) & 1) + 8 * (n & 1);
 
+  // Every tile is 8 load instructions per wave, issued in the order K_t, V_t,
+  // K_{t+1}, V_{t+1}, K_{t+2}, ...: before a tile is read, the loads issued
+  // after its own are the ones allowed in flight (24 inside the loop, then
+  // 24, 16, 8, 0 for the last two tiles).
+  //
   // S^T = K Qf for the staged K tile: d[i] = S[row 4G+i][column n]; column
   // n+4 holds the low part
-  auto scores = [&](const _Float16 *sk) {
+  auto scores = [&](const _Float16 *sk, auto wait) {
+    vm_wait<decltype(wait)::value>();
     const char *kbase = reinterpret_cast<const char *>(sk);
     half8_t kf[8];
 #pragma unroll
@@ -1007,7 +1115,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
     return d;
   };
   // online softmax of tile t's scores and O += P V from the staged V tile
-  auto process = [&](floatx4_t d, const _Float16 *sv, int t) {
+  auto process = [&](floatx4_t d, const _Float16 *sv, int t, auto wait) {
     float sc[4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -1052,6 +1160,7 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
       pf[i] = n < 4 ? hi : (n < 8 ? (_Float16)(pv - (float)hi) : (_Float16)0.f);
     }
     // O += P V; B fragments by transposed reads of the staged tile
+    vm_wait<decltype(wait)::value>();
     const char *base = reinterpret_cast<const char *>(sv);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
@@ -1063,22 +1172,29 @@ __device__ __forceinline__ void attn_partial_wave(const AttnParams &p, int w, _F
   // A K buffer is refilled as soon as its scores are formed (the MFMAs have
   // consumed every read of it), a V buffer after O += P V; sched_barrier keeps
   // each refill behind the reads of its buffer.
+  using in_flight_24 = std::integral_constant<int, 24>;
   for (int t = 0; t + 2 < ne; t += 2) {
-    floatx4_t d = scores(sk0);
+    floatx4_t d = scores(sk0, in_flight_24{});
     __builtin_amdgcn_sched_barrier(0);
     load_k(sk0, t + 2);
-    process(d, sv0, t);
+    process(d, sv0, t, in_flight_24{});
     __builtin_amdgcn_sched_barrier(0);
     load_v(sv0, t + 2);
-    d = scores(sk1);
+    d = scores(sk1, in_flight_24{});
     __builtin_amdgcn_sched_barrier(0);
     load_k(sk1, t + 3);
-    process(d, sv1, t + 1);
+    process(d, sv1, t + 1, in_flight_24{});
     __builtin_amdgcn_sched_barrier(0);
     load_v(sv1, t + 3);
   }
-  process(scores(sk0), sv0, ne - 2);
-  process(scores(sk1), sv1, ne - 1);
+  {
+    const floatx4_t d = scores(sk0, in_flight_24{});
+    process(d, sv0, ne - 2, std::integral_constant<int, 16>{});
+  }
+  {
+    const floatx4_t d = scores(sk1, std::integral_constant<int, 8>{});
+    process(d, sv1, ne - 1, std::integral_constant<int, 0>{});
+  }
 
   // ---- this wave's partial: add the high and low rows, stage (m, l, O) ----
   l_run = sum_across_rows(l_run);
@@ -1113,6 +1229,35 @@ __device__ __forceinline__ float sink_term(const float *sinks, int h, float M) {
   return sinks ? __builtin_amdgcn_exp2f(fmaf(sinks[h], 1.4426950408889634f, -M)) : 0.f;
 }
 
+// The W waves' (m, l, O) of query head i (staged by attn_partial_wave: (m, l)
+// at the start of each wave's sq, O in the first 4 KB of its sv0) merged into
+// one partial: M the largest m, L and lane l's elements 4l .. 4l+3 of O
+// weighed by 2^(m - M), waves in order.
+template <int W>
+__device__ __forceinline__ void merge_waves(const _Float16 (*sq)[2 * kGroup * kHeadDim],
+                                            const _Float16 (*sv0)[kTileHalves], int i, int lane, float &M, float &L,
+                                            float4 &o) {
+  auto m_of = [&](int ww) { return reinterpret_cast<const float *>(sq[ww])[i]; };
+  auto l_of = [&](int ww) { return reinterpret_cast<const float *>(sq[ww])[kGroup + i]; };
+  M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) M = fmaxf(M, m_of(ww));
+  L = 0.f;
+  o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) {
+    const float mw = m_of(ww);
+    const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);   // a wave without rows
+    L = fmaf(wt, l_of(ww), L);
+    const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(sv0[ww]) +
+                                                       i * kHeadDim + lane * 4);
+    o.x = fmaf(wt, v.x, o.x);
+    o.y = fmaf(wt, v.y, o.y);
+    o.z = fmaf(wt, v.z, o.z);
+    o.w = fmaf(wt, v.w, o.w);
+  }
+}
+
 // Workgroup = (chunk cid, KV head g); its W waves split the chunk's rows and
 // then merge in LDS, so one partial per (chunk, query head) is written.
 // 36 KB of LDS per wave: W = 4 (144 KB) runs one workgroup per CU, W = 2
@@ -1121,7 +1266,7 @@ __device__ __forceinline__ float sink_term(const float *sinks, int h, float M) {
 // with 256; on one 32K sequence W = 2 was slower (26.5 against 26.1 us, and
 // 128 chunks slow the fused merge + o_proj).
 template <int W>
-__global__ __launch_bounds__(64 * W, 4 / W) void attn_partial_kernel(const AttnParams p) {
+__global__ __launch_bounds__(64 * W, 1) void attn_partial_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) _Float16 s_k0[W][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_k1[W][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_v0[W][kTileHalves];
@@ -1130,8 +1275,14 @@ __global__ __launch_bounds__(64 * W, 4 / W) void attn_partial_kernel(const AttnP
   __shared__ __attribute__((aligned(16))) _Float16 s_q[W][2 * kGroup * kHeadDim];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, kept scalar
+  const int Hk = p.num_kv_heads;
+  const int Hq = Hk * kGroup;
+  int cid, g;
+  partial_unit(p, cid, g);
+  const int b = find_seq(p, cid);
   float m_run, l_run;
-  attn_partial_wave<W>(p, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w], s_q[w], m_run, l_run);
+  attn_partial_wave<W>(p.q + (size_t)b * p.ld_q, p.seq[b], cid - p.seq[b].chunk_begin, p.chunk, Hk, p.qscale, g, w,
+                       s_k0[w], s_k1[w], s_v0[w], s_v1[w], s_q[w], m_run, l_run);
   if (lane < kGroup) {
     float *ml = reinterpret_cast<float *>(s_q[w]);
     ml[lane] = m_run;
@@ -1140,30 +1291,10 @@ __global__ __launch_bounds__(64 * W, 4 / W) void attn_partial_kernel(const AttnP
   __syncthreads();
   // wave w merges query heads i = w, w + W, ... of this KV head: lane l owns
   // elements 4l .. 4l+3
-  const int Hk = p.num_kv_heads;
-  const int Hq = Hk * kGroup;
-  int cid, g;
-  partial_unit(p, cid, g);
   for (int i = w; i < kGroup; i += W) {
-    auto m_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[i]; };
-    auto l_of = [&](int ww) { return reinterpret_cast<const float *>(s_q[ww])[kGroup + i]; };
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww) M = fmaxf(M, m_of(ww));
-    float L = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      const float mw = m_of(ww);
-      const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);   // a wave without rows
-      L = fmaf(wt, l_of(ww), L);
-      const float4 v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(s_v0[ww]) +
-                                                         i * kHeadDim + lane * 4);
-      o.x = fmaf(wt, v.x, o.x);
-      o.y = fmaf(wt, v.y, o.y);
-      o.z = fmaf(wt, v.z, o.z);
-      o.w = fmaf(wt, v.w, o.w);
-    }
+    float M, L;
+    float4 o;
+    merge_waves<W>(s_q, s_v0, i, lane, M, L, o);
     if (p.direct) {
       // the chunk is the whole window of sequence cid: normalise, gate, write
       const int qh = g * kGroup + i;
@@ -1182,8 +1313,6 @@ __global__ __launch_bounds__(64 * W, 4 / W) void attn_partial_kernel(const AttnP
     *reinterpret_cast<float4 *>(p.part_o + row * kHeadDim + lane * 4) = o;
     if (lane == 0) *reinterpret_cast<float2 *>(p.part_ml + row * 2) = make_float2(M, L);
   }
-  if (!p.direct && blockIdx.x == 0 && p.zero_out)
-    for (int k = threadIdx.x; k < p.zero_n; k += 64 * W) p.zero_out[k] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1608,133 +1737,6 @@ __global__ __launch_bounds__(kThreads) void attn_combine_mid_kernel(const AttnPa
 }
 
 // ---------------------------------------------------------------------------
-// Merge of one sequence's split-K partials, the headwise gate and o_proj in
-// one launch.
-//
-// o_proj is linear in the gated attention output, y = sum_h W_o[:, h] a_h
-// (W_o's column block h: head h's 256 dims), so the product splits over
-// query heads.  Workgroup (h, s) merges head h's chunk partials into a_h,
-// multiplies it into rows [s * ROWS, +ROWS) of column block h and
-// adds the result into y with fp32 atomics.  Every wave forms the chunk
-// weights itself (lane c holds chunk c's), wave w sums chunk group w of the
-// partials (chunks w, w + 4, ...), and one barrier joins the four groups in
-// LDS.  Vector-memory loads return in issue order, so the loads are issued
-// as: (m, l) of chunks 0..63, the O values of the first kOprojBatch chunks of
-// each group, then the weights; the merge waits only for what it reads while
-// the weight bytes stream.  (Chunks past those are loaded after the weights
-// and wait for them.)
-// The sum over the Hq heads happens in the order the atomics land: y can
-// differ between runs by rounding, by at most the fp32 error of an Hq-term
-// sum.  y must hold zeros (plain product: the partial kernel writes them) or
-// the residual stream (layer) before the launch.
-// ---------------------------------------------------------------------------
-// PAIRS = row pairs per wave (at most 32, the lanes of a half wave); a
-// workgroup covers ROWS = 2 * PAIRS * 4 rows.  Each row slice re-reads the
-// head's 64 KB of partials from L2, so fewer, taller slices read less, as
-// long as the grid still fills the chip: 20 pairs (160 rows, 256 workgroups
-// at hidden 2560) measured 40.1 us per 32K block against 40.4-40.8 with 10
-// pairs and 41.5-41.9 with 14 or 16; at hidden 1024 (112 workgroups) 20
-// pairs were slower than 10 (cfg3 block 18.0 against 17.0-17.3 us).
-constexpr int kOprojBatch = 16;                                // chunks per thread loaded up front
-template <int PAIRS>
-__global__ __launch_bounds__(kThreads) void combine_oproj_kernel(const OprojParams p) {
-  static_assert(PAIRS >= 1 && PAIRS <= 32, "one row pair per lane of a half wave");
-  constexpr int ROWS = 2 * PAIRS * (kThreads / 64);
-  __shared__ float4 s_acc[kThreads / 64][64];  // per chunk group: elements 4q .. 4q+3
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x;
-  const int Hq = p.num_heads;
-  const int nch = p.nchunks;
-  const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)nch * Hq * 8u);
-  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)nch * Hq * kHeadDim * 4u);
-
-  // (m, l) of chunk `lane`; O of chunks w + 4j (j < kOprojBatch), elements 4 lane .. +3
-  const float2 ml0 = __builtin_bit_cast(float2, buf_load8(rml, ((unsigned)lane * Hq + h) * 8u));
-  float4 o[kOprojBatch];
-#pragma unroll
-  for (int j = 0; j < kOprojBatch; ++j) {
-    const unsigned c = (unsigned)(w + 4 * j);
-    o[j] = __builtin_bit_cast(float4, buf_load16(rpo, ((c * Hq + h) * kHeadDim + 4u * lane) * 4u));
-  }
-  // weights: lane (half, cg) holds rows rbase + 2i, columns h*256 + 8cg .. +8
-  const int half = lane >> 5, cg = lane & 31;
-  const unsigned row_bytes = (unsigned)Hq * kHeadDim * 2u;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_o, (unsigned)p.hidden * row_bytes);
-  const int rbase = blockIdx.y * ROWS + w * 2 * PAIRS + half;
-  uint4 wv[PAIRS];
-#pragma unroll
-  for (int i = 0; i < PAIRS; ++i) {
-    const int r = rbase + 2 * i;
-    wv[i] = buf_load16_p<kWeightPolicy>(rw, r < p.hidden ? (unsigned)r * row_bytes + (unsigned)(h * kHeadDim + cg * 8) * 2u
-                                        : kOutOfRange);
-  }
-
-  // ---- merge, per wave (no barrier): M = max_c m_c, w_c = exp2(m_c - M),
-  // L = sum_c w_c l_c; lane c < 64 keeps w_c ----
-  auto ml_of = [&](int c) { return *reinterpret_cast<const float2 *>(p.part_ml + ((size_t)c * Hq + h) * 2); };
-  const float m0 = lane < nch ? ml0.x : -INFINITY;
-  float m = m0;
-  for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, ml_of(c).x);
-  const float M = wave_max(m);
-  const float wt = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
-  float lsum = wt * ml0.y;
-  for (int c = lane + 64; c < nch; c += 64) {
-    const float2 ml = ml_of(c);
-    lsum = fmaf(ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M), ml.y, lsum);
-  }
-  const float L = wave_sum(lsum);
-
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int j = 0; j < kOprojBatch; ++j) {
-    const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), w + 4 * j));   // 0 past nch
-    acc.x = fmaf(wc, o[j].x, acc.x);
-    acc.y = fmaf(wc, o[j].y, acc.y);
-    acc.z = fmaf(wc, o[j].z, acc.z);
-    acc.w = fmaf(wc, o[j].w, acc.w);
-  }
-  for (int c = w + 4 * kOprojBatch; c < nch; c += 4) {
-    const float mc = ml_of(c).x;
-    const float wc = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-    const float4 v = *reinterpret_cast<const float4 *>(p.part_o + ((size_t)c * Hq + h) * kHeadDim + 4 * lane);
-    acc.x = fmaf(wc, v.x, acc.x);
-    acc.y = fmaf(wc, v.y, acc.y);
-    acc.z = fmaf(wc, v.z, acc.z);
-    acc.w = fmaf(wc, v.w, acc.w);
-  }
-  s_acc[w][lane] = acc;
-  __syncthreads();
-
-  // ---- a_h at this lane's 8 dims 8cg .. 8cg+7: element e = n * 16 + c holds
-  // dim 16c + n, so dim 8cg + k is element (8 (cg & 1) + k) * 16 + cg / 2 ----
-  const float sc = (1.0f / (1.0f + expf(-p.gate[h]))) / (L + sink_term(p.sinks, h, M));
-  const float *sa = reinterpret_cast<const float *>(s_acc);
-  float xv[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int e = (8 * (cg & 1) + k) * 16 + (cg >> 1);
-    float v = 0.f;
-#pragma unroll
-    for (int g = 0; g < kThreads / 64; ++g) v += sa[g * kHeadDim + e];
-    xv[k] = v * sc;
-  }
-  const float4 xa = make_float4(xv[0], xv[1], xv[2], xv[3]);
-  const float4 xb = make_float4(xv[4], xv[5], xv[6], xv[7]);
-
-  // ---- rows: dot with a_h, sum over the 32 lanes of each half, add into y ----
-  float mine = 0.f;
-#pragma unroll
-  for (int i = 0; i < PAIRS; ++i) {
-    const float2 t = pair16(row_sum16(dot8_bf16(wv[i], xa, xb, 0.f)));
-    if (cg == i) mine = t.x + t.y;
-  }
-  const int r = rbase + 2 * cg;
-  if (cg < PAIRS && r < p.hidden) unsafeAtomicAdd(p.y + r, mine);
-}
-
-// ---------------------------------------------------------------------------
 // RMSNorm with a bf16 weight: one workgroup per row.
 // ---------------------------------------------------------------------------
 // `out` may equal `h`: each thread reads h[c] before it writes out[c].
@@ -1793,6 +1795,422 @@ hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
   if (p.batch == 1) return qkv_launch_rb<NIT, 1, true>(p, stream);
   if constexpr (NIT <= 8) return qkv_launch_rb<NIT, 2, false>(p, stream);
   return qkv_launch_rb<NIT, 1, false>(p, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The whole block for one sequence in one launch.
+//
+// Run as separate launches, each step of the block pays a dispatch ramp
+// (workgroups start over several microseconds, XCD by XCD) and a tail in
+// which finished CUs idle, and a 31 MB projection launch on its own cannot
+// fill the memory pipeline.  block_fused_kernel runs the steps as one task
+// list in one persistent launch of one workgroup per CU:
+//   projection tasks  4 * P RoPE pairs each (P per wave), grouped by KV head
+//                     (its 4 query heads, then its k and v heads), then the
+//                     gate rows; each pair computed as qkv_rope_kernel does
+//   attention tasks   (chunk, KV head), chunk-major: attn_partial_wave and
+//                     the 4-wave merge of attn_partial_kernel, one partial
+//                     per query head
+//   merge tasks       (query head, quarter of its elements): the chunks'
+//                     partials merged in a fixed order, the sigmoid gate and
+//                     any sink applied, written to a
+//   o_proj tasks      4 * RW rows of W_o, each row computed as
+//                     gemv_bf16_kernel does (y = W_o a, or y += for the layer)
+// Workgroup b takes the tasks b, b + G, b + 2G, ... of each phase in phase
+// order (the merge tasks on the last workgroups, which have no o_proj task).
+// A task waits only for tasks of earlier phases: an attention task for the
+// projections of its KV head group, a merge task for the attention of its
+// group and the gate rows, an o_proj task for every merge.  The workgroup
+// holding the lowest unfinished task never waits on an unfinished one, so
+// the launch always progresses while its workgroups are resident (one per
+// CU, at most the CU count).  Before it waits, an attention task issues its
+// first K/V tiles (except the chunk holding this token's row) and an o_proj
+// task its rows of W_o, so one phase's end overlaps the next one's start.
+//
+// Values that cross workgroups (q, gate logits, this token's cache row,
+// partials, a) are stored and loaded device-coherently (the sc1 scope bit),
+// per access, instead of writing back and invalidating whole caches.  A task
+// marks itself done by storing the call's flag value in its own flag word
+// once its waves' stores have completed; waiting is polling those words.
+// The flag value is derived from an epoch word that every workgroup reads at
+// its start and that the last task of the list (which follows, through its
+// waits, the first task of every workgroup) advances, so flags need no
+// clearing and arbitrary initial workspace contents match a flag only with
+// probability 2^-64 per word.  Every value is computed by the code, and in
+// the order, of the step kernels: the block's output is bit-identical to its
+// steps' and the same on every run.
+//
+// Workspace words (64-bit): [0] epoch, then from word 8 one flag per
+// projection task, per attention task, per merge task.
+// ---------------------------------------------------------------------------
+constexpr int kFlagBase = 8;
+static_assert((kFlagBase + 800 + kFusedMaxChunks * 8 + 32 * 4) * 8 <= kSyncBytes, "flag words fit their bytes");
+// A wait gives up after this many polls (about a second): reached only if
+// calls overlap on one workspace, or if other work holds CUs the launch
+// needs; the kernel then still ends.
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kPairsPerGroup = (kGroup + 2) * (kHeadDim / 2);   // 4 q heads, k, v: 768 pairs
+constexpr int kFusedRowsPerWave = 32 / (kFusedMaxQDim / 512);   // o_proj rows per wave (4)
+
+__device__ __forceinline__ unsigned long long flag_value(unsigned long long epoch) {
+  return epoch * 0x9E3779B97F4A7C15ull ^ 0xD1B54A32D192ED03ull;
+}
+
+// Wave 0 polls the flags first + k * stride, k < count, until every one
+// holds fv; then the workgroup continues.  Every wave must call it.
+__device__ __forceinline__ void await_flags(const unsigned long long *flags, int first, int count, int stride,
+                                            unsigned long long fv) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    for (int i = 0; i < kSpinLimit; ++i) {
+      bool done = true;
+      for (int k = lane; k < count; k += 64)
+        done &= __hip_atomic_load(flags + first + k * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fv;
+      if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// The task's stores have completed in every wave; then its flag is set.
+__device__ __forceinline__ void set_flag(unsigned long long *flag, unsigned long long fv) {
+  vm_wait<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, fv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Projection task i: pairs [4 P i, 4 P (i + 1)) of q_k_v_proj in group-major
+// order, P per wave (the gate rows are computed by the merge tasks).  x is
+// staged in LDS by the workgroup's first projection task.
+template <int NIT, bool NORM, int P>
+__device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool staged,
+                                               float4 (*s_x)[StagedX<NIT>::kSlots], float *s_ss, int lane, int w) {
+  const int Hq = p.num_heads, Hk = p.num_kv_heads;
+  const unsigned row_bytes = (unsigned)p.hidden * 2u;
+  const int qkv_rows = (Hq + 2 * Hk) * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.w_qkv, (unsigned)qkv_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)p.hidden * 4u);
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u);
+  StagedX<NIT> xs;
+  if (!staged) xs.template issue<NORM>(rx, 0u, rn);
+  PairRows pr[P];
+  uint4 wa[P][NIT], wb[P][NIT];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int u = (i * 4 + w) * P + j;   // wave-uniform, < Hk * kPairsPerGroup
+    const int g = u / kPairsPerGroup, r = u - g * kPairsPerGroup;
+    int sec, head, pi;
+    if (r < kGroup * 128) {
+      sec = 0; head = g * kGroup + (r >> 7); pi = r & 127;
+    } else if (r < (kGroup + 1) * 128) {
+      sec = 1; head = g; pi = r - kGroup * 128;
+    } else {
+      sec = 2; head = g; pi = r - (kGroup + 1) * 128;
+    }
+    pr[j] = pair_rows(sec, head, pi, Hq, Hk, p.rotary_dim);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int col = (it * 64 + lane) * 8;
+      const bool ok = col < p.hidden;
+      wa[j][it] = buf_load16_p<kWeightPolicy>(
+          rq, ok ? (unsigned)(pr[j].base_row + pr[j].dA) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+      wb[j][it] = buf_load16_p<kWeightPolicy>(
+          rq, ok ? (unsigned)(pr[j].base_row + pr[j].dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+    }
+  }
+  // the rotations, while the loads are in flight
+  float sn[P], cs[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    sn[j] = 0.f;
+    cs[j] = 1.f;
+    if (pr[j].rotate) rope_sincos(p.seq.position, pr[j].pi, p.rotary_dim, p.log2_theta, sn[j], cs[j]);
+  }
+  if (!staged) {
+    const float ss = wave_sum(xs.template store<NORM>(s_x));
+    if (NORM && lane == 0) s_ss[w] = ss;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    float ya, yb;
+    pair_dots<NIT, NORM>(wa[j], wb[j], s_x[0], s_x[1], s_ss, p.hidden, p.rms_eps, lane, ya, yb);
+    if (lane == 0) pair_store<true>(p.q, p.gate, p.seq, Hk, pr[j], sn[j], cs[j], ya, yb);
+  }
+}
+
+// Merge task (query head h, elements 64 qd .. 64 qd + 63 of its partials):
+// the chunks merged in a fixed order, gated, written to a.  Lane c of every
+// wave takes chunks c, c + 64, ... for the reference max and the sum; thread
+// (cg, eq) sums elements 4 eq .. +3 of chunks cg, cg + 16, ..., and the 16
+// chunk groups are added in order.  The partials were written in this
+// launch: they are read coherently, and a is written so.  gl is the head's
+// gate logit.
+__device__ __forceinline__ void fused_merge_task(const FusedParams &p, int h, int qd, float gl, float2 *s_ml,
+                                                 float4 *s_acc, int tid, int lane) {
+  const int Hq = p.num_heads;
+  const int nch = p.nchunks;
+  const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)nch * Hq * 8u);
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)nch * Hq * kHeadDim * 4u);
+  for (int c = tid; c < nch; c += kThreads)
+    s_ml[c] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rml, ((unsigned)c * Hq + h) * 8u, 0,
+                                                                              kCoherent));
+  __syncthreads();
+  float m = -INFINITY;
+  for (int c = lane; c < nch; c += 64) m = fmaxf(m, s_ml[c].x);
+  const float M = wave_max(m);
+  float l = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const float2 ml = s_ml[c];
+    l = fmaf(ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M), ml.y, l);
+  }
+  const float L = wave_sum(l);
+  const int eq = tid & 15, cg = tid >> 4;
+  const unsigned po = ((unsigned)h * kHeadDim + 64u * qd + 4u * eq) * 4u;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = cg; c0 < nch; c0 += 4 * 16) {
+    float4 v[4];
+    float wc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + 16 * k;
+      v[k] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(rpo, c < nch ? po + (unsigned)c * Hq * kHeadDim * 4u
+                                                                              : kOutOfRange));
+      const float mc = c < nch ? s_ml[c].x : -INFINITY;
+      wc[k] = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc.x = fmaf(wc[k], v[k].x, acc.x);
+      acc.y = fmaf(wc[k], v[k].y, acc.y);
+      acc.z = fmaf(wc[k], v[k].z, acc.z);
+      acc.w = fmaf(wc[k], v[k].w, acc.w);
+    }
+  }
+  s_acc[cg * 16 + eq] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float4 tot = s_acc[tid];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) {
+      const float4 t = s_acc[k * 16 + tid];
+      tot.x += t.x;
+      tot.y += t.y;
+      tot.z += t.z;
+      tot.w += t.w;
+    }
+    const float sc = (1.0f / (1.0f + expf(-gl))) / (L + sink_term(p.sinks, h, M));
+    const float v[4] = {tot.x, tot.y, tot.z, tot.w};
+    float *dst = p.a + (size_t)h * kHeadDim;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 64 * qd + 4 * tid + j;             // element e holds dim 16 (e % 16) + e / 16
+      store_f32<true>(dst + 16 * (e & 15) + (e >> 4), v[j] * sc);
+    }
+  }
+}
+
+// The gate logit of query head h, computed by wave 0 as qkv_rope_kernel
+// computes g_proj's row pair (h / 2): x staged in LDS by the whole workgroup
+// (sum of squares for NORM as well), the two dot products over the wave.
+// The weight and x loads are issued by gate_issue before the merge task
+// waits; gate_finish stages x and returns the logit in every lane of wave 0.
+template <int NIT, bool NORM>
+struct GateRows {
+  StagedX<NIT> xs;
+  uint4 wa[NIT], wb[NIT];
+  __device__ __forceinline__ void issue(const FusedParams &p, int h, int lane) {
+    const unsigned row_bytes = (unsigned)p.hidden * 2u;
+    xs.template issue<NORM>(make_rsrc(p.x, (unsigned)p.hidden * 4u), 0u,
+                            make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.w_g, (unsigned)p.num_heads * row_bytes);
+    const int r = h & ~1;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int col = (it * 64 + lane) * 8;
+      const bool ok = threadIdx.x < 64 && col < p.hidden;
+      wa[it] = buf_load16_p<kWeightPolicy>(rg, ok ? (unsigned)r * row_bytes + (unsigned)col * 2u : kOutOfRange);
+      wb[it] = buf_load16_p<kWeightPolicy>(rg, ok ? (unsigned)(r + 1) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+    }
+  }
+  __device__ __forceinline__ float finish(const FusedParams &p, int h, float4 (*s_x)[StagedX<NIT>::kSlots],
+                                          float *s_ss, int lane, int w) {
+    const float ss = wave_sum(xs.template store<NORM>(s_x));
+    if (NORM && lane == 0) s_ss[w] = ss;
+    __syncthreads();
+    float ya = 0.f, yb = 0.f;
+    if (w == 0) pair_dots<NIT, NORM>(wa, wb, s_x[0], s_x[1], s_ss, p.hidden, p.rms_eps, lane, ya, yb);
+    return (h & 1) ? yb : ya;
+  }
+};
+
+template <int NIT, bool NORM>
+__global__ __launch_bounds__(kThreads, 1) void block_fused_kernel(const FusedParams p) {
+  constexpr int W = kThreads / 64;
+  constexpr int P = fused_pairs_per_wave(NIT);
+  constexpr int NITO = kFusedMaxQDim / 512;
+  constexpr int RW = kFusedRowsPerWave;
+  static_assert(kPairsPerGroup % (W * P) == 0, "a projection task stays inside one KV head group");
+  __shared__ __attribute__((aligned(1024))) _Float16 s_k0[W][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_k1[W][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v0[W][kTileHalves];
+  __shared__ __attribute__((aligned(1024))) _Float16 s_v1[W][kTileHalves];
+  __shared__ __attribute__((aligned(16))) _Float16 s_q[W][2 * kGroup * kHeadDim];
+  __shared__ float s_ss[W];
+  __shared__ float s_gate;
+  __shared__ unsigned long long s_epoch;
+  using XS = StagedX<NIT>;
+  static_assert(2 * XS::kSlots * sizeof(float4) <= sizeof(s_k0), "staged x fits the first K buffers");
+  static_assert(kFusedMaxChunks * sizeof(float2) <= sizeof(s_v0) && 256 * sizeof(float4) <= sizeof(s_v1),
+                "merge scratch fits the V buffers");
+  // x (projection tasks) shares the K buffers, the merge scratch the V
+  // buffers: a workgroup's tasks come in phase order
+  float4 (*s_x)[XS::kSlots] = reinterpret_cast<float4 (*)[XS::kSlots]>(&s_k0[0][0]);
+  float2 *s_ml = reinterpret_cast<float2 *>(&s_v0[0][0]);
+  float4 *s_acc = reinterpret_cast<float4 *>(&s_v1[0][0]);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hq = p.num_heads, Hk = p.num_kv_heads;
+  const int G = gridDim.x, b = blockIdx.x;
+  unsigned long long *const words = p.sync;
+  unsigned long long *const f_qkv = words + kFlagBase;
+  unsigned long long *const f_attn = f_qkv + p.t_qkv;
+  unsigned long long *const f_merge = f_attn + p.t_attn;
+  const bool has_qkv = p.t_qkv > 0;
+
+  if (tid == 0) s_epoch = __hip_atomic_load(words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned long long epoch = s_epoch;
+  const unsigned long long fv = flag_value(epoch);
+  // the last task of the list advances the epoch for the next call
+  const bool last_is_oproj = p.t_oproj > 0;
+  auto advance_epoch = [&]() {
+    if (tid == 0) __hip_atomic_store(words, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // ---- projections ----
+  bool staged = false;
+  for (int t = b; t < p.t_qkv; t += G) {
+    fused_qkv_task<NIT, NORM, P>(p, t, staged, s_x, s_ss, lane, w);
+    staged = true;
+    set_flag(f_qkv + t, fv);
+  }
+
+  // ---- attention ----
+  for (int t = b; t < p.t_attn; t += G) {
+    const int c = t / Hk, g = t - c * Hk;
+    auto wait_q = [&]() {
+      if (has_qkv) await_flags(f_qkv, g * p.qkv_per_group, p.qkv_per_group, 1, fv);
+    };
+    float m_run, l_run;
+    if (!has_qkv)
+      attn_partial_wave<W, false, false>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w],
+                                         s_v1[w], s_q[w], m_run, l_run, wait_q);
+    else if (c == p.nchunks - 1)   // holds this token's cache row
+      attn_partial_wave<W, true, true>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w],
+                                       s_q[w], m_run, l_run, wait_q);
+    else
+      attn_partial_wave<W, true, false>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w],
+                                        s_v1[w], s_q[w], m_run, l_run, wait_q);
+    if (lane < kGroup) {
+      float *ml = reinterpret_cast<float *>(s_q[w]);
+      ml[lane] = m_run;
+      ml[kGroup + lane] = l_run;
+    }
+    __syncthreads();
+    float M, L;
+    float4 o;
+    merge_waves<W>(s_q, s_v0, w, lane, M, L, o);   // wave w: query head g * 4 + w
+    const unsigned row = (unsigned)c * Hq + g * kGroup + w;
+    const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)p.nchunks * Hq * kHeadDim * 4u);
+    const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)p.nchunks * Hq * 8u);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), rpo, (row * kHeadDim + lane * 4) * 4u, 0,
+                                           kCoherent);
+    if (lane == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, make_float2(M, L)), rml, row * 8u, 0, kCoherent);
+    set_flag(f_attn + t, fv);
+    __syncthreads();   // s_q and s_v0 are rewritten by the next task
+  }
+
+  // ---- merge: on the last workgroups (they have no o_proj task) ----
+  for (int t = (b + p.t_merge) % G; t < p.t_merge; t += G) {
+    const int h = t >> 2, qd = t & 3;
+    // in the one-launch block the head's gate logit is computed here: its
+    // loads go out before the wait
+    GateRows<NIT, NORM> gate;
+    if (has_qkv) gate.issue(p, h, lane);
+    // the attention of this head's group: chunk c is attention task c * Hk + g.
+    // Without o_proj tasks the last merge task is the list's last task and
+    // waits for every attention task (so that it follows every workgroup's
+    // first task) before it advances the epoch.
+    const bool final_task = !last_is_oproj && t == p.t_merge - 1;
+    if (final_task)
+      await_flags(f_attn, 0, p.t_attn, 1, fv);
+    else
+      await_flags(f_attn, h / kGroup, p.nchunks, Hk, fv);
+    float gl;
+    if (has_qkv) {
+      const float v = gate.finish(p, h, s_x, s_ss, lane, w);
+      if (tid == 0) s_gate = v;   // to every wave
+      __syncthreads();
+      gl = s_gate;
+    } else {
+      gl = p.gate[h];
+    }
+    fused_merge_task(p, h, qd, gl, s_ml, s_acc, tid, lane);
+    set_flag(f_merge + t, fv);
+    if (final_task) advance_epoch();
+    __syncthreads();   // LDS is rewritten by the next task
+  }
+
+  // ---- o_proj ----
+  for (int t = b; t < p.t_oproj; t += G) {
+    // rows r0 .. r0 + RW - 1 of this wave: the W_o loads go out before the wait for a
+    const int r0 = (t * W + w) * RW;
+    const int qdim = Hq * kHeadDim;
+    const unsigned row_bytes = (unsigned)qdim * 2u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_o, (unsigned)p.hidden * row_bytes);
+    uint4 wv[RW][NITO];
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+#pragma unroll
+      for (int it = 0; it < NITO; ++it) {
+        const int col = (it * 64 + lane) * 8;
+        const int r = r0 + k;
+        wv[k][it] = buf_load16_p<kWeightPolicy>(
+            rw, (r < p.hidden && col < qdim) ? (unsigned)r * row_bytes + (unsigned)col * 2u : kOutOfRange);
+      }
+    if (p.t_merge > 0) await_flags(f_merge, 0, p.t_merge, 1, fv);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)qdim * 4u);
+    float4 xa[NITO], xb[NITO];
+#pragma unroll
+    for (int it = 0; it < NITO; ++it) {
+      const unsigned col = (unsigned)(it * 64 + lane) * 8u;
+      xa[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u));
+      xb[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u + 16u));
+    }
+#pragma unroll
+    for (int k = 0; k < RW; ++k) {
+      float acc = 0.f;
+#pragma unroll
+      for (int it = 0; it < NITO; ++it) acc = dot8_bf16(wv[k][it], xa[it], xb[it], acc);
+      const float s = wave_sum(acc);
+      const int r = r0 + k;
+      if (lane == 0 && r < p.hidden) p.y[r] = p.accumulate ? p.y[r] + s : s;
+    }
+    if (t == p.t_oproj - 1) advance_epoch();
+  }
+}
+
+template <int NIT>
+hipError_t fused_launch(const FusedParams &p, dim3 grid, hipStream_t stream) {
+  if (p.w_norm != nullptr)
+    hipLaunchKernelGGL((block_fused_kernel<NIT, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((block_fused_kernel<NIT, false>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1864,17 +2282,44 @@ hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream) {
   }
 }
 
-hipError_t launch_combine_oproj(const OprojParams &p, hipStream_t stream) {
-  // the taller slices when they still give every CU a workgroup
-  constexpr int kTall = 20, kShort = 10;
-  const int tall_slices = (p.hidden + 8 * kTall - 1) / (8 * kTall);
-  if ((long)tall_slices * p.num_heads >= kAttnTargetWgs) {
-    hipLaunchKernelGGL(combine_oproj_kernel<kTall>, dim3(p.num_heads, tall_slices), dim3(kThreads), 0, stream, p);
-  } else {
-    const int slices = (p.hidden + 8 * kShort - 1) / (8 * kShort);
-    hipLaunchKernelGGL(combine_oproj_kernel<kShort>, dim3(p.num_heads, slices), dim3(kThreads), 0, stream, p);
+void fused_tasks(FusedParams &p) {
+  const int Hq = p.num_heads, Hk = p.num_kv_heads;
+  const int per_task = (kThreads / 64) * fused_pairs_per_wave((p.hidden + 511) / 512);
+  p.qkv_per_group = kPairsPerGroup / per_task;
+  p.t_qkv = (p.phases & kPhaseQkv) ? Hk * p.qkv_per_group : 0;
+  p.t_attn = (p.phases & kPhaseAttn) ? p.nchunks * Hk : 0;
+  p.t_merge = (p.phases & kPhaseAttn) ? Hq * 4 : 0;
+  const int rows = (kThreads / 64) * kFusedRowsPerWave;
+  p.t_oproj = (p.phases & kPhaseOproj) ? (p.hidden + rows - 1) / rows : 0;
+}
+
+// One workgroup per CU, and no more workgroups than the largest of the
+// projection, attention and merge phases has tasks, so that every workgroup
+// runs one of them (the list's last task then follows every workgroup's
+// start); without o_proj tasks, no more than the attention tasks.
+hipError_t launch_block_fused(const FusedParams &p, hipStream_t stream) {
+  static int cu_count[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int cus = dev >= 0 && dev < 64 ? __atomic_load_n(&cu_count[dev], __ATOMIC_RELAXED) : 0;
+  if (cus <= 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) __atomic_store_n(&cu_count[dev], cus, __ATOMIC_RELAXED);
   }
-  return hipGetLastError();
+  const int cover = p.t_oproj > 0 ? std::max(p.t_qkv, std::max(p.t_attn, p.t_merge)) : p.t_attn;
+  const dim3 grid((unsigned)std::max(1, std::min(cus, cover)));
+  switch ((p.hidden + 511) / 512) {
+    case 1: return fused_launch<1>(p, grid, stream);
+    case 2: return fused_launch<2>(p, grid, stream);
+    case 3: return fused_launch<3>(p, grid, stream);
+    case 4: return fused_launch<4>(p, grid, stream);
+    case 5: return fused_launch<5>(p, grid, stream);
+    case 6: return fused_launch<6>(p, grid, stream);
+    case 7: return fused_launch<7>(p, grid, stream);
+    default: return fused_launch<8>(p, grid, stream);
+  }
 }
 
 // gate[i] <- gelu_erf(gate[i]) * up[i] for i < n ([mod] transcribed layer:

@@ -197,14 +197,26 @@ gqa_status gqa_split_plan(const gqa_arch *arch, int is_full, const gqa_kv_seq *s
  *   x_normed        device fp32 [batch][H]: the already-normed layer input
  *   out             device fp32 [batch][H]: W_o (sigmoid-gated attention)
  *   workspace       device, at least gqa_workspace_size(...) bytes for the
- *                   largest seq_len in `seqs`; contents on entry are ignored
+ *                   largest seq_len in `seqs`; its contents on entry are
+ *                   ignored (see the one-launch form below)
  * Side effect: each sequence's cache slot row for `position` is written.
  * x_normed and out must not overlap each other, the workspace or a cache.
- * Determinism: with batch 1 and a window of more than 128 rows, the split-K
- * merge, the gate and W_o run in one launch that sums the query heads' parts
- * of `out` with fp32 atomics, so `out` can differ between runs by fp32
- * rounding of that sum; `out` must then be ordinary (coarse-grained) device
- * memory.  Every other case, and the cache rows always, are bit-reproducible. */
+ * One launch: for one sequence whose window is longer than 128 rows (at most
+ * 256 split-K chunks, hidden <= 4096, num_heads * head_dim <= 4096) the whole
+ * block runs as ONE persistent launch of one workgroup per CU whose tasks
+ * wait for each other through flag words at the start of the workspace.
+ * That launch needs its workgroups resident together: a call running
+ * concurrently with other work on the same GPU (another stream) is delayed
+ * until the CUs it needs are free, and two such calls must not overlap on
+ * one GPU (their waits would time out after about a second and the outputs
+ * would be wrong).  The flags carry a per-call epoch kept in the workspace,
+ * so arbitrary workspace contents are accepted (a false match has
+ * probability 2^-64 per flag word).  Other shapes run the projection, the
+ * attention + merge and o_proj as separate launches.
+ * Determinism: every case is bit-reproducible from run to run, and the
+ * output equals, bit for bit, that of the step entry points below run in
+ * order on the same inputs (each value is computed by the same code in the
+ * same order). */
 gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weights *weights,
                                       int is_full, const gqa_kv_seq *seqs, int32_t batch,
                                       const float *x_normed, float *out, void *workspace,
@@ -271,7 +283,7 @@ gqa_status gqa_attention_block_chunk(const gqa_arch *arch, const gqa_layer_weigh
  *   weights, is_full, seqs, workspace as for gqa_attention_block_decode (the
  *   workspace size is the block's).
  * Side effect: each sequence's cache slot row for `position` is written.
- * Determinism as for gqa_attention_block_decode (h takes the atomic adds).
+ * Determinism and the one-launch form as for gqa_attention_block_decode.
  * Errors: those of gqa_attention_block_decode, and rms_eps < 0 or not finite. */
 gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weights *weights,
                                       const void *w_norm, int is_full, const gqa_kv_seq *seqs,
@@ -280,10 +292,11 @@ gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weig
 
 /* ---------------------------------------------------------------------------
  * Step entry points: the block's steps one launch each, exposed so each
- * step can be checked and timed on its own.  They are the kernels the block
- * launches, except that for one sequence with a window over 128 rows the
- * block merges, gates and projects in a single launch instead of
- * gqa_attention_gated's merge plus gqa_o_proj_gemv.
+ * step can be checked and timed on its own.  They run the block's own code:
+ * the same kernels where the block launches its steps separately, and, where
+ * it runs as one launch, kernels that compute every value as its tasks do
+ * (gqa_attention_gated runs the one-launch kernel's attention and merge
+ * tasks themselves), so the steps' output equals the block's bit for bit.
  * ------------------------------------------------------------------------- */
 
 /* [attn] the fused q_k_v_proj GEMV and the g_proj GEMV over the same input,
@@ -309,6 +322,9 @@ gqa_status gqa_qkv_rope_kv(const gqa_arch *arch, const gqa_layer_weights *weight
  *                same logits for every sequence)
  *   attn_gated   device fp32 [batch][Hq*D]: head h at [h*D, (h+1)*D)
  *   seqs, is_full, workspace as for gqa_attention_block_decode.
+ * One sequence with a window longer than 128 rows runs as one launch of the
+ * block's one-launch kernel restricted to its attention and merge tasks
+ * (the residency note of gqa_attention_block_decode applies).
  * Reads the caches only. */
 gqa_status gqa_attention_gated(const gqa_arch *arch, int is_full, const gqa_kv_seq *seqs,
                                int32_t batch, const float *q_roped, const float *gate_logits,

@@ -29,10 +29,13 @@ def _round_up(x, a):
     return (x + a - 1) // a * a
 
 
+SYNC_BYTES = 32768   # the one-launch block's flag words at the start of every workspace
+
+
 def _layout_bytes(arch, batch, chunks):
-    """The block's workspace: q, gate logits, gated attention, partial O and
-    partial (m, l), each rounded up to 256 bytes."""
-    q = _round_up(batch * arch.q_dim * 4, 256)
+    """The block's workspace: the synchronisation words, q, gate logits, gated
+    attention, partial O and partial (m, l), each rounded up to 256 bytes."""
+    q = SYNC_BYTES + _round_up(batch * arch.q_dim * 4, 256)
     g = _round_up(batch * arch.num_heads * 4, 256)
     a = _round_up(batch * arch.q_dim * 4, 256)
     po = _round_up(chunks * arch.num_heads * arch.head_dim * 4, 256)
