@@ -10,10 +10,12 @@ workload is the full (causal) layer at 32K context: hidden 2560, position
 total exceeds 1 GiB.
 
 Prints ONE JSON line with the throughput (tokens/s), a roofline object for
-the dominant kernel (attn_partial_kernel, the split-K pass: its algorithmic
-HBM bytes over its average duration, timed with HIP events around a run of
-back-to-back launches on the stream it is launched on), and the fp64 CPU
-oracle timed on the host as a baseline.  `--calibrate-copy MIB` only runs a
+the dominant kernel (for one sequence over more than one attention chunk the
+whole block is one launch of block_fused_kernel: the block's algorithmic HBM
+bytes over that launch's average duration, timed with HIP events around the
+timed region on the stream it is launched on; otherwise the split-K pass
+attn_partial_kernel with its K/V bytes), and the fp64 CPU oracle timed on the
+host as a baseline.  `--calibrate-copy MIB` only runs a
 plain device copy of known size, to scale rocprofv3's HBM byte counters.
 """
 from __future__ import annotations
@@ -86,7 +88,7 @@ def attention_bytes(case) -> int:
 
 
 def kv_bytes(case) -> int:
-    """Algorithmic HBM bytes of the split-K pass (the dominant kernel): the
+    """Algorithmic HBM bytes of the split-K pass: the
     attended K/V rows, fp16, all KV heads, each read once.  The q it reads
     (16 KB) and the partials it writes are workspace traffic, not counted."""
     a = case.arch
@@ -98,10 +100,10 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counted_traffic(workload: str):
-    """HBM bytes per launch of attn_partial_kernel from a committed rocprofv3
-    PMC summary of the same kernel source, or None."""
-    path = os.path.join(PROFILE_DIR, f"attn_partial_kernel_{workload}_hbm_counters.md")
+def counted_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 PMC summary
+    of the same kernel source, or None."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -175,13 +177,15 @@ def stack_bytes(st) -> int:
 
 
 def bench_stack(args):
-    """The 36-layer stack (RMSNorm -> block -> residual add per layer, each
-    layer one gqa_attention_layer_decode call) at position 8191: 9 full layers
-    over 8192 rows, 27 sliding layers over a wrapped 512-slot ring.  With
+    """The 36-layer stack (RMSNorm -> block -> residual add per layer) at
+    position 8191: 9 full layers over 8192 rows, 27 sliding layers over a
+    wrapped 512-slot ring.  The stack runs as one gqa_attention_stack_decode
+    call per token (one persistent launch for all 36 layers), or with
+    --layer-calls as one gqa_attention_layer_decode call per layer.  With
     --workload decoder every layer also runs its MLP (gqa_mlp_decode:
     post-attention norm, erf-GELU gated MLP with intermediate 3 x hidden,
-    residual add), i.e. a whole decode step.  One step = one token through
-    all 36 layers."""
+    residual add), i.e. a whole decode step, layer call by layer call.  One
+    step = one token through all 36 layers."""
     import numpy as np
     import torch
     import gqa_attention_block_amd as gqa
@@ -204,12 +208,21 @@ def bench_stack(args):
                           device="cuda:0") if mlp else None)
 
     # per layer: h += block(RMSNorm(h) * w) [, then h += mlp(h)], each call
-    # marshalled once (the binding's prepared calls)
+    # marshalled once (the binding's prepared calls); the attention-only stack
+    # as one call for all layers unless --layer-calls
+    one_call = not mlp and not args.layer_calls
     calls = []
-    for L in layers:
-        calls.append(gqa.PreparedLayer(a, L["w_norm"], L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], h, ws))
-        if mlp:
-            calls.append(gqa.PreparedMlp(a, *L["mlp"], h, ws_mlp))
+    if one_call:
+        calls.append(gqa.PreparedStack(a, [gqa.StackLayer(w_norm=L["w_norm"], w_qkv=L["w_qkv"], w_g=L["w_g"],
+                                                          w_o=L["w_o"], is_full=L["full"], seq=L["seq"])
+                                           for L in layers], h, ws))
+    else:
+        for L in layers:
+            calls.append(gqa.PreparedLayer(a, L["w_norm"], L["w_qkv"], L["w_g"], L["w_o"], L["full"], [L["seq"]], h,
+                                           ws))
+            if mlp:
+                calls.append(gqa.PreparedMlp(a, *L["mlp"], h, ws_mlp))
+    launch = ("one_launch_stack" if one_call else "layer_calls") + ("+hip_graph" if args.graph else "")
 
     def step():
         for c in calls:
@@ -238,7 +251,7 @@ def bench_stack(args):
     assert torch.isfinite(h).all(), "non-finite residual stream"
     ms = 1e3 * elapsed / args.steps
     sb = stack_bytes(st)
-    log(f"stack ({'graph' if args.graph else 'eager'}): {ms * 1e3:.1f} us/token, host submit "
+    log(f"stack ({launch}): {ms * 1e3:.1f} us/token, host submit "
         f"{submitted / args.steps * 1e6:.1f} us/token, {sb / 1e9:.3f} GB/token -> "
         f"{sb / (ms * 1e-3) / 1e9:.1f} GB/s")
     cpu = None
@@ -264,7 +277,7 @@ def bench_stack(args):
         "data": "synthetic",
         "config": {"workload": st.name, "hidden": a.hidden, "batch": 1, "layers": len(st.layers),
                    "positions": [st.layers[0].cache.position], "weights": "bf16", "kv_cache": "fp16",
-                   "stack_bytes_per_token": sb, "launch": "hip_graph" if args.graph else "eager"},
+                   "stack_bytes_per_token": sb, "launch": launch},
         "block_hbm_gbs": round(sb / (ms * 1e-3) / 1e9, 1),
         "block_frac_of_peak": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "host_submit_us_per_step": round(submitted / args.steps * 1e6, 3),
@@ -388,6 +401,8 @@ def main():
                     help="CPU oracle sample length (0 skips the baseline)")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per step instead of launching from the host")
+    ap.add_argument("--layer-calls", action="store_true",
+                    help="cfg4: one gqa_attention_layer_decode call per layer instead of one stack call per token")
     ap.add_argument("--sinks", action="store_true",
                     help="block workloads: pass per-head attention-sink logits (seeded, fp32 [Hq])")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -458,8 +473,8 @@ def main():
     def block_step(c):
         prepared[c].step()
 
-    # dominant kernel: the attention step (split-K attention over the window,
-    # combine + gate), on a q produced once by the projection step
+    # the attention step (split-K attention over the window, merge + gate),
+    # on a q produced once by the projection step
     q = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda:0")
     gl = torch.empty((case.batch, a.num_heads), dtype=torch.float32, device="cuda:0")
     attn = torch.empty((case.batch, a.q_dim), dtype=torch.float32, device="cuda:0")
@@ -500,12 +515,19 @@ def main():
     for i in range(args.warmup):
         run_block(i % copies)
     torch.cuda.synchronize()
+    # HIP events on the stream the block is launched on, around the timed
+    # region: with one launch per step, their average is that kernel's
+    # average launch duration (back to back, inter-launch gaps included)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
         run_block(i % copies)
+    ev1.record()
     submitted = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    launch_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
     assert torch.isfinite(out).all(), "non-finite block output"
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_s = case.batch * args.steps / elapsed
@@ -516,8 +538,15 @@ def main():
         f"{tokens_per_s:.1f} tokens/s, {bb / 1e6:.2f} MB/step -> "
         f"{bb / (ms_per_step * 1e-3) / 1e9:.1f} GB/s")
 
-    # dominant kernel: the split-K pass alone, launched back to back over the
-    # copies; one event pair around the whole run gives its average duration
+    # one sequence whose window takes more than one chunk: the whole block is
+    # one launch of block_fused_kernel (the library's rule, restated here for
+    # the report); else the split-K pass is the dominant kernel
+    plan = gqa.split_plan(a, case.is_full, [s.position for s in case.seqs], case.seqs[0].ring_capacity,
+                          capacities=[s.k.shape[0] for s in case.seqs])
+    one_launch = (case.batch == 1 and not plan.direct and plan.groups == 1 and plan.max_group_chunks <= 256
+                  and a.hidden <= 4096 and a.q_dim <= 4096)
+    # the split-K pass alone, launched back to back over the copies; one event
+    # pair around the whole run gives its average duration
     part_o = torch.empty((1024, a.num_heads, a.head_dim), dtype=torch.float32, device="cuda:0")
     part_ml = torch.empty((part_o.shape[0], a.num_heads, 2), dtype=torch.float32, device="cuda:0")
 
@@ -549,11 +578,19 @@ def main():
     log(f"attention step (partials + combine): {att_s * 1e6:.2f} us avg, {ab / 1e6:.2f} MB -> "
         f"{ab / att_s / 1e9:.1f} GB/s")
 
-    traffic = counted_traffic(args.workload)
-    roofline = {"kernel": "attn_partial_kernel", "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "us_per_launch": round(part_s * 1e6, 3),
-                "algorithmic_bytes_per_launch": pb}
+    split_k = {"kernel": "attn_partial_kernel", "achieved": round(achieved, 1), "unit": "GB/s",
+               "frac": round(achieved / HBM_PEAK_GBS, 4), "us_per_launch": round(part_s * 1e6, 3),
+               "kv_bytes_per_launch": pb}
+    if one_launch:
+        kname, kbytes, ks = "block_fused_kernel", bb, launch_s
+    else:
+        kname, kbytes, ks = "attn_partial_kernel", pb, part_s
+    kach = kbytes / ks / 1e9
+    log(f"{kname}: {ks * 1e6:.2f} us per launch, {kbytes / 1e6:.2f} MB -> {kach:.1f} GB/s = "
+        f"{kach / HBM_PEAK_GBS:.3f} of peak")
+    roofline = {"kernel": kname, "bound": "hbm", "achieved": round(kach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kach / HBM_PEAK_GBS, 4), "traffic": counted_traffic(args.workload, kname),
+                "us_per_launch": round(ks * 1e6, 3), "algorithmic_bytes_per_launch": kbytes}
     # the block as a whole (what the metric names): its algorithmic bytes over
     # the wall time of a step
     block_gbs = bb / (ms_per_step * 1e-3) / 1e9
@@ -582,6 +619,7 @@ def main():
         "block_frac_of_peak": round(bb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "block_roofline": block_roofline,
+        "split_k_pass": split_k,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -12,12 +12,15 @@ from .binding import (  # noqa: F401
     PreparedBlock,
     PreparedLayer,
     PreparedMlp,
+    PreparedStack,
+    StackLayer,
     attention_block_chunk,
     attention_block_decode,
     attention_block_decode_noalloc,
     attention_gated,
     attention_layer_decode,
     attention_partials,
+    attention_stack_decode,
     embed_tokens,
     kv_slot,
     kv_window,

@@ -54,6 +54,11 @@ class _KvSeq(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class _StackLayer(ctypes.Structure):
+    _fields_ = [("weights", _Weights), ("w_norm", ctypes.c_void_p), ("cache", _KvSeq),
+                ("is_full", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
@@ -75,6 +80,7 @@ def _load():
         "gqa_attention_block_decode": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_attention_block_decode_noalloc": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P]),
         "gqa_attention_layer_decode": (ctypes.c_int, [A, W, P, ctypes.c_int, K, I32, P, P, S, P]),
+        "gqa_attention_stack_decode": (ctypes.c_int, [A, ctypes.POINTER(_StackLayer), I32, P, P, S, P]),
         "gqa_attention_block_chunk": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, S, P]),
         "gqa_qkv_rope_kv": (ctypes.c_int, [A, W, ctypes.c_int, K, I32, P, P, P, P]),
         "gqa_attention_gated": (ctypes.c_int, [A, ctypes.c_int, K, I32, P, P, P, P, P, S, P]),
@@ -103,7 +109,8 @@ _lib = _load()
 #: symbols the header declares; tests check the library exports all of them
 EXPORTED_SYMBOLS = (
     "gqa_rope_params_for", "gqa_kv_window", "gqa_kv_slot", "gqa_workspace_size", "gqa_split_plan",
-    "gqa_attention_block_decode", "gqa_attention_block_decode_noalloc", "gqa_attention_block_chunk", "gqa_attention_layer_decode", "gqa_qkv_rope_kv",
+    "gqa_attention_block_decode", "gqa_attention_block_decode_noalloc", "gqa_attention_block_chunk",
+    "gqa_attention_layer_decode", "gqa_attention_stack_decode", "gqa_qkv_rope_kv",
     "gqa_attention_gated",
     "gqa_attention_partials", "gqa_o_proj_gemv", "gqa_rms_norm_bf16w", "gqa_residual_add", "gqa_status_string",
     "gqa_last_error", "gqa_mlp_workspace_size", "gqa_mlp_decode", "gqa_embed_tokens", "gqa_lm_head_workspace_size",
@@ -159,6 +166,19 @@ class KvSeq:
     v: torch.Tensor
     position: int
     ring_capacity: int = 0
+
+
+@dataclass
+class StackLayer:
+    """One layer of a stack for attention_stack_decode: its input-norm weight,
+    projection weights (bf16 or raw 16-bit bits), class and cache."""
+    w_norm: torch.Tensor
+    w_qkv: torch.Tensor
+    w_g: torch.Tensor
+    w_o: torch.Tensor
+    is_full: bool
+    seq: KvSeq
+    sinks: Optional[torch.Tensor] = None
 
 
 def rope_params_for(is_full: bool, full_rotary_dim: int, head_dim: int, full_theta: float,
@@ -375,6 +395,41 @@ class PreparedLayer(_Prepared):
                                *[t for q in seqs for t in (q.k, q.v)]))
 
 
+def _stack_layers(arch: Arch, layers: Sequence[StackLayer]):
+    arr = (_StackLayer * max(1, len(layers)))()
+    for i, ly in enumerate(layers):
+        arr[i] = _StackLayer(_weights(arch, ly.w_qkv, ly.w_g, ly.w_o, ly.sinks),
+                             _wptr(ly.w_norm, f"layers[{i}].w_norm", arch.hidden), _seqs(arch, [ly.seq])[0],
+                             int(ly.is_full), 0)
+    return arr
+
+
+def _stack_keep(layers: Sequence[StackLayer]):
+    return [t for ly in layers for t in (ly.w_norm, ly.w_qkv, ly.w_g, ly.w_o, ly.sinks, ly.seq.k, ly.seq.v)]
+
+
+class PreparedStack(_Prepared):
+    """attention_stack_decode (one token through the layers, h updated in
+    place) with fixed layers, h and workspace; step(position) moves every
+    layer's cache to that position."""
+
+    def __init__(self, arch: Arch, layers: Sequence[StackLayer], h: torch.Tensor, workspace: torch.Tensor,
+                 stream=None):
+        self._a = arch._c()
+        self._layers = _stack_layers(arch, layers)
+        super().__init__(_lib.gqa_attention_stack_decode, "gqa_attention_stack_decode", None,
+                         (ctypes.byref(self._a), self._layers, len(layers),
+                          _ptr(h, torch.float32, "h", arch.hidden),
+                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel()), stream,
+                         keep=(h, workspace, *_stack_keep(layers)))
+
+    def step(self, position: Optional[int] = None):
+        if position is not None:
+            for i in range(self._args[2]):
+                self._layers[i].cache.position = int(position)
+        super().step()
+
+
 class PreparedMlp(_Prepared):
     """mlp_decode (h += down(gelu_erf(gate x) * up x), in place) with fixed
     weights, h and workspace."""
@@ -420,6 +475,18 @@ def attention_layer_decode(arch: Arch, w_norm, w_qkv, w_g, w_o, is_full: bool, s
         _ptr(h, torch.float32, "h", b * arch.hidden),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
         "gqa_attention_layer_decode")
+
+
+def attention_stack_decode(arch: Arch, layers: Sequence[StackLayer], h: torch.Tensor, workspace: torch.Tensor,
+                           stream=None):
+    """One token of one sequence through the layers in order: for each layer
+    h += block(RMSNorm(h) * w_norm), in place (h: [hidden] or [1, hidden])."""
+    a = arch._c()
+    arr = _stack_layers(arch, layers)
+    _check(_lib.gqa_attention_stack_decode(
+        ctypes.byref(a), arr, len(layers), _ptr(h, torch.float32, "h", arch.hidden),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+        "gqa_attention_stack_decode")
 
 
 def mlp_workspace_size(arch: Arch, intermediate: int, batch: int) -> int:
@@ -584,3 +651,4 @@ def c_seq_array(n: int):
 
 c_weights = _Weights
 c_kv_seq = _KvSeq
+c_stack_layer = _StackLayer

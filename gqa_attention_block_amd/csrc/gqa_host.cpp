@@ -598,6 +598,34 @@ size_t mlp_bytes(const gqa_arch *a, int32_t inter, int32_t batch) {
          2 * round_up((size_t)batch * inter * sizeof(float), 256);
 }
 
+// Two layers of a stack whose attention runs alike: window, slot, chunking, RoPE.
+bool same_shape(const StackDesc &a, const StackDesc &b) {
+  return a.seq.kv_start == b.seq.kv_start && a.seq.n == b.seq.n && a.seq.ring == b.seq.ring &&
+         a.seq.slot == b.seq.slot && a.seq.position == b.seq.position && a.seq.cache_bytes == b.seq.cache_bytes &&
+         a.chunk == b.chunk && a.nchunks == b.nchunks && a.rotary_dim == b.rotary_dim &&
+         a.log2_theta == b.log2_theta;
+}
+
+// The layer (h += block(RMSNorm(h) * w_norm)) for resolved sequences whose
+// plan and workspace layout are known: the one-launch block when it takes
+// them, else projections -> attention -> o_proj with the residual add.
+gqa_status run_layer(const gqa_arch *arch, const gqa_layer_weights *weights, const uint16_t *w_norm, int is_full,
+                     const std::vector<SeqDesc> &descs, const Plan &plan, float *h, char *ws, const Layout &L,
+                     hipStream_t s) {
+  const int32_t batch = (int32_t)descs.size();
+  if (fused_attention(arch, plan, batch))
+    return run_fused_block(arch, weights, is_full, descs[0], plan, h, w_norm, h, true, ws, L, s);
+  float *q = reinterpret_cast<float *>(ws + L.q);
+  float *gate = reinterpret_cast<float *>(ws + L.gate);
+  float *attn = reinterpret_cast<float *>(ws + L.attn);
+  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
+  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+  gqa_status st;
+  if ((st = run_qkv_rope(arch, weights, is_full, descs, h, q, gate, s, w_norm)) != GQA_OK) return st;
+  if ((st = run_attention(arch, descs, plan, q, gate, weights->sinks, attn, part_o, part_ml, s)) != GQA_OK) return st;
+  return run_o_proj(arch, weights, batch, attn, h, s, true);
+}
+
 // The block for resolved sequence descriptors (one per token or sequence):
 // pointers and the workspace size are checked here, then qkv -> attention ->
 // o_proj are enqueued.
@@ -954,24 +982,104 @@ gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weig
   if (workspace_bytes < L.total)
     return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the layer needs %zu", workspace_bytes,
                 L.total);
-  char *ws = static_cast<char *>(workspace);
-  float *q = reinterpret_cast<float *>(ws + L.q);
-  float *gate = reinterpret_cast<float *>(ws + L.gate);
-  float *attn = reinterpret_cast<float *>(ws + L.attn);
-  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
-  float *part_ml = reinterpret_cast<float *>(ws + L.part_ml);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (fused_attention(arch, plan, batch)) {
-    st = run_fused_block(arch, weights, is_full, descs[0], plan, h, static_cast<const uint16_t *>(w_norm), h, true, ws,
-                         L, s);
-    return st == GQA_OK ? ok() : st;
+  st = run_layer(arch, weights, static_cast<const uint16_t *>(w_norm), is_full, descs, plan, h,
+                 static_cast<char *>(workspace), L, static_cast<hipStream_t>(stream));
+  return st == GQA_OK ? ok() : st;
+}
+
+gqa_status gqa_attention_stack_decode(const gqa_arch *arch, const gqa_stack_layer *layers, int32_t num_layers,
+                                      float *h, void *workspace, size_t workspace_bytes, void *stream) {
+  gqa_status st;
+  if ((st = check_arch(arch)) != GQA_OK) return st;
+  if (!(arch->rms_eps >= 0.f) || !isfinite(arch->rms_eps))
+    return fail(GQA_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
+  if (num_layers < 0) return fail(GQA_ERR_INVALID_ARGUMENT, "num_layers=%d must be >= 0", num_layers);
+  if (num_layers == 0) return ok();
+  if (!layers) return fail(GQA_ERR_INVALID_ARGUMENT, "layers is null");
+  // every layer checked before anything is enqueued
+  std::vector<std::vector<SeqDesc>> descs(num_layers);
+  std::vector<Plan> plans(num_layers);
+  size_t max_chunks = 0;
+  for (int32_t l = 0; l < num_layers; ++l) {
+    const gqa_stack_layer &ly = layers[l];
+    if (ly.reserved != 0) return fail(GQA_ERR_INVALID_ARGUMENT, "layers[%d].reserved must be 0", l);
+    if ((st = check_weights(&ly.weights, true, true)) != GQA_OK)
+      return report(st, "layers[%d]: %s", l, gqa_last_error());
+    if ((st = check_ptr(ly.w_norm, "w_norm")) != GQA_OK) return report(st, "layers[%d]: %s", l, gqa_last_error());
+    if ((st = resolve_seqs(arch, ly.is_full, &ly.cache, 1, &descs[l])) != GQA_OK)
+      return report(st, "layers[%d]: %s", l, gqa_last_error());
+    plans[l] = make_plan(descs[l], arch->num_kv_heads, true);
+    max_chunks = std::max(max_chunks, plans[l].max_group_chunks);
   }
-  if ((st = run_qkv_rope(arch, weights, is_full, descs, h, q, gate, s, static_cast<const uint16_t *>(w_norm))) !=
-      GQA_OK)
-    return st;
-  if ((st = run_attention(arch, descs, plan, q, gate, weights->sinks, attn, part_o, part_ml, s)) != GQA_OK)
-    return st;
-  if ((st = run_o_proj(arch, weights, batch, attn, h, s, true)) != GQA_OK) return st;
+  if ((st = check_ptr(h, "h")) != GQA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace")) != GQA_OK) return st;
+  const Layout L = block_layout(arch, 1, max_chunks);
+  if (workspace_bytes < L.total)
+    return fail(GQA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the stack needs %zu", workspace_bytes,
+                L.total);
+  char *ws = static_cast<char *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // runs of consecutive layers that the one-launch block takes go out as one
+  // launch each (at most kStackMaxLayers layers and kStackMaxDescs attention
+  // shapes); any other layer runs as gqa_attention_layer_decode runs it
+  const bool whole = fused_whole(arch);
+  int32_t l = 0;
+  while (l < num_layers) {
+    if (!whole || !fused_attention(arch, plans[l], 1)) {
+      const gqa_stack_layer &ly = layers[l];
+      if ((st = run_layer(arch, &ly.weights, static_cast<const uint16_t *>(ly.w_norm), ly.is_full, descs[l], plans[l],
+                          h, ws, L, s)) != GQA_OK)
+        return st;
+      ++l;
+      continue;
+    }
+    StackParams sp{};
+    sp.base = fused_params(arch, layers[l].is_full, descs[l][0], plans[l], kPhaseQkv | kPhaseAttn | kPhaseOproj,
+                           reinterpret_cast<float *>(ws + L.q), reinterpret_cast<float *>(ws + L.gate), nullptr,
+                           reinterpret_cast<float *>(ws + L.part_o), reinterpret_cast<float *>(ws + L.part_ml),
+                           reinterpret_cast<float *>(ws + L.attn), ws);
+    sp.base.x = h;
+    sp.base.y = h;
+    sp.base.accumulate = 1;
+    fused_tasks(sp.base);
+    int nd = 0;
+    while (l < num_layers && sp.num_layers < kStackMaxLayers && fused_attention(arch, plans[l], 1)) {
+      const gqa_stack_layer &ly = layers[l];
+      StackDesc d{};
+      d.seq = descs[l][0];
+      d.seq.k = nullptr;
+      d.seq.v = nullptr;
+      d.seq.chunk_begin = 0;
+      d.chunk = plans[l].chunk;
+      d.nchunks = plans[l].groups[0].total_chunks;
+      d.t_attn = d.nchunks * arch->num_kv_heads;
+      int32_t rdim;
+      double theta;
+      gqa_rope_params_for(ly.is_full, arch->full_rotary_dim, arch->head_dim, arch->full_rope_theta,
+                          arch->rope_theta, &rdim, &theta);
+      d.rotary_dim = rdim;
+      d.log2_theta = log2(theta);
+      int di = 0;
+      while (di < nd && !same_shape(sp.desc[di], d)) ++di;
+      if (di == nd) {
+        if (nd == kStackMaxDescs) break;   // a fifth shape starts the next launch
+        sp.desc[nd++] = d;
+      }
+      const int n = sp.num_layers++;
+      sp.desc_of[n] = (unsigned char)di;
+      sp.t_attn_max = std::max(sp.t_attn_max, d.t_attn);
+      sp.w_norm[n] = static_cast<const uint16_t *>(ly.w_norm);
+      sp.w_qkv[n] = static_cast<const uint16_t *>(ly.weights.q_k_v_proj);
+      sp.w_g[n] = static_cast<const uint16_t *>(ly.weights.g_proj);
+      sp.w_o[n] = static_cast<const uint16_t *>(ly.weights.o_proj);
+      sp.k[n] = descs[l][0].k;
+      sp.v[n] = descs[l][0].v;
+      sp.sinks[n] = ly.weights.sinks;
+      ++l;
+    }
+    hipError_t e = launch_stack_fused(sp, s);
+    if (e != hipSuccess) return gpu_error(e, "one-launch stack");
+  }
   return ok();
 }
 

@@ -177,6 +177,37 @@ struct FusedParams {
   int qkv_per_group;      // projection tasks per KV head group
 };
 
+// A stack of layers for ONE sequence as one persistent launch
+// (stack_fused_kernel): layer l's tasks follow layer l - 1's, the projections
+// of layer l waiting for every o_proj task of layer l - 1 (h complete).  The
+// layers' attention shapes (window, chunking, RoPE class) come from a small
+// table of distinct descriptors, the weights and caches per layer.
+constexpr int kStackMaxLayers = 40;  // layers per launch (more run as further launches)
+constexpr int kStackMaxDescs = 4;    // distinct attention shapes per launch
+struct StackDesc {
+  SeqDesc seq;            // window and slot of the token (k and v are per layer)
+  int chunk;              // rows per chunk
+  int nchunks;
+  int t_attn;             // attention tasks: nchunks * Hk
+  int rotary_dim;
+  double log2_theta;
+};
+struct StackParams {
+  FusedParams base;       // shared fields: shapes, workspace buffers, x = y = h, task counts
+  int num_layers;
+  int t_attn_max;         // attention flag words reserved per layer
+  unsigned char desc_of[kStackMaxLayers];
+  StackDesc desc[kStackMaxDescs];
+  const uint16_t *w_norm[kStackMaxLayers];
+  const uint16_t *w_qkv[kStackMaxLayers];
+  const uint16_t *w_g[kStackMaxLayers];
+  const uint16_t *w_o[kStackMaxLayers];
+  _Float16 *k[kStackMaxLayers];
+  _Float16 *v[kStackMaxLayers];
+  const float *sinks[kStackMaxLayers];
+};
+static_assert(sizeof(StackParams) <= 3072, "the stack's kernel arguments stay under 3 KB");
+
 // The embedding gather: h[b] = table[ids[b]] (bf16 row -> fp32), up to
 // kMaxEmbedIds tokens per launch; ids are checked on the host.
 constexpr int kMaxEmbedIds = 64;
@@ -222,6 +253,8 @@ struct GemvParams {
 // fused_tasks fills the task counts of p for its phases (hidden, heads, nchunks set).
 void fused_tasks(FusedParams &p);
 hipError_t launch_block_fused(const FusedParams &p, hipStream_t stream);
+// sp.base's task counts as fused_tasks gives them (t_attn unused: per descriptor)
+hipError_t launch_stack_fused(const StackParams &sp, hipStream_t stream);
 hipError_t launch_gemv(const GemvParams &p, hipStream_t stream);
 hipError_t launch_qkv_rope(const QkvParams &p, hipStream_t stream);
 hipError_t launch_attention(const AttnParams &p, int num_heads, hipStream_t stream);

@@ -170,12 +170,13 @@ struct StagedX {
   // conditional store lets the compiler sink its load behind the weight
   // loads): float4s past the row read as zeros from the resource bound and
   // land in the slots past kGroups, which are never read.
-  template <bool NORM>
+  // (XPOL: the cache policy of the x loads)
+  template <bool NORM, int XPOL = 0>
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rx, unsigned base, __amdgpu_buffer_rsrc_t rn) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const unsigned f = threadIdx.x + k * kThreads;
-      v[k] = __builtin_bit_cast(float4, buf_load16(rx, base + f * 16u));
+      v[k] = __builtin_bit_cast(float4, buf_load16_p<XPOL>(rx, base + f * 16u));
       if constexpr (NORM) wn[k] = buf_load8(rn, f * 8u);
     }
   }
@@ -400,6 +401,27 @@ __device__ __forceinline__ void pair_dots(const uint4 (&wa)[NIT], const uint4 (&
   for (int it = 0; it < NIT; ++it) {
     a = dot8_bf16(wa[it], s0[it * 64 + lane], s1[it * 64 + lane], a);
     c = dot8_bf16(wb[it], s0[it * 64 + lane], s1[it * 64 + lane], c);
+  }
+  ya = wave_sum(a);
+  yb = wave_sum(c);
+  if constexpr (NORM) {
+    const float inv = rsqrtf((ss[0] + ss[1] + ss[2] + ss[3]) / (float)hidden + eps);
+    ya *= inv;
+    yb *= inv;
+  }
+}
+
+// pair_dots with x already in registers (x0[it], x1[it]: the staged slots
+// it * 64 + lane of s0 and s1): the same arithmetic in the same order.
+template <int NIT, bool NORM>
+__device__ __forceinline__ void pair_dots_x(const uint4 (&wa)[NIT], const uint4 (&wb)[NIT], const float4 (&x0)[NIT],
+                                            const float4 (&x1)[NIT], const float *ss, int hidden, float eps,
+                                            float &ya, float &yb) {
+  float a = 0.f, c = 0.f;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    a = dot8_bf16(wa[it], x0[it], x1[it], a);
+    c = dot8_bf16(wb[it], x0[it], x1[it], c);
   }
   ya = wave_sum(a);
   yb = wave_sum(c);
@@ -950,16 +972,19 @@ struct NoWait {
   __device__ __forceinline__ void operator()() const {}
 };
 
-// QC: q is read coherently (other workgroups of the same launch wrote it);
-// its first tiles are then issued before before_q() waits for it.  TC: the
-// tiles are read coherently too and issued after the wait (the chunk holding
-// this token's cache row, written in the same launch).
-template <int W, bool QC = false, bool TC = false, typename BeforeQ = NoWait>
+// QC: q is read coherently (other workgroups of the same launch wrote it),
+// and so are the tiles (the chunk holding this token's cache row reads the
+// row written in the same launch; every chunk takes the same path, so that
+// the fused kernel carries one copy of this code).  The first tiles are
+// issued before before_q() waits for q, or with tc after it (the chunk
+// holding this token's row, which the wait makes visible).
+template <int W, bool QC = false, typename BeforeQ = NoWait>
 __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqDesc &sd, int ci, int chunk, int Hk,
                                                   float qscale, int g, int w, _Float16 *__restrict__ sk0,
                                                   _Float16 *__restrict__ sk1, _Float16 *__restrict__ sv0,
                                                   _Float16 *__restrict__ sv1, _Float16 *__restrict__ sq,
-                                                  float &m_out, float &l_out, BeforeQ before_q = BeforeQ()) {
+                                                  float &m_out, float &l_out, BeforeQ before_q = BeforeQ(),
+                                                  bool tc = false) {
   const int lane = threadIdx.x & 63;
   const int t0 = sd.kv_start + ci * chunk;
   const int nrows = min(chunk, sd.kv_start + sd.n - t0);
@@ -999,7 +1024,7 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
       const unsigned off = row_off((W * t + w) * kTileRows + r);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sbuf + jj * 512), 16,
                                                off == kOutOfRange ? off : off + 16u * (unsigned)pc, 0, 0,
-                                               (is_k ? kKPolicy : kVPolicy) | (TC ? kCoherent : 0));
+                                               (is_k ? kKPolicy : kVPolicy) | (QC ? kCoherent : 0));
     }
   };
   auto load_k = [&](_Float16 *sk, int t) { load_tile(sk, t, std::true_type{}); };
@@ -1032,13 +1057,10 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
       for (int i = 0; i < kGroup; ++i) qv[i] = *reinterpret_cast<const float4 *>(qh + i * kHeadDim);
     }
   };
-  if constexpr (TC) {
+  if constexpr (QC) {
+    if (!tc) first_tiles();
     before_q();
-    first_tiles();
-    load_q();
-  } else if constexpr (QC) {
-    first_tiles();
-    before_q();
+    if (tc) first_tiles();
     load_q();
   } else {
     before_q();
@@ -1844,7 +1866,10 @@ hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
 // projection task, per attention task, per merge task.
 // ---------------------------------------------------------------------------
 constexpr int kFlagBase = 8;
-static_assert((kFlagBase + 800 + kFusedMaxChunks * 8 + 32 * 4) * 8 <= kSyncBytes, "flag words fit their bytes");
+// flag words: projection tasks (at most 800), attention tasks (256 chunks x 8
+// KV heads), merge tasks (32 query heads x 4), o_proj tasks (4096 rows / 16)
+static_assert((kFlagBase + 800 + kFusedMaxChunks * 8 + 32 * 4 + kFusedMaxHidden / 16) * 8 <= kSyncBytes,
+              "flag words fit their bytes");
 // A wait gives up after this many polls (about a second): reached only if
 // calls overlap on one workspace, or if other work holds CUs the launch
 // needs; the kernel then still ends.
@@ -1880,43 +1905,92 @@ __device__ __forceinline__ void set_flag(unsigned long long *flag, unsigned long
   if (threadIdx.x == 0) __hip_atomic_store(flag, fv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One wave's four 8 KB tile buffers, addressed as 1 KB blocks 0 .. 31.
+struct WaveBufs {
+  _Float16 *b[4];
+  __device__ __forceinline__ _Float16 *block(int m) const { return b[m >> 3] + (m & 7) * 512; }
+};
+
+// Output pair j of wave w in projection task i: pairs in group-major order
+// (per KV head group: its 4 query heads, then its k and v heads).
+template <int P>
+__device__ __forceinline__ PairRows task_pair(const FusedParams &p, int i, int w, int j) {
+  const int u = (i * 4 + w) * P + j;   // wave-uniform, < Hk * kPairsPerGroup
+  const int g = u / kPairsPerGroup, r = u - g * kPairsPerGroup;
+  int sec, head, pi;
+  if (r < kGroup * 128) {
+    sec = 0; head = g * kGroup + (r >> 7); pi = r & 127;
+  } else if (r < (kGroup + 1) * 128) {
+    sec = 1; head = g; pi = r - kGroup * 128;
+  } else {
+    sec = 2; head = g; pi = r - (kGroup + 1) * 128;
+  }
+  return pair_rows(sec, head, pi, p.num_heads, p.num_kv_heads, p.rotary_dim);
+}
+
+// The weight rows of wave w's pairs in projection task i, from HBM straight
+// into LDS (buffer_load ... lds) in sw: row 2j (A) and 2j + 1 (B) of pair j
+// in blocks (2j + ab) NIT + it, block it of a row holding columns
+// (it * 64 + lane) * 8 .. +7 at 16 B * lane, the layout the task's register
+// loads have.  Columns past the row read as zeros (out-of-range offsets).
+// The loads complete in the wave's vector-memory count; the task waits for
+// them before reading sw.
+template <int NIT, int P>
+__device__ __forceinline__ void fused_qkv_prefetch(const FusedParams &p, int i, const WaveBufs &sw, int lane, int w) {
+  const unsigned row_bytes = (unsigned)p.hidden * 2u;
+  const int qkv_rows = (p.num_heads + 2 * p.num_kv_heads) * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.w_qkv, (unsigned)qkv_rows * row_bytes);
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const PairRows pr = task_pair<P>(p, i, w, j);
+#pragma unroll
+    for (int ab = 0; ab < 2; ++ab) {
+      const unsigned row = (unsigned)(pr.base_row + (ab ? pr.dB : pr.dA));
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int col = (it * 64 + lane) * 8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq, (lds_void_t *)sw.block((2 * j + ab) * NIT + it), 16,
+            col < p.hidden ? row * row_bytes + (unsigned)col * 2u : kOutOfRange, 0, 0, kWeightPolicy);
+      }
+    }
+  }
+}
+
 // Projection task i: pairs [4 P i, 4 P (i + 1)) of q_k_v_proj in group-major
 // order, P per wave (the gate rows are computed by the merge tasks).  x is
-// staged in LDS by the workgroup's first projection task.
-template <int NIT, bool NORM, int P>
+// staged in LDS by the workgroup's first projection task (of the layer).  In
+// a stack (STACK) x is h as the previous layer left it: the weight loads go
+// out first, then wait_h() waits for that layer's o_proj, then x is read
+// coherently.  LDSW: the weights were put in LDS at sw by fused_qkv_prefetch
+// (this wave's rows) and are read from there.
+template <int NIT, bool NORM, int P, bool STACK = false, bool LDSW = false, typename WaitH = NoWait>
 __device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool staged,
-                                               float4 (*s_x)[StagedX<NIT>::kSlots], float *s_ss, int lane, int w) {
-  const int Hq = p.num_heads, Hk = p.num_kv_heads;
+                                               float4 (*s_x)[StagedX<NIT>::kSlots], float *s_ss, int lane, int w,
+                                               WaitH wait_h = WaitH(), const WaveBufs *sw = nullptr) {
+  const int Hk = p.num_kv_heads;
   const unsigned row_bytes = (unsigned)p.hidden * 2u;
-  const int qkv_rows = (Hq + 2 * Hk) * kHeadDim;
+  const int qkv_rows = (p.num_heads + 2 * Hk) * kHeadDim;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.w_qkv, (unsigned)qkv_rows * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (unsigned)p.hidden * 4u);
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u);
   StagedX<NIT> xs;
-  if (!staged) xs.template issue<NORM>(rx, 0u, rn);
+  if (!STACK && !staged) xs.template issue<NORM>(rx, 0u, rn);
   PairRows pr[P];
   uint4 wa[P][NIT], wb[P][NIT];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    const int u = (i * 4 + w) * P + j;   // wave-uniform, < Hk * kPairsPerGroup
-    const int g = u / kPairsPerGroup, r = u - g * kPairsPerGroup;
-    int sec, head, pi;
-    if (r < kGroup * 128) {
-      sec = 0; head = g * kGroup + (r >> 7); pi = r & 127;
-    } else if (r < (kGroup + 1) * 128) {
-      sec = 1; head = g; pi = r - kGroup * 128;
-    } else {
-      sec = 2; head = g; pi = r - (kGroup + 1) * 128;
-    }
-    pr[j] = pair_rows(sec, head, pi, Hq, Hk, p.rotary_dim);
+    pr[j] = task_pair<P>(p, i, w, j);
+    if constexpr (!LDSW) {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int col = (it * 64 + lane) * 8;
-      const bool ok = col < p.hidden;
-      wa[j][it] = buf_load16_p<kWeightPolicy>(
-          rq, ok ? (unsigned)(pr[j].base_row + pr[j].dA) * row_bytes + (unsigned)col * 2u : kOutOfRange);
-      wb[j][it] = buf_load16_p<kWeightPolicy>(
-          rq, ok ? (unsigned)(pr[j].base_row + pr[j].dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+      for (int it = 0; it < NIT; ++it) {
+        const int col = (it * 64 + lane) * 8;
+        const bool ok = col < p.hidden;
+        wa[j][it] = buf_load16_p<kWeightPolicy>(
+            rq, ok ? (unsigned)(pr[j].base_row + pr[j].dA) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+        wb[j][it] = buf_load16_p<kWeightPolicy>(
+            rq, ok ? (unsigned)(pr[j].base_row + pr[j].dB) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+      }
     }
   }
   // the rotations, while the loads are in flight
@@ -1927,15 +2001,41 @@ __device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool
     cs[j] = 1.f;
     if (pr[j].rotate) rope_sincos(p.seq.position, pr[j].pi, p.rotary_dim, p.log2_theta, sn[j], cs[j]);
   }
+  if constexpr (STACK) {
+    // (the empty asm keeps the rotations here, ahead of the wait, instead of
+    // being moved to their use after it)
+#pragma unroll
+    for (int j = 0; j < P; ++j) asm volatile("" : "+v"(sn[j]), "+v"(cs[j]));
+    wait_h();
+    if (!staged) xs.template issue<NORM, kCoherent>(rx, 0u, rn);
+  }
   if (!staged) {
     const float ss = wave_sum(xs.template store<NORM>(s_x));
     if (NORM && lane == 0) s_ss[w] = ss;
     __syncthreads();
   }
+  // x into registers once for all P pairs (each LDS read's latency is
+  // exposed: one wave per SIMD)
+  float4 x0[NIT], x1[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    x0[it] = s_x[0][it * 64 + lane];
+    x1[it] = s_x[1][it * 64 + lane];
+  }
+  if constexpr (LDSW) {
+    vm_wait<0>();   // this wave's prefetched rows are in LDS
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        wa[j][it] = *reinterpret_cast<const uint4 *>(sw->block((2 * j) * NIT + it) + lane * 8);
+        wb[j][it] = *reinterpret_cast<const uint4 *>(sw->block((2 * j + 1) * NIT + it) + lane * 8);
+      }
+  }
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     float ya, yb;
-    pair_dots<NIT, NORM>(wa[j], wb[j], s_x[0], s_x[1], s_ss, p.hidden, p.rms_eps, lane, ya, yb);
+    pair_dots_x<NIT, NORM>(wa[j], wb[j], x0, x1, s_ss, p.hidden, p.rms_eps, ya, yb);
     if (lane == 0) pair_store<true>(p.q, p.gate, p.seq, Hk, pr[j], sn[j], cs[j], ya, yb);
   }
 }
@@ -1953,6 +2053,20 @@ __device__ __forceinline__ void fused_merge_task(const FusedParams &p, int h, in
   const int nch = p.nchunks;
   const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)nch * Hq * 8u);
   const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)nch * Hq * kHeadDim * 4u);
+  const int eq = tid & 15, cg = tid >> 4;
+  const unsigned po = ((unsigned)h * kHeadDim + 64u * qd + 4u * eq) * 4u;
+  // partials of chunks c0 + 16 k, k < 4 (out of range past the last chunk)
+  auto load_group = [&](int c0, float4 (&v)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + 16 * k;
+      v[k] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(rpo, c < nch ? po + (unsigned)c * Hq * kHeadDim * 4u
+                                                                              : kOutOfRange));
+    }
+  };
+  // the first chunk group's partials go out with the (m, l) loads: one round trip
+  float4 v0[4];
+  load_group(cg, v0);
   for (int c = tid; c < nch; c += kThreads)
     s_ml[c] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rml, ((unsigned)c * Hq + h) * 8u, 0,
                                                                               kCoherent));
@@ -1966,17 +2080,19 @@ __device__ __forceinline__ void fused_merge_task(const FusedParams &p, int h, in
     l = fmaf(ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M), ml.y, l);
   }
   const float L = wave_sum(l);
-  const int eq = tid & 15, cg = tid >> 4;
-  const unsigned po = ((unsigned)h * kHeadDim + 64u * qd + 4u * eq) * 4u;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = cg; c0 < nch; c0 += 4 * 16) {
     float4 v[4];
     float wc[4];
+    if (c0 == cg) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = v0[k];
+    } else {
+      load_group(c0, v);
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = c0 + 16 * k;
-      v[k] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(rpo, c < nch ? po + (unsigned)c * Hq * kHeadDim * 4u
-                                                                              : kOutOfRange));
       const float mc = c < nch ? s_ml[c].x : -INFINITY;
       wc[k] = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
     }
@@ -2020,10 +2136,11 @@ template <int NIT, bool NORM>
 struct GateRows {
   StagedX<NIT> xs;
   uint4 wa[NIT], wb[NIT];
+  template <int XPOL = 0>
   __device__ __forceinline__ void issue(const FusedParams &p, int h, int lane) {
     const unsigned row_bytes = (unsigned)p.hidden * 2u;
-    xs.template issue<NORM>(make_rsrc(p.x, (unsigned)p.hidden * 4u), 0u,
-                            make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u));
+    xs.template issue<NORM, XPOL>(make_rsrc(p.x, (unsigned)p.hidden * 4u), 0u,
+                                  make_rsrc(NORM ? p.w_norm : nullptr, NORM ? (unsigned)p.hidden * 2u : 0u));
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.w_g, (unsigned)p.num_heads * row_bytes);
     const int r = h & ~1;
 #pragma unroll
@@ -2045,13 +2162,26 @@ struct GateRows {
   }
 };
 
-template <int NIT, bool NORM>
-__global__ __launch_bounds__(kThreads, 1) void block_fused_kernel(const FusedParams p) {
+// The tasks of one launch: one layer (block_fused_kernel) or, with STACK,
+// the layers of a stack in order (stack_fused_kernel; sp its StackParams).
+// Layer l's flags hold the value derived from (epoch, l), so a word still
+// holding an earlier layer's value never satisfies a wait.  In a stack, x and
+// y are both h: a projection task and a merge task (its gate row reads h)
+// wait for every o_proj task of the previous layer before they read h, and
+// an o_proj task reads and writes its rows of h coherently and then sets its
+// flag.  Every task of a layer is awaited, directly or through later tasks of
+// the layer, by the layer's o_proj tasks, and those by the next layer's
+// projections, so a word is rewritten only after every wait on it has ended.
+template <int NIT, bool NORM, bool STACK, bool HAS_QKV, typename SP>
+__device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   constexpr int W = kThreads / 64;
   constexpr int P = fused_pairs_per_wave(NIT);
   constexpr int NITO = kFusedMaxQDim / 512;
   constexpr int RW = kFusedRowsPerWave;
   static_assert(kPairsPerGroup % (W * P) == 0, "a projection task stays inside one KV head group");
+  // the attention's staged tiles: K (two buffers) and V (two buffers), per
+  // wave (four arrays, so that the compiler can tell a buffer's loads from
+  // another's)
   __shared__ __attribute__((aligned(1024))) _Float16 s_k0[W][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_k1[W][kTileHalves];
   __shared__ __attribute__((aligned(1024))) _Float16 s_v0[W][kTileHalves];
@@ -2061,155 +2191,255 @@ __global__ __launch_bounds__(kThreads, 1) void block_fused_kernel(const FusedPar
   __shared__ float s_gate;
   __shared__ unsigned long long s_epoch;
   using XS = StagedX<NIT>;
-  static_assert(2 * XS::kSlots * sizeof(float4) <= sizeof(s_k0), "staged x fits the first K buffers");
+  static_assert(2 * XS::kSlots * sizeof(float4) <= sizeof(s_k0) && 2 * XS::kSlots * sizeof(float4) <= sizeof(s_q),
+                "staged x fits the first K buffers and the q staging");
   static_assert(kFusedMaxChunks * sizeof(float2) <= sizeof(s_v0) && 256 * sizeof(float4) <= sizeof(s_v1),
                 "merge scratch fits the V buffers");
-  // x (projection tasks) shares the K buffers, the merge scratch the V
-  // buffers: a workgroup's tasks come in phase order
-  float4 (*s_x)[XS::kSlots] = reinterpret_cast<float4 (*)[XS::kSlots]>(&s_k0[0][0]);
+  // x (projection tasks) shares the K buffers (in a stack the q staging,
+  // since the tile buffers then hold the next projection task's weights), the
+  // merge scratch the V buffers: a workgroup's tasks come in phase order
+  float4 (*s_x)[XS::kSlots] = reinterpret_cast<float4 (*)[XS::kSlots]>(STACK ? &s_q[0][0] : &s_k0[0][0]);
   float2 *s_ml = reinterpret_cast<float2 *>(&s_v0[0][0]);
   float4 *s_acc = reinterpret_cast<float4 *>(&s_v1[0][0]);
+  // In a stack the weight rows of the workgroup's first projection task of
+  // the next layer are loaded into the tile buffers as soon as the workgroup
+  // is done with LDS for this layer (before its o_proj task), so that they
+  // stream while this layer finishes: 2 P rows of H bf16 per wave, in 1 KB
+  // blocks over the wave's four 8 KB tile buffers.
+  constexpr bool PF = STACK && 2 * P * NIT <= 4 * (int)(sizeof(s_k0[0]) / 1024);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Hq = p.num_heads, Hk = p.num_kv_heads;
+  const WaveBufs s_w{s_k0[w], s_k1[w], s_v0[w], s_v1[w]};   // this wave's prefetched rows
+  const int Hq = p0.num_heads, Hk = p0.num_kv_heads;
   const int G = gridDim.x, b = blockIdx.x;
-  unsigned long long *const words = p.sync;
+  int t_attn_slots = p0.t_attn;
+  int num_layers = 1;
+  if constexpr (STACK) {
+    t_attn_slots = sp.t_attn_max;
+    num_layers = sp.num_layers;
+  }
+  unsigned long long *const words = p0.sync;
   unsigned long long *const f_qkv = words + kFlagBase;
-  unsigned long long *const f_attn = f_qkv + p.t_qkv;
-  unsigned long long *const f_merge = f_attn + p.t_attn;
-  const bool has_qkv = p.t_qkv > 0;
+  unsigned long long *const f_attn = f_qkv + p0.t_qkv;
+  unsigned long long *const f_merge = f_attn + t_attn_slots;
+  unsigned long long *const f_oproj = f_merge + p0.t_merge;
+  constexpr bool has_qkv = HAS_QKV;   // the projections run in this launch (t_qkv > 0)
 
   if (tid == 0) s_epoch = __hip_atomic_load(words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const unsigned long long epoch = s_epoch;
-  const unsigned long long fv = flag_value(epoch);
   // the last task of the list advances the epoch for the next call
-  const bool last_is_oproj = p.t_oproj > 0;
+  const bool last_is_oproj = p0.t_oproj > 0;
   auto advance_epoch = [&]() {
     if (tid == 0) __hip_atomic_store(words, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
-  // ---- projections ----
-  bool staged = false;
-  for (int t = b; t < p.t_qkv; t += G) {
-    fused_qkv_task<NIT, NORM, P>(p, t, staged, s_x, s_ss, lane, w);
-    staged = true;
-    set_flag(f_qkv + t, fv);
+  // layer l's parameters (a stack's layers differ in weights, cache and shape)
+  auto layer_params = [&](int l) {
+    FusedParams p = p0;
+    if constexpr (STACK) {
+      const StackDesc &d = sp.desc[sp.desc_of[l]];
+      p.w_norm = sp.w_norm[l];
+      p.w_qkv = sp.w_qkv[l];
+      p.w_g = sp.w_g[l];
+      p.w_o = sp.w_o[l];
+      p.sinks = sp.sinks[l];
+      p.seq = d.seq;
+      p.seq.k = sp.k[l];
+      p.seq.v = sp.v[l];
+      p.chunk = d.chunk;
+      p.nchunks = d.nchunks;
+      p.t_attn = d.t_attn;
+      p.rotary_dim = d.rotary_dim;
+      p.log2_theta = d.log2_theta;
+    }
+    return p;
+  };
+  if constexpr (PF) {
+    if (b < p0.t_qkv) fused_qkv_prefetch<NIT, P>(layer_params(0), b, s_w, lane, w);
   }
 
-  // ---- attention ----
-  for (int t = b; t < p.t_attn; t += G) {
-    const int c = t / Hk, g = t - c * Hk;
-    auto wait_q = [&]() {
-      if (has_qkv) await_flags(f_qkv, g * p.qkv_per_group, p.qkv_per_group, 1, fv);
+  for (int l = 0; l < num_layers; ++l) {
+    const FusedParams p = layer_params(l);
+    const unsigned long long fv = flag_value((epoch << 8) | (unsigned)l);
+    // h as the previous layer of the stack leaves it
+    auto wait_h = [&]() {
+      if (STACK && l > 0) await_flags(f_oproj, 0, p.t_oproj, 1, flag_value((epoch << 8) | (unsigned)(l - 1)));
     };
-    float m_run, l_run;
-    if (!has_qkv)
-      attn_partial_wave<W, false, false>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w],
-                                         s_v1[w], s_q[w], m_run, l_run, wait_q);
-    else if (c == p.nchunks - 1)   // holds this token's cache row
-      attn_partial_wave<W, true, true>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w],
-                                       s_q[w], m_run, l_run, wait_q);
-    else
-      attn_partial_wave<W, true, false>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w],
-                                        s_v1[w], s_q[w], m_run, l_run, wait_q);
-    if (lane < kGroup) {
-      float *ml = reinterpret_cast<float *>(s_q[w]);
-      ml[lane] = m_run;
-      ml[kGroup + lane] = l_run;
-    }
-    __syncthreads();
-    float M, L;
-    float4 o;
-    merge_waves<W>(s_q, s_v0, w, lane, M, L, o);   // wave w: query head g * 4 + w
-    const unsigned row = (unsigned)c * Hq + g * kGroup + w;
-    const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)p.nchunks * Hq * kHeadDim * 4u);
-    const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)p.nchunks * Hq * 8u);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), rpo, (row * kHeadDim + lane * 4) * 4u, 0,
-                                           kCoherent);
-    if (lane == 0)
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, make_float2(M, L)), rml, row * 8u, 0, kCoherent);
-    set_flag(f_attn + t, fv);
-    __syncthreads();   // s_q and s_v0 are rewritten by the next task
-  }
 
-  // ---- merge: on the last workgroups (they have no o_proj task) ----
-  for (int t = (b + p.t_merge) % G; t < p.t_merge; t += G) {
-    const int h = t >> 2, qd = t & 3;
-    // in the one-launch block the head's gate logit is computed here: its
-    // loads go out before the wait
-    GateRows<NIT, NORM> gate;
-    if (has_qkv) gate.issue(p, h, lane);
-    // the attention of this head's group: chunk c is attention task c * Hk + g.
-    // Without o_proj tasks the last merge task is the list's last task and
-    // waits for every attention task (so that it follows every workgroup's
-    // first task) before it advances the epoch.
-    const bool final_task = !last_is_oproj && t == p.t_merge - 1;
-    if (final_task)
-      await_flags(f_attn, 0, p.t_attn, 1, fv);
-    else
-      await_flags(f_attn, h / kGroup, p.nchunks, Hk, fv);
-    float gl;
-    if (has_qkv) {
-      const float v = gate.finish(p, h, s_x, s_ss, lane, w);
-      if (tid == 0) s_gate = v;   // to every wave
+    // ---- projections ----
+    bool staged = false;
+    for (int t = b; t < p.t_qkv; t += G) {
+      if (PF && t == b)
+        fused_qkv_task<NIT, NORM, P, STACK, PF>(p, t, staged, s_x, s_ss, lane, w, wait_h, &s_w);
+      else
+        fused_qkv_task<NIT, NORM, P, STACK>(p, t, staged, s_x, s_ss, lane, w, wait_h);
+      staged = true;
+      set_flag(f_qkv + t, fv);
+    }
+
+    // ---- attention ----
+    for (int t = b; t < p.t_attn; t += G) {
+      const int c = t / Hk, g = t - c * Hk;
+      auto wait_q = [&]() {
+        if (has_qkv) await_flags(f_qkv, g * p.qkv_per_group, p.qkv_per_group, 1, fv);
+      };
+      float m_run, l_run;
+      if constexpr (!has_qkv)
+        attn_partial_wave<W, false>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w],
+                                    s_q[w], m_run, l_run, wait_q);
+      else   // the last chunk holds this token's cache row
+        attn_partial_wave<W, true>(p.q, p.seq, c, p.chunk, Hk, p.qscale, g, w, s_k0[w], s_k1[w], s_v0[w], s_v1[w],
+                                   s_q[w], m_run, l_run, wait_q, c == p.nchunks - 1);
+      if (lane < kGroup) {
+        float *ml = reinterpret_cast<float *>(s_q[w]);
+        ml[lane] = m_run;
+        ml[kGroup + lane] = l_run;
+      }
       __syncthreads();
-      gl = s_gate;
-    } else {
-      gl = p.gate[h];
+      float M, L;
+      float4 o;
+      merge_waves<W>(s_q, s_v0, w, lane, M, L, o);   // wave w: query head g * 4 + w
+      const unsigned row = (unsigned)c * Hq + g * kGroup + w;
+      const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)p.nchunks * Hq * kHeadDim * 4u);
+      const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)p.nchunks * Hq * 8u);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), rpo, (row * kHeadDim + lane * 4) * 4u, 0,
+                                             kCoherent);
+      if (lane == 0)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, make_float2(M, L)), rml, row * 8u, 0,
+                                              kCoherent);
+      set_flag(f_attn + t, fv);
+      __syncthreads();   // s_q and s_v0 are rewritten by the next task
     }
-    fused_merge_task(p, h, qd, gl, s_ml, s_acc, tid, lane);
-    set_flag(f_merge + t, fv);
-    if (final_task) advance_epoch();
-    __syncthreads();   // LDS is rewritten by the next task
-  }
 
-  // ---- o_proj ----
-  for (int t = b; t < p.t_oproj; t += G) {
-    // rows r0 .. r0 + RW - 1 of this wave: the W_o loads go out before the wait for a
-    const int r0 = (t * W + w) * RW;
-    const int qdim = Hq * kHeadDim;
-    const unsigned row_bytes = (unsigned)qdim * 2u;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_o, (unsigned)p.hidden * row_bytes);
-    uint4 wv[RW][NITO];
+    // ---- merge: on the last workgroups (they have no o_proj task) ----
+    for (int t = (b + p.t_merge) % G; t < p.t_merge; t += G) {
+      const int h = t >> 2, qd = t & 3;
+      // in the one-launch block the head's gate logit is computed here: its
+      // loads go out before the wait
+      GateRows<NIT, NORM> gate;
+      if constexpr (has_qkv) {
+        if constexpr (STACK) {
+          wait_h();
+          gate.template issue<kCoherent>(p, h, lane);
+        } else {
+          gate.issue(p, h, lane);
+        }
+      }
+      // the attention of this head's group: chunk c is attention task c * Hk + g.
+      // Without o_proj tasks the last merge task is the list's last task and
+      // waits for every attention task (so that it follows every workgroup's
+      // first task) before it advances the epoch.
+      const bool final_task = !last_is_oproj && t == p.t_merge - 1;
+      if (final_task)
+        await_flags(f_attn, 0, p.t_attn, 1, fv);
+      else
+        await_flags(f_attn, h / kGroup, p.nchunks, Hk, fv);
+      float gl;
+      if constexpr (has_qkv) {
+        const float v = gate.finish(p, h, s_x, s_ss, lane, w);
+        if (tid == 0) s_gate = v;   // to every wave
+        __syncthreads();
+        gl = s_gate;
+      } else {
+        gl = p.gate[h];
+      }
+      fused_merge_task(p, h, qd, gl, s_ml, s_acc, tid, lane);
+      set_flag(f_merge + t, fv);
+      if (final_task) advance_epoch();
+      __syncthreads();   // LDS is rewritten by the next task
+    }
+    if constexpr (PF) {
+      // every LDS task of the layer has ended (each ends in a barrier)
+      if (l + 1 < num_layers && b < p.t_qkv) fused_qkv_prefetch<NIT, P>(layer_params(l + 1), b, s_w, lane, w);
+    }
+
+    // ---- o_proj ----
+    for (int t = b; t < p.t_oproj; t += G) {
+      // rows r0 .. r0 + RW - 1 of this wave: the W_o loads go out before the wait for a
+      const int r0 = (t * W + w) * RW;
+      const int qdim = Hq * kHeadDim;
+      const unsigned row_bytes = (unsigned)qdim * 2u;
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_o, (unsigned)p.hidden * row_bytes);
+      uint4 wv[RW][NITO];
 #pragma unroll
-    for (int k = 0; k < RW; ++k)
+      for (int k = 0; k < RW; ++k)
+#pragma unroll
+        for (int it = 0; it < NITO; ++it) {
+          const int col = (it * 64 + lane) * 8;
+          const int r = r0 + k;
+          wv[k][it] = buf_load16_p<kWeightPolicy>(
+              rw, (r < p.hidden && col < qdim) ? (unsigned)r * row_bytes + (unsigned)col * 2u : kOutOfRange);
+        }
+      // in a stack: this wave's RW rows of h (a multiple of 4 rows: one 16 B
+      // load), which this wave itself wrote in the previous layer
+      static_assert(RW == 4, "one float4 of h per wave");
+      const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.y, (unsigned)p.hidden * 4u);
+      float4 yold = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (STACK)
+        yold = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ry, r0 < p.hidden ? (unsigned)r0 * 4u : kOutOfRange));
+      if (p.t_merge > 0) await_flags(f_merge, 0, p.t_merge, 1, fv);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)qdim * 4u);
+      float4 xa[NITO], xb[NITO];
 #pragma unroll
       for (int it = 0; it < NITO; ++it) {
-        const int col = (it * 64 + lane) * 8;
-        const int r = r0 + k;
-        wv[k][it] = buf_load16_p<kWeightPolicy>(
-            rw, (r < p.hidden && col < qdim) ? (unsigned)r * row_bytes + (unsigned)col * 2u : kOutOfRange);
+        const unsigned col = (unsigned)(it * 64 + lane) * 8u;
+        xa[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u));
+        xb[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u + 16u));
       }
-    if (p.t_merge > 0) await_flags(f_merge, 0, p.t_merge, 1, fv);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)qdim * 4u);
-    float4 xa[NITO], xb[NITO];
+      float ynew[RW];
 #pragma unroll
-    for (int it = 0; it < NITO; ++it) {
-      const unsigned col = (unsigned)(it * 64 + lane) * 8u;
-      xa[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u));
-      xb[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u + 16u));
+      for (int k = 0; k < RW; ++k) {
+        float acc = 0.f;
+#pragma unroll
+        for (int it = 0; it < NITO; ++it) acc = dot8_bf16(wv[k][it], xa[it], xb[it], acc);
+        const float s = wave_sum(acc);
+        const int r = r0 + k;
+        if constexpr (STACK) {
+          ynew[k] = (k == 0 ? yold.x : k == 1 ? yold.y : k == 2 ? yold.z : yold.w) + s;
+        } else {
+          if (lane == 0 && r < p.hidden) p.y[r] = p.accumulate ? p.y[r] + s : s;
+        }
+      }
+      if constexpr (STACK) {
+        if (lane == 0)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4_t, make_float4(ynew[0], ynew[1], ynew[2], ynew[3])), ry,
+              r0 < p.hidden ? (unsigned)r0 * 4u : kOutOfRange, 0, kCoherent);
+        set_flag(f_oproj + t, fv);
+      }
+      if (l == num_layers - 1 && t == p.t_oproj - 1) advance_epoch();
     }
-#pragma unroll
-    for (int k = 0; k < RW; ++k) {
-      float acc = 0.f;
-#pragma unroll
-      for (int it = 0; it < NITO; ++it) acc = dot8_bf16(wv[k][it], xa[it], xb[it], acc);
-      const float s = wave_sum(acc);
-      const int r = r0 + k;
-      if (lane == 0 && r < p.hidden) p.y[r] = p.accumulate ? p.y[r] + s : s;
-    }
-    if (t == p.t_oproj - 1) advance_epoch();
   }
+}
+
+// HAS_QKV: the whole block (projections in the launch); else its attention
+// and merge alone, on a q and gate logits already in memory.
+template <int NIT, bool NORM, bool HAS_QKV>
+__global__ __launch_bounds__(kThreads, 1) void block_fused_kernel(const FusedParams p) {
+  fused_run<NIT, NORM, false, HAS_QKV>(p, p);
+}
+
+template <int NIT>
+__global__ __launch_bounds__(kThreads, 1) void stack_fused_kernel(const StackParams sp) {
+  fused_run<NIT, true, true, true>(sp.base, sp);
 }
 
 template <int NIT>
 hipError_t fused_launch(const FusedParams &p, dim3 grid, hipStream_t stream) {
-  if (p.w_norm != nullptr)
-    hipLaunchKernelGGL((block_fused_kernel<NIT, true>), grid, dim3(kThreads), 0, stream, p);
+  if (p.t_qkv == 0)   // attention + merge only (no norm: x is not read)
+    hipLaunchKernelGGL((block_fused_kernel<NIT, false, false>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.w_norm != nullptr)
+    hipLaunchKernelGGL((block_fused_kernel<NIT, true, true>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((block_fused_kernel<NIT, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((block_fused_kernel<NIT, false, true>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int NIT>
+hipError_t stack_launch(const StackParams &sp, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((stack_fused_kernel<NIT>), grid, dim3(kThreads), 0, stream, sp);
   return hipGetLastError();
 }
 
@@ -2293,21 +2523,34 @@ void fused_tasks(FusedParams &p) {
   p.t_oproj = (p.phases & kPhaseOproj) ? (p.hidden + rows - 1) / rows : 0;
 }
 
+namespace {
+
+// The CU count of the current device, asked once per device.
+hipError_t device_cus(int *cus) {
+  static int cu_count[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int n = dev >= 0 && dev < 64 ? __atomic_load_n(&cu_count[dev], __ATOMIC_RELAXED) : 0;
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) __atomic_store_n(&cu_count[dev], n, __ATOMIC_RELAXED);
+  }
+  *cus = n;
+  return hipSuccess;
+}
+
+}  // namespace
+
 // One workgroup per CU, and no more workgroups than the largest of the
 // projection, attention and merge phases has tasks, so that every workgroup
 // runs one of them (the list's last task then follows every workgroup's
 // start); without o_proj tasks, no more than the attention tasks.
 hipError_t launch_block_fused(const FusedParams &p, hipStream_t stream) {
-  static int cu_count[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
-  int cus = dev >= 0 && dev < 64 ? __atomic_load_n(&cu_count[dev], __ATOMIC_RELAXED) : 0;
-  if (cus <= 0) {
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) __atomic_store_n(&cu_count[dev], cus, __ATOMIC_RELAXED);
-  }
   const int cover = p.t_oproj > 0 ? std::max(p.t_qkv, std::max(p.t_attn, p.t_merge)) : p.t_attn;
   const dim3 grid((unsigned)std::max(1, std::min(cus, cover)));
   switch ((p.hidden + 511) / 512) {
@@ -2319,6 +2562,26 @@ hipError_t launch_block_fused(const FusedParams &p, hipStream_t stream) {
     case 6: return fused_launch<6>(p, grid, stream);
     case 7: return fused_launch<7>(p, grid, stream);
     default: return fused_launch<8>(p, grid, stream);
+  }
+}
+
+// As the block: one workgroup per CU, at most the largest phase of any layer.
+hipError_t launch_stack_fused(const StackParams &sp, hipStream_t stream) {
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const FusedParams &p = sp.base;
+  const int cover = std::max(p.t_qkv, std::max(sp.t_attn_max, p.t_merge));
+  const dim3 grid((unsigned)std::max(1, std::min(cus, cover)));
+  switch ((p.hidden + 511) / 512) {
+    case 1: return stack_launch<1>(sp, grid, stream);
+    case 2: return stack_launch<2>(sp, grid, stream);
+    case 3: return stack_launch<3>(sp, grid, stream);
+    case 4: return stack_launch<4>(sp, grid, stream);
+    case 5: return stack_launch<5>(sp, grid, stream);
+    case 6: return stack_launch<6>(sp, grid, stream);
+    case 7: return stack_launch<7>(sp, grid, stream);
+    default: return stack_launch<8>(sp, grid, stream);
   }
 }
 

@@ -290,6 +290,47 @@ gqa_status gqa_attention_layer_decode(const gqa_arch *arch, const gqa_layer_weig
                                       int32_t batch, float *h, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* One layer of a stack for gqa_attention_stack_decode: its weights, its input
+ * RMSNorm weight (device bf16 [H]), its cache of the one sequence (the token's
+ * position), and its class. */
+typedef struct {
+  gqa_layer_weights weights;
+  const void *w_norm;
+  gqa_kv_seq cache;
+  int32_t is_full;
+  int32_t reserved;          /* must be 0 */
+} gqa_stack_layer;
+
+/* One decode token of ONE sequence through a stack of attention layers, in
+ * layer order ([mod] `produce_real_spark_inner`: the layer loop encodes every
+ * layer of the token into one pass that is committed once):
+ *   for l in 0 .. num_layers-1:  h += block_l(RMSNorm(h) * layers[l].w_norm)
+ * i.e. gqa_attention_layer_decode for each layer in turn, with the same
+ * result bit for bit.  Consecutive layers that the one-launch block takes
+ * (see gqa_attention_block_decode; the window longer than 128 rows) run as
+ * ONE persistent launch per up to 40 layers with at most 4 distinct
+ * attention shapes (window, chunking, RoPE class), each layer's projections
+ * starting as soon as the previous layer's o_proj has finished; other layers
+ * run as gqa_attention_layer_decode runs them.
+ *   layers     host array of num_layers descriptors (read during the call
+ *              only); each layer's weights and cache as for
+ *              gqa_attention_layer_decode, batch 1
+ *   num_layers >= 0 (0: nothing is done)
+ *   h          device fp32 [H], read and updated in place
+ *   workspace  device, at least the largest of the layers' block workspaces
+ *              (gqa_workspace_size(arch, 1, position + 1) is enough); the
+ *              layers run one after another through it
+ * Side effect: each layer's cache slot row for its position is written.
+ * Residency and overlap: as for the one-launch block (its workgroups, one
+ * per CU, must all be resident; calls on one workspace must not overlap).
+ * Determinism: bit-reproducible, and equal to the layer-by-layer calls.
+ * Errors: those of gqa_attention_layer_decode for any layer (the message
+ * names the layer; nothing is enqueued then), INVALID_ARGUMENT for
+ * num_layers < 0, a null layers array or a nonzero reserved field. */
+gqa_status gqa_attention_stack_decode(const gqa_arch *arch, const gqa_stack_layer *layers,
+                                      int32_t num_layers, float *h, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Step entry points: the block's steps one launch each, exposed so each
  * step can be checked and timed on its own.  They run the block's own code:

@@ -7,6 +7,8 @@ set of rows read is exactly the window).
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -739,6 +741,116 @@ def test_stack36_of_fused_layers_matches_oracle(phase_full_first):
     assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "36-layer fused stack residual delta")
     for li in range(len(case.layers)):
         assert_parity(contrib[li], ref.block_outs[li], f"36-layer fused stack layer {li} contribution")
+
+
+def _stack_layers_dev(case, sinks=False):
+    """The case's layers on the device (caches included) as StackLayer records."""
+    out = []
+    for li, L in enumerate(case.layers):
+        out.append(gqa.StackLayer(
+            w_norm=bits_to_dev(L.w_norm), w_qkv=bits_to_dev(L.w_qkv), w_g=bits_to_dev(L.w_g),
+            w_o=bits_to_dev(L.w_o), is_full=L.is_full,
+            seq=gqa.KvSeq(k=f16_to_dev(L.cache.k), v=f16_to_dev(L.cache.v), position=L.cache.position,
+                          ring_capacity=L.cache.ring_capacity),
+            sinks=torch.from_numpy(synth.random_sinks(case.arch, 0, 40 + li)).cuda() if sinks else None))
+    return out
+
+
+def _stack_vs_layers(case, sinks=False):
+    """h after gqa_attention_stack_decode, after gqa_attention_layer_decode
+    layer by layer, and after the stack call once more (same device caches:
+    each call rewrites every layer's slot row with the same values)."""
+    a = arch_of(case.arch)
+    layers = _stack_layers_dev(case, sinks)
+    ws = torch.empty(gqa.workspace_size(a, 1, max(L.cache.position for L in case.layers) + 1),
+                     dtype=torch.uint8, device="cuda")
+    h_stack = f32_to_dev(case.h)
+    gqa.attention_stack_decode(a, layers, h_stack, ws)
+    h_layers = f32_to_dev(case.h)
+    for ly in layers:
+        gqa.attention_layer_decode(a, ly.w_norm, ly.w_qkv, ly.w_g, ly.w_o, ly.is_full, [ly.seq], h_layers, ws,
+                                   sinks=ly.sinks)
+    h_again = f32_to_dev(case.h)
+    gqa.attention_stack_decode(a, layers, h_again, ws)
+    torch.cuda.synchronize()
+    return h_stack, h_layers, h_again
+
+
+def _assert_same_bits(got: torch.Tensor, ref: torch.Tensor, what: str):
+    g, r = got.view(torch.int32).cpu(), ref.view(torch.int32).cpu()
+    n = int((g != r).sum())
+    assert n == 0, f"{what}: {n} of {g.numel()} values differ in their bits"
+
+
+@pytest.mark.parametrize("phase_full_first", [False, True])
+def test_stack36_one_launch_matches_oracle(phase_full_first):
+    """The one-launch stack at the benchmarked configuration (36 layers at
+    position 8191, 9 full over 8192 rows, 27 sliding over wrapped 512-slot
+    rings): the residual delta against the oracle, and bit-identical to the
+    36 layer calls and to itself run again."""
+    case, ref = _stack_and_ref("attention", phase_full_first)
+    say(f"one-launch stack {case.name} phase_full_first={phase_full_first}")
+    h_stack, h_layers, h_again = _stack_vs_layers(case)
+    delta = h_stack.cpu().numpy().astype(np.float64) - np.asarray(case.h, np.float64)
+    assert_parity(delta, ref.h - np.asarray(case.h, np.float64), "one-launch 36-layer stack residual delta")
+    _assert_same_bits(h_stack, h_layers, "one-launch stack vs its layer calls")
+    _assert_same_bits(h_again, h_stack, "one-launch stack run twice")
+
+
+def _stack_case_positions(num_layers, position, hidden, positions=None, sliding_window=None):
+    case = synth.cfg4_stack(num_layers=num_layers, position=position, hidden=hidden, case_id=41)
+    if sliding_window is not None:
+        case.arch = dataclasses.replace(case.arch, sliding_window=sliding_window)
+    if positions is not None:
+        for L, p in zip(case.layers, positions):
+            L.cache.position = p
+    return case
+
+
+STACK_SPLIT_CASES = [
+    # 45 layers: a launch of 40, then one of 5
+    ("layers45_pos1000", dict(num_layers=45, position=1000, hidden=1024)),
+    # sliding layers over 96 rows (the direct form, one layer each) between
+    # full layers over 301 rows (one-launch runs of one layer)
+    ("window96_mixed", dict(num_layers=8, position=300, hidden=1024, sliding_window=96)),
+    # 6 distinct positions over 10 layers: more shapes than one launch holds
+    ("positions6", dict(num_layers=10, position=1200, hidden=1024,
+                        positions=[1200, 1100, 1000, 900, 800, 700, 1200, 1100, 1000, 900])),
+    # hidden 2560, 12 layers at a position whose full window is 65 chunks
+    ("h2560_pos4100", dict(num_layers=12, position=4100, hidden=2560)),
+]
+
+
+@pytest.mark.parametrize("name,kw", STACK_SPLIT_CASES, ids=[c[0] for c in STACK_SPLIT_CASES])
+def test_stack_launch_runs_match_oracle(name, kw):
+    """How the stack entry splits its layers into launches (the 40-layer and
+    4-shape limits, layers the one-launch block does not take): each case
+    against the oracle and bit-identical to the layer calls."""
+    case = _stack_case_positions(**kw)
+    say(f"stack runs {name}")
+    ref = oracle.stack_decode(case.arch, case.h, case.layers)
+    h_stack, h_layers, h_again = _stack_vs_layers(case)
+    delta = h_stack.cpu().numpy().astype(np.float64) - np.asarray(case.h, np.float64)
+    assert_parity(delta, ref.h - np.asarray(case.h, np.float64), f"stack {name} residual delta")
+    _assert_same_bits(h_stack, h_layers, f"stack {name} vs its layer calls")
+    _assert_same_bits(h_again, h_stack, f"stack {name} run twice")
+
+
+def test_stack_with_sinks_equals_layer_calls():
+    """Per-layer sink logits reach each layer of a one-launch stack: the
+    result is bit-identical to the layer calls with the same sinks (those are
+    checked against the oracle with sinks elsewhere)."""
+    case = _stack_case_positions(num_layers=6, position=2000, hidden=1024)
+    say("stack with sinks")
+    h_stack, h_layers, h_again = _stack_vs_layers(case, sinks=True)
+    h_plain = f32_to_dev(case.h)
+    a = arch_of(case.arch)
+    gqa.attention_stack_decode(a, _stack_layers_dev(case), h_plain,
+                               torch.empty(gqa.workspace_size(a, 1, 2001), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    _assert_same_bits(h_stack, h_layers, "stack with sinks vs its layer calls")
+    _assert_same_bits(h_again, h_stack, "stack with sinks run twice")
+    assert not torch.equal(h_plain, h_stack), "the sinks changed nothing"
 
 
 @pytest.mark.parametrize("phase_full_first", [False, True])

@@ -47,7 +47,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not available")
     mirrors = {"gqa_arch": B._Arch, "gqa_layer_weights": B._Weights, "gqa_kv_seq": B._KvSeq,
-               "gqa_mlp_weights": B._MlpWeights}
+               "gqa_mlp_weights": B._MlpWeights, "gqa_stack_layer": B._StackLayer}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
     for cname, py in mirrors.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -264,6 +264,45 @@ def test_layer_entry_validates():
                       FAKE, FAKE, 1024, None) == WS_SMALL
     assert B.raw_call("gqa_attention_layer_decode", ctypes.byref(a), ctypes.byref(w), 0, 1, None, 0,
                       0, 0, 0, None) == OK                  # batch 0: nothing to do
+
+
+def test_stack_entry_validates():
+    """gqa_attention_stack_decode checks every layer before it enqueues
+    anything (FAKE device pointers are never touched: a GQA_OK with layers
+    would mean a launch), and names the failing layer."""
+    a = B.c_arch(gqa.Arch(hidden=1024))
+
+    def layer(**kw):
+        w = B.c_weights(FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000)
+        ly = B.c_stack_layer(w, FAKE, _seq(pos=300, cap=400), 1, 0)
+        for k, v in kw.items():
+            setattr(ly, k, v)
+        return ly
+
+    def call(layers, n=None, h=FAKE, ws_bytes=1 << 30, arch=a):
+        arr = (B.c_stack_layer * max(1, len(layers)))(*layers)
+        return B.raw_call("gqa_attention_stack_decode", ctypes.byref(arch), arr if layers else None,
+                          len(layers) if n is None else n, h, FAKE + 0x200000, ws_bytes, None)
+
+    assert call([]) == OK                                     # nothing to do
+    assert call([], n=-1) == INVALID
+    assert call([], n=2) == INVALID                           # layers is null
+    assert call([layer(), layer(reserved=1)]) == INVALID
+    assert "layers[1]" in B.last_error()
+    assert call([layer(), layer(w_norm=0)]) == INVALID
+    assert "layers[1]" in B.last_error()
+    assert call([layer(), layer(w_norm=MISALIGNED)]) == INVALID
+    bad = layer()
+    bad.cache = _seq(pos=400, cap=400)                        # linear cache too short
+    assert call([layer(), layer(), bad]) == INVALID
+    assert "layers[2]" in B.last_error()
+    bad = layer()
+    bad.weights = B.c_weights(FAKE, 0, FAKE)                  # no g_proj
+    assert call([bad]) == INVALID
+    assert call([layer()], h=MISALIGNED) == INVALID
+    assert call([layer()], ws_bytes=1024) == WS_SMALL
+    assert call([layer()], arch=B.c_arch(gqa.Arch(hidden=1024, rms_eps=-1.0))) == INVALID
+    assert call([layer()], arch=B.c_arch(gqa.Arch(hidden=1024, head_dim=128))) == UNSUPPORTED
 
 
 def test_chunk_entry_validates():
