@@ -1209,14 +1209,18 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
     __builtin_amdgcn_sched_barrier(0);
     load_v(sv1, t + 3);
   }
-  {
+  // The last two tiles; a wave with fewer than two tiles of rows skips the
+  // padding tiles' arithmetic (a fully masked tile adds exactly nothing; its
+  // out-of-range loads still complete before the buffers are reused).
+  if (ntiles >= ne - 1) {
     const floatx4_t d = scores(sk0, in_flight_24{});
     process(d, sv0, ne - 2, std::integral_constant<int, 16>{});
   }
-  {
+  if (ntiles >= ne) {
     const floatx4_t d = scores(sk1, std::integral_constant<int, 8>{});
     process(d, sv1, ne - 1, std::integral_constant<int, 0>{});
   }
+  vm_wait<0>();   // (a skipped tile's loads land in sv0 / sv1 before they are reused below)
 
   // ---- this wave's partial: add the high and low rows, stage (m, l, O) ----
   l_run = sum_across_rows(l_run);
