@@ -895,7 +895,8 @@ __global__ __launch_bounds__(kProjThreads) void proj_mfma_kernel(const Params p)
 // buffers each per wave).  Buffer loads whose offsets are out of range return
 // zeros without an HBM access, which pads the last tile.  The W waves then
 // merge their (m, l, O) in LDS and the workgroup writes one partial per query
-// head; a combine kernel (or the fused merge + o_proj) merges the chunks.
+// head; a combine kernel, or the merge tasks of the one-launch kernels,
+// merge the chunks.
 // ---------------------------------------------------------------------------
 
 // Workgroup -> (chunk cid, KV head g).  The hardware deals workgroups to the
@@ -1289,8 +1290,7 @@ __device__ __forceinline__ void merge_waves(const _Float16 (*sq)[2 * kGroup * kH
 // 36 KB of LDS per wave: W = 4 (144 KB) runs one workgroup per CU, W = 2
 // (72 KB) two; either way one wave per SIMD.  Measured on 32 sequences of up
 // to 16K rows: W = 2 with 512 workgroups 202.4 us against 209.6 us for W = 4
-// with 256; on one 32K sequence W = 2 was slower (26.5 against 26.1 us, and
-// 128 chunks slow the fused merge + o_proj).
+// with 256; on one 32K sequence W = 2 was slower (26.5 against 26.1 us).
 template <int W>
 __global__ __launch_bounds__(64 * W, 1) void attn_partial_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) _Float16 s_k0[W][kTileHalves];
