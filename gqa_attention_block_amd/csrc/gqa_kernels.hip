@@ -2329,16 +2329,23 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
     // ---- merge: on the last workgroups (they have no o_proj task) ----
     for (int t = (b + p.t_merge) % G; t < p.t_merge; t += G) {
       const int h = t >> 2, qd = t & 3;
-      // in the one-launch block the head's gate logit is computed here: its
-      // loads go out before the wait
-      GateRows<NIT, NORM> gate;
+      // in the one-launch block the head's gate logit is computed here,
+      // before the wait for the attention (it needs only x)
+      float gl;
       if constexpr (has_qkv) {
+        GateRows<NIT, NORM> gate;
         if constexpr (STACK) {
           wait_h();
           gate.template issue<kCoherent>(p, h, lane);
         } else {
           gate.issue(p, h, lane);
         }
+        const float v = gate.finish(p, h, s_x, s_ss, lane, w);
+        if (tid == 0) s_gate = v;   // to every wave
+        __syncthreads();
+        gl = s_gate;
+      } else {
+        gl = p.gate[h];
       }
       // the attention of this head's group: chunk c is attention task c * Hk + g.
       // Without o_proj tasks the last merge task is the list's last task and
@@ -2349,15 +2356,6 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
         await_flags(f_attn, 0, p.t_attn, 1, fv);
       else
         await_flags(f_attn, h / kGroup, p.nchunks, Hk, fv);
-      float gl;
-      if constexpr (has_qkv) {
-        const float v = gate.finish(p, h, s_x, s_ss, lane, w);
-        if (tid == 0) s_gate = v;   // to every wave
-        __syncthreads();
-        gl = s_gate;
-      } else {
-        gl = p.gate[h];
-      }
       fused_merge_task(p, h, qd, gl, s_ml, s_acc, tid, lane);
       set_flag(f_merge + t, fv);
       if (final_task) advance_epoch();
