@@ -966,19 +966,17 @@ __device__ __forceinline__ void vload_block(__amdgpu_buffer_rsrc_t rs, _Float16 
 // The chunk: rows [t0, t0 + chunk) of sequence sd (chunk index ci inside
 // the sequence), KV head g, whose 4 query heads start at q_seq + g * 4 * D.
 // before_q() runs after the first tiles' loads are issued and before q is
-// read (the fused block kernel waits there for q); with tiles_after_wait the
-// first tiles are issued after it instead (the chunk holding this token's
-// row, which the wait makes visible).
+// read (the fused block kernel waits there for q).
 struct NoWait {
   __device__ __forceinline__ void operator()() const {}
 };
 
 // QC: q is read coherently (other workgroups of the same launch wrote it),
-// and so are the tiles (the chunk holding this token's cache row reads the
-// row written in the same launch; every chunk takes the same path, so that
-// the fused kernel carries one copy of this code).  The first tiles are
-// issued before before_q() waits for q, or with tc after it (the chunk
-// holding this token's row, which the wait makes visible).
+// and so are the tiles.  tc (with QC): the chunk holds this token's cache
+// row, written in the same launch; its first tiles are still issued before
+// before_q() waits, and the one row the wait makes visible is loaded again
+// after it (every chunk takes the same path, so that the fused kernel
+// carries one copy of this code).
 template <int W, bool QC = false, typename BeforeQ = NoWait>
 __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqDesc &sd, int ci, int chunk, int Hk,
                                                   float qscale, int g, int w, _Float16 *__restrict__ sk0,
@@ -1014,19 +1012,20 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
   // lines, which the non-temporal policy needs.  Row r's piece p sits at
   // position p ^ swz(r) (K: swz = r % 16; V: swz = 2 (r % 8)), chosen so
   // that the fragment reads below hit distinct LDS banks.
-  auto load_tile = [&](_Float16 *sbuf, int t, auto k_tag) {
+  auto load_piece = [&](_Float16 *sbuf, int t, int jj, auto k_tag) {
     constexpr bool is_k = decltype(k_tag)::value;
     const __amdgpu_buffer_rsrc_t rs = is_k ? krs : vrs;
     const int pos = lane & 31;
+    const int r = 2 * jj + (lane >> 5);
+    const int pc = is_k ? (pos & 16) | ((pos ^ r) & 15) : pos ^ (2 * (r & 7));
+    const unsigned off = row_off((W * t + w) * kTileRows + r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sbuf + jj * 512), 16,
+                                             off == kOutOfRange ? off : off + 16u * (unsigned)pc, 0, 0,
+                                             (is_k ? kKPolicy : kVPolicy) | (QC ? kCoherent : 0));
+  };
+  auto load_tile = [&](_Float16 *sbuf, int t, auto k_tag) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int r = 2 * jj + (lane >> 5);
-      const int pc = is_k ? (pos & 16) | ((pos ^ r) & 15) : pos ^ (2 * (r & 7));
-      const unsigned off = row_off((W * t + w) * kTileRows + r);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sbuf + jj * 512), 16,
-                                               off == kOutOfRange ? off : off + 16u * (unsigned)pc, 0, 0,
-                                               (is_k ? kKPolicy : kVPolicy) | (QC ? kCoherent : 0));
-    }
+    for (int jj = 0; jj < 8; ++jj) load_piece(sbuf, t, jj, k_tag);
   };
   auto load_k = [&](_Float16 *sk, int t) { load_tile(sk, t, std::true_type{}); };
   auto load_v = [&](_Float16 *sv, int t) { load_tile(sv, t, std::false_type{}); };
@@ -1068,9 +1067,23 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
     }
   };
   if constexpr (QC) {
-    if (!tc) first_tiles();
+    first_tiles();
     before_q();
-    if (tc) first_tiles();
+    if (tc) {
+      // This chunk holds this token's cache row (its last row), written in
+      // this launch: the wave whose first tiles hold it loads that row's
+      // piece of K and V again now that the wait has made it visible, once
+      // its earlier loads into the same LDS have landed.  (A row in a later
+      // tile is loaded after the wait anyway.)
+      const int rel = nrows - 1;
+      const int T = rel / kTileRows;
+      if (T % W == w && T / W < 2) {
+        vm_wait<0>();
+        const int jj = (rel % kTileRows) / 2;
+        load_piece(T / W == 0 ? sk0 : sk1, T / W, jj, std::true_type{});
+        load_piece(T / W == 0 ? sv0 : sv1, T / W, jj, std::false_type{});
+      }
+    }
     load_q();
   } else {
     before_q();
