@@ -30,6 +30,10 @@ HIPCC_FLAGS = [
     "-Wall",
     "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core accumulators in ordinary VGPRs: the attention rescales its
+    # accumulators with VALU multiplies, and with the AGPR form the compiler
+    # copied all 64 of them between the two register files on every tile.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -1154,13 +1154,24 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
     half8_t kf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const half8_t *>(kbase + kaddr[s & 3] + (s >> 2) * 256);
+    __builtin_amdgcn_sched_barrier(0);   // all 8 reads in flight before the first product
     floatx4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[s], qf[s], d, 0, 0, 0);
     return d;
   };
-  // online softmax of tile t's scores and O += P V from the staged V tile
+  // online softmax of tile t's scores and O += P V from the staged V tile.
+  // The 16 B fragments of V are read first, into registers of their own, so
+  // that their LDS latency overlaps the softmax (read into one register pair
+  // each, the reads and products would run one LDS round trip at a time).
   auto process = [&](floatx4_t d, const _Float16 *sv, int t, auto wait) {
+    vm_wait<decltype(wait)::value>();
+    const char *base = reinterpret_cast<const char *>(sv);
+    short4_t vt[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      vt[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(base + vaddr[c & 7] + (c >> 3) * 256));
+    __builtin_amdgcn_sched_barrier(0);
     float sc[4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -1174,18 +1185,23 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
     // it by more than kRescaleSlack (log2 units), so P = exp2(s - m_run) stays
     // <= 2^kRescaleSlack (exact in fp16 hi + lo) and the 64 accumulators are
     // rescaled only on the rare tiles where the max jumps.
+    // While no head has a finite reference max, no score has been taken
+    // in: O and l are still zero and there is nothing to rescale.
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
+      const bool seen = __builtin_amdgcn_ballot_w64(m_run != -INFINITY) != 0;
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-      float al[kGroup];
+      if (seen) {
+        float al[kGroup];
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) al[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
+        for (int i = 0; i < kGroup; ++i) al[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), i));
 #pragma unroll
-      for (int c = 0; c < 16; ++c)
+        for (int c = 0; c < 16; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[c][i] *= al[i];
+          for (int i = 0; i < 4; ++i) acc[c][i] *= al[i];
+      }
     }
     float pr[4];
     float psum = 0.f;
@@ -1204,15 +1220,10 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
       const _Float16 hi = (_Float16)pv;
       pf[i] = n < 4 ? hi : (n < 8 ? (_Float16)(pv - (float)hi) : (_Float16)0.f);
     }
-    // O += P V; B fragments by transposed reads of the staged tile
-    vm_wait<decltype(wait)::value>();
-    const char *base = reinterpret_cast<const char *>(sv);
+    // O += P V
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const short4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4_t *)(base + vaddr[c & 7] + (c >> 3) * 256));
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pf, __builtin_bit_cast(half4_t, vt), acc[c], 0, 0, 0);
-    }
+    for (int c = 0; c < 16; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pf, __builtin_bit_cast(half4_t, vt[c]), acc[c], 0, 0, 0);
   };
   // A K buffer is refilled as soon as its scores are formed (the MFMAs have
   // consumed every read of it), a V buffer after O += P V; sched_barrier keeps
