@@ -1095,7 +1095,8 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
   // splits its dims (pre-scaled by scale * log2(e)) into fp16 high and low
   // parts in the wave's staging area sq = [hi, lo][query head][dim]; then the
   // Qf B-fragments: lane (G, n) holds column n, dims 32s + 8G .. +8 of
-  // n < 4: hi(q_n); 4 <= n < 8: lo(q_{n-4}); else 0.
+  // hi(q_{n % 4}) for n % 8 < 4, else lo(q_{n % 4}).  Columns 8-15 repeat
+  // columns 0-7; only columns 0-7 of the scores are used.
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) {
     const float x[4] = {qv[i].x * qscale, qv[i].y * qscale, qv[i].z * qscale, qv[i].w * qscale};
@@ -1113,8 +1114,7 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
     const _Float16 *src = sq + (((n >> 2) & 1) * kGroup + (n & 3)) * kHeadDim + G * 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const half8_t v = *reinterpret_cast<const half8_t *>(src + s * 32);
-      qf[s] = n < 8 ? v : (half8_t){};
+      qf[s] = *reinterpret_cast<const half8_t *>(src + s * 32);
     }
   }
 
@@ -1257,24 +1257,29 @@ __device__ __forceinline__ void attn_partial_wave(const float *q_seq, const SeqD
   vm_wait<0>();   // (a skipped tile's loads land in sv0 / sv1 before they are reused below)
 
   // ---- this wave's partial: add the high and low rows, stage (m, l, O) ----
+  // One row swap serves two accumulators: swapping rows 1 / 3 of acc[c][i]
+  // with rows 0 / 2 of acc[c + 8][i] and adding leaves, in lane group 0,
+  // high + low of acc[c][i] and, in lane group 1, high + low of acc[c + 8][i].
   l_run = sum_across_rows(l_run);
+  float o8[8][4];   // lane group 0: dims 16c + n; lane group 1: dims 16 (c + 8) + n
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float2 hl = pair16(acc[c][i]);
-      acc[c][i] = hl.x + hl.y;
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[c][i]), __float_as_uint(acc[c + 8][i]),
+                                                      false, false);
+      o8[c][i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
   // staged per query head i in the first 4 KB of sv0 (idle now): element
   // n * 16 + c holds dim 16c + n, the layout of the partials
-  if (G == 0) {
-    float *st = reinterpret_cast<float *>(sv0);
+  if (G < 2) {
+    float *st = reinterpret_cast<float *>(sv0) + n * 16 + G * 8;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i)
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4)
-        *reinterpret_cast<float4 *>(st + i * kHeadDim + n * 16 + c4 * 4) =
-            make_float4(acc[c4 * 4][i], acc[c4 * 4 + 1][i], acc[c4 * 4 + 2][i], acc[c4 * 4 + 3][i]);
+      for (int c4 = 0; c4 < 2; ++c4)
+        *reinterpret_cast<float4 *>(st + i * kHeadDim + c4 * 4) =
+            make_float4(o8[c4 * 4][i], o8[c4 * 4 + 1][i], o8[c4 * 4 + 2][i], o8[c4 * 4 + 3][i]);
   }
   m_out = m_run;
   l_out = l_run;
