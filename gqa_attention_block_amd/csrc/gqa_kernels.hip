@@ -2322,7 +2322,14 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
     }
 
     // ---- attention ----
-    for (int t = b; t < p.t_attn; t += G) {
+    // When the attention tasks fit on the workgroups that have neither an
+    // o_proj nor a merge task, they run there (task t on workgroup
+    // t + t_oproj): an o_proj workgroup then issues its W_o loads right after
+    // its projection task instead of after an attention task.  (A merge
+    // workgroup with an attention task would form its gate logit only after
+    // it, so otherwise the tasks stay on the first workgroups.)
+    const int a_off = p.t_oproj + p.t_attn + p.t_merge <= G ? p.t_oproj : 0;
+    for (int t = (b - a_off + G) % G; t < p.t_attn; t += G) {
       const int c = t / Hk, g = t - c * Hk;
       auto wait_q = [&]() {
         if (has_qkv) await_flags(f_qkv, g * p.qkv_per_group, p.qkv_per_group, 1, fv);
