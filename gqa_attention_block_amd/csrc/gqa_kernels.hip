@@ -1910,7 +1910,7 @@ hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
 constexpr int kFlagBase = 8;
 // flag words: projection tasks (at most 800), attention tasks (256 chunks x 8
 // KV heads), merge tasks (32 query heads x 4), o_proj tasks (4096 rows / 16)
-static_assert((kFlagBase + 800 + kFusedMaxChunks * 8 + 32 * 4 + kFusedMaxHidden / 16) * 8 <= kSyncBytes,
+static_assert((kFlagBase + 800 + kFusedMaxChunks * 8 + 32 * 4 + kFusedMaxHidden / 16 + 2 * 8) * 8 <= kSyncBytes,
               "flag words fit their bytes");
 // A wait gives up after this many polls (about a second): reached only if
 // calls overlap on one workspace, or if other work holds CUs the launch
@@ -2169,6 +2169,101 @@ __device__ __forceinline__ void fused_merge_task(const FusedParams &p, int h, in
   }
 }
 
+// A layer whose chunks are few (at most kGroupMergeMaxChunks) has no merge
+// tasks: the attention task of a KV head group that finishes last (a counter
+// per group, cleared by the group's first projection task, tells it) merges
+// the group's 4 query heads itself and sets one flag per group for o_proj.
+// Each of its waves takes one query head (lane l: elements 4l .. 4l+3 of the
+// partial layout) with the arithmetic of fused_merge_task, operation for
+// operation (chunk group cg adds chunks cg, cg + 16, ... in an fmaf chain, a
+// chunk past the end counting as weight 0 times 0; the 16 groups are added
+// in order), so the result is the same to the bit.
+constexpr int kGroupMergeMaxChunks = 16;
+
+// The g_proj row pair of query head h in every lane of the calling wave
+// (issued ahead of the attention task's tiles, finished on x staged in LDS).
+template <int NIT, bool NORM>
+struct GateWave {
+  uint4 wa[NIT], wb[NIT];
+  __device__ __forceinline__ void issue(const FusedParams &p, int h, int lane) {
+    const unsigned row_bytes = (unsigned)p.hidden * 2u;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.w_g, (unsigned)p.num_heads * row_bytes);
+    const int r = h & ~1;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int col = (it * 64 + lane) * 8;
+      const bool ok = col < p.hidden;
+      wa[it] = buf_load16_p<kWeightPolicy>(rg, ok ? (unsigned)r * row_bytes + (unsigned)col * 2u : kOutOfRange);
+      wb[it] = buf_load16_p<kWeightPolicy>(rg, ok ? (unsigned)(r + 1) * row_bytes + (unsigned)col * 2u : kOutOfRange);
+    }
+  }
+  __device__ __forceinline__ float finish(const FusedParams &p, int h, float4 (*s_x)[StagedX<NIT>::kSlots],
+                                          const float *s_ss, int lane) {
+    float ya, yb;
+    pair_dots<NIT, NORM>(wa, wb, s_x[0], s_x[1], s_ss, p.hidden, p.rms_eps, lane, ya, yb);
+    return (h & 1) ? yb : ya;
+  }
+};
+
+// The last attention task of KV head group g merges its query heads (wave w:
+// head g * 4 + w, gate logit gl); a is written coherently.
+__device__ __forceinline__ void fused_group_merge(const FusedParams &p, int g, int w, int lane, float gl) {
+  const int Hq = p.num_heads;
+  const int nch = p.nchunks;   // <= kGroupMergeMaxChunks
+  const int h = g * kGroup + w;
+  const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml, (unsigned)nch * Hq * 8u);
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o, (unsigned)nch * Hq * kHeadDim * 4u);
+  // (m, l) of chunk c in lane c; the partials of every chunk, one round trip
+  const float2 ml = __builtin_bit_cast(
+      float2, __builtin_amdgcn_raw_buffer_load_b64(rml, lane < nch ? ((unsigned)lane * Hq + h) * 8u : kOutOfRange, 0,
+                                                   kCoherent));
+  float4 v[kGroupMergeMaxChunks];
+  const unsigned po = ((unsigned)h * kHeadDim + 4u * lane) * 4u;
+#pragma unroll
+  for (int c = 0; c < kGroupMergeMaxChunks; ++c)
+    v[c] = __builtin_bit_cast(
+        float4, buf_load16_p<kCoherent>(rpo, c < nch ? po + (unsigned)c * Hq * kHeadDim * 4u : kOutOfRange));
+  const float M = wave_max(lane < nch ? ml.x : -INFINITY);
+  const float mc = lane < nch ? ml.x : -INFINITY;
+  const float wl = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);   // chunk lane's weight
+  const float L = wave_sum(lane < nch ? fmaf(wl, ml.y, 0.f) : 0.f);
+  float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int cg = 0; cg < 16; ++cg) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (cg < nch) {
+      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), cg));
+      acc.x = fmaf(wc, v[cg].x, acc.x);
+      acc.y = fmaf(wc, v[cg].y, acc.y);
+      acc.z = fmaf(wc, v[cg].z, acc.z);
+      acc.w = fmaf(wc, v[cg].w, acc.w);
+#pragma unroll
+      for (int k = 1; k < 4; ++k) {   // chunks cg + 16 k are past the end: weight 0 times 0
+        acc.x = fmaf(0.f, 0.f, acc.x);
+        acc.y = fmaf(0.f, 0.f, acc.y);
+        acc.z = fmaf(0.f, 0.f, acc.z);
+        acc.w = fmaf(0.f, 0.f, acc.w);
+      }
+    }
+    if (cg == 0) {
+      tot = acc;
+    } else {
+      tot.x += acc.x;
+      tot.y += acc.y;
+      tot.z += acc.z;
+      tot.w += acc.w;
+    }
+  }
+  const float sc = (1.0f / (1.0f + expf(-gl))) / (L + sink_term(p.sinks, h, M));
+  const float vv[4] = {tot.x, tot.y, tot.z, tot.w};
+  float *dst = p.a + (size_t)h * kHeadDim;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;   // element e holds dim 16 (e % 16) + e / 16
+    store_f32<true>(dst + 16 * (e & 15) + (e >> 4), vv[j] * sc);
+  }
+}
+
 // The gate logit of query head h, computed by wave 0 as qkv_rope_kernel
 // computes g_proj's row pair (h / 2): x staged in LDS by the whole workgroup
 // (sum of squares for NORM as well), the two dot products over the wave.
@@ -2214,7 +2309,7 @@ struct GateRows {
 // flag.  Every task of a layer is awaited, directly or through later tasks of
 // the layer, by the layer's o_proj tasks, and those by the next layer's
 // projections, so a word is rewritten only after every wait on it has ended.
-template <int NIT, bool NORM, bool STACK, bool HAS_QKV, typename SP>
+template <int NIT, bool NORM, bool STACK, bool HAS_QKV, bool GM, typename SP>
 __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   constexpr int W = kThreads / 64;
   constexpr int P = fused_pairs_per_wave(NIT);
@@ -2231,16 +2326,19 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   __shared__ __attribute__((aligned(16))) _Float16 s_q[W][2 * kGroup * kHeadDim];
   __shared__ float s_ss[W];
   __shared__ float s_gate;
+  __shared__ float s_gate4[4];
+  __shared__ int s_last;
   __shared__ unsigned long long s_epoch;
   using XS = StagedX<NIT>;
   static_assert(2 * XS::kSlots * sizeof(float4) <= sizeof(s_k0) && 2 * XS::kSlots * sizeof(float4) <= sizeof(s_q),
                 "staged x fits the first K buffers and the q staging");
   static_assert(kFusedMaxChunks * sizeof(float2) <= sizeof(s_v0) && 256 * sizeof(float4) <= sizeof(s_v1),
                 "merge scratch fits the V buffers");
-  // x (projection tasks) shares the K buffers (in a stack the q staging,
-  // since the tile buffers then hold the next projection task's weights), the
-  // merge scratch the V buffers: a workgroup's tasks come in phase order
-  float4 (*s_x)[XS::kSlots] = reinterpret_cast<float4 (*)[XS::kSlots]>(STACK ? &s_q[0][0] : &s_k0[0][0]);
+  // x (projection tasks) is staged in the q staging area (in a stack the
+  // tile buffers hold the next projection task's weights meanwhile; x stays
+  // there until the attention task builds its q fragments), the merge
+  // scratch is in the V buffers: a workgroup's tasks come in phase order
+  float4 (*s_x)[XS::kSlots] = reinterpret_cast<float4 (*)[XS::kSlots]>(&s_q[0][0]);
   float2 *s_ml = reinterpret_cast<float2 *>(&s_v0[0][0]);
   float4 *s_acc = reinterpret_cast<float4 *>(&s_v1[0][0]);
   // In a stack the weight rows of the workgroup's first projection task of
@@ -2266,6 +2364,8 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   unsigned long long *const f_attn = f_qkv + p0.t_qkv;
   unsigned long long *const f_merge = f_attn + t_attn_slots;
   unsigned long long *const f_oproj = f_merge + p0.t_merge;
+  unsigned long long *const f_group = f_oproj + p0.t_oproj;   // per KV head group: merged (layers without merge tasks)
+  unsigned long long *const g_count = f_group + 8;             // per KV head group: attention tasks done
   constexpr bool has_qkv = HAS_QKV;   // the projections run in this launch (t_qkv > 0)
 
   if (tid == 0) s_epoch = __hip_atomic_load(words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2310,26 +2410,52 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       if (STACK && l > 0) await_flags(f_oproj, 0, p.t_oproj, 1, flag_value((epoch << 8) | (unsigned)(l - 1)));
     };
 
+    // A layer with few chunks merges in its last attention task per group.
+    // Every workgroup then runs a projection task first (there are at least
+    // as many as workgroups) and at most one attention task, so x is still
+    // staged when its attention task starts.
+    const bool group_merge =
+        GM && has_qkv && p.t_oproj > 0 && p.nchunks <= kGroupMergeMaxChunks && p.t_qkv >= G && p.t_attn <= G;
+    const int t_merge = group_merge ? 0 : p.t_merge;
+
+    // this workgroup's attention task (see below), if any
+    const int a_off = p.t_oproj + p.t_attn + t_merge <= G ? p.t_oproj : 0;
+    const int t_a0 = (b - a_off + G) % G;
+
     // ---- projections ----
     bool staged = false;
     for (int t = b; t < p.t_qkv; t += G) {
+      // with group_merge each wave forms the gate logit of one query head of
+      // its attention task's group right after the projection task (x is
+      // staged; its g_proj rows load with the task's weights)
+      const bool gate_here = group_merge && t == b && t_a0 < p.t_attn;
+      GateWave<NIT, NORM> gate_w;
+      if (gate_here) gate_w.issue(p, (t_a0 % Hk) * kGroup + w, lane);
       if (PF && t == b)
         fused_qkv_task<NIT, NORM, P, STACK, PF>(p, t, staged, s_x, s_ss, lane, w, wait_h, &s_w);
       else
         fused_qkv_task<NIT, NORM, P, STACK>(p, t, staged, s_x, s_ss, lane, w, wait_h);
       staged = true;
+      // the group's first task clears its counter (every attention task of
+      // the group waits for this task's flag before it counts itself)
+      if (group_merge && tid == 0 && t % p.qkv_per_group == 0)
+        __hip_atomic_store(g_count + t / p.qkv_per_group, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       set_flag(f_qkv + t, fv);
+      if (gate_here) {
+        const float gv = gate_w.finish(p, (t_a0 % Hk) * kGroup + w, s_x, s_ss, lane);
+        if (lane == 0) s_gate4[w] = gv;   // read after the attention task's barriers
+      }
     }
 
     // ---- attention ----
     // When the attention tasks fit on the workgroups that have neither an
     // o_proj nor a merge task, they run there (task t on workgroup
-    // t + t_oproj): an o_proj workgroup then issues its W_o loads right after
-    // its projection task instead of after an attention task.  (A merge
-    // workgroup with an attention task would form its gate logit only after
-    // it, so otherwise the tasks stay on the first workgroups.)
-    const int a_off = p.t_oproj + p.t_attn + p.t_merge <= G ? p.t_oproj : 0;
-    for (int t = (b - a_off + G) % G; t < p.t_attn; t += G) {
+    // t + t_oproj, a_off above): an o_proj workgroup then issues its W_o
+    // loads right after its projection task instead of after an attention
+    // task.  (A merge workgroup with an attention task would form its gate
+    // logit only after it, so otherwise the tasks stay on the first
+    // workgroups.)
+    for (int t = t_a0; t < p.t_attn; t += G) {
       const int c = t / Hk, g = t - c * Hk;
       auto wait_q = [&]() {
         if (has_qkv) await_flags(f_qkv, g * p.qkv_per_group, p.qkv_per_group, 1, fv);
@@ -2358,12 +2484,26 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       if (lane == 0)
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, make_float2(M, L)), rml, row * 8u, 0,
                                               kCoherent);
-      set_flag(f_attn + t, fv);
+      if (group_merge) {
+        // the partial has landed; the task that counts last merges the group
+        vm_wait<0>();
+        __syncthreads();
+        if (tid == 0)
+          s_last = __hip_atomic_fetch_add(g_count + g, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (unsigned long long)(p.nchunks - 1);
+        __syncthreads();
+        if (s_last) {
+          fused_group_merge(p, g, w, lane, s_gate4[w]);
+          set_flag(f_group + g, fv);
+        }
+      } else {
+        set_flag(f_attn + t, fv);
+      }
       __syncthreads();   // s_q and s_v0 are rewritten by the next task
     }
 
     // ---- merge: on the last workgroups (they have no o_proj task) ----
-    for (int t = (b + p.t_merge) % G; t < p.t_merge; t += G) {
+    for (int t = (b + t_merge) % G; t < t_merge; t += G) {
       const int h = t >> 2, qd = t & 3;
       // in the one-launch block the head's gate logit is computed here,
       // before the wait for the attention (it needs only x)
@@ -2426,7 +2566,10 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       float4 yold = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (STACK)
         yold = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ry, r0 < p.hidden ? (unsigned)r0 * 4u : kOutOfRange));
-      if (p.t_merge > 0) await_flags(f_merge, 0, p.t_merge, 1, fv);
+      if (group_merge)
+        await_flags(f_group, 0, Hk, 1, fv);
+      else if (p.t_merge > 0)
+        await_flags(f_merge, 0, p.t_merge, 1, fv);
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)qdim * 4u);
       float4 xa[NITO], xb[NITO];
 #pragma unroll
@@ -2463,24 +2606,32 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
 
 // HAS_QKV: the whole block (projections in the launch); else its attention
 // and merge alone, on a q and gate logits already in memory.
-template <int NIT, bool NORM, bool HAS_QKV>
+// GM: the launch may merge in the attention tasks (layers with few chunks);
+// its code is left out of the launches that never do.
+template <int NIT, bool NORM, bool HAS_QKV, bool GM>
 __global__ __launch_bounds__(kThreads, 1) void block_fused_kernel(const FusedParams p) {
-  fused_run<NIT, NORM, false, HAS_QKV>(p, p);
+  fused_run<NIT, NORM, false, HAS_QKV, GM>(p, p);
 }
 
 template <int NIT>
 __global__ __launch_bounds__(kThreads, 1) void stack_fused_kernel(const StackParams sp) {
-  fused_run<NIT, true, true, true>(sp.base, sp);
+  fused_run<NIT, true, true, true, true>(sp.base, sp);
 }
 
 template <int NIT>
 hipError_t fused_launch(const FusedParams &p, dim3 grid, hipStream_t stream) {
+  const int G = (int)grid.x;
+  const bool gm = p.t_oproj > 0 && p.nchunks <= kGroupMergeMaxChunks && p.t_qkv >= G && p.t_attn <= G;
   if (p.t_qkv == 0)   // attention + merge only (no norm: x is not read)
-    hipLaunchKernelGGL((block_fused_kernel<NIT, false, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((block_fused_kernel<NIT, false, false, false>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.w_norm != nullptr && gm)
+    hipLaunchKernelGGL((block_fused_kernel<NIT, true, true, true>), grid, dim3(kThreads), 0, stream, p);
   else if (p.w_norm != nullptr)
-    hipLaunchKernelGGL((block_fused_kernel<NIT, true, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((block_fused_kernel<NIT, true, true, false>), grid, dim3(kThreads), 0, stream, p);
+  else if (gm)
+    hipLaunchKernelGGL((block_fused_kernel<NIT, false, true, true>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((block_fused_kernel<NIT, false, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((block_fused_kernel<NIT, false, true, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
