@@ -137,7 +137,7 @@ struct QkvParams {
 constexpr int kPhaseQkv = 1;      // projections, split, RoPE, KV-slot write
 constexpr int kPhaseAttn = 2;     // split-K attention and the merge with the gate
 constexpr int kPhaseOproj = 4;    // o_proj
-constexpr int kSyncBytes = 32768; // synchronisation words at the start of the workspace
+constexpr int kSyncBytes = 524288;  // synchronisation words at the start of the workspace (one flag per 128 B)
 constexpr int kFusedMaxChunks = 256;   // chunks per sequence the merge tasks take
 constexpr int kFusedMaxHidden = 4096;  // x staged in LDS beside the attention buffers
 constexpr int kFusedMaxQDim = 4096;    // o_proj rows held in registers

@@ -1904,13 +1904,17 @@ hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
 // the order, of the step kernels: the block's output is bit-identical to its
 // steps' and the same on every run.
 //
-// Workspace words (64-bit): [0] epoch, then from word 8 one flag per
-// projection task, per attention task, per merge task.
+// Workspace words (64-bit): [0] epoch, then one flag per projection task,
+// per attention task, per merge task, per o_proj task, and per KV head group
+// a merged flag and a counter, each flag in a 128-byte line of its own: flags
+// that shared lines (several writers, and every poller reading the line)
+// measured 4% slower over a 36-layer stack.
 // ---------------------------------------------------------------------------
-constexpr int kFlagBase = 8;
-// flag words: projection tasks (at most 800), attention tasks (256 chunks x 8
-// KV heads), merge tasks (32 query heads x 4), o_proj tasks (4096 rows / 16)
-static_assert((kFlagBase + 800 + kFusedMaxChunks * 8 + 32 * 4 + kFusedMaxHidden / 16 + 2 * 8) * 8 <= kSyncBytes,
+constexpr int kFlagStride = 16;   // 64-bit words per flag (128 bytes)
+// flags: projection tasks (at most 800), attention tasks (256 chunks x 8 KV
+// heads), merge tasks (32 query heads x 4), o_proj tasks (4096 rows / 16),
+// group flags and counters (8 KV heads each), after the epoch's line
+static_assert((1 + 800 + kFusedMaxChunks * 8 + 32 * 4 + kFusedMaxHidden / 16 + 2 * 8) * kFlagStride * 8 <= kSyncBytes,
               "flag words fit their bytes");
 // A wait gives up after this many polls (about a second): reached only if
 // calls overlap on one workspace, or if other work holds CUs the launch
@@ -1923,16 +1927,37 @@ __device__ __forceinline__ unsigned long long flag_value(unsigned long long epoc
   return epoch * 0x9E3779B97F4A7C15ull ^ 0xD1B54A32D192ED03ull;
 }
 
-// Wave 0 polls the flags first + k * stride, k < count, until every one
-// holds fv; then the workgroup continues.  Every wave must call it.
+// Flag i of the array starting at f.
+__device__ __forceinline__ unsigned long long *flag_at(unsigned long long *f, int i) { return f + i * kFlagStride; }
+
+// Wave 0 polls flags first + k * stride (flag indices), k < count, until
+// every one holds fv; then the workgroup continues.  Every wave must call it.
+// A poll reads up to 4 flags per lane with one round trip.
 __device__ __forceinline__ void await_flags(const unsigned long long *flags, int first, int count, int stride,
                                             unsigned long long fv) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     for (int i = 0; i < kSpinLimit; ++i) {
       bool done = true;
-      for (int k = lane; k < count; k += 64)
-        done &= __hip_atomic_load(flags + first + k * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fv;
+      for (int k0 = 0; k0 < count; k0 += 256) {
+        // only the 64-flag slots that hold flags are read (a uniform
+        // branch), all before the first wait; lanes past the end read a flag
+        // of their own slot again
+        const int nj = min(4, (count - k0 + 63) >> 6);
+        unsigned long long v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = fv;
+          if (j < nj) {
+            const int base = k0 + 64 * j;
+            const int k = base + lane % min(64, count - base);
+            v[j] = __hip_atomic_load(flags + (first + k * stride) * kFlagStride, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) done &= v[j] == fv;
+      }
       if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
       __builtin_amdgcn_s_sleep(2);
     }
@@ -2360,12 +2385,12 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
     num_layers = sp.num_layers;
   }
   unsigned long long *const words = p0.sync;
-  unsigned long long *const f_qkv = words + kFlagBase;
-  unsigned long long *const f_attn = f_qkv + p0.t_qkv;
-  unsigned long long *const f_merge = f_attn + t_attn_slots;
-  unsigned long long *const f_oproj = f_merge + p0.t_merge;
-  unsigned long long *const f_group = f_oproj + p0.t_oproj;   // per KV head group: merged (layers without merge tasks)
-  unsigned long long *const g_count = f_group + 8;             // per KV head group: attention tasks done
+  unsigned long long *const f_qkv = words + kFlagStride;   // flag i at f_qkv + i * kFlagStride (flag_at)
+  unsigned long long *const f_attn = flag_at(f_qkv, p0.t_qkv);
+  unsigned long long *const f_merge = flag_at(f_attn, t_attn_slots);
+  unsigned long long *const f_oproj = flag_at(f_merge, p0.t_merge);
+  unsigned long long *const f_group = flag_at(f_oproj, p0.t_oproj);   // per KV head group: merged (no merge tasks)
+  unsigned long long *const g_count = flag_at(f_group, 8);             // per KV head group: attention tasks done
   constexpr bool has_qkv = HAS_QKV;   // the projections run in this launch (t_qkv > 0)
 
   if (tid == 0) s_epoch = __hip_atomic_load(words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2439,8 +2464,8 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       // the group's first task clears its counter (every attention task of
       // the group waits for this task's flag before it counts itself)
       if (group_merge && tid == 0 && t % p.qkv_per_group == 0)
-        __hip_atomic_store(g_count + t / p.qkv_per_group, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      set_flag(f_qkv + t, fv);
+        __hip_atomic_store(flag_at(g_count, t / p.qkv_per_group), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      set_flag(flag_at(f_qkv, t), fv);
       if (gate_here) {
         const float gv = gate_w.finish(p, (t_a0 % Hk) * kGroup + w, s_x, s_ss, lane);
         if (lane == 0) s_gate4[w] = gv;   // read after the attention task's barriers
@@ -2489,15 +2514,15 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
         vm_wait<0>();
         __syncthreads();
         if (tid == 0)
-          s_last = __hip_atomic_fetch_add(g_count + g, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          s_last = __hip_atomic_fetch_add(flag_at(g_count, g), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned long long)(p.nchunks - 1);
         __syncthreads();
         if (s_last) {
           fused_group_merge(p, g, w, lane, s_gate4[w]);
-          set_flag(f_group + g, fv);
+          set_flag(flag_at(f_group, g), fv);
         }
       } else {
-        set_flag(f_attn + t, fv);
+        set_flag(flag_at(f_attn, t), fv);
       }
       __syncthreads();   // s_q and s_v0 are rewritten by the next task
     }
@@ -2533,7 +2558,7 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       else
         await_flags(f_attn, h / kGroup, p.nchunks, Hk, fv);
       fused_merge_task(p, h, qd, gl, s_ml, s_acc, tid, lane);
-      set_flag(f_merge + t, fv);
+      set_flag(flag_at(f_merge, t), fv);
       if (final_task) advance_epoch();
       __syncthreads();   // LDS is rewritten by the next task
     }
@@ -2597,7 +2622,7 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
           __builtin_amdgcn_raw_buffer_store_b128(
               __builtin_bit_cast(u32x4_t, make_float4(ynew[0], ynew[1], ynew[2], ynew[3])), ry,
               r0 < p.hidden ? (unsigned)r0 * 4u : kOutOfRange, 0, kCoherent);
-        set_flag(f_oproj + t, fv);
+        set_flag(flag_at(f_oproj, t), fv);
       }
       if (l == num_layers - 1 && t == p.t_oproj - 1) advance_epoch();
     }

@@ -240,7 +240,8 @@ gqa_status gqa_attention_block_decode(const gqa_arch *arch, const gqa_layer_weig
  * Errors: those of gqa_attention_block_decode; GQA_ERR_WORKSPACE_TOO_SMALL
  * when these sequences need more than the 8 MiB (the need grows with the
  * batch: at the published head counts one sequence of any length takes about
- * 1 MiB and 96 sequences about 4 MiB; gqa_workspace_size is an upper bound);
+ * 1.5 MiB and 96 sequences about 4.5 MiB; gqa_workspace_size is an upper
+ * bound);
  * GQA_ERR_GPU when the scratch's address cannot be obtained. */
 gqa_status gqa_attention_block_decode_noalloc(const gqa_arch *arch, const gqa_layer_weights *weights,
                                               int is_full, const gqa_kv_seq *seqs, int32_t batch,
