@@ -2423,8 +2423,12 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
     }
     return p;
   };
+  bool pf_ready = false;   // this workgroup's next projection task has its weights in LDS
   if constexpr (PF) {
-    if (b < p0.t_qkv) fused_qkv_prefetch<NIT, P>(layer_params(0), b, s_w, lane, w);
+    if (b < p0.t_qkv) {
+      fused_qkv_prefetch<NIT, P>(layer_params(0), b, s_w, lane, w);
+      pf_ready = true;
+    }
   }
 
   for (int l = 0; l < num_layers; ++l) {
@@ -2443,9 +2447,14 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
         GM && has_qkv && p.t_oproj > 0 && p.nchunks <= kGroupMergeMaxChunks && p.t_qkv >= G && p.t_attn <= G;
     const int t_merge = group_merge ? 0 : p.t_merge;
 
-    // this workgroup's attention task (see below), if any
+    // this workgroup's attention task (see below) and merge task, if any
     const int a_off = p.t_oproj + p.t_attn + t_merge <= G ? p.t_oproj : 0;
     const int t_a0 = (b - a_off + G) % G;
+    const int t_m0 = (b + t_merge) % G;
+    // in a stack, a workgroup with a projection task and a merge task forms
+    // the merge's gate logit right after the projection (its attention task
+    // would otherwise delay it)
+    const bool mgate = STACK && t_m0 < t_merge && b < p.t_qkv;
 
     // ---- projections ----
     bool staged = false;
@@ -2454,9 +2463,11 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       // its attention task's group right after the projection task (x is
       // staged; its g_proj rows load with the task's weights)
       const bool gate_here = group_merge && t == b && t_a0 < p.t_attn;
+      const bool mgate_here = mgate && t == b;
       GateWave<NIT, NORM> gate_w;
       if (gate_here) gate_w.issue(p, (t_a0 % Hk) * kGroup + w, lane);
-      if (PF && t == b)
+      if (mgate_here) gate_w.issue(p, t_m0 >> 2, lane);
+      if (PF && t == b && pf_ready)
         fused_qkv_task<NIT, NORM, P, STACK, PF>(p, t, staged, s_x, s_ss, lane, w, wait_h, &s_w);
       else
         fused_qkv_task<NIT, NORM, P, STACK>(p, t, staged, s_x, s_ss, lane, w, wait_h);
@@ -2469,6 +2480,10 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       if (gate_here) {
         const float gv = gate_w.finish(p, (t_a0 % Hk) * kGroup + w, s_x, s_ss, lane);
         if (lane == 0) s_gate4[w] = gv;   // read after the attention task's barriers
+      }
+      if (mgate_here) {
+        const float gv = gate_w.finish(p, t_m0 >> 2, s_x, s_ss, lane);
+        if (tid == 0) s_gate = gv;   // read by the merge task (barriers in between)
       }
     }
 
@@ -2533,7 +2548,9 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       // in the one-launch block the head's gate logit is computed here,
       // before the wait for the attention (it needs only x)
       float gl;
-      if constexpr (has_qkv) {
+      if (mgate && t == t_m0) {   // formed after the projection task
+        gl = s_gate;
+      } else if constexpr (has_qkv) {
         GateRows<NIT, NORM> gate;
         if constexpr (STACK) {
           wait_h();
@@ -2563,8 +2580,13 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       __syncthreads();   // LDS is rewritten by the next task
     }
     if constexpr (PF) {
-      // every LDS task of the layer has ended (each ends in a barrier)
-      if (l + 1 < num_layers && b < p.t_qkv) fused_qkv_prefetch<NIT, P>(layer_params(l + 1), b, s_w, lane, w);
+      // every LDS task of the layer has ended (each ends in a barrier).  A
+      // workgroup that ran an attention task and has an o_proj task does not
+      // prefetch: its W_o loads would queue behind the prefetch, and its
+      // next projection task loads its weights itself.
+      const bool oproj_after_attn = b < p.t_oproj && t_a0 < p.t_attn;
+      pf_ready = l + 1 < num_layers && b < p.t_qkv && !oproj_after_attn;
+      if (pf_ready) fused_qkv_prefetch<NIT, P>(layer_params(l + 1), b, s_w, lane, w);
     }
 
     // ---- o_proj ----
