@@ -454,12 +454,15 @@ def test_block_equals_its_steps(name):
 
 
 @pytest.mark.parametrize("num_kv_heads,position,hidden", [(1, 8191, 1024), (2, 5000, 1024), (8, 3000, 1024),
-                                                           (4, 3000, 6144), (4, 20000, 4096), (4, 700, 8)])
+                                                           (4, 3000, 6144), (4, 20000, 4096), (4, 700, 8),
+                                                           (1, 200, 1024), (2, 300, 1024), (4, 1023, 2560)])
 def test_block_one_launch_other_shapes(num_kv_heads, position, hidden):
     """One sequence on a full layer with shapes other than the family's: the
     one-launch block over Hq query heads with 256 chunks at Hk = 1 (the merge
     past one wave's 64 lanes), q_dim 2048, the widest x it stages (hidden
-    4096) and a tiny one (8); and its fallback, projections + its
+    4096) and a tiny one (8); with few chunks (positions 200, 300, 1023: 4 to
+    16 chunks), where the last attention task of each KV head group merges
+    it, at Hk = 1, 2 and 4; and its fallback, projections + its
     attention/merge phase + o_proj, for q_dim 8192 (Hk = 8) and hidden 6144."""
     arch = synth.Arch(hidden=hidden, num_heads=4 * num_kv_heads, num_kv_heads=num_kv_heads)
     case = synth.block_case(f"fused_hk{num_kv_heads}_h{hidden}", hidden, True, [position], seed=0, case_id=31,
