@@ -133,6 +133,28 @@ __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, unsigned of
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (to nearest even), packed low | high << 16.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 bf16 weights against x split into bf16 high and low parts (same columns),
+// accumulated into a: per weight pair, the high product pair then the low one.
+__device__ __forceinline__ float dot8_bf16_split(uint4 q, uint4 xh, uint4 xl, float a) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w}, h[4] = {xh.x, xh.y, xh.z, xh.w}, l[4] = {xl.x, xl.y, xl.z, xl.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]), __builtin_bit_cast(bf16x2_t, h[k]), a,
+                                        false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]), __builtin_bit_cast(bf16x2_t, l[k]), a,
+                                        false);
+  }
+  return a;
+}
+
 __device__ __forceinline__ float dot8_bf16(uint4 q, float4 xa, float4 xb, float a) {
   a = fmaf(bf16_lo(q.x), xa.x, a);
   a = fmaf(bf16_hi(q.x), xa.y, a);
@@ -180,7 +202,33 @@ struct StagedX {
       if constexpr (NORM) wn[k] = buf_load8(rn, f * 8u);
     }
   }
-  // writes LDS; returns this thread's sum of squares of x (NORM) or 0
+  // The projections' form: slot g of s[0] holds the bf16 high parts of
+  // columns 8g .. 8g+7 and slot g of s[1] their bf16 low parts (x - high),
+  // so that a dot product takes two v_dot2 per pair of bf16 weights, with
+  // x to 16 significant bits.  Returns this thread's sum of squares of x
+  // (NORM, in fp32 before the split) or 0.
+  template <bool NORM>
+  __device__ __forceinline__ float store_split(float4 (*s)[kSlots]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const unsigned f = threadIdx.x + k * kThreads;
+      float4 x = v[k];
+      if constexpr (NORM) {
+        ss = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, ss))));
+        x = make_float4(x.x * bf16_lo(wn[k].x), x.y * bf16_hi(wn[k].x), x.z * bf16_lo(wn[k].y),
+                        x.w * bf16_hi(wn[k].y));
+      }
+      const uint2 hi = make_uint2(pack_bf16(x.x, x.y), pack_bf16(x.z, x.w));
+      const uint2 lo = make_uint2(pack_bf16(x.x - bf16_lo(hi.x), x.y - bf16_hi(hi.x)),
+                                  pack_bf16(x.z - bf16_lo(hi.y), x.w - bf16_hi(hi.y)));
+      reinterpret_cast<uint2 *>(&s[0][f >> 1])[f & 1] = hi;
+      reinterpret_cast<uint2 *>(&s[1][f >> 1])[f & 1] = lo;
+    }
+    return ss;
+  }
+  // writes LDS (fp32 x, as the batched GEMVs read it); returns this
+  // thread's sum of squares of x (NORM) or 0
   template <bool NORM>
   __device__ __forceinline__ float store(float4 (*s)[kSlots]) {
     float ss = 0.f;
@@ -399,8 +447,10 @@ __device__ __forceinline__ void pair_dots(const uint4 (&wa)[NIT], const uint4 (&
   float a = 0.f, c = 0.f;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    a = dot8_bf16(wa[it], s0[it * 64 + lane], s1[it * 64 + lane], a);
-    c = dot8_bf16(wb[it], s0[it * 64 + lane], s1[it * 64 + lane], c);
+    const uint4 xh = __builtin_bit_cast(uint4, s0[it * 64 + lane]);
+    const uint4 xl = __builtin_bit_cast(uint4, s1[it * 64 + lane]);
+    a = dot8_bf16_split(wa[it], xh, xl, a);
+    c = dot8_bf16_split(wb[it], xh, xl, c);
   }
   ya = wave_sum(a);
   yb = wave_sum(c);
@@ -420,8 +470,10 @@ __device__ __forceinline__ void pair_dots_x(const uint4 (&wa)[NIT], const uint4 
   float a = 0.f, c = 0.f;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    a = dot8_bf16(wa[it], x0[it], x1[it], a);
-    c = dot8_bf16(wb[it], x0[it], x1[it], c);
+    const uint4 xh = __builtin_bit_cast(uint4, x0[it]);
+    const uint4 xl = __builtin_bit_cast(uint4, x1[it]);
+    a = dot8_bf16_split(wa[it], xh, xl, a);
+    c = dot8_bf16_split(wb[it], xh, xl, c);
   }
   ya = wave_sum(a);
   yb = wave_sum(c);
@@ -491,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_kernel(const QkvParams p) {
     if (rotate && b < p.batch) rope_sincos(p.seq[b].position, pi, p.rotary_dim, p.log2_theta, sn, cs);
   };
   auto stage = [&](int m) {
-    const float ss = wave_sum(xs[m].template store<NORM>(s_x[m]));
+    const float ss = wave_sum(xs[m].template store_split<NORM>(s_x[m]));
     if (NORM && lane == 0) s_ss[m][wv] = ss;
   };
   // the pair's dot products with staged x row m, then the epilogue for batch row b
@@ -2077,7 +2129,7 @@ __device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool
     if (!staged) xs.template issue<NORM, kCoherent>(rx, 0u, rn);
   }
   if (!staged) {
-    const float ss = wave_sum(xs.template store<NORM>(s_x));
+    const float ss = wave_sum(xs.template store_split<NORM>(s_x));
     if (NORM && lane == 0) s_ss[w] = ss;
     __syncthreads();
   }
@@ -2315,7 +2367,7 @@ struct GateRows {
   }
   __device__ __forceinline__ float finish(const FusedParams &p, int h, float4 (*s_x)[StagedX<NIT>::kSlots],
                                           float *s_ss, int lane, int w) {
-    const float ss = wave_sum(xs.template store<NORM>(s_x));
+    const float ss = wave_sum(xs.template store_split<NORM>(s_x));
     if (NORM && lane == 0) s_ss[w] = ss;
     __syncthreads();
     float ya = 0.f, yb = 0.f;
