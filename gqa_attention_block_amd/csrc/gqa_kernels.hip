@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p)
       float a = 0.f;
 #pragma unroll
       for (int it = 0; it < NIT; ++it)
-        a = dot8_bf16(w[r][it], s_x[m][0][it * 64 + lane], s_x[m][1][it * 64 + lane], a);
+        a = dot8_bf16_split(w[r][it], __builtin_bit_cast(uint4, s_x[m][0][it * 64 + lane]),
+                            __builtin_bit_cast(uint4, s_x[m][1][it * 64 + lane]), a);
       const float s = wave_sum(a);
       const int row = row0 + r;
       if (lane == r && row < total && b < p.batch) {
@@ -308,14 +309,14 @@ __global__ __launch_bounds__(kThreads) void gemv_bf16_kernel(const GemvParams p)
     }
   };
   if constexpr (ONE) {
-    xs[0].template store<false>(s_x[0]);
+    xs[0].template store_split<false>(s_x[0]);
     __syncthreads();
     emit(0, 0);
   } else {
     for (int b0 = 0; b0 < p.batch; b0 += RB) {
 #pragma unroll
       for (int m = 0; m < RB; ++m) {
-        xs[m].template store<false>(s_x[m]);
+        xs[m].template store_split<false>(s_x[m]);
         // next rows: unconditional (past the batch the resource is empty, no
         // traffic), so the compiler's waits stay exact
         xs[m].template issue<false>(xrow(b0 + RB + m), 0u, xrow(0));
@@ -2159,6 +2160,30 @@ __device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool
   }
 }
 
+// The gated attention a as the one-launch blocks with o_proj keep it: per
+// 8-dim group g of a head, the 8 bf16 high parts and then the 8 bf16 low
+// parts (value - high) of dims 8g .. 8g+7, i.e. the split that
+// StagedX::store_split makes of an fp32 a, so that o_proj reads its x as its
+// step kernel stages it.  Written coherently (o_proj runs in the same launch).
+__device__ __forceinline__ void store_a_split(float *head, int d, float v) {
+  asm volatile("" : "+v"(v));  // v is final: keep the product that formed it out of v - hi
+  const uint32_t hi = pack_bf16(v, 0.f) & 0xFFFFu;
+  const uint32_t lo = pack_bf16(v - bf16_lo(hi), 0.f) & 0xFFFFu;
+  uint16_t *g = reinterpret_cast<uint16_t *>(head) + (d >> 3) * 16 + (d & 7);
+  __hip_atomic_store(g, (uint16_t)hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(g + 8, (uint16_t)lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// (the empty asm makes v opaque: without it the product that formed v can be
+// contracted with v - hi into one fma, whose low part then differs from the
+// split of the rounded fp32 value)
+template <bool SPLIT>
+__device__ __forceinline__ void store_a(float *head, int d, float v) {
+  if constexpr (SPLIT)
+    store_a_split(head, d, v);
+  else
+    store_f32<true>(head + d, v);
+}
+
 // Merge task (query head h, elements 64 qd .. 64 qd + 63 of its partials):
 // the chunks merged in a fixed order, gated, written to a.  Lane c of every
 // wave takes chunks c, c + 64, ... for the reference max and the sum; thread
@@ -2166,6 +2191,7 @@ __device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool
 // chunk groups are added in order.  The partials were written in this
 // launch: they are read coherently, and a is written so.  gl is the head's
 // gate logit.
+template <bool SPLIT>
 __device__ __forceinline__ void fused_merge_task(const FusedParams &p, int h, int qd, float gl, float2 *s_ml,
                                                  float4 *s_acc, int tid, int lane) {
   const int Hq = p.num_heads;
@@ -2241,7 +2267,7 @@ __device__ __forceinline__ void fused_merge_task(const FusedParams &p, int h, in
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 64 * qd + 4 * tid + j;             // element e holds dim 16 (e % 16) + e / 16
-      store_f32<true>(dst + 16 * (e & 15) + (e >> 4), v[j] * sc);
+      store_a<SPLIT>(dst, 16 * (e & 15) + (e >> 4), v[j] * sc);
     }
   }
 }
@@ -2283,7 +2309,7 @@ struct GateWave {
 };
 
 // The last attention task of KV head group g merges its query heads (wave w:
-// head g * 4 + w, gate logit gl); a is written coherently.
+// head g * 4 + w, gate logit gl); a is written coherently, in the split form.
 __device__ __forceinline__ void fused_group_merge(const FusedParams &p, int g, int w, int lane, float gl) {
   const int Hq = p.num_heads;
   const int nch = p.nchunks;   // <= kGroupMergeMaxChunks
@@ -2337,7 +2363,7 @@ __device__ __forceinline__ void fused_group_merge(const FusedParams &p, int g, i
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = 4 * lane + j;   // element e holds dim 16 (e % 16) + e / 16
-    store_f32<true>(dst + 16 * (e & 15) + (e >> 4), vv[j] * sc);
+    store_a<true>(dst, 16 * (e & 15) + (e >> 4), vv[j] * sc);
   }
 }
 
@@ -2626,7 +2652,7 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
         await_flags(f_attn, 0, p.t_attn, 1, fv);
       else
         await_flags(f_attn, h / kGroup, p.nchunks, Hk, fv);
-      fused_merge_task(p, h, qd, gl, s_ml, s_acc, tid, lane);
+      fused_merge_task<HAS_QKV>(p, h, qd, gl, s_ml, s_acc, tid, lane);
       set_flag(flag_at(f_merge, t), fv);
       if (final_task) advance_epoch();
       __syncthreads();   // LDS is rewritten by the next task
@@ -2641,8 +2667,9 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       if (pf_ready) fused_qkv_prefetch<NIT, P>(layer_params(l + 1), b, s_w, lane, w);
     }
 
-    // ---- o_proj ----
-    for (int t = b; t < p.t_oproj; t += G) {
+    // ---- o_proj ---- (only with the projections in the launch: it reads a
+    // in the split form, which only those launches' merges write)
+    for (int t = b; HAS_QKV && t < p.t_oproj; t += G) {
       // rows r0 .. r0 + RW - 1 of this wave: the W_o loads go out before the wait for a
       const int r0 = (t * W + w) * RW;
       const int qdim = Hq * kHeadDim;
@@ -2669,6 +2696,8 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
         await_flags(f_group, 0, Hk, 1, fv);
       else if (p.t_merge > 0)
         await_flags(f_merge, 0, p.t_merge, 1, fv);
+      // a in the split form (8-dim group g: 16 B of bf16 high parts, then 16 B
+      // of low parts), read as the GEMV's staged x
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)qdim * 4u);
       float4 xa[NITO], xb[NITO];
 #pragma unroll
@@ -2682,7 +2711,8 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       for (int k = 0; k < RW; ++k) {
         float acc = 0.f;
 #pragma unroll
-        for (int it = 0; it < NITO; ++it) acc = dot8_bf16(wv[k][it], xa[it], xb[it], acc);
+        for (int it = 0; it < NITO; ++it)
+          acc = dot8_bf16_split(wv[k][it], __builtin_bit_cast(uint4, xa[it]), __builtin_bit_cast(uint4, xb[it]), acc);
         const float s = wave_sum(acc);
         const int r = r0 + k;
         if constexpr (STACK) {

@@ -48,13 +48,13 @@
  *     maximum: |q_i| < 7.2e5 at the published scale 1/16.  Larger values
  *     overflow to inf.  Softmax weights are split the same way and are at
  *     most 2^8.
- *   - In the q_k_v_proj and g_proj GEMVs each activation element (after the
- *     RMSNorm weight, where there is one) is carried as a bf16 high part
- *     plus a bf16 low part, i.e. to within 2^-16 of its magnitude (about 16
- *     significant bits), while the bf16 weights are exact: below batch 4 on
- *     VALU dot products (v_dot2 of bf16 pairs into fp32), from batch 4 on
- *     bf16 matrix cores.  o_proj below batch 4 and the MLP GEMVs take the
- *     activations in fp32.
+ *   - In the q_k_v_proj, g_proj, o_proj, MLP down-projection and head GEMVs each
+ *     activation element (after the RMSNorm weight, where there is one) is
+ *     carried as a bf16 high part plus a bf16 low part, i.e. to within 2^-16
+ *     of its magnitude (about 16 significant bits), while the bf16 weights
+ *     are exact: below batch 4 on VALU dot products (v_dot2 of bf16 pairs
+ *     into fp32), from batch 4 on bf16 matrix cores.  The MLP gate/up GEMV
+ *     below batch 4 takes its activations in fp32.
  *   - RoPE angles are formed and reduced mod 2 pi in fp64; sin and cos are
  *     then taken in fp32.  k and v are rounded to fp16 once, after RoPE.
  */
