@@ -2697,14 +2697,25 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       else if (p.t_merge > 0)
         await_flags(f_merge, 0, p.t_merge, 1, fv);
       // a in the split form (8-dim group g: 16 B of bf16 high parts, then 16 B
-      // of low parts), read as the GEMV's staged x
+      // of low parts), read as the GEMV's staged x: once per workgroup (16 B
+      // per lane, coalesced) into LDS, where all four waves read it; read by
+      // every wave from memory it put four times the coherent reads on the
+      // same few lines.  Slots past q_dim hold zeros (out-of-range loads).
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, (unsigned)qdim * 4u);
+      uint4 *s_a = reinterpret_cast<uint4 *>(&s_q[0][0]);
+      static_assert(sizeof(s_q) == kFusedMaxQDim * 4, "a in the split form fills s_q");
+      constexpr int kA16 = kFusedMaxQDim * 4 / 16 / kThreads;
+      uint4 av[kA16];
+#pragma unroll
+      for (int k = 0; k < kA16; ++k) av[k] = buf_load16_p<kCoherent>(ra, (unsigned)(k * kThreads + tid) * 16u);
+#pragma unroll
+      for (int k = 0; k < kA16; ++k) s_a[k * kThreads + tid] = av[k];
+      __syncthreads();
       float4 xa[NITO], xb[NITO];
 #pragma unroll
       for (int it = 0; it < NITO; ++it) {
-        const unsigned col = (unsigned)(it * 64 + lane) * 8u;
-        xa[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u));
-        xb[it] = __builtin_bit_cast(float4, buf_load16_p<kCoherent>(ra, col * 4u + 16u));
+        xa[it] = __builtin_bit_cast(float4, s_a[(it * 64 + lane) * 2]);
+        xb[it] = __builtin_bit_cast(float4, s_a[(it * 64 + lane) * 2 + 1]);
       }
       float ynew[RW];
 #pragma unroll
