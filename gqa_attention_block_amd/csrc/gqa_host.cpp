@@ -1060,23 +1060,24 @@ gqa_status gqa_attention_stack_decode(const gqa_arch *arch, const gqa_stack_laye
       d.rotary_dim = rdim;
       d.log2_theta = log2(theta);
       int di = 0;
-      while (di < nd && !same_shape(sp.desc[di], d)) ++di;
+      while (di < nd && !same_shape(sp.tab.desc[di], d)) ++di;
       if (di == nd) {
         if (nd == kStackMaxDescs) break;   // a fifth shape starts the next launch
-        sp.desc[nd++] = d;
+        sp.tab.desc[nd++] = d;
       }
       const int n = sp.num_layers++;
-      sp.desc_of[n] = (unsigned char)di;
+      sp.tab.desc_of[n] = (unsigned char)di;
       sp.t_attn_max = std::max(sp.t_attn_max, d.t_attn);
-      sp.w_norm[n] = static_cast<const uint16_t *>(ly.w_norm);
-      sp.w_qkv[n] = static_cast<const uint16_t *>(ly.weights.q_k_v_proj);
-      sp.w_g[n] = static_cast<const uint16_t *>(ly.weights.g_proj);
-      sp.w_o[n] = static_cast<const uint16_t *>(ly.weights.o_proj);
-      sp.k[n] = descs[l][0].k;
-      sp.v[n] = descs[l][0].v;
-      sp.sinks[n] = ly.weights.sinks;
+      sp.tab.w_norm[n] = static_cast<const uint16_t *>(ly.w_norm);
+      sp.tab.w_qkv[n] = static_cast<const uint16_t *>(ly.weights.q_k_v_proj);
+      sp.tab.w_g[n] = static_cast<const uint16_t *>(ly.weights.g_proj);
+      sp.tab.w_o[n] = static_cast<const uint16_t *>(ly.weights.o_proj);
+      sp.tab.k[n] = descs[l][0].k;
+      sp.tab.v[n] = descs[l][0].v;
+      sp.tab.sinks[n] = ly.weights.sinks;
       ++l;
     }
+    sp.num_descs = nd;
     hipError_t e = launch_stack_fused(sp, s);
     if (e != hipSuccess) return gpu_error(e, "one-launch stack");
   }

@@ -192,10 +192,11 @@ struct StackDesc {
   int rotary_dim;
   double log2_theta;
 };
-struct StackParams {
-  FusedParams base;       // shared fields: shapes, workspace buffers, x = y = h, task counts
-  int num_layers;
-  int t_attn_max;         // attention flag words reserved per layer
+// The per-layer part of a stack's arguments.  The kernel copies it into LDS
+// at its start and reads each layer's pointers and shape from there: read
+// from the kernel arguments at each layer's start, they cost a chain of
+// dependent memory round trips on the layer's critical path.
+struct StackTables {
   unsigned char desc_of[kStackMaxLayers];
   StackDesc desc[kStackMaxDescs];
   const uint16_t *w_norm[kStackMaxLayers];
@@ -205,6 +206,14 @@ struct StackParams {
   _Float16 *k[kStackMaxLayers];
   _Float16 *v[kStackMaxLayers];
   const float *sinks[kStackMaxLayers];
+};
+static_assert(sizeof(StackTables) % 4 == 0, "the tables are copied as 32-bit words");
+struct StackParams {
+  FusedParams base;       // shared fields: shapes, workspace buffers, x = y = h, task counts
+  int num_layers;
+  int t_attn_max;         // attention flag words reserved per layer
+  int num_descs;          // distinct shapes in desc (1 .. kStackMaxDescs)
+  StackTables tab;
 };
 static_assert(sizeof(StackParams) <= 3072, "the stack's kernel arguments stay under 3 KB");
 

@@ -2048,6 +2048,21 @@ __device__ __forceinline__ PairRows task_pair(const FusedParams &p, int i, int w
   return pair_rows(sec, head, pi, p.num_heads, p.num_kv_heads, p.rotary_dim);
 }
 
+// A copy of an LDS value that every lane holds alike, in scalar registers
+// (read word by word with readfirstlane, so that pointers and sizes built
+// from it stay wave-uniform).
+template <typename T>
+__device__ __forceinline__ T lds_uniform(const T &src) {
+  static_assert(sizeof(T) % 4 == 0, "whole words");
+  uint32_t wd[sizeof(T) / 4];
+  __builtin_memcpy(wd, &src, sizeof(T));
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) wd[i] = __builtin_amdgcn_readfirstlane(wd[i]);
+  T r;
+  __builtin_memcpy(&r, wd, sizeof(T));
+  return r;
+}
+
 // The weight rows of wave w's pairs in projection task i, from HBM straight
 // into LDS (buffer_load ... lds) in sw: row 2j (A) and 2j + 1 (B) of pair j
 // in blocks (2j + ab) NIT + it, block it of a row holding columns
@@ -2087,7 +2102,8 @@ __device__ __forceinline__ void fused_qkv_prefetch(const FusedParams &p, int i, 
 template <int NIT, bool NORM, int P, bool STACK = false, bool LDSW = false, typename WaitH = NoWait>
 __device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool staged,
                                                float4 (*s_x)[StagedX<NIT>::kSlots], float *s_ss, int lane, int w,
-                                               WaitH wait_h = WaitH(), const WaveBufs *sw = nullptr) {
+                                               WaitH wait_h = WaitH(), const WaveBufs *sw = nullptr,
+                                               const float2 *rot = nullptr) {
   const int Hk = p.num_kv_heads;
   const unsigned row_bytes = (unsigned)p.hidden * 2u;
   const int qkv_rows = (p.num_heads + 2 * Hk) * kHeadDim;
@@ -2113,13 +2129,19 @@ __device__ __forceinline__ void fused_qkv_task(const FusedParams &p, int i, bool
       }
     }
   }
-  // the rotations, while the loads are in flight
+  // the rotations, while the loads are in flight (rot: this wave's, formed
+  // at the start of the launch)
   float sn[P], cs[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     sn[j] = 0.f;
     cs[j] = 1.f;
-    if (pr[j].rotate) rope_sincos(p.seq.position, pr[j].pi, p.rotary_dim, p.log2_theta, sn[j], cs[j]);
+    if (rot) {
+      sn[j] = rot[j].x;
+      cs[j] = rot[j].y;
+    } else if (pr[j].rotate) {
+      rope_sincos(p.seq.position, pr[j].pi, p.rotary_dim, p.log2_theta, sn[j], cs[j]);
+    }
   }
   if constexpr (STACK) {
     // (the empty asm keeps the rotations here, ahead of the wait, instead of
@@ -2432,6 +2454,10 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   __shared__ float s_gate4[4];
   __shared__ int s_last;
   __shared__ unsigned long long s_epoch;
+  // a stack's per-layer pointers and shapes, and per shape the rotations of
+  // each wave's pairs in the workgroup's first projection task
+  __shared__ StackTables s_tab;
+  __shared__ float2 s_rot[kStackMaxDescs][W][P];
   using XS = StagedX<NIT>;
   static_assert(2 * XS::kSlots * sizeof(float4) <= sizeof(s_k0) && 2 * XS::kSlots * sizeof(float4) <= sizeof(s_q),
                 "staged x fits the first K buffers and the q staging");
@@ -2472,6 +2498,11 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   constexpr bool has_qkv = HAS_QKV;   // the projections run in this launch (t_qkv > 0)
 
   if (tid == 0) s_epoch = __hip_atomic_load(words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (STACK) {
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(&sp.tab);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(&s_tab);
+    for (int i = tid; i < (int)(sizeof(StackTables) / 4); i += kThreads) dst[i] = src[i];
+  }
   __syncthreads();
   const unsigned long long epoch = s_epoch;
   // the last task of the list advances the epoch for the next call
@@ -2484,15 +2515,15 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   auto layer_params = [&](int l) {
     FusedParams p = p0;
     if constexpr (STACK) {
-      const StackDesc &d = sp.desc[sp.desc_of[l]];
-      p.w_norm = sp.w_norm[l];
-      p.w_qkv = sp.w_qkv[l];
-      p.w_g = sp.w_g[l];
-      p.w_o = sp.w_o[l];
-      p.sinks = sp.sinks[l];
+      const StackDesc d = lds_uniform(s_tab.desc[__builtin_amdgcn_readfirstlane((int)s_tab.desc_of[l])]);
+      p.w_norm = lds_uniform(s_tab.w_norm[l]);
+      p.w_qkv = lds_uniform(s_tab.w_qkv[l]);
+      p.w_g = lds_uniform(s_tab.w_g[l]);
+      p.w_o = lds_uniform(s_tab.w_o[l]);
+      p.sinks = lds_uniform(s_tab.sinks[l]);
       p.seq = d.seq;
-      p.seq.k = sp.k[l];
-      p.seq.v = sp.v[l];
+      p.seq.k = lds_uniform(s_tab.k[l]);
+      p.seq.v = lds_uniform(s_tab.v[l]);
       p.chunk = d.chunk;
       p.nchunks = d.nchunks;
       p.t_attn = d.t_attn;
@@ -2508,9 +2539,29 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       pf_ready = true;
     }
   }
+  if constexpr (STACK) {
+    // the rotations of the workgroup's first projection task, per shape (the
+    // same in every layer of that shape), while the first weights stream in
+    if (b < p0.t_qkv) {
+      for (int d = 0; d < sp.num_descs; ++d) {
+        const StackDesc dd = lds_uniform(s_tab.desc[d]);
+        FusedParams pd = p0;
+        pd.rotary_dim = dd.rotary_dim;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const PairRows pr = task_pair<P>(pd, b, w, j);
+          float sn = 0.f, cs = 1.f;
+          if (pr.rotate) rope_sincos(dd.seq.position, pr.pi, dd.rotary_dim, dd.log2_theta, sn, cs);
+          if (lane == 0) s_rot[d][w][j] = make_float2(sn, cs);
+        }
+      }
+    }
+  }
 
   for (int l = 0; l < num_layers; ++l) {
     const FusedParams p = layer_params(l);
+    const float2 *rot_l = nullptr;   // this layer's shape's rotations (first projection task)
+    if constexpr (STACK) rot_l = &s_rot[__builtin_amdgcn_readfirstlane((int)s_tab.desc_of[l])][w][0];
     const unsigned long long fv = flag_value((epoch << 8) | (unsigned)l);
     // h as the previous layer of the stack leaves it
     auto wait_h = [&]() {
@@ -2546,9 +2597,10 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       if (gate_here) gate_w.issue(p, (t_a0 % Hk) * kGroup + w, lane);
       if (mgate_here) gate_w.issue(p, t_m0 >> 2, lane);
       if (PF && t == b && pf_ready)
-        fused_qkv_task<NIT, NORM, P, STACK, PF>(p, t, staged, s_x, s_ss, lane, w, wait_h, &s_w);
+        fused_qkv_task<NIT, NORM, P, STACK, PF>(p, t, staged, s_x, s_ss, lane, w, wait_h, &s_w, rot_l);
       else
-        fused_qkv_task<NIT, NORM, P, STACK>(p, t, staged, s_x, s_ss, lane, w, wait_h);
+        fused_qkv_task<NIT, NORM, P, STACK>(p, t, staged, s_x, s_ss, lane, w, wait_h, nullptr,
+                                            t == b ? rot_l : nullptr);
       staged = true;
       // the group's first task clears its counter (every attention task of
       // the group waits for this task's flag before it counts itself)
