@@ -1966,8 +1966,11 @@ hipError_t qkv_launch(const QkvParams &p, hipStream_t stream) {
 constexpr int kFlagStride = 16;   // 64-bit words per flag (128 bytes)
 // flags: projection tasks (at most 800), attention tasks (256 chunks x 8 KV
 // heads), merge tasks (32 query heads x 4), o_proj tasks (4096 rows / 16),
-// group flags and counters (8 KV heads each), after the epoch's line
-static_assert((1 + 800 + kFusedMaxChunks * 8 + 32 * 4 + kFusedMaxHidden / 16 + 2 * 8) * kFlagStride * 8 <= kSyncBytes,
+// group flags and counters (8 KV heads each), attention tasks' first tiles
+// issued (at most 256: only when they run beside the o_proj workgroups),
+// after the epoch's line
+static_assert((1 + 800 + kFusedMaxChunks * 8 + 32 * 4 + kFusedMaxHidden / 16 + 2 * 8 + 256) * kFlagStride * 8 <=
+                  kSyncBytes,
               "flag words fit their bytes");
 // A wait gives up after this many polls (about a second): reached only if
 // calls overlap on one workspace, or if other work holds CUs the launch
@@ -2495,6 +2498,7 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
   unsigned long long *const f_oproj = flag_at(f_merge, p0.t_merge);
   unsigned long long *const f_group = flag_at(f_oproj, p0.t_oproj);   // per KV head group: merged (no merge tasks)
   unsigned long long *const g_count = flag_at(f_group, 8);             // per KV head group: attention tasks done
+  unsigned long long *const f_tiles = flag_at(g_count, 8);             // per attention task: first tiles issued
   constexpr bool has_qkv = HAS_QKV;   // the projections run in this launch (t_qkv > 0)
 
   if (tid == 0) s_epoch = __hip_atomic_load(words, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2578,6 +2582,9 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
 
     // this workgroup's attention task (see below) and merge task, if any
     const int a_off = p.t_oproj + p.t_attn + t_merge <= G ? p.t_oproj : 0;
+    // in a stack, attention tasks beside the o_proj workgroups announce their
+    // first tiles (those workgroups' prefetch waits for them)
+    const bool pf_after_tiles = PF && a_off > 0 && p.t_attn <= 256;
     const int t_a0 = (b - a_off + G) % G;
     const int t_m0 = (b + t_merge) % G;
     // in a stack, a workgroup with a projection task and a merge task forms
@@ -2628,6 +2635,8 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
     for (int t = t_a0; t < p.t_attn; t += G) {
       const int c = t / Hk, g = t - c * Hk;
       auto wait_q = [&]() {
+        if (pf_after_tiles && tid == 0)
+          __hip_atomic_store(flag_at(f_tiles, t), fv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (has_qkv) await_flags(f_qkv, g * p.qkv_per_group, p.qkv_per_group, 1, fv);
       };
       float m_run, l_run;
@@ -2716,6 +2725,11 @@ __device__ __forceinline__ void fused_run(const FusedParams &p0, const SP &sp) {
       // next projection task loads its weights itself.
       const bool oproj_after_attn = b < p.t_oproj && t_a0 < p.t_attn;
       pf_ready = l + 1 < num_layers && b < p.t_qkv && !oproj_after_attn;
+      // an o_proj workgroup without an attention task holds its prefetch
+      // until every attention task has issued its first tiles: started at
+      // once, its loads slowed the issue of those tiles (the layer's
+      // critical path) several times over
+      if (pf_ready && pf_after_tiles && b < p.t_oproj) await_flags(f_tiles, 0, p.t_attn, 1, fv);
       if (pf_ready) fused_qkv_prefetch<NIT, P>(layer_params(l + 1), b, s_w, lane, w);
     }
 
