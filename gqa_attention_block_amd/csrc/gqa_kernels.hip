@@ -2215,8 +2215,7 @@ __device__ __forceinline__ void store_a(float *head, int d, float v) {
 // (cg, eq) sums elements 4 eq .. +3 of chunks cg, cg + 16, ..., and the 16
 // chunk groups are added in order.  The partials were written in this
 // launch: they are read coherently, and a is written so.  gl is the head's
-// gate logit.  SPLIT: a in the split form o_proj reads in the same launch
-// (store_a_split), else fp32.
+// gate logit.
 template <bool SPLIT>
 __device__ __forceinline__ void fused_merge_task(const FusedParams &p, int h, int qd, float gl, float2 *s_ml,
                                                  float4 *s_acc, int tid, int lane) {
